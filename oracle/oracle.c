@@ -1,0 +1,371 @@
+/*
+ * oracle.c - CPU oracle for the low-bit linear layer.
+ *
+ * TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the bench's CPU
+ * baseline are its only callers.  Plain scalar C, one loop per definition,
+ * OpenMP only across independent rows/domains.  Built with
+ * -O2 -ffp-contract=off and no fast-math, so every float operation below is a
+ * single IEEE-754 binary32 (or binary64 where stated) operation rounded to
+ * nearest-even, in the order written.
+ *
+ * Sources (cited by page title and section):
+ *  [NBT]  "M8.8 - Native Binary and Ternary Transformers"
+ *  [A1B]  Atomic-1Bit README ("Run language models using only addition and
+ *         subtraction")
+ *  [T4NT] "T4NT-0.5B" model card (Tanh 4-bit Neural Transformer)
+ *
+ * Readings taken where the pages leave a step open are marked READING.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int orc_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* ------------------------------------------------------------------ layout */
+
+/*
+ * Packed row sizes.
+ *  binary : [NBT] 0x06E binary pack reference - bit = (1 - s) / 2, packed
+ *           little-bit-first along K, ceil(K / 8) bytes per row.
+ *  ternary: READING - 2-bit two's-complement fields ([NBT] 0x01A: fixed-width
+ *           ternary takes two physical bits; [A1B]: four codes per byte),
+ *           grouped in 32-bit words of 16 codes, so rows are whole words.
+ *  int4   : READING - 4-bit two's-complement fields, 8 codes per 32-bit word.
+ */
+int64_t orc_row_bytes(int fmt, int64_t k) {
+    if (k < 1) return -1;
+    switch (fmt) {
+        case ORC_TERNARY: return 4 * ((k + 15) / 16);
+        case ORC_BINARY:  return (k + 7) / 8;
+        case ORC_INT4:    return 4 * ((k + 7) / 8);
+        default:          return -1;
+    }
+}
+
+int64_t orc_n_groups(int scale_mode, int64_t k, int64_t group) {
+    if (scale_mode != ORC_SCALE_GROUP) return 1;
+    if (group < 1) return -1;
+    return (k + group - 1) / group;
+}
+
+static int fmt_ok(int fmt) { return fmt == ORC_TERNARY || fmt == ORC_BINARY || fmt == ORC_INT4; }
+
+/*
+ * Where code k of a row lives.
+ *  ternary: word w = k / 16, j = k % 16; byte 4w + (j % 4); bits 2 (j / 4) .. +1.
+ *  int4   : word w = k / 8,  j = k % 8;  byte 4w + (j % 4); nibble j / 4 (0 = low).
+ *  binary : byte k / 8, bit k % 8.
+ */
+static void code_position(int fmt, int64_t k, int64_t* byte, int* shift) {
+    if (fmt == ORC_TERNARY) {
+        int64_t w = k / 16; int j = (int)(k % 16);
+        *byte = 4 * w + (j % 4); *shift = 2 * (j / 4);
+    } else if (fmt == ORC_INT4) {
+        int64_t w = k / 8; int j = (int)(k % 8);
+        *byte = 4 * w + (j % 4); *shift = 4 * (j / 4);
+    } else {
+        *byte = k / 8; *shift = (int)(k % 8);
+    }
+}
+
+static int field_bits(int fmt) { return fmt == ORC_TERNARY ? 2 : (fmt == ORC_INT4 ? 4 : 1); }
+
+/* code -> field value.  binary: bit = (1 - s) / 2 ([NBT] 0x06E).
+ * ternary/int4: the code's two's-complement low bits. */
+static int encode_field(int fmt, int code) {
+    if (fmt == ORC_BINARY) return (1 - code) / 2;
+    return code & ((1 << field_bits(fmt)) - 1);
+}
+
+/* field value -> code, or 99 for a reserved pattern (ternary 10, int4 1000) */
+static int decode_field(int fmt, int f) {
+    if (fmt == ORC_BINARY) return 1 - 2 * f;
+    if (fmt == ORC_TERNARY) {
+        if (f == 2) return 99;
+        return f == 3 ? -1 : f;
+    }
+    if (f == 8) return 99;
+    return f >= 8 ? f - 16 : f;
+}
+
+int orc_pack(int fmt, int64_t n, int64_t k, const int8_t* codes, uint8_t* packed) {
+    if (!fmt_ok(fmt) || n < 1 || k < 1 || !codes || !packed) return ORC_E_ARG;
+    const int64_t rb = orc_row_bytes(fmt, k);
+    const int lo = fmt == ORC_TERNARY ? -1 : (fmt == ORC_INT4 ? -7 : -1);
+    const int hi = fmt == ORC_TERNARY ? 1 : (fmt == ORC_INT4 ? 7 : 1);
+    for (int64_t i = 0; i < n * k; ++i) {
+        int c = codes[i];
+        if (c < lo || c > hi || (fmt == ORC_BINARY && c == 0)) return ORC_E_FORMAT;
+    }
+    memset(packed, 0, (size_t)(n * rb));   /* fields past k stay zero */
+    for (int64_t r = 0; r < n; ++r) {
+        for (int64_t c = 0; c < k; ++c) {
+            int64_t byte; int shift;
+            code_position(fmt, c, &byte, &shift);
+            packed[r * rb + byte] |= (uint8_t)(encode_field(fmt, codes[r * k + c]) << shift);
+        }
+    }
+    return 0;
+}
+
+/* [NBT] 0x06E binary unpack reference and 0x0BB "reserved patterns reject":
+ * checks the extent, rejects reserved fields and any nonzero field past k. */
+int orc_unpack(int fmt, int64_t n, int64_t k, const uint8_t* packed, int8_t* codes) {
+    if (!fmt_ok(fmt) || n < 1 || k < 1 || !codes || !packed) return ORC_E_ARG;
+    const int64_t rb = orc_row_bytes(fmt, k);
+    const int bits = field_bits(fmt);
+    const int64_t slots = rb * 8 / bits;    /* every field slot of a row */
+    for (int64_t r = 0; r < n; ++r) {
+        for (int64_t c = 0; c < slots; ++c) {
+            int64_t byte; int shift;
+            code_position(fmt, c, &byte, &shift);
+            int f = (packed[r * rb + byte] >> shift) & ((1 << bits) - 1);
+            if (c >= k) {
+                if (f != 0) return ORC_E_FORMAT;        /* noncanonical padding */
+                continue;
+            }
+            int v = decode_field(fmt, f);
+            if (v == 99) return ORC_E_FORMAT;           /* reserved pattern */
+            codes[r * k + c] = (int8_t)v;
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------- weight quantiser */
+
+static float clampf(float v, float lo, float hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+/*
+ * Latent weights -> codes and fp32 scales, one scale domain at a time
+ * (tensor: all of W; row: one row; group: `group` consecutive columns of one
+ * row, the last group possibly shorter).
+ *
+ * ternary: [NBT] 0x05A (b1.58 absmean): s = mean |W| over the domain,
+ *          code = RoundClip(W / s, -1, 1).  READING: no epsilon (the zero
+ *          domain is special-cased to s = 0, codes 0), the mean is a
+ *          sequential binary64 sum in ascending index order divided by the
+ *          count and rounded once to fp32, and W / s is an fp32 division
+ *          rounded half-to-even.  Exact ties |W / s| = 0.5 go to 0 ([NBT]
+ *          0x05B thresholds +-s/2, ties left to the rounding policy).
+ * binary : [NBT] 0x06E total sign rule, +1 if w >= 0 (either signed zero)
+ *          else -1; scale = mean |W| over the domain ([NBT] 0x02B).
+ * int4   : [T4NT] "What is T4NT?": symmetric levels -7..+7; READING: scale =
+ *          max |W| / 7 over the domain in fp32, code = clip(rint(W / s)).
+ * premap : [T4NT] tanh soft clipping w -> tanh(w / 3) * 3, evaluated in
+ *          binary64 and rounded once to fp32, before any of the above.
+ */
+int orc_weight_codes(int fmt, int scale_mode, int64_t group, int premap,
+                     int64_t n, int64_t k, const float* w, int8_t* codes, float* scales) {
+    if (!fmt_ok(fmt) || n < 1 || k < 1 || !w || !codes || !scales) return ORC_E_ARG;
+    if (scale_mode < ORC_SCALE_TENSOR || scale_mode > ORC_SCALE_GROUP) return ORC_E_ARG;
+    if (scale_mode == ORC_SCALE_GROUP && group < 1) return ORC_E_ARG;
+    for (int64_t i = 0; i < n * k; ++i)
+        if (!isfinite(w[i])) return ORC_E_NONFINITE;
+
+    float* wp = (float*)malloc((size_t)(n * k) * sizeof(float));
+    if (!wp) return ORC_E_ARG;
+    for (int64_t i = 0; i < n * k; ++i)
+        wp[i] = premap ? (float)(3.0 * tanh((double)w[i] / 3.0)) : w[i];
+
+    const int64_t G = orc_n_groups(scale_mode, k, group);
+    /* domain list: (row0, row1, col0, col1) */
+    int64_t n_dom = scale_mode == ORC_SCALE_TENSOR ? 1 : (scale_mode == ORC_SCALE_ROW ? n : n * G);
+
+    #pragma omp parallel for schedule(static)
+    for (int64_t d = 0; d < n_dom; ++d) {
+        int64_t r0, r1, c0, c1;
+        if (scale_mode == ORC_SCALE_TENSOR) { r0 = 0; r1 = n; c0 = 0; c1 = k; }
+        else if (scale_mode == ORC_SCALE_ROW) { r0 = d; r1 = d + 1; c0 = 0; c1 = k; }
+        else {
+            r0 = d / G; r1 = r0 + 1;
+            c0 = (d % G) * group; c1 = c0 + group < k ? c0 + group : k;
+        }
+        float s;
+        if (fmt == ORC_INT4) {
+            float m = 0.0f;
+            for (int64_t r = r0; r < r1; ++r)
+                for (int64_t c = c0; c < c1; ++c) {
+                    float a = fabsf(wp[r * k + c]);
+                    if (a > m) m = a;
+                }
+            s = m / 7.0f;
+        } else {
+            double sum = 0.0;
+            for (int64_t r = r0; r < r1; ++r)
+                for (int64_t c = c0; c < c1; ++c)
+                    sum += fabs((double)wp[r * k + c]);
+            s = (float)(sum / (double)((r1 - r0) * (c1 - c0)));
+        }
+        scales[d] = s;
+        for (int64_t r = r0; r < r1; ++r)
+            for (int64_t c = c0; c < c1; ++c) {
+                float v = wp[r * k + c];
+                int8_t code;
+                if (fmt == ORC_BINARY) {
+                    code = v >= 0.0f ? 1 : -1;
+                } else if (s == 0.0f) {
+                    code = 0;
+                } else {
+                    float lim = fmt == ORC_INT4 ? 7.0f : 1.0f;
+                    float qv = v / s;
+                    code = (int8_t)clampf(rintf(qv), -lim, lim);
+                }
+                codes[r * k + c] = code;
+            }
+    }
+    free(wp);
+    return 0;
+}
+
+/* --------------------------------------------------- activation quantiser */
+
+/*
+ * Per-token absmax int8 quantisation, [NBT] 0x02C and 0x05C (the 127-based
+ * per-token realisation):  m = max_k |x|;  q = clip(rint(x * 127 / m));
+ * s_x = m / 127;  an all-zero row gives zero codes and s_x = 0.
+ * READING: no epsilon; r = 127 / m is one fp32 division, q = rint(x * r) one
+ * fp32 multiply rounded half-to-even, clip to [-127, 127]; s_x = m / 127 in
+ * fp32.  A row with a non-finite entry, or whose 127 / m overflows, is
+ * rejected ([NBT] 0x05C: the reference rejects non-finite rows and
+ * unrepresentable scales).
+ */
+int64_t orc_act_quant(int64_t t, int64_t k, const float* x, int8_t* q, float* sx,
+                      int32_t* row_status) {
+    if (t < 1 || k < 1 || !x || !q || !sx || !row_status) return ORC_E_ARG;
+    int64_t rejected = 0;
+    #pragma omp parallel for schedule(static) reduction(+ : rejected)
+    for (int64_t i = 0; i < t; ++i) {
+        const float* xr = x + i * k;
+        int8_t* qr = q + i * k;
+        int finite = 1;
+        float m = 0.0f;
+        for (int64_t c = 0; c < k; ++c) {
+            if (!isfinite(xr[c])) { finite = 0; break; }
+            float a = fabsf(xr[c]);
+            if (a > m) m = a;
+        }
+        if (!finite) {
+            memset(qr, 0, (size_t)k); sx[i] = NAN; row_status[i] = ORC_ROW_NONFINITE; ++rejected;
+            continue;
+        }
+        if (m == 0.0f) {
+            memset(qr, 0, (size_t)k); sx[i] = 0.0f; row_status[i] = ORC_ROW_OK;
+            continue;
+        }
+        float r = 127.0f / m;
+        if (!isfinite(r)) {
+            memset(qr, 0, (size_t)k); sx[i] = NAN; row_status[i] = ORC_ROW_OVERFLOW; ++rejected;
+            continue;
+        }
+        for (int64_t c = 0; c < k; ++c) {
+            float v = xr[c] * r;
+            qr[c] = (int8_t)clampf(rintf(v), -127.0f, 127.0f);
+        }
+        sx[i] = m / 127.0f;
+        row_status[i] = ORC_ROW_OK;
+    }
+    return rejected;
+}
+
+/* ------------------------------------------------------- integer product */
+
+/*
+ * acc = Q8(x) . Q(W)^T in 64-bit integers, the plain definition of
+ * [NBT] 0x02D and 0x09C (the reference decoder's int64 matmul), kept per
+ * scale group: acc[t, n, g] sums columns [g * group_cols, (g+1) * group_cols).
+ * group_cols <= 0 means one group spanning all of k.
+ */
+int orc_int_matmul(int64_t t, int64_t n, int64_t k, int64_t group_cols,
+                   const int8_t* q, const int8_t* codes, int64_t* acc) {
+    if (t < 1 || n < 1 || k < 1 || !q || !codes || !acc) return ORC_E_ARG;
+    const int64_t gc = group_cols > 0 ? group_cols : k;
+    const int64_t G = (k + gc - 1) / gc;
+    #pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t i = 0; i < t; ++i)
+        for (int64_t r = 0; r < n; ++r) {
+            const int8_t* qi = q + i * k;
+            const int8_t* cr = codes + r * k;
+            for (int64_t g = 0; g < G; ++g) {
+                int64_t c0 = g * gc, c1 = c0 + gc < k ? c0 + gc : k;
+                int64_t s = 0;
+                for (int64_t c = c0; c < c1; ++c) s += (int64_t)qi[c] * (int64_t)cr[c];
+                acc[(i * n + r) * G + g] = s;
+            }
+        }
+    return 0;
+}
+
+/*
+ * Rescale, [NBT] 0x02D / 0x09C: y = acc * s_x * s_w.
+ * READING (fp32, left to right, no fused multiply-add):
+ *   tensor / row scales: y = (float)acc * (s_x[t] * s_w[n])
+ *   group scales       : y = s_x[t] * sum_{g ascending} (s_w[n, g] * (float)acc[t, n, g])
+ * y64 is the same expression evaluated in binary64 from the same inputs.
+ */
+int orc_epilogue(int scale_mode, int64_t t, int64_t n, int64_t n_groups,
+                 const int64_t* acc, const float* sx, const float* scales,
+                 float* y32, double* y64) {
+    if (t < 1 || n < 1 || n_groups < 1 || !acc || !sx || !scales || !y32 || !y64) return ORC_E_ARG;
+    #pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t i = 0; i < t; ++i)
+        for (int64_t r = 0; r < n; ++r) {
+            const int64_t* a = acc + (i * n + r) * n_groups;
+            if (scale_mode == ORC_SCALE_GROUP) {
+                float s32 = 0.0f;
+                double s64 = 0.0;
+                for (int64_t g = 0; g < n_groups; ++g) {
+                    float term = scales[r * n_groups + g] * (float)a[g];
+                    s32 = s32 + term;
+                    s64 = s64 + (double)scales[r * n_groups + g] * (double)a[g];
+                }
+                y32[i * n + r] = sx[i] * s32;
+                y64[i * n + r] = (double)sx[i] * s64;
+            } else {
+                float sw = scale_mode == ORC_SCALE_TENSOR ? scales[0] : scales[r];
+                float prod = sx[i] * sw;
+                y32[i * n + r] = (float)a[0] * prod;
+                y64[i * n + r] = (double)a[0] * (double)sx[i] * (double)sw;
+            }
+        }
+    return 0;
+}
+
+/* worst case of [NBT] 0x09C: |acc| <= k * 127 * qmax must fit a signed 32-bit
+ * accumulator (127 is the largest activation code this quantiser emits). */
+int orc_acc_bound_ok(int fmt, int64_t k) {
+    int64_t qmax = fmt == ORC_INT4 ? 7 : 1;
+    if (k < 1) return 0;
+    return k <= (int64_t)2147483647 / (127 * qmax);
+}
+
+int orc_linear(int fmt, int scale_mode, int64_t group, int64_t n, int64_t k,
+               const uint8_t* packed, const float* scales,
+               int64_t t, const int8_t* q, const float* sx,
+               float* y32, double* y64, int64_t* acc) {
+    if (!fmt_ok(fmt) || n < 1 || k < 1 || t < 1) return ORC_E_ARG;
+    if (!orc_acc_bound_ok(fmt, k)) return ORC_E_RANGE;
+    const int64_t G = orc_n_groups(scale_mode, k, group);
+    if (G < 1) return ORC_E_ARG;
+    int8_t* codes = (int8_t*)malloc((size_t)(n * k));
+    if (!codes) return ORC_E_ARG;
+    int rc = orc_unpack(fmt, n, k, packed, codes);
+    if (rc == 0)
+        rc = orc_int_matmul(t, n, k, scale_mode == ORC_SCALE_GROUP ? group : 0, q, codes, acc);
+    if (rc == 0)
+        rc = orc_epilogue(scale_mode, t, n, G, acc, sx, scales, y32, y64);
+    free(codes);
+    return rc;
+}
