@@ -1,0 +1,344 @@
+#!/usr/bin/env python3
+"""Throughput of the low-bit linear layer on one MI355X.
+
+Metric: ternary GEMV HBM GB/s (% of peak) at batch 1, and batched GEMM int8
+TOPS (% of MFMA peak).
+
+One step = one pass of the hot path over one batch of seeded synthetic input:
+per-token int8 activation quantisation of every matrix's input, then the
+low-bit product of every weight matrix of the workload, with packed weights,
+scales and inputs already resident in HBM.  Packing (the offline export step)
+is done before timing.  The step is captured once in a HIP graph and replayed.
+
+Default workload (the GEMV line, `value`): the 4B-class ternary decode pass -
+36 layer-equivalents x {4 x [2560, 2560], 2 x [9728, 2560], 1 x [2560, 9728]},
+group-128 scales, 1 token per call (1.03 GB of packed codes + scales).
+The batched-GEMM figure is measured in the same run on the int4 prefill pass
+(20 layers x {[3840,1280], [1280,1280], 2 x [3584,1280], [1280,3584]},
+4096 tokens) and reported under "gemm".
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--tokens 1]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+I8_PEAK_TOPS = 5000.0          # MI355X dense int8 MFMA, TOPS
+METRIC = "ternary GEMV HBM GB/s (% peak) at batch 1; batched GEMM int8 TOPS (% MFMA peak)"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ set-up
+
+class Pass:
+    """Every matrix of one workload pass, packed and resident on the GPU, with
+    per-call activations stacked by k so one act-quant launch serves all
+    inputs of equal width."""
+
+    def __init__(self, wl, tokens, entry, layers=None, threads=16):
+        import torch
+        import bit_weight_linear_bitlinear_amd as lb
+        import workloads
+
+        self.wl, self.t, self.entry = wl, tokens, entry
+        self.lb = lb
+        n_layers = wl.layers if layers is None else layers
+        self.mats = [(layer, mi, m) for layer in range(n_layers) for mi, m in enumerate(wl.matrices)
+                     if layer < m.count]
+        fmt, scale = lb.FORMATS[wl.fmt], lb.SCALES[wl.scale]
+        flags = lb.FLAG_TANH3 if wl.tanh_premap else 0
+
+        def prep(item):
+            layer, mi, m = item
+            d = lb.lowbit_describe(fmt, scale, m.n, m.k, wl.group, flags)
+            w = workloads.latent_weights(wl.index, layer, mi, m.n, m.k)
+            packed = np.empty(d.packed_bytes, np.uint8)
+            scales = np.empty(d.n_scales, np.float32)
+            lb.lowbit_pack(d, w, packed, scales)
+            x = workloads.workload_activations(wl, layer, mi, tokens, m.k)
+            return d, packed, scales, x
+
+        t0 = time.time()
+        self.desc, self.packed, self.scales = [], [], []
+        xs = []
+        with ThreadPoolExecutor(threads) as ex:
+            for d, packed, scales, x in ex.map(prep, self.mats):
+                self.desc.append(d)
+                self.packed.append(torch.from_numpy(packed).cuda())
+                self.scales.append(torch.from_numpy(scales).cuda())
+                xs.append(x)
+        log(f"[bench] {wl.name}: {len(self.mats)} matrices generated and packed in {time.time() - t0:.1f}s")
+
+        # activations stacked per k; q / sx / y views per matrix
+        self.kgroups = {}
+        for i, (_, _, m) in enumerate(self.mats):
+            self.kgroups.setdefault(m.k, []).append(i)
+        self.x, self.q, self.sx = {}, {}, {}
+        self.views = [None] * len(self.mats)
+        for k, idx in self.kgroups.items():
+            rows = len(idx) * tokens
+            self.x[k] = torch.from_numpy(np.concatenate([xs[i] for i in idx], axis=0)).cuda()
+            self.q[k] = torch.empty((rows, k), dtype=torch.int8, device="cuda")
+            self.sx[k] = torch.empty((rows,), dtype=torch.float32, device="cuda")
+            for j, i in enumerate(idx):
+                self.views[i] = (self.q[k][j * tokens:(j + 1) * tokens], self.sx[k][j * tokens:(j + 1) * tokens])
+        self.y = [torch.empty((tokens, m.n), dtype=torch.float32, device="cuda") for _, _, m in self.mats]
+        self.xs = xs
+        self.fn = lb.lowbit_linear if entry == "gemv" else lb.lowbit_linear_batched
+
+        # algorithmic accounting
+        self.linear_bytes = [d.packed_bytes + 4 * d.n_scales + tokens * d.k + 4 * tokens + 4 * tokens * d.n
+                             for d in self.desc]
+        self.linear_ops = [2 * tokens * d.n * d.k for d in self.desc]
+        self.aq_bytes = sum(len(idx) * tokens * (5 * k + 4) for k, idx in self.kgroups.items())
+
+    def act_quant(self):
+        for k in self.kgroups:
+            self.lb.lowbit_act_quant(self.x[k], self.q[k], self.sx[k])
+
+    def linears(self):
+        for i, d in enumerate(self.desc):
+            q, sx = self.views[i]
+            self.fn(d, self.packed[i], self.scales[i], q, sx, self.y[i])
+
+    def step(self):
+        self.act_quant()
+        self.linears()
+
+    @property
+    def step_bytes(self):
+        return sum(self.linear_bytes) + self.aq_bytes
+
+
+def capture(fn):
+    """Capture fn's launches into a HIP graph; returns a replay callable or None."""
+    import torch
+    try:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        torch.cuda.synchronize()
+        return g.replay
+    except Exception as e:   # eager launches are still correct, just slower
+        log(f"[bench] graph capture unavailable ({e}); timing eager launches")
+        return None
+
+
+def time_steps(run, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    return e0.elapsed_time(e1) / 1e3, wall
+
+
+def per_launch(p: Pass, reps: int):
+    """Average duration of the product kernel, from HIP events recorded on the
+    launching stream around every launch (act-quant excluded)."""
+    import torch
+    p.act_quant()
+    torch.cuda.synchronize()
+    n = len(p.desc)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n * reps)]
+    for r in range(reps):
+        for i, d in enumerate(p.desc):
+            q, sx = p.views[i]
+            a, b = evs[r * n + i]
+            a.record()
+            p.fn(d, p.packed[i], p.scales[i], q, sx, p.y[i])
+            b.record()
+    torch.cuda.synchronize()
+    total = sum(a.elapsed_time(b) for a, b in evs) / 1e3
+    return total / (n * reps), sum(p.linear_bytes) / n, sum(p.linear_ops) / n
+
+
+# ------------------------------------------------------------- correctness
+
+def sampled_check(p: Pass, picks, rows_per=48, seed=0):
+    """Full-size parity on sampled outputs: the oracle recomputes sampled weight
+    rows (group/row scales are row-local) for every token of picked matrices."""
+    import torch
+    import oracle
+    import workloads
+    wl = p.wl
+    rng = np.random.default_rng(seed)
+    worst = 0.0
+    for i in picks:
+        layer, mi, m = p.mats[i]
+        d = p.desc[i]
+        q, sx = p.views[i]
+        y = torch.empty((p.t, m.n), dtype=torch.float32, device="cuda")
+        acc = torch.empty((p.t, m.n, d.n_groups), dtype=torch.int32, device="cuda")
+        p.fn(d, p.packed[i], p.scales[i], q, sx, y, acc)
+        torch.cuda.synchronize()
+        rows = np.sort(rng.choice(m.n, size=min(rows_per, m.n), replace=False))
+        w = workloads.latent_weights(wl.index, layer, mi, m.n, m.k)[rows]
+        if wl.scale == "tensor":
+            raise RuntimeError("sampled rows need row-local scales")
+        pk, sc, _ = oracle.quantize_and_pack(w, wl.fmt, wl.scale, wl.group, wl.tanh_premap)
+        q_ref, sx_ref, _ = oracle.act_quant(p.xs[i])
+        assert (q.cpu().numpy() == q_ref).all(), "activation codes differ"
+        y32, y64, acc_ref = oracle.linear(pk, sc, wl.fmt, wl.scale, wl.group, m.k, q_ref, sx_ref)
+        a = acc.cpu().numpy()[:, rows]
+        assert (a == acc_ref).all(), f"matrix {i}: accumulators differ"
+        yy = y.cpu().numpy()[:, rows].astype(np.float64)
+        err = np.abs(yy - y32)
+        assert (err <= 1e-6 + 1e-5 * np.abs(y32)).all(), f"matrix {i}: y out of tolerance"
+        worst = max(worst, float((err / (1e-6 + 1e-5 * np.abs(y32))).max()))
+    return {"matrices": len(picks), "rows_each": rows_per, "acc_bit_exact": True,
+            "y_worst_frac_of_tol": round(worst, 4)}
+
+
+# --------------------------------------------------------------- CPU oracle
+
+def cpu_baseline(wl, tokens, budget_s=12.0, sample_layers=4):
+    """The oracle as it stands, on the host's cores: act-quant + unpack +
+    integer product + epilogue over the first `sample_layers` layer-equivalents
+    of the same workload, repeated until ~budget_s of timed CPU work (weights
+    are packed by the oracle beforehand, untimed)."""
+    import oracle
+    import workloads
+    items = [(layer, mi, m) for layer in range(min(sample_layers, wl.layers))
+             for mi, m in enumerate(wl.matrices) if layer < m.count]
+
+    def prep(item):
+        layer, mi, m = item
+        w = workloads.latent_weights(wl.index, layer, mi, m.n, m.k)
+        pk, sc, _ = oracle.quantize_and_pack(w, wl.fmt, wl.scale, wl.group, wl.tanh_premap)
+        x = workloads.workload_activations(wl, layer, mi, tokens, m.k)
+        return m, pk, sc, x
+
+    with ThreadPoolExecutor(8) as ex:
+        prepped = list(ex.map(prep, items))
+    spent, nbytes, nops, passes = 0.0, 0, 0, 0
+    while spent < budget_s:
+        for m, pk, sc, x in prepped:
+            t0 = time.perf_counter()
+            q, sx, _ = oracle.act_quant(x)
+            oracle.linear(pk, sc, wl.fmt, wl.scale, wl.group, m.k, q, sx)
+            spent += time.perf_counter() - t0
+            nbytes += (pk.size + 4 * sc.size + tokens * m.k + 4 * tokens + 4 * tokens * m.n
+                       + tokens * (5 * m.k + 4))
+            nops += 2 * tokens * m.n * m.k
+        passes += 1
+    return {"value": round(nbytes / spent / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{len(items)} matrices ({min(sample_layers, wl.layers)} of {wl.layers} layer-equivalents) "
+                      f"x {passes} passes, T={tokens}: act-quant + unpack + int64 product + fp32 epilogue, "
+                      f"{spent:.1f}s timed",
+            "gops": round(nops / spent / 1e9, 3)}
+
+
+# ------------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--tokens", type=int, default=1)
+    ap.add_argument("--layers", type=int, default=None, help="fewer layer-equivalents (debug only)")
+    ap.add_argument("--skip-gemm", action="store_true")
+    ap.add_argument("--skip-cpu", action="store_true")
+    ap.add_argument("--skip-check", action="store_true")
+    ap.add_argument("--no-graph", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import torch
+    import workloads
+    torch.cuda.set_device(0)
+    out = {"metric": METRIC}
+
+    # ---- GEMV line: ternary_4b decode pass
+    wl = workloads.BY_NAME["ternary_4b"]
+    p = Pass(wl, args.tokens, "gemv", layers=args.layers)
+    run = None if args.no_graph else capture(p.step)
+    run = run or p.step
+    elapsed, wall = time_steps(run, args.steps, args.warmup)
+    step_s = elapsed / args.steps
+    value = p.step_bytes / step_s / 1e9
+    dur, bytes_per_launch, _ = per_launch(p, reps=3)
+    achieved = bytes_per_launch / dur / 1e9
+    check = None if args.skip_check else sampled_check(p, [0, 4, 6, len(p.mats) - 1])
+
+    out.update({
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+        "config": {"workload": f"ternary_4b decode pass: {len(p.mats)} ternary group-128 GEMVs "
+                               f"(K=2560/9728, N=2560/9728), T={args.tokens}, act-quant included",
+                   "tokens": args.tokens, "matrices": len(p.mats),
+                   "bytes_per_step": p.step_bytes, "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+                   "graph": run is not p.step, "wall_s": round(wall, 3)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "gemv_kernel", "avg_launch_us": round(dur * 1e6, 3),
+                     "bytes_per_launch": round(bytes_per_launch)},
+    })
+    if check:
+        out["check"] = check
+    log(f"[bench] gemv pass: {value:.1f} GB/s, {step_s * 1e3:.3f} ms/step; per launch {dur * 1e6:.2f} us "
+        f"-> {achieved:.1f} GB/s")
+
+    # ---- batched GEMM figure: int4_t4nt prefill pass
+    if not args.skip_gemm:
+        wl4 = workloads.BY_NAME["int4_t4nt"]
+        p4 = Pass(wl4, wl4.tokens[0], "gemm")
+        r4 = (None if args.no_graph else capture(p4.step)) or p4.step
+        el4, _ = time_steps(r4, max(3, args.steps // 4), 1)
+        st4 = el4 / max(3, args.steps // 4)
+        ops4 = sum(p4.linear_ops)
+        d4, _, ops_per_launch = per_launch(p4, reps=1)
+        tops_launch = ops_per_launch / d4 / 1e12
+        chk4 = None if args.skip_check else sampled_check(p4, [0, 1, 4], rows_per=32)
+        out["gemm"] = {"workload": "int4_t4nt prefill pass: 100 int4 row-scale GEMMs, T=4096, act-quant included",
+                       "tops_step": round(ops4 / st4 / 1e12, 2), "ms_per_step": round(st4 * 1e3, 4),
+                       "tops_per_launch": round(tops_launch, 2),
+                       "pct_mfma_peak": round(100 * tops_launch / I8_PEAK_TOPS, 2),
+                       "avg_launch_us": round(d4 * 1e6, 2), "kernel": "gemm_kernel", "check": chk4}
+        log(f"[bench] gemm pass: {ops4 / st4 / 1e12:.1f} TOPS/step; per launch {tops_launch:.1f} TOPS")
+        del p4
+
+    if not args.skip_cpu:
+        out["cpu_baseline"] = cpu_baseline(wl, args.tokens)
+        log(f"[bench] cpu oracle: {out['cpu_baseline']}")
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

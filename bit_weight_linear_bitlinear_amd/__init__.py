@@ -1,0 +1,160 @@
+"""Python binding of liblowbit.so, the MI355X low-bit linear layer.
+
+Argument marshalling only: every step (packing, activation quantisation, the
+integer products and their epilogues) runs in the native library.  The
+functions keep the C names of include/lowbit.h.  Device buffers are torch
+tensors on the GPU (the library reads their data pointers and launches on
+torch's current stream); host buffers are NumPy arrays.  The library
+allocates nothing, so callers pass every output buffer.
+
+If the shared library has not been built this module raises ImportError: there
+is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblowbit.so")
+
+TERNARY2, BINARY1, INT4 = 0, 1, 2
+SCALE_TENSOR, SCALE_ROW, SCALE_GROUP = 0, 1, 2
+FLAG_TANH3 = 1
+ACT_NONFINITE, ACT_OVERFLOW = 1, 2
+FORMATS = {"ternary": TERNARY2, "binary": BINARY1, "int4": INT4}
+SCALES = {"tensor": SCALE_TENSOR, "row": SCALE_ROW, "group": SCALE_GROUP}
+STATUS = {0: "LOWBIT_OK", 1: "LOWBIT_E_ARG", 2: "LOWBIT_E_RANGE", 3: "LOWBIT_E_NONFINITE",
+          4: "LOWBIT_E_FORMAT", 5: "LOWBIT_E_HIP"}
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -m bit_weight_linear_bitlinear_amd.build` "
+                      "(or __graft_entry__.build()) first")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+
+class lowbit_desc(ctypes.Structure):
+    _fields_ = [("format", ctypes.c_int32), ("scale", ctypes.c_int32), ("n", ctypes.c_int32),
+                ("k", ctypes.c_int32), ("group", ctypes.c_int32), ("flags", ctypes.c_int32),
+                ("row_bytes", ctypes.c_int64), ("packed_bytes", ctypes.c_int64),
+                ("n_groups", ctypes.c_int64), ("n_scales", ctypes.c_int64)]
+
+    def __repr__(self):
+        return (f"lowbit_desc(format={self.format}, scale={self.scale}, n={self.n}, k={self.k}, "
+                f"group={self.group}, flags={self.flags}, row_bytes={self.row_bytes}, "
+                f"packed_bytes={self.packed_bytes}, n_groups={self.n_groups}, n_scales={self.n_scales})")
+
+
+_P = ctypes.c_void_p
+_D = ctypes.POINTER(lowbit_desc)
+_i32 = ctypes.c_int32
+_lib.lowbit_describe.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _D]
+_lib.lowbit_pack.argtypes = [_D, _P, _P, _P]
+_lib.lowbit_act_quant.argtypes = [_P, _i32, _i32, _P, _P, _P, _P]
+_lib.lowbit_linear.argtypes = [_D, _P, _P, _P, _P, _i32, _P, _P, _P]
+_lib.lowbit_linear_batched.argtypes = [_D, _P, _P, _P, _P, _i32, _P, _P, _P]
+_lib.lowbit_max_k.argtypes = [_i32]
+_lib.lowbit_max_k.restype = _i32
+_lib.lowbit_status_string.argtypes = [_i32]
+_lib.lowbit_status_string.restype = ctypes.c_char_p
+_lib.lowbit_abi_version.restype = _i32
+for _f in ("lowbit_describe", "lowbit_pack", "lowbit_act_quant", "lowbit_linear", "lowbit_linear_batched"):
+    getattr(_lib, _f).restype = _i32
+
+EXPORTS = ("lowbit_describe", "lowbit_pack", "lowbit_act_quant", "lowbit_linear", "lowbit_linear_batched",
+           "lowbit_max_k", "lowbit_status_string", "lowbit_abi_version")
+
+
+class LowbitError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        msg = _lib.lowbit_status_string(status).decode()
+        super().__init__(f"{call}: {STATUS.get(status, status)} ({msg})")
+        self.status = status
+
+
+def _check(status: int, call: str) -> None:
+    if status != 0:
+        raise LowbitError(status, call)
+
+
+def _dev(t, name, nbytes=None):
+    """Data pointer of a contiguous device tensor holding >= nbytes (None -> NULL)."""
+    if t is None:
+        return None
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous GPU tensor")
+    if nbytes is not None and t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{name}: buffer holds {t.numel() * t.element_size()} bytes, needs {nbytes}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _host(a: np.ndarray, name, dtype, count=None):
+    if not isinstance(a, np.ndarray) or a.dtype != dtype or not a.flags.c_contiguous:
+        raise ValueError(f"{name}: expected a C-contiguous numpy {np.dtype(dtype).name} array")
+    if count is not None and a.size < count:
+        raise ValueError(f"{name}: array holds {a.size} elements, needs {count}")
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def lowbit_describe(format: int, scale: int, n: int, k: int, group: int = 0, flags: int = 0) -> lowbit_desc:
+    d = lowbit_desc()
+    _check(_lib.lowbit_describe(format, scale, n, k, group, flags, ctypes.byref(d)), "lowbit_describe")
+    return d
+
+
+def lowbit_pack(d: lowbit_desc, w: np.ndarray, packed: np.ndarray, scales: np.ndarray) -> None:
+    """Host: latent fp32 w[n, k] -> packed uint8[packed_bytes], scales fp32[n_scales]."""
+    _check(_lib.lowbit_pack(ctypes.byref(d), _host(w, "w", np.float32, d.n * d.k),
+                            _host(packed, "packed", np.uint8, d.packed_bytes),
+                            _host(scales, "scales", np.float32, d.n_scales)), "lowbit_pack")
+
+
+def lowbit_act_quant(x, q, sx, status=None, stream=None) -> None:
+    """Device: x fp32[t, k] -> q int8[t, k], sx fp32[t]; status int32[1] or None."""
+    t, k = x.shape
+    _check(_lib.lowbit_act_quant(_dev(x, "x", 4 * t * k), t, k, _dev(q, "q", t * k), _dev(sx, "sx", 4 * t),
+                                 _dev(status, "status", 4), _stream(stream)), "lowbit_act_quant")
+
+
+def _linear_ptrs(d, packed, scales, q, sx, y, acc):
+    t = q.shape[0]
+    if q.dim() != 2 or q.shape[1] != d.k:
+        raise ValueError(f"q: expected [t, {d.k}], got {tuple(q.shape)}")
+    return (_dev(packed, "packed", d.packed_bytes), _dev(scales, "scales", 4 * d.n_scales),
+            _dev(q, "q", t * d.k), _dev(sx, "sx", 4 * t), t, _dev(y, "y", 4 * t * d.n),
+            _dev(acc, "acc", 4 * t * d.n * d.n_groups))
+
+
+def lowbit_linear(d: lowbit_desc, packed, scales, q, sx, y, acc=None, stream=None) -> None:
+    """Device GEMV: y fp32[t, n] (and acc int32[t, n, n_groups] if given)."""
+    _check(_lib.lowbit_linear(ctypes.byref(d), *_linear_ptrs(d, packed, scales, q, sx, y, acc), _stream(stream)),
+           "lowbit_linear")
+
+
+def lowbit_linear_batched(d: lowbit_desc, packed, scales, q, sx, y, acc=None, stream=None) -> None:
+    """Device GEMM on the matrix cores: same contract as lowbit_linear."""
+    _check(_lib.lowbit_linear_batched(ctypes.byref(d), *_linear_ptrs(d, packed, scales, q, sx, y, acc),
+                                      _stream(stream)), "lowbit_linear_batched")
+
+
+def lowbit_max_k(format: int) -> int:
+    return int(_lib.lowbit_max_k(format))
+
+
+def lowbit_abi_version() -> int:
+    return int(_lib.lowbit_abi_version())
+
+
+def raw_library() -> ctypes.CDLL:
+    """The loaded ctypes handle (for callers that marshal arguments themselves)."""
+    return _lib

@@ -1,0 +1,32 @@
+// kernels.hpp - internal launcher interface between the C ABI layer and the
+// HIP kernels.  Arguments have been validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lowbit.h"
+
+namespace lowbit {
+
+struct LinearArgs {
+    int fmt;             // FMT_*
+    int scale;           // 0 tensor, 1 row, 2 group
+    int group;           // group mode: columns per group
+    int n_groups;        // group mode: ceil(k / group), else 1
+    int n, k, t;
+    int64_t row_bytes;
+    const uint8_t* packed;
+    const float* scales;
+    const int8_t* q;
+    const float* sx;
+    float* y;
+    int32_t* acc;        // nullable
+};
+
+hipError_t launch_act_quant(const float* x, int t, int k, int8_t* q, float* sx, int32_t* status,
+                            hipStream_t stream);
+hipError_t launch_gemv(const LinearArgs& a, hipStream_t stream);
+hipError_t launch_gemm(const LinearArgs& a, hipStream_t stream);
+
+}  // namespace lowbit

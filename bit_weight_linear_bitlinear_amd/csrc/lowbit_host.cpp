@@ -1,0 +1,264 @@
+// lowbit_host.cpp - the C ABI of include/lowbit.h: argument checks, the host
+// weight quantiser/packer, and dispatch to the HIP kernels.
+//
+// The packer is the export step of M8.8 "Native Binary and Ternary
+// Transformers" (0x04D: export freezes the final code/scale contract): it
+// runs once per weight matrix, offline, on host threads, and writes the packed
+// layout the kernels stream.
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstring>
+#include <thread>
+#include <vector>
+
+#include "kernels.hpp"
+#include "lowbit.h"
+
+namespace {
+
+constexpr int32_t kAbiVersion = 1;
+
+int64_t packed_row_bytes(int32_t fmt, int64_t k) {
+    switch (fmt) {
+        case LOWBIT_TERNARY2: return ((k + 15) / 16) * 4;   // whole 16-code words
+        case LOWBIT_INT4:     return ((k + 7) / 8) * 4;     // whole 8-code words
+        case LOWBIT_BINARY1:  return (k + 7) / 8;           // packbits rows
+        default:              return -1;
+    }
+}
+
+int32_t max_k_of(int32_t fmt) {
+    // int32 sums of (scaled code) x (activation code): |sum| <= k * 127 * qmax * scale
+    switch (fmt) {
+        case LOWBIT_TERNARY2:
+        case LOWBIT_BINARY1: return (int32_t)(2147483647LL / (127LL * 1 * 64));
+        case LOWBIT_INT4:    return (int32_t)(2147483647LL / (127LL * 7 * 16));
+        default:             return 0;
+    }
+}
+
+lowbit_status fill_desc(int32_t format, int32_t scale, int32_t n, int32_t k, int32_t group, int32_t flags,
+                        lowbit_desc* out) {
+    if (!out) return LOWBIT_E_ARG;
+    if (format < LOWBIT_TERNARY2 || format > LOWBIT_INT4) return LOWBIT_E_ARG;
+    if (scale < LOWBIT_SCALE_TENSOR || scale > LOWBIT_SCALE_GROUP) return LOWBIT_E_ARG;
+    if (n < 1 || k < 1) return LOWBIT_E_ARG;
+    if ((flags & ~LOWBIT_FLAG_TANH3) != 0) return LOWBIT_E_ARG;
+    if (scale == LOWBIT_SCALE_GROUP) {
+        const int32_t step = format == LOWBIT_BINARY1 ? 128 : 64;
+        if (group < step || group % step != 0) return LOWBIT_E_ARG;
+    } else if (group != 0) {
+        return LOWBIT_E_ARG;
+    }
+    if (k > max_k_of(format)) return LOWBIT_E_RANGE;
+    lowbit_desc d;
+    d.format = format; d.scale = scale; d.n = n; d.k = k; d.group = group; d.flags = flags;
+    d.row_bytes = packed_row_bytes(format, k);
+    d.packed_bytes = d.row_bytes * (int64_t)n;
+    d.n_groups = scale == LOWBIT_SCALE_GROUP ? ((int64_t)k + group - 1) / group : 1;
+    d.n_scales = scale == LOWBIT_SCALE_TENSOR ? 1 : (scale == LOWBIT_SCALE_ROW ? n : (int64_t)n * d.n_groups);
+    *out = d;
+    return LOWBIT_OK;
+}
+
+// A descriptor is accepted only if it is exactly what lowbit_describe returns.
+lowbit_status check_desc(const lowbit_desc* d) {
+    if (!d) return LOWBIT_E_ARG;
+    lowbit_desc ref;
+    lowbit_status st = fill_desc(d->format, d->scale, d->n, d->k, d->group, d->flags, &ref);
+    if (st != LOWBIT_OK) return st;
+    if (ref.row_bytes != d->row_bytes || ref.packed_bytes != d->packed_bytes || ref.n_groups != d->n_groups ||
+        ref.n_scales != d->n_scales)
+        return LOWBIT_E_ARG;
+    return LOWBIT_OK;
+}
+
+// ---------------------------------------------------------------- packer
+
+inline float premapped(float w, bool tanh3) {
+    return tanh3 ? (float)(3.0 * std::tanh((double)w / 3.0)) : w;
+}
+
+// Scale of one domain of `count` values handed out by get(i), i ascending.
+template <class Get>
+float domain_scale(int32_t fmt, int64_t count, Get get) {
+    if (fmt == LOWBIT_INT4) {
+        float peak = 0.0f;
+        for (int64_t i = 0; i < count; ++i) peak = std::max(peak, std::fabs(get(i)));
+        return peak / 7.0f;
+    }
+    double total = 0.0;   // binary64, ascending order: absmean of M8.8 0x05A / 0x02B
+    for (int64_t i = 0; i < count; ++i) total += (double)std::fabs(get(i));
+    return (float)(total / (double)count);
+}
+
+// One code from a (premapped) weight and its domain scale.
+inline int code_of(int32_t fmt, float v, float s) {
+    if (fmt == LOWBIT_BINARY1) return v >= 0.0f ? 1 : -1;
+    if (s == 0.0f) return 0;
+    const float lim = fmt == LOWBIT_INT4 ? 7.0f : 1.0f;
+    float r = std::rint(v / s);
+    return (int)std::min(lim, std::max(-lim, r));
+}
+
+struct RowPacker {
+    const lowbit_desc& d;
+    const float* w;
+    uint8_t* packed;
+    float* scales;
+    float tensor_scale;
+    std::atomic<int>* bad;
+
+    void operator()(int64_t r0, int64_t r1) const {
+        const int64_t K = d.k;
+        const bool tanh3 = (d.flags & LOWBIT_FLAG_TANH3) != 0;
+        std::vector<float> row((size_t)K);
+        std::vector<int8_t> codes((size_t)K);
+        for (int64_t r = r0; r < r1; ++r) {
+            const float* wr = w + r * K;
+            for (int64_t c = 0; c < K; ++c) {
+                if (!std::isfinite(wr[c])) { bad->store(1); return; }
+                row[(size_t)c] = premapped(wr[c], tanh3);
+            }
+            // scale domains of this row
+            const int64_t span = d.scale == LOWBIT_SCALE_GROUP ? d.group : K;
+            for (int64_t c0 = 0, gi = 0; c0 < K; c0 += span, ++gi) {
+                const int64_t c1 = std::min(K, c0 + span);
+                float s = tensor_scale;
+                if (d.scale != LOWBIT_SCALE_TENSOR) {
+                    s = domain_scale(d.format, c1 - c0, [&](int64_t i) { return row[(size_t)(c0 + i)]; });
+                    scales[d.scale == LOWBIT_SCALE_ROW ? r : r * d.n_groups + gi] = s;
+                }
+                for (int64_t c = c0; c < c1; ++c) codes[(size_t)c] = (int8_t)code_of(d.format, row[(size_t)c], s);
+            }
+            emit_row(codes.data(), packed + r * d.row_bytes);
+        }
+    }
+
+    // write one row of codes in the packed layout of lowbit.h
+    void emit_row(const int8_t* c, uint8_t* out) const {
+        const int64_t K = d.k;
+        std::memset(out, 0, (size_t)d.row_bytes);
+        if (d.format == LOWBIT_BINARY1) {
+            for (int64_t b = 0; b * 8 < K; ++b) {
+                uint32_t byte = 0;
+                for (int j = 0; j < 8 && b * 8 + j < K; ++j) byte |= (uint32_t)(c[b * 8 + j] < 0) << j;
+                out[b] = (uint8_t)byte;
+            }
+            return;
+        }
+        const int per_word = d.format == LOWBIT_TERNARY2 ? 16 : 8;
+        const int bits = d.format == LOWBIT_TERNARY2 ? 2 : 4;
+        const uint32_t mask = (1u << bits) - 1u;
+        for (int64_t wi = 0; wi * per_word < K; ++wi) {
+            uint32_t word = 0;
+            for (int j = 0; j < per_word && wi * per_word + j < K; ++j) {
+                const uint32_t field = (uint32_t)c[wi * per_word + j] & mask;   // two's complement
+                word |= field << (8 * (j % 4) + bits * (j / 4));
+            }
+            out[4 * wi + 0] = (uint8_t)(word);
+            out[4 * wi + 1] = (uint8_t)(word >> 8);
+            out[4 * wi + 2] = (uint8_t)(word >> 16);
+            out[4 * wi + 3] = (uint8_t)(word >> 24);
+        }
+    }
+};
+
+lowbit_status hip_status(hipError_t e) { return e == hipSuccess ? LOWBIT_OK : LOWBIT_E_HIP; }
+
+lowbit_status linear_common(const lowbit_desc* d, const uint8_t* packed, const float* scales, const int8_t* q,
+                            const float* sx, int32_t t, float* y, int32_t* acc, lowbit::LinearArgs* out) {
+    lowbit_status st = check_desc(d);
+    if (st != LOWBIT_OK) return st;
+    if (!packed || !scales || !q || !sx || !y || t < 1) return LOWBIT_E_ARG;
+    lowbit::LinearArgs a;
+    a.fmt = d->format; a.scale = d->scale; a.group = d->group; a.n_groups = (int)d->n_groups;
+    a.n = d->n; a.k = d->k; a.t = t; a.row_bytes = d->row_bytes;
+    a.packed = packed; a.scales = scales; a.q = q; a.sx = sx; a.y = y; a.acc = acc;
+    *out = a;
+    return LOWBIT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+lowbit_status lowbit_describe(int32_t format, int32_t scale, int32_t n, int32_t k, int32_t group, int32_t flags,
+                              lowbit_desc* out) {
+    return fill_desc(format, scale, n, k, group, flags, out);
+}
+
+lowbit_status lowbit_pack(const lowbit_desc* d, const float* w, uint8_t* packed, float* scales) {
+    lowbit_status st = check_desc(d);
+    if (st != LOWBIT_OK) return st;
+    if (!w || !packed || !scales) return LOWBIT_E_ARG;
+    const int64_t N = d->n, K = d->k;
+    const bool tanh3 = (d->flags & LOWBIT_FLAG_TANH3) != 0;
+
+    float tensor_scale = 0.0f;
+    if (d->scale == LOWBIT_SCALE_TENSOR) {   // one sequential pass over all of W
+        for (int64_t i = 0; i < N * K; ++i)
+            if (!std::isfinite(w[i])) return LOWBIT_E_NONFINITE;
+        tensor_scale = domain_scale(d->format, N * K, [&](int64_t i) { return premapped(w[i], tanh3); });
+        scales[0] = tensor_scale;
+    }
+
+    std::atomic<int> bad{0};
+    RowPacker job{*d, w, packed, scales, tensor_scale, &bad};
+    const int64_t work = N * K;
+    unsigned hw = std::max(1u, std::thread::hardware_concurrency());
+    unsigned nthreads = (unsigned)std::min<int64_t>({(int64_t)hw, N, std::max<int64_t>(1, work / (1 << 16))});
+    if (nthreads <= 1) {
+        job(0, N);
+    } else {
+        std::vector<std::thread> pool;
+        for (unsigned i = 0; i < nthreads; ++i) {
+            const int64_t r0 = N * i / nthreads, r1 = N * (i + 1) / nthreads;
+            pool.emplace_back([&job, r0, r1] { job(r0, r1); });
+        }
+        for (auto& th : pool) th.join();
+    }
+    return bad.load() ? LOWBIT_E_NONFINITE : LOWBIT_OK;
+}
+
+lowbit_status lowbit_act_quant(const float* x, int32_t t, int32_t k, int8_t* q, float* sx, int32_t* status,
+                               void* hip_stream) {
+    if (!x || !q || !sx || t < 1 || k < 1) return LOWBIT_E_ARG;
+    return hip_status(lowbit::launch_act_quant(x, t, k, q, sx, status, (hipStream_t)hip_stream));
+}
+
+lowbit_status lowbit_linear(const lowbit_desc* d, const uint8_t* packed, const float* scales, const int8_t* q,
+                            const float* sx, int32_t t, float* y, int32_t* acc, void* hip_stream) {
+    lowbit::LinearArgs a;
+    lowbit_status st = linear_common(d, packed, scales, q, sx, t, y, acc, &a);
+    if (st != LOWBIT_OK) return st;
+    return hip_status(lowbit::launch_gemv(a, (hipStream_t)hip_stream));
+}
+
+lowbit_status lowbit_linear_batched(const lowbit_desc* d, const uint8_t* packed, const float* scales,
+                                    const int8_t* q, const float* sx, int32_t t, float* y, int32_t* acc,
+                                    void* hip_stream) {
+    lowbit::LinearArgs a;
+    lowbit_status st = linear_common(d, packed, scales, q, sx, t, y, acc, &a);
+    if (st != LOWBIT_OK) return st;
+    return hip_status(lowbit::launch_gemm(a, (hipStream_t)hip_stream));
+}
+
+int32_t lowbit_max_k(int32_t format) { return max_k_of(format); }
+
+const char* lowbit_status_string(lowbit_status s) {
+    switch (s) {
+        case LOWBIT_OK: return "ok";
+        case LOWBIT_E_ARG: return "invalid argument";
+        case LOWBIT_E_RANGE: return "k exceeds the int32 accumulator bound";
+        case LOWBIT_E_NONFINITE: return "non-finite latent weight";
+        case LOWBIT_E_FORMAT: return "invalid packed data";
+        case LOWBIT_E_HIP: return "HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+int32_t lowbit_abi_version(void) { return kAbiVersion; }
+
+}  // extern "C"

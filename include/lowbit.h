@@ -1,0 +1,186 @@
+/*
+ * lowbit.h - C ABI of the MI355X low-bit linear layer
+ *
+ *     y = s_w * s_x * (Q(W) . Q8(x))
+ *
+ * following the operator statement of "M8.8 - Native Binary and Ternary
+ * Transformers" (sections 0x02C-0x02D, 0x05A-0x05D and the reference decoder
+ * of 0x09C): latent weights become packed 1-, 2- or 4-bit codes with fp32
+ * scales, activations become int8 codes with one fp32 scale per token, the
+ * product is accumulated exactly in int32, and an fp32 epilogue rescales it.
+ *
+ * Conventions
+ *  - Every matrix is row-major.  W is [n, k] (k contiguous), x and q are
+ *    [t, k], y is [t, n].
+ *  - Host pointers are plain CPU memory.  Device pointers are HIP device
+ *    memory on the current device (e.g. torch tensor data pointers).
+ *  - The caller owns every buffer.  The library allocates nothing and keeps no
+ *    state between calls; all entry points are reentrant and thread-safe.
+ *  - Device calls are asynchronous on `hip_stream` (a hipStream_t, NULL = the
+ *    null stream); their outputs are valid once the stream has synchronised.
+ *  - No entry point reads device memory on the host.  Argument checks are
+ *    synchronous and happen before any launch; a rejected call launches
+ *    nothing.  No exception crosses this interface.
+ *
+ * Packed weight layout (bytes per row = lowbit_desc.row_bytes, rows back to
+ * back, fields past k are zero):
+ *  - LOWBIT_BINARY1: one bit per code, bit = (1 - s) / 2, little-bit-first
+ *    along k, ceil(k / 8) bytes per row (the binary export reference of M8.8
+ *    section 0x06E).
+ *  - LOWBIT_TERNARY2: 2-bit two's-complement fields (+1 = 01, 0 = 00,
+ *    -1 = 11, 10 reserved) - the two physical bits per ternary code of M8.8
+ *    section 0x01A, four codes per byte.  Codes are grouped in 32-bit
+ *    little-endian words of 16: code j of a word sits in byte (j mod 4), bits
+ *    2*(j div 4).  Rows are whole words: 4 * ceil(k / 16) bytes.
+ *  - LOWBIT_INT4: 4-bit two's-complement fields for the symmetric levels
+ *    -7..+7 of the T4NT model card (1000 reserved), two codes per byte, 8 per
+ *    32-bit word: code j of a word sits in byte (j mod 4), nibble (j div 4)
+ *    (0 = low).  Rows are whole words: 4 * ceil(k / 8) bytes.
+ * Scales are fp32 arrays: [1] (tensor), [n] (row) or [n, n_groups] (group of
+ * `group` consecutive columns of a row, the last one possibly shorter).
+ */
+#ifndef LOWBIT_H
+#define LOWBIT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum lowbit_status {
+    LOWBIT_OK = 0,
+    LOWBIT_E_ARG = 1,        /* null pointer, bad size, unknown enum, inconsistent descriptor */
+    LOWBIT_E_RANGE = 2,      /* the int32 accumulator could overflow for this k */
+    LOWBIT_E_NONFINITE = 3,  /* lowbit_pack: a latent weight is NaN or infinite */
+    LOWBIT_E_FORMAT = 4,     /* reserved for packed-data format errors */
+    LOWBIT_E_HIP = 5         /* a HIP launch failed (hipGetLastError) */
+} lowbit_status;
+
+typedef enum lowbit_format {
+    LOWBIT_TERNARY2 = 0,     /* {-1, 0, +1} */
+    LOWBIT_BINARY1 = 1,      /* {-1, +1} */
+    LOWBIT_INT4 = 2          /* -7..+7 */
+} lowbit_format;
+
+typedef enum lowbit_scale {
+    LOWBIT_SCALE_TENSOR = 0, /* one scale for all of W */
+    LOWBIT_SCALE_ROW = 1,    /* one scale per output row */
+    LOWBIT_SCALE_GROUP = 2   /* one scale per (row, group of `group` columns) */
+} lowbit_scale;
+
+/* lowbit_desc.flags */
+#define LOWBIT_FLAG_TANH3 1  /* lowbit_pack maps w -> 3 tanh(w / 3) first (T4NT soft clipping) */
+
+/* lowbit_act_quant *status bits */
+#define LOWBIT_ACT_NONFINITE 1   /* some row held NaN or Inf */
+#define LOWBIT_ACT_OVERFLOW 2    /* some row's 127 / max|x| overflowed fp32 */
+
+/* Shape and size of one packed weight matrix.  Fill it with lowbit_describe;
+ * every other call re-derives the size fields and rejects a mismatch. */
+typedef struct lowbit_desc {
+    int32_t format;          /* lowbit_format */
+    int32_t scale;           /* lowbit_scale */
+    int32_t n;               /* output rows, >= 1 */
+    int32_t k;               /* input columns, >= 1 */
+    int32_t group;           /* group mode: columns per group; else 0 */
+    int32_t flags;           /* LOWBIT_FLAG_* */
+    int64_t row_bytes;       /* packed bytes per row */
+    int64_t packed_bytes;    /* n * row_bytes */
+    int64_t n_groups;        /* ceil(k / group) in group mode, else 1 */
+    int64_t n_scales;        /* 1, n, or n * n_groups */
+} lowbit_desc;
+
+/*
+ * lowbit_describe - validate a weight shape and fill *out with its sizes.
+ *   group: group mode needs a positive multiple of 64 (ternary, int4) or of
+ *          128 (binary) - the k-extent of one matrix-core step of the kernels;
+ *          it must be 0 otherwise.
+ *   flags: LOWBIT_FLAG_TANH3 or 0.
+ * Errors: LOWBIT_E_ARG for any invalid field or a null `out`;
+ *         LOWBIT_E_RANGE when k exceeds lowbit_max_k(format).
+ */
+lowbit_status lowbit_describe(int32_t format, int32_t scale, int32_t n, int32_t k,
+                              int32_t group, int32_t flags, lowbit_desc* out);
+
+/*
+ * lowbit_pack - quantise latent fp32 weights and pack them (host, offline).
+ *   w      host float [n, k]           latent weights
+ *   packed host uint8  [packed_bytes]  out: codes in the layout above
+ *   scales host float  [n_scales]      out: fp32 scales
+ * Per scale domain (M8.8 0x05A, 0x06E; T4NT model card):
+ *   ternary: s = mean |w| (binary64 sum in ascending index order / count,
+ *            rounded once to fp32); code = clip(rint(w / s), -1, 1) in fp32
+ *            with ties to even; a zero domain gets s = 0 and codes 0.
+ *   binary : s = mean |w| as above; code = +1 if w >= 0 (either zero) else -1.
+ *   int4   : s = max |w| / 7 in fp32; code = clip(rint(w / s), -7, 7).
+ *   LOWBIT_FLAG_TANH3 first maps w -> fp32(3 tanh(w / 3)) (binary64 tanh).
+ * Runs on host threads; reads and writes host memory only.
+ * Errors: LOWBIT_E_ARG (null pointer, bad descriptor), LOWBIT_E_NONFINITE
+ * (a NaN or infinite weight; the outputs are then unspecified).
+ */
+lowbit_status lowbit_pack(const lowbit_desc* d, const float* w, uint8_t* packed, float* scales);
+
+/*
+ * lowbit_act_quant - per-token absmax int8 quantisation (M8.8 0x02C, 0x05C).
+ *   x      device float [t, k]
+ *   q      device int8  [t, k]   out: clip(rint(x * (127 / m)), -127, 127), fp32,
+ *                                ties to even, m = max_k |x[row]|
+ *   sx     device float [t]      out: m / 127 (fp32); 0 for an all-zero row
+ *   status device int32 [1] or NULL: the kernel ORs LOWBIT_ACT_* bits into it
+ *          (the caller clears it beforehand).  A row holding NaN/Inf, or whose
+ *          127 / m overflows, gets zero codes and sx = NaN, so any output
+ *          computed from it is visibly NaN.
+ *   t, k   >= 1
+ * Errors: LOWBIT_E_ARG, LOWBIT_E_HIP.
+ */
+lowbit_status lowbit_act_quant(const float* x, int32_t t, int32_t k, int8_t* q, float* sx,
+                               int32_t* status, void* hip_stream);
+
+/*
+ * lowbit_linear - decode-shaped product (GEMV), tuned for t <= 16 and correct
+ * for any t (tokens are processed 16 at a time).
+ *   d       descriptor of the packed matrix (from lowbit_describe)
+ *   packed  device uint8 [packed_bytes]    from lowbit_pack
+ *   scales  device float [n_scales]
+ *   q, sx   device int8 [t, k], device float [t]   from lowbit_act_quant
+ *   y       device float [t, n]  out:
+ *             tensor/row: y = fp32(acc) * (sx[t] * s_w[n])
+ *             group     : y = sx[t] * sum_g s_w[n, g] * fp32(acc[t, n, g])
+ *   acc     device int32 [t, n, n_groups] or NULL: when given, the exact
+ *           integer products sum_k q[t, k] * code[n, k] (per group in group
+ *           mode) are written too.
+ * Accumulation is exact in int32; y may differ from a sequential fp32
+ * evaluation by rounding order only.
+ * Errors: LOWBIT_E_ARG (null pointer, t < 1, descriptor mismatch),
+ *         LOWBIT_E_RANGE (k > lowbit_max_k(format)), LOWBIT_E_HIP.
+ */
+lowbit_status lowbit_linear(const lowbit_desc* d, const uint8_t* packed, const float* scales,
+                            const int8_t* q, const float* sx, int32_t t,
+                            float* y, int32_t* acc, void* hip_stream);
+
+/*
+ * lowbit_linear_batched - prefill-shaped product (GEMM on the matrix cores),
+ * tuned for large t and correct for any t.  Same arguments, outputs and
+ * errors as lowbit_linear; the two produce identical acc.
+ */
+lowbit_status lowbit_linear_batched(const lowbit_desc* d, const uint8_t* packed, const float* scales,
+                                    const int8_t* q, const float* sx, int32_t t,
+                                    float* y, int32_t* acc, void* hip_stream);
+
+/* Largest k the kernels accept for a format.  The operator's own bound
+ * (M8.8 0x09C) is k * 127 * qmax < 2^31; the kernels hold each code scaled
+ * by 64 (ternary, binary) or 16 (int4) in int8 lanes, so their int32 sums need
+ * k * 127 * qmax * scale < 2^31: k <= 264208 (ternary, binary), 150976 (int4). */
+int32_t lowbit_max_k(int32_t format);
+
+const char* lowbit_status_string(lowbit_status s);
+
+/* ABI version: bump on any incompatible change. */
+int32_t lowbit_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LOWBIT_H */

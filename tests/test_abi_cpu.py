@@ -1,0 +1,163 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads and exports
+every symbol include/lowbit.h declares, descriptors and argument checks behave
+as documented, and the host packer matches the oracle bit-for-bit."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from tests.conftest import ROOT
+
+lb = pytest.importorskip("bit_weight_linear_bitlinear_amd")
+
+FMT = {"ternary": lb.TERNARY2, "binary": lb.BINARY1, "int4": lb.INT4}
+SC = {"tensor": lb.SCALE_TENSOR, "row": lb.SCALE_ROW, "group": lb.SCALE_GROUP}
+
+
+def _header_functions():
+    with open(os.path.join(ROOT, "include", "lowbit.h")) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(lowbit_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    names = _header_functions()
+    assert set(names) >= {"lowbit_describe", "lowbit_pack", "lowbit_act_quant", "lowbit_linear",
+                          "lowbit_linear_batched", "lowbit_status_string", "lowbit_max_k", "lowbit_abi_version"}
+    lib = ctypes.CDLL(lb.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lb.lowbit_abi_version() == 1
+
+
+def test_describe_sizes():
+    d = lb.lowbit_describe(lb.TERNARY2, lb.SCALE_GROUP, 9728, 2560, 128)
+    assert (d.row_bytes, d.packed_bytes, d.n_groups, d.n_scales) == (640, 9728 * 640, 20, 9728 * 20)
+    d = lb.lowbit_describe(lb.BINARY1, lb.SCALE_ROW, 96, 192)
+    assert (d.row_bytes, d.n_scales, d.n_groups) == (24, 96, 1)
+    d = lb.lowbit_describe(lb.INT4, lb.SCALE_ROW, 3840, 1280, 0, lb.FLAG_TANH3)
+    assert d.row_bytes == 640 and d.flags == 1
+    d = lb.lowbit_describe(lb.TERNARY2, lb.SCALE_TENSOR, 5, 17)
+    assert d.row_bytes == 8 and d.n_scales == 1
+    d = lb.lowbit_describe(lb.INT4, lb.SCALE_GROUP, 3, 200, 64)
+    assert d.row_bytes == 4 * 25 and d.n_groups == 4
+    for fmt in ("ternary", "binary", "int4"):
+        for k in (1, 7, 16, 100, 2560):
+            assert lb.lowbit_describe(FMT[fmt], 0, 1, k).row_bytes == oracle.row_bytes(fmt, k)
+
+
+@pytest.mark.parametrize("args", [
+    (3, 0, 4, 4, 0, 0),          # unknown format
+    (0, 3, 4, 4, 0, 0),          # unknown scale mode
+    (0, 0, 0, 4, 0, 0),          # n < 1
+    (0, 0, 4, 0, 0, 0),          # k < 1
+    (0, 0, 4, 4, 64, 0),         # group given without group mode
+    (0, 2, 4, 256, 96, 0),       # group not a multiple of 64
+    (1, 2, 4, 256, 64, 0),       # binary groups need multiples of 128
+    (0, 0, 4, 4, 0, 2),          # unknown flag
+])
+def test_describe_rejects(args):
+    with pytest.raises(lb.LowbitError) as e:
+        lb.lowbit_describe(*args)
+    assert e.value.status == 1
+
+
+def test_describe_range_bound():
+    for fmt in (lb.TERNARY2, lb.BINARY1, lb.INT4):
+        kmax = lb.lowbit_max_k(fmt)
+        lb.lowbit_describe(fmt, 0, 1, kmax)
+        with pytest.raises(lb.LowbitError) as e:
+            lb.lowbit_describe(fmt, 0, 1, kmax + 1)
+        assert e.value.status == 2
+    assert lb.lowbit_max_k(lb.TERNARY2) * 127 * 64 < 2**31 <= (lb.lowbit_max_k(lb.TERNARY2) + 1) * 127 * 64
+    assert lb.lowbit_max_k(lb.INT4) * 127 * 7 * 16 < 2**31 <= (lb.lowbit_max_k(lb.INT4) + 1) * 127 * 7 * 16
+
+
+def test_device_calls_reject_bad_arguments_before_launch():
+    """Null pointers, t < 1 and tampered descriptors return E_ARG without any
+    HIP call (safe on a machine with no GPU)."""
+    lib = lb.raw_library()
+    d = lb.lowbit_describe(lb.TERNARY2, lb.SCALE_TENSOR, 16, 64)
+    one = ctypes.c_void_p(16)    # never dereferenced: every call below fails validation first
+    assert lib.lowbit_act_quant(None, 1, 64, one, one, None, None) == 1
+    assert lib.lowbit_act_quant(one, 0, 64, one, one, None, None) == 1
+    assert lib.lowbit_linear(ctypes.byref(d), one, one, one, one, 0, one, None, None) == 1
+    assert lib.lowbit_linear(ctypes.byref(d), None, one, one, one, 1, one, None, None) == 1
+    assert lib.lowbit_linear_batched(ctypes.byref(d), one, one, None, one, 1, one, None, None) == 1
+    bad = lb.lowbit_describe(lb.TERNARY2, lb.SCALE_TENSOR, 16, 64)
+    bad.row_bytes += 4
+    assert lib.lowbit_linear(ctypes.byref(bad), one, one, one, one, 1, one, None, None) == 1
+    assert lib.lowbit_linear_batched(None, one, one, one, one, 1, one, None, None) == 1
+
+
+def _pack_lib(w, fmt, scale, group=0, tanh=False):
+    n, k = w.shape
+    d = lb.lowbit_describe(FMT[fmt], SC[scale], n, k, group, lb.FLAG_TANH3 if tanh else 0)
+    packed = np.empty(d.packed_bytes, np.uint8)
+    scales = np.empty(d.n_scales, np.float32)
+    lb.lowbit_pack(d, np.ascontiguousarray(w), packed, scales)
+    return packed.reshape(n, d.row_bytes), scales
+
+
+def _pack_oracle(w, fmt, scale, group=0, tanh=False):
+    p, s, _ = oracle.quantize_and_pack(w, fmt, scale, group, tanh)
+    return p, s.ravel()
+
+
+@pytest.mark.parametrize("wl", workloads.WORKLOADS, ids=lambda w: w.name)
+def test_host_pack_matches_oracle_on_workload_shapes(wl):
+    seen = set()
+    for mi, m in enumerate(wl.matrices):
+        if (m.n, m.k) in seen:
+            continue
+        seen.add((m.n, m.k))
+        w = workloads.latent_weights(wl.index, 0, mi, m.n, m.k)
+        p1, s1 = _pack_lib(w, wl.fmt, wl.scale, wl.group, wl.tanh_premap)
+        p2, s2 = _pack_oracle(w, wl.fmt, wl.scale, wl.group, wl.tanh_premap)
+        assert (p1 == p2).all(), (wl.name, m.name)
+        assert (s1.view(np.uint32) == s2.view(np.uint32)).all(), (wl.name, m.name)
+
+
+@pytest.mark.parametrize("fmt", ["ternary", "binary", "int4"])
+@pytest.mark.parametrize("scale", ["tensor", "row", "group"])
+def test_host_pack_matches_oracle_ragged(fmt, scale):
+    group = (128 if fmt == "binary" else 64) if scale == "group" else 0
+    for seed, (n, k) in enumerate([(1, 1), (3, 5), (17, 100), (33, 257), (5, 1000)]):
+        w, _ = workloads.random_case(seed, n, k, 1)
+        w[0, 0] = 0.0
+        if k > 2:
+            w[-1, 1] = -0.0
+        for tanh in (False, True):
+            p1, s1 = _pack_lib(w, fmt, scale, group, tanh)
+            p2, s2 = _pack_oracle(w, fmt, scale, group, tanh)
+            assert (p1 == p2).all() and (s1.view(np.uint32) == s2.view(np.uint32)).all(), (n, k, tanh)
+
+
+def test_host_pack_ties_and_zero_domains():
+    g = np.array([[0.25, -0.75, 0.75, -0.25, 0.5, -0.5, 0.0, 1.0]], np.float32)
+    p, s = _pack_lib(g, "ternary", "tensor")
+    assert s[0] == 0.5
+    assert (oracle.unpack(p, "ternary", 8)[0] == np.array([0, -1, 1, 0, 1, -1, 0, 1])).all()
+    z = np.zeros((2, 130), np.float32)
+    z[1, 129] = 1.0
+    for fmt, scale, group in (("ternary", "group", 64), ("int4", "row", 0), ("binary", "group", 128)):
+        p1, s1 = _pack_lib(z, fmt, scale, group)
+        p2, s2 = _pack_oracle(z, fmt, scale, group)
+        assert (p1 == p2).all() and (s1 == s2).all()
+
+
+def test_host_pack_rejects_nonfinite_and_bad_buffers():
+    w = np.ones((4, 32), np.float32)
+    w[2, 7] = np.nan
+    for scale in ("tensor", "row"):
+        with pytest.raises(lb.LowbitError) as e:
+            _pack_lib(w, "ternary", scale)
+        assert e.value.status == 3
+    d = lb.lowbit_describe(lb.TERNARY2, lb.SCALE_TENSOR, 4, 32)
+    with pytest.raises(ValueError):
+        lb.lowbit_pack(d, np.ones((4, 32), np.float32), np.empty(3, np.uint8), np.empty(1, np.float32))

@@ -1,0 +1,162 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, element
+by element, on the seeded workloads at their real shapes and on ragged edge
+cases.  Codes, scales and int32 accumulators must match bit-for-bit; y within
+1e-5 relative + 1e-6 absolute."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from tests.gpu_common import act_quant_dev, check_y, linear_dev, pack_upload, run_layer, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _distinct_matrices(wl):
+    seen = {}
+    for mi, m in enumerate(wl.matrices):
+        seen.setdefault((m.n, m.k), (mi, m))
+    return list(seen.values())
+
+
+# ------------------------------------------------------------- workloads
+
+def test_single_ternary_both_entry_points():
+    wl = workloads.BY_NAME["single_ternary"]
+    m = wl.matrices[0]
+    w = workloads.latent_weights(wl.index, 0, 0, m.n, m.k)
+    x = workloads.workload_activations(wl, 0, 0, wl.tokens[0], m.k)
+    run_layer(w, x, wl.fmt, wl.scale, wl.group, wl.tanh_premap, label="single_ternary")
+
+
+def test_decode_stack_all_matrices():
+    wl = workloads.BY_NAME["decode_stack"]
+    for layer in range(wl.layers):
+        for mi, m in enumerate(wl.matrices):
+            if layer >= m.count:
+                continue
+            w = workloads.latent_weights(wl.index, layer, mi, m.n, m.k)
+            x = workloads.workload_activations(wl, layer, mi, 1, m.k)
+            entries = ("gemv", "gemm") if layer == 0 else ("gemv",)
+            run_layer(w, x, wl.fmt, wl.scale, wl.group, wl.tanh_premap, entries=entries,
+                      label=f"decode_stack L{layer} {m.name}")
+
+
+def test_binary_gqa_layer0_sampled_tokens():
+    wl = workloads.BY_NAME["binary_gqa"]
+    rng = np.random.default_rng(0)
+    for mi, m in _distinct_matrices(wl):
+        w = workloads.latent_weights(wl.index, 0, mi, m.n, m.k)
+        x = workloads.workload_activations(wl, 0, mi, wl.tokens[0], m.k)
+        sample = np.sort(rng.choice(wl.tokens[0], size=384, replace=False))
+        sample[0], sample[-1] = 0, wl.tokens[0] - 1
+        run_layer(w, x, wl.fmt, wl.scale, wl.group, wl.tanh_premap, token_sample=sample,
+                  label=f"binary_gqa {m.name}")
+
+
+@pytest.mark.parametrize("t", [1, 4, 16])
+def test_ternary_4b_layer0(t):
+    wl = workloads.BY_NAME["ternary_4b"]
+    for mi, m in _distinct_matrices(wl):
+        w = workloads.latent_weights(wl.index, 0, mi, m.n, m.k)
+        x = workloads.workload_activations(wl, 0, mi, t, m.k)
+        run_layer(w, x, wl.fmt, wl.scale, wl.group, wl.tanh_premap, label=f"ternary_4b T={t} {m.name}")
+
+
+def test_int4_t4nt_layer0_sampled_tokens():
+    wl = workloads.BY_NAME["int4_t4nt"]
+    rng = np.random.default_rng(1)
+    for mi, m in _distinct_matrices(wl):
+        w = workloads.latent_weights(wl.index, 0, mi, m.n, m.k)
+        x = workloads.workload_activations(wl, 0, mi, wl.tokens[0], m.k)
+        sample = np.sort(rng.choice(wl.tokens[0], size=192, replace=False))
+        sample[0], sample[-1] = 0, wl.tokens[0] - 1
+        run_layer(w, x, wl.fmt, wl.scale, wl.group, wl.tanh_premap, token_sample=sample,
+                  label=f"int4_t4nt {m.name}")
+
+
+# ------------------------------------------------------- ragged / random
+
+RAGGED = [(1, 1, 1), (16, 64, 1), (17, 100, 3), (5, 257, 2), (33, 1000, 17), (130, 520, 5), (64, 4100, 16),
+          (40, 384, 130)]
+
+
+@pytest.mark.parametrize("fmt", ["ternary", "binary", "int4"])
+@pytest.mark.parametrize("scale", ["tensor", "row", "group"])
+def test_ragged_shapes(fmt, scale):
+    for i, (n, k, t) in enumerate(RAGGED):
+        group = (128 if fmt == "binary" else 64) * (1 + i % 2) if scale == "group" else 0
+        w, x = workloads.random_case(100 + i, n, k, t)
+        run_layer(w, x, fmt, scale, group, fmt == "int4", label=f"ragged {i}")
+
+
+def test_act_quant_edge_rows():
+    """Zero rows, rows with NaN/Inf and rows whose 127/max overflows: zero
+    codes, sx = NaN for the rejected ones, status bits set; good rows exact."""
+    import torch
+    x = np.random.default_rng(3).standard_normal((8, 203)).astype(np.float32)
+    x[1] = 0.0
+    x[2, 17] = np.nan
+    x[3, 0] = -np.inf
+    x[4] = np.float32(1e-45)
+    x[5] = np.float32(5e-37)     # tiny but representable: 127 / m finite
+    x[6, :] = np.arange(203, dtype=np.float32) - 101
+    say("[case] act_quant edge rows")
+    q, sx, st = act_quant_dev(to_dev(x))
+    torch.cuda.synchronize()
+    q_ref, sx_ref, rs = oracle.act_quant(x)
+    qh, sxh = q.cpu().numpy(), sx.cpu().numpy()
+    ok = rs == 0
+    assert (qh[ok] == q_ref[ok]).all() and (sxh[ok].view(np.uint32) == sx_ref[ok].view(np.uint32)).all()
+    assert (qh[~ok] == 0).all() and np.isnan(sxh[~ok]).all()
+    assert rs.tolist()[2:5] == [1, 1, 2]
+    assert int(st.cpu()[0]) == 3
+    # aligned/vector path and scalar path agree (k % 4 != 0 above; now k % 4 == 0)
+    x2 = np.random.default_rng(4).standard_normal((37, 256)).astype(np.float32) * 3
+    q2, sx2, st2 = act_quant_dev(to_dev(x2))
+    q2r, sx2r, _ = oracle.act_quant(x2)
+    assert (q2.cpu().numpy() == q2r).all() and (sx2.cpu().numpy() == sx2r).all() and int(st2.cpu()[0]) == 0
+
+
+def test_accumulator_bound_worst_case():
+    """At the largest accepted k every activation code 127 times every weight
+    code at its extreme must still be exact (the scaled int32 sums sit one
+    step below 2^31)."""
+    import torch
+    lb = pytest.importorskip("bit_weight_linear_bitlinear_amd")
+    for fmt, code_w, qmax in (("ternary", 0.5, 1), ("int4", 1.0, 7), ("binary", -0.5, 1)):
+        k = lb.lowbit_max_k(lb.FORMATS[fmt])
+        n, t = 16, 2
+        say(f"[case] worst-case accumulator fmt={fmt} k={k}")
+        w = np.full((n, k), code_w, np.float32)
+        w[1::2] *= -1
+        x = np.ones((t, k), np.float32)
+        x[1] *= -1
+        d, packed, scales, _, sh = pack_upload(w, fmt, "row")
+        q, sx, st = act_quant_dev(to_dev(x))
+        for entry in ("gemv", "gemm"):
+            y, acc = linear_dev(entry, d, packed, scales, q, sx)
+            torch.cuda.synchronize()
+            a = acc.cpu().numpy()[:, :, 0].astype(np.int64)
+            sign_w = np.where(np.arange(n) % 2 == 0, 1, -1) * (1 if code_w > 0 else -1)
+            expect = np.outer(np.array([127, -127]), sign_w * qmax) * k
+            assert (a == expect).all(), (fmt, entry)
+
+
+def test_entry_points_agree_on_random_large():
+    """Moderately large random layer: GEMV and GEMM produce identical acc."""
+    import torch
+    w, x = workloads.random_case(7, 1000, 2048, 40)
+    say("[case] gemv vs gemm random 1000x2048, t=40")
+    d, packed, scales, _, _ = pack_upload(w, "ternary", "group", 128)
+    q, sx, _ = act_quant_dev(to_dev(x))
+    y0, a0 = linear_dev("gemv", d, packed, scales, q, sx)
+    y1, a1 = linear_dev("gemm", d, packed, scales, q, sx)
+    torch.cuda.synchronize()
+    assert torch.equal(a0, a1)
+    q_ref, sx_ref, _ = oracle.act_quant(x)
+    p_ref, s_ref, _ = oracle.quantize_and_pack(w, "ternary", "group", 128)
+    y32, y64, acc_ref = oracle.linear(p_ref, s_ref, "ternary", "group", 128, 2048, q_ref, sx_ref)
+    assert (a0.cpu().numpy() == acc_ref).all()
+    check_y(y0.cpu().numpy(), y32, y64, "gemv")
+    check_y(y1.cpu().numpy(), y32, y64, "gemm")
