@@ -33,6 +33,13 @@ if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run `python -m bit_weight_linear_bitlinear_amd.build` "
                       "(or __graft_entry__.build()) first")
 
+# torch's wheel ships its own HIP runtime.  Importing torch first makes the
+# library bind to that same runtime (the dynamic linker reuses the loaded
+# libamdhip64.so.7), so device pointers and streams from torch tensors are
+# valid in our launches; loading the library first would put a second HIP
+# runtime in the process.
+import torch  # noqa: E402,F401
+
 _lib = ctypes.CDLL(LIB_PATH)
 
 
@@ -56,21 +63,28 @@ _lib.lowbit_pack.argtypes = [_D, _P, _P, _P]
 _lib.lowbit_act_quant.argtypes = [_P, _i32, _i32, _P, _P, _P, _P]
 _lib.lowbit_linear.argtypes = [_D, _P, _P, _P, _P, _i32, _P, _P, _P]
 _lib.lowbit_linear_batched.argtypes = [_D, _P, _P, _P, _P, _i32, _P, _P, _P]
+_PP = ctypes.POINTER(ctypes.c_void_p)
+_lib.lowbit_linear_grouped.argtypes = [_i32, _D, _PP, _PP, _PP, _PP, _i32, _PP, _PP, _P]
+_lib.lowbit_linear_grouped.restype = _i32
 _lib.lowbit_max_k.argtypes = [_i32]
 _lib.lowbit_max_k.restype = _i32
 _lib.lowbit_status_string.argtypes = [_i32]
 _lib.lowbit_status_string.restype = ctypes.c_char_p
 _lib.lowbit_abi_version.restype = _i32
+_lib.lowbit_last_hip_error.restype = ctypes.c_char_p
 for _f in ("lowbit_describe", "lowbit_pack", "lowbit_act_quant", "lowbit_linear", "lowbit_linear_batched"):
     getattr(_lib, _f).restype = _i32
 
 EXPORTS = ("lowbit_describe", "lowbit_pack", "lowbit_act_quant", "lowbit_linear", "lowbit_linear_batched",
-           "lowbit_max_k", "lowbit_status_string", "lowbit_abi_version")
+           "lowbit_linear_grouped",
+           "lowbit_max_k", "lowbit_status_string", "lowbit_abi_version", "lowbit_last_hip_error")
 
 
 class LowbitError(RuntimeError):
     def __init__(self, status: int, call: str):
         msg = _lib.lowbit_status_string(status).decode()
+        if status == 5:
+            msg += ": " + _lib.lowbit_last_hip_error().decode()
         super().__init__(f"{call}: {STATUS.get(status, status)} ({msg})")
         self.status = status
 
@@ -145,6 +159,42 @@ def lowbit_linear_batched(d: lowbit_desc, packed, scales, q, sx, y, acc=None, st
     """Device GEMM on the matrix cores: same contract as lowbit_linear."""
     _check(_lib.lowbit_linear_batched(ctypes.byref(d), *_linear_ptrs(d, packed, scales, q, sx, y, acc),
                                       _stream(stream)), "lowbit_linear_batched")
+
+
+class GroupedCall:
+    """Marshalled arguments of one lowbit_linear_grouped call (the pointer
+    arrays are built once, so replaying the call costs no Python work beyond
+    the foreign call itself)."""
+
+    def __init__(self, descs, packed, scales, q, sx, y, acc=None):
+        n = len(descs)
+        if not (n == len(packed) == len(scales) == len(q) == len(sx) == len(y)) or n < 1:
+            raise ValueError("lowbit_linear_grouped: argument lists differ in length")
+        t = q[0].shape[0]
+        arr = lambda ptrs: (ctypes.c_void_p * n)(*[p.value if p is not None else None for p in ptrs])
+        cols = [_linear_ptrs(d, pk, sc, qq, ss, yy, aa) for d, pk, sc, qq, ss, yy, aa in
+                zip(descs, packed, scales, q, sx, y, acc if acc is not None else [None] * n)]
+        if any(c[4] != t for c in cols):
+            raise ValueError("lowbit_linear_grouped: every q must have the same token count")
+        self.count = n
+        self.t = t
+        self.descs = (lowbit_desc * n)(*descs)
+        self.packed = arr([c[0] for c in cols])
+        self.scales = arr([c[1] for c in cols])
+        self.q = arr([c[2] for c in cols])
+        self.sx = arr([c[3] for c in cols])
+        self.y = arr([c[5] for c in cols])
+        self.acc = arr([c[6] for c in cols]) if acc is not None else None
+        self._keep = (packed, scales, q, sx, y, acc)    # the tensors must outlive the call
+
+    def __call__(self, stream=None):
+        _check(_lib.lowbit_linear_grouped(self.count, self.descs, self.packed, self.scales, self.q, self.sx,
+                                          self.t, self.y, self.acc, _stream(stream)), "lowbit_linear_grouped")
+
+
+def lowbit_linear_grouped(descs, packed, scales, q, sx, y, acc=None, stream=None) -> None:
+    """Device: several independent GEMVs of equal k in one launch."""
+    GroupedCall(descs, packed, scales, q, sx, y, acc)(stream)
 
 
 def lowbit_max_k(format: int) -> int:

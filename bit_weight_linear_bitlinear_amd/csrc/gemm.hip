@@ -245,10 +245,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
             if constexpr (GROUP) {
                 // k covered so far: ternary/int4 slots are 64-column blocks;
                 // a binary step's two slots share all 128 columns
-                int kdone;
-                if constexpr (FMT == FMT_BINARY) kdone = slot == 1 ? (s + 1) * BK : 0;
-                else kdone = s * BK + 64 * (slot + 1);
-                if (kdone > 0) {
+                // (only a slot that holds valid columns can close a group)
+                int kbeg, kdone;
+                if constexpr (FMT == FMT_BINARY) { kbeg = s * BK; kdone = slot == 1 ? (s + 1) * BK : 0; }
+                else { kbeg = s * BK + 64 * slot; kdone = kbeg + 64; }
+                if (kdone > 0 && kbeg < a.K) {
                     if (kdone > a.K) kdone = a.K;
                     if (kdone % a.group == 0 || kdone == a.K) group_epilogue(kdone);
                 }

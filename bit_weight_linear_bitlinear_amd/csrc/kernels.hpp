@@ -27,6 +27,8 @@ struct LinearArgs {
 hipError_t launch_act_quant(const float* x, int t, int k, int8_t* q, float* sx, int32_t* status,
                             hipStream_t stream);
 hipError_t launch_gemv(const LinearArgs& a, hipStream_t stream);
+// several matrices of equal fmt / scale mode / group / k and t <= 16 in one launch
+hipError_t launch_gemv_group(const LinearArgs* mats, int count, hipStream_t stream);
 hipError_t launch_gemm(const LinearArgs& a, hipStream_t stream);
 
 }  // namespace lowbit

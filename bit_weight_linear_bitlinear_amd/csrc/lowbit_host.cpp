@@ -12,6 +12,7 @@
 #include <thread>
 #include <vector>
 
+#include "gemv.hpp"
 #include "kernels.hpp"
 #include "lowbit.h"
 
@@ -165,7 +166,18 @@ struct RowPacker {
     }
 };
 
-lowbit_status hip_status(hipError_t e) { return e == hipSuccess ? LOWBIT_OK : LOWBIT_E_HIP; }
+thread_local hipError_t g_last_hip_error = hipSuccess;
+
+// Launch errors are read with hipGetLastError, which also returns errors left
+// behind by earlier, unrelated runtime calls of the caller; the error state is
+// therefore cleared right before each launch (see clear_hip_error).
+void clear_hip_error() { (void)hipGetLastError(); }
+
+lowbit_status hip_status(hipError_t e) {
+    if (e == hipSuccess) return LOWBIT_OK;
+    g_last_hip_error = e;
+    return LOWBIT_E_HIP;
+}
 
 lowbit_status linear_common(const lowbit_desc* d, const uint8_t* packed, const float* scales, const int8_t* q,
                             const float* sx, int32_t t, float* y, int32_t* acc, lowbit::LinearArgs* out) {
@@ -225,6 +237,7 @@ lowbit_status lowbit_pack(const lowbit_desc* d, const float* w, uint8_t* packed,
 lowbit_status lowbit_act_quant(const float* x, int32_t t, int32_t k, int8_t* q, float* sx, int32_t* status,
                                void* hip_stream) {
     if (!x || !q || !sx || t < 1 || k < 1) return LOWBIT_E_ARG;
+    clear_hip_error();
     return hip_status(lowbit::launch_act_quant(x, t, k, q, sx, status, (hipStream_t)hip_stream));
 }
 
@@ -233,6 +246,7 @@ lowbit_status lowbit_linear(const lowbit_desc* d, const uint8_t* packed, const f
     lowbit::LinearArgs a;
     lowbit_status st = linear_common(d, packed, scales, q, sx, t, y, acc, &a);
     if (st != LOWBIT_OK) return st;
+    clear_hip_error();
     return hip_status(lowbit::launch_gemv(a, (hipStream_t)hip_stream));
 }
 
@@ -242,7 +256,44 @@ lowbit_status lowbit_linear_batched(const lowbit_desc* d, const uint8_t* packed,
     lowbit::LinearArgs a;
     lowbit_status st = linear_common(d, packed, scales, q, sx, t, y, acc, &a);
     if (st != LOWBIT_OK) return st;
+    clear_hip_error();
     return hip_status(lowbit::launch_gemm(a, (hipStream_t)hip_stream));
+}
+
+lowbit_status lowbit_linear_grouped(int32_t count, const lowbit_desc* descs, const uint8_t* const* packed,
+                                    const float* const* scales, const int8_t* const* q, const float* const* sx,
+                                    int32_t t, float* const* y, int32_t* const* acc, void* hip_stream) {
+    if (count < 1 || !descs || !packed || !scales || !q || !sx || !y || t < 1) return LOWBIT_E_ARG;
+    std::vector<lowbit::LinearArgs> args((size_t)count);
+    for (int32_t i = 0; i < count; ++i) {
+        const lowbit_desc& d0 = descs[0];
+        const lowbit_desc& d = descs[i];
+        if (d.format != d0.format || d.scale != d0.scale || d.group != d0.group || d.flags != d0.flags ||
+            d.k != d0.k)
+            return LOWBIT_E_ARG;
+        lowbit_status st = linear_common(&d, packed[i], scales[i], q[i], sx[i], t, y[i], acc ? acc[i] : nullptr,
+                                         &args[(size_t)i]);
+        if (st != LOWBIT_OK) return st;
+    }
+    clear_hip_error();
+    const hipStream_t stream = (hipStream_t)hip_stream;
+    for (int32_t t0 = 0; t0 < t; t0 += 16) {              // 16 tokens per launch
+        const int32_t tc = std::min(16, t - t0);
+        std::vector<lowbit::LinearArgs> chunk(args);
+        for (auto& a : chunk) {
+            a.t = tc;
+            a.q += (size_t)t0 * a.k;
+            a.sx += t0;
+            a.y += (size_t)t0 * a.n;
+            if (a.acc) a.acc += (size_t)t0 * a.n * a.n_groups;
+        }
+        for (int32_t b = 0; b < count; b += lowbit::kGemvMaxMats) {
+            const int32_t c = std::min(count - b, lowbit::kGemvMaxMats);
+            lowbit_status st = hip_status(lowbit::launch_gemv_group(chunk.data() + b, c, stream));
+            if (st != LOWBIT_OK) return st;
+        }
+    }
+    return LOWBIT_OK;
 }
 
 int32_t lowbit_max_k(int32_t format) { return max_k_of(format); }
@@ -260,5 +311,7 @@ const char* lowbit_status_string(lowbit_status s) {
 }
 
 int32_t lowbit_abi_version(void) { return kAbiVersion; }
+
+const char* lowbit_last_hip_error(void) { return hipGetErrorString(g_last_hip_error); }
 
 }  // extern "C"

@@ -168,6 +168,27 @@ lowbit_status lowbit_linear_batched(const lowbit_desc* d, const uint8_t* packed,
                                     const int8_t* q, const float* sx, int32_t t,
                                     float* y, int32_t* acc, void* hip_stream);
 
+/*
+ * lowbit_linear_grouped - `count` independent decode products in as few
+ * launches as possible (up to 40 matrices per launch), e.g. the projections
+ * that read one input (q/k/v, gate/up) or any set of same-width layers whose
+ * inputs are ready.  Each matrix i computes exactly what lowbit_linear
+ * computes for (descs[i], packed[i], scales[i], q[i], sx[i], t, y[i], acc[i]).
+ *   count   >= 1
+ *   descs   host array [count]; all must share format, scale mode, group, flags
+ *           and k (n may differ)
+ *   packed, scales, q, sx, y: host arrays [count] of device pointers
+ *   acc     host array [count] of device pointers (entries may be NULL), or NULL
+ *   t       tokens per matrix, the same for all (>= 1; 16 per launch)
+ * One persistent kernel streams every matrix's tiles back to back, so small
+ * matrices share one launch's ramp-up instead of paying one each.
+ * Errors: as lowbit_linear, plus LOWBIT_E_ARG when the descriptors disagree.
+ */
+lowbit_status lowbit_linear_grouped(int32_t count, const lowbit_desc* descs, const uint8_t* const* packed,
+                                    const float* const* scales, const int8_t* const* q,
+                                    const float* const* sx, int32_t t, float* const* y,
+                                    int32_t* const* acc, void* hip_stream);
+
 /* Largest k the kernels accept for a format.  The operator's own bound
  * (M8.8 0x09C) is k * 127 * qmax < 2^31; the kernels hold each code scaled
  * by 64 (ternary, binary) or 16 (int4) in int8 lanes, so their int32 sums need
@@ -175,6 +196,10 @@ lowbit_status lowbit_linear_batched(const lowbit_desc* d, const uint8_t* packed,
 int32_t lowbit_max_k(int32_t format);
 
 const char* lowbit_status_string(lowbit_status s);
+
+/* Text of the HIP error behind the calling thread's most recent LOWBIT_E_HIP
+ * ("no error" if there was none).  The returned string is static. */
+const char* lowbit_last_hip_error(void);
 
 /* ABI version: bump on any incompatible change. */
 int32_t lowbit_abi_version(void);

@@ -161,3 +161,13 @@ def test_host_pack_rejects_nonfinite_and_bad_buffers():
     d = lb.lowbit_describe(lb.TERNARY2, lb.SCALE_TENSOR, 4, 32)
     with pytest.raises(ValueError):
         lb.lowbit_pack(d, np.ones((4, 32), np.float32), np.empty(3, np.uint8), np.empty(1, np.float32))
+
+
+def test_single_hip_runtime_in_process():
+    """The binding must bind the library to torch's HIP runtime: two copies of
+    libamdhip64 in one process make torch's device pointers invalid for our
+    launches."""
+    import re
+    with open("/proc/self/maps") as f:
+        paths = set(re.findall(r"\S*libamdhip64\S*", f.read()))
+    assert len(paths) == 1, paths

@@ -160,3 +160,43 @@ def test_entry_points_agree_on_random_large():
     assert (a0.cpu().numpy() == acc_ref).all()
     check_y(y0.cpu().numpy(), y32, y64, "gemv")
     check_y(y1.cpu().numpy(), y32, y64, "gemm")
+
+
+@pytest.mark.parametrize("fmt,scale,group,t", [("ternary", "group", 128, 1), ("ternary", "tensor", 0, 3),
+                                               ("int4", "row", 0, 16), ("binary", "row", 0, 20),
+                                               ("ternary", "group", 64, 5)])
+def test_grouped_matches_single_and_oracle(fmt, scale, group, t):
+    """lowbit_linear_grouped over 45 matrices of equal k and mixed n (two
+    launches of at most 40) equals per-matrix lowbit_linear bit-for-bit in acc
+    and y, and the oracle on a few of them."""
+    import torch
+    lb = pytest.importorskip("bit_weight_linear_bitlinear_amd")
+    k = 640 if fmt != "binary" else 768
+    ns = [16 * (1 + (i * 7) % 13) + (i % 3) for i in range(45)]
+    say(f"[case] grouped fmt={fmt} scale={scale} group={group} t={t} k={k} count={len(ns)}")
+    descs, packed, scales, qs, sxs, ys, accs, refs = [], [], [], [], [], [], [], []
+    for i, n in enumerate(ns):
+        w, x = workloads.random_case(500 + i, n, k, t)
+        d, p, s, _, _ = pack_upload(w, fmt, scale, group, fmt == "int4")
+        q, sx, _ = act_quant_dev(to_dev(x))
+        descs.append(d); packed.append(p); scales.append(s); qs.append(q); sxs.append(sx)
+        ys.append(torch.full((t, n), float("nan"), device="cuda"))
+        accs.append(torch.full((t, n, d.n_groups), -7, dtype=torch.int32, device="cuda") if i % 4 != 3 else None)
+        refs.append((w, x))
+    lb.lowbit_linear_grouped(descs, packed, scales, qs, sxs, ys, accs)
+    for i in range(len(ns)):
+        y1, a1 = linear_dev("gemv", descs[i], packed[i], scales[i], qs[i], sxs[i])
+        torch.cuda.synchronize()
+        if scale != "group":    # integer partials: identical y whatever the k-split
+            assert torch.equal(ys[i], y1), i
+        else:                   # fp32 group partials may be combined in another order
+            assert torch.allclose(ys[i], y1, rtol=1e-5, atol=1e-6), i
+        if accs[i] is not None:
+            assert torch.equal(accs[i], a1), i
+    for i in (0, 17, 44):
+        w, x = refs[i]
+        p_ref, s_ref, _ = oracle.quantize_and_pack(w, fmt, scale, group, fmt == "int4")
+        q_ref, sx_ref, _ = oracle.act_quant(x)
+        y32, y64, acc_ref = oracle.linear(p_ref, s_ref, fmt, scale, group, k, q_ref, sx_ref)
+        assert (accs[i].cpu().numpy() == acc_ref).all()
+        check_y(ys[i].cpu().numpy(), y32, y64, f"grouped {i}")
