@@ -235,6 +235,27 @@ def per_launch(p: Pass, reps: int):
     return total / (n * reps), sum(p.linear_bytes) / n, sum(p.linear_ops) / n
 
 
+def copy_calibration(nbytes=1 << 30, reps=5):
+    """A plain copy of known size (torch's copy kernel): its rate is the
+    practical streaming ceiling of this GPU, and its FETCH_SIZE / WRITE_SIZE
+    counters scale the GEMV's counters into bytes."""
+    import torch
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / 1e3 / reps
+    del a, b
+    return {"bytes_read": nbytes, "bytes_written": nbytes, "GBps_read_plus_write": round(2 * nbytes / t / 1e9, 1),
+            "us": round(t * 1e6, 1)}
+
+
 # ------------------------------------------------------------- correctness
 
 def sampled_check(p: Pass, picks, rows_per=48, seed=0):
@@ -326,6 +347,8 @@ def main():
     ap.add_argument("--skip-check", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--quick", action="store_true", help="grouped schedule only")
+    ap.add_argument("--profile-pass", action="store_true",
+                    help="copy calibration + grouped GEMV pass only (for profiler runs)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -337,6 +360,10 @@ def main():
     import workloads
     torch.cuda.set_device(0)
     out = {"metric": METRIC}
+    if args.profile_pass:
+        args.quick = args.skip_gemm = args.skip_cpu = args.skip_check = True
+    calib = copy_calibration()
+    log(f"[bench] copy calibration: {calib}")
 
     # ---- GEMV line: ternary_4b decode pass
     wl = workloads.BY_NAME["ternary_4b"]
@@ -376,6 +403,7 @@ def main():
                      "kernel": "gemv_kernel (grouped schedule)", "avg_launch_us": round(dur * 1e6, 3),
                      "bytes_per_launch": round(bytes_per_launch)},
     })
+    out["copy_calibration"] = calib
     if check:
         out["check"] = check
     log(f"[bench] gemv grouped per launch {dur * 1e6:.2f} us -> {achieved:.1f} GB/s")

@@ -65,15 +65,18 @@ template <int FMT, int WPL> struct StepShape {
     }
 };
 
-// MFMAs of one k-step (decoded weights x activation chunks)
-template <int FMT, int WPL>
+// MFMAs of one k-step (decoded weights x activation chunks).  FRESH: the
+// step starts a new accumulation (its first MFMA adds to zero, not to C).
+template <int FMT, int WPL, bool FRESH = false>
 __device__ __forceinline__ void step_mfma(const uint32_t* wv, const i32x4* a, i32x4& C) {
+    const i32x4 zero = {0, 0, 0, 0};
     if constexpr (FMT == FMT_TERNARY) {
         #pragma unroll
-        for (int i = 0; i < WPL; ++i) C = mfma16(a[i], decode_ternary(wv[i]), C);
+        for (int i = 0; i < WPL; ++i) C = mfma16(a[i], decode_ternary(wv[i]), (FRESH && i == 0) ? zero : C);
     } else if constexpr (FMT == FMT_INT4) {
         #pragma unroll
-        for (int i = 0; i < WPL / 2; ++i) C = mfma16(a[i], decode_int4(wv[2 * i], wv[2 * i + 1]), C);
+        for (int i = 0; i < WPL / 2; ++i)
+            C = mfma16(a[i], decode_int4(wv[2 * i], wv[2 * i + 1]), (FRESH && i == 0) ? zero : C);
     } else {
         #pragma unroll
         for (int i = 0; i < WPL; ++i) {
@@ -83,55 +86,87 @@ __device__ __forceinline__ void step_mfma(const uint32_t* wv, const i32x4* a, i3
             i32x4 a0, a1, b0, b1;
             perm_binary_a(X, a0, a1);
             decode_binary(wv[i], b0, b1);
-            C = mfma16(a0, b0, C);
+            C = mfma16(a0, b0, (FRESH && i == 0) ? zero : C);
             C = mfma16(a1, b1, C);
         }
     }
 }
 
-// Position of a wavefront in its flat (tile, k-step) sequence.  All fields
-// are wavefront-uniform.
-struct Cursor {
-    int it;      // tile-group iteration of this workgroup
-    int j;       // k-step within this wavefront's part of the row
-    int tile;    // global tile index (across matrices)
-    int mi;      // matrix of that tile
+// Where one wavefront reads one 16-row tile: uniform base pointers of its
+// part of the k-range, set up once per tile.
+struct TileCtx {
+    const uint8_t* w;     // packed row (row0) at this part's first k-step
+    const int8_t* q;      // activation codes at this part's first k
+    const float* sc;      // group mode: scales[row0, first group]; else scales (+ row0 if per row)
+    const float* sx;
+    float* y;             // y + row0
+    int32_t* acc;         // acc + row0 * G (nullable)
+    int n;                // rows of the matrix (y row stride)
+    int rows;             // valid rows of the tile (<= 0: padding tile)
 };
 
-// FAST: every row is a whole number of BPL-byte chunks, packed and q are
-// 16-byte aligned and K % 16 == 0 - loads are single vector loads masked per
-// lane; otherwise byte-safe loaders handle ragged rows and tails.
-template <int FMT, int WPL, int NR, bool GROUP, bool FAST>
+// FAST: every row is a whole number of k-steps, k % 16 == 0, scale groups are
+// a power-of-two number of k-steps and pointers are 16-byte aligned - so no
+// load ever needs a bounds mask; otherwise byte-safe loaders handle ragged
+// rows and tails.  D: k-steps of loads in flight per wavefront.
+// ACC: also write the exact integer products (the acc output); kept out of
+// the streaming instantiations because optional stores inside the k-loop
+// would make the compiler's wait counting conservative.
+template <int FMT, int WPL, int NR, bool GROUP, bool FAST, int D, bool ACC>
 __global__ __launch_bounds__(256) void gemv_kernel(const GemvParams p) {
-    constexpr int BPL = 4 * WPL;                 // packed bytes per lane per k-step
+    constexpr int BPL = 4 * WPL;                             // packed bytes per lane per k-step
+    constexpr int SB = 4 * BPL;                              // packed bytes per row per k-step
+    constexpr int KS = 4 * WPL * Fmt<FMT>::kCodesPerWord;     // k per k-step
     constexpr int SHIFT = Fmt<FMT>::kShift;
     constexpr int NA = StepShape<FMT, WPL>::kChunks;
-    constexpr int D = 4;                         // k-steps of loads in flight per wavefront
-    __shared__ int32_t red[4][4][64];            // [wave][C register][lane], k-split partials
+    __shared__ int32_t red[4][4][64];                        // [wave][C register][lane], k-split partials
 
     // the wavefront index is uniform; saying so keeps every value derived
     // from it (tile, matrix, k-range) in scalar registers and scalar loads
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const int g = lane >> 4;                     // lane group: quarter of the k-step
-    const int rl = lane & 15;                    // weight row within the tile
+    const int g = lane >> 4;                                 // lane group: quarter of each k-step
+    const int rl = lane & 15;                                // weight row within the tile
     const int part = wave % p.ksplit;
     const int wslot = wave / p.ksplit;
     const bool tok_ok = rl < p.T;
 
     const int n_iter = (p.n_tile_groups - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
-    const int F = n_iter * p.part_steps;
-    const int s_begin = part * p.part_steps;                       // first row k-step of this part
-    const int s_end = min(p.n_steps, s_begin + p.part_steps);
+    const int s_begin = part * p.part_len;                   // first row k-step of this part
+    const int s_real = max(0, min(p.n_steps, s_begin + p.part_len) - s_begin);
+    const int S = p.loop_steps;                              // part_len rounded up to D
 
-    auto set_iter = [&](Cursor& c, int it) {
-        c.it = it;
-        c.j = 0;
-        c.tile = ((int)blockIdx.x + it * (int)gridDim.x) * p.tpw + wslot;
-        while (c.mi + 1 < p.n_mats && c.tile >= p.m[c.mi + 1].tile0) ++c.mi;
-    };
-    auto advance = [&](Cursor& c) {
-        if (++c.j == p.part_steps) set_iter(c, c.it + 1);
+    // per-lane offsets, fixed for the whole kernel
+    const uint32_t lw_row = (uint32_t)rl * (uint32_t)p.row_bytes + (uint32_t)(g * BPL);
+    const uint32_t lw_row0 = (uint32_t)(g * BPL);
+    const uint32_t la = (tok_ok ? (uint32_t)rl * (uint32_t)p.K : 0u) + (uint32_t)((KS / 4) * g);
+    const uint32_t ls_row = GROUP ? (uint32_t)rl * (uint32_t)p.G : (p.scale_per_row ? (uint32_t)rl : 0u);
+    int sxi[NR];
+    #pragma unroll
+    for (int r = 0; r < NR; ++r) sxi[r] = min(4 * g + r, p.T - 1);
+
+    auto make_ctx = [&](int it, int& mi) -> TileCtx {
+        const int tile = ((int)blockIdx.x + it * (int)gridDim.x) * p.tpw + wslot;
+        TileCtx c;
+        if (it >= n_iter || tile >= p.total_tiles) {     // padding: valid addresses, nothing stored
+            const GemvMat& m0 = p.m[0];
+            c.w = m0.packed; c.q = m0.q; c.sc = m0.scales; c.sx = m0.sx; c.y = m0.y; c.acc = nullptr;
+            c.n = m0.n; c.rows = 0;
+            return c;
+        }
+        while (mi + 1 < p.n_mats && tile >= p.m[mi + 1].tile0) ++mi;
+        const GemvMat& m = p.m[mi];
+        const int row0 = (tile - m.tile0) * 16;
+        c.w = m.packed + (size_t)row0 * (size_t)p.row_bytes + (size_t)s_begin * SB;
+        c.q = m.q + (size_t)s_begin * KS;
+        if constexpr (GROUP) c.sc = m.scales + (size_t)row0 * p.G + (s_begin >> p.spu_shift);
+        else c.sc = m.scales + (p.scale_per_row ? row0 : 0);
+        c.sx = m.sx;
+        c.y = m.y + row0;
+        c.acc = m.acc ? m.acc + (size_t)row0 * p.G : nullptr;
+        c.n = m.n;
+        c.rows = min(16, m.n - row0);
+        return c;
     };
 
     // ring of D prefetched k-steps
@@ -140,63 +175,44 @@ __global__ __launch_bounds__(256) void gemv_kernel(const GemvParams p) {
     float sg[D];           // group scale (group mode) or the row's scale (tensor/row mode)
     float sxs[D][NR];      // activation scales of the tokens this lane's C registers hold
 
-    auto load_slot = [&](int u, const Cursor& c) {
-        const int s = s_begin + c.j;
-        const bool live = c.it < n_iter && s < s_end && c.tile < p.total_tiles;   // uniform
-        const GemvMat& m = p.m[c.mi];
-        const int row = (c.tile - m.tile0) * 16 + rl;
-        const bool row_ok = live && row < m.n;
-        const int64_t off = (int64_t)s * 4 * BPL + g * BPL;
-        const int word0 = s * 4 * WPL + g * WPL;
+    auto load_slot = [&](int u, const TileCtx& c, int j) {
+        const bool row_ok = rl < c.rows;
         if constexpr (FAST) {
-            // Every load is issued unconditionally and nothing is done with
-            // its value here, so the compiler's wait counting never assumes a
-            // skipped load and never waits on a load right after issuing it.
-            // Lanes with nothing to read use clamped, valid addresses: a row
-            // past n or a token past t only pollutes outputs that are never
-            // stored, and weights past the row are zeroed when consumed.
-            const bool wok = row_ok && off < p.row_bytes;
-            load_words<WPL>(m.packed + (wok ? (size_t)row * (size_t)p.row_bytes + off : 0), BPL, true, wv[u]);
+            // Unconditional loads, values untouched until consumed: the
+            // compiler's wait counting then keeps all D steps in flight.
+            // Rows past n use the tile's first row (outputs never stored);
+            // dead steps past this part re-read its first step (never used).
+            const int jj = j < s_real ? j : 0;
+            load_words<WPL>(c.w + (row_ok ? lw_row : lw_row0) + (size_t)jj * SB, BPL, true, wv[u]);
             #pragma unroll
-            for (int i = 0; i < NA; ++i) {
-                const int k0 = StepShape<FMT, WPL>::chunk_k(word0, i);
-                const bool aok = live && tok_ok && k0 < p.K;
-                av[u][i] = *reinterpret_cast<const i32x4*>(m.q + (aok ? (size_t)rl * (size_t)p.K + k0 : 0));
-            }
-            // scale of the group this step belongs to / of the row; the
-            // tokens' activation scales ride along so the tile's last step has
-            // every epilogue operand in the ring
-            if constexpr (GROUP)
-                sg[u] = m.scales[row_ok ? (size_t)row * p.G + s / p.spu : 0];
-            else
-                sg[u] = m.scales[p.scale_per_row && row_ok ? row : 0];
-            #pragma unroll
-            for (int r = 0; r < NR; ++r) sxs[u][r] = m.sx[min(4 * g + r, p.T - 1)];
+            for (int i = 0; i < NA; ++i)
+                av[u][i] = *reinterpret_cast<const i32x4*>(c.q + la + (size_t)jj * KS + 16 * i);
+            if constexpr (GROUP) sg[u] = c.sc[(row_ok ? ls_row : 0u) + (uint32_t)(jj >> p.spu_shift)];
+            else sg[u] = c.sc[row_ok ? ls_row : 0u];
         } else {
             #pragma unroll
             for (int i = 0; i < WPL; ++i) wv[u][i] = 0u;
             #pragma unroll
             for (int i = 0; i < NA; ++i) av[u][i] = i32x4{0, 0, 0, 0};
             sg[u] = 0.0f;
-            if (!live) return;
-            const int64_t rem = row_ok ? p.row_bytes - off : 0;
-            const int valid = rem <= 0 ? 0 : (rem >= BPL ? BPL : (int)rem);
-            if (valid > 0)
-                load_words<WPL>(m.packed + (size_t)(row_ok ? row : 0) * (size_t)p.row_bytes + off, valid, false, wv[u]);
-            const int8_t* qrow = m.q + (size_t)(tok_ok ? rl : 0) * (size_t)p.K;
-            #pragma unroll
-            for (int i = 0; i < NA; ++i)
-                av[u][i] = load_a16<false>(qrow, StepShape<FMT, WPL>::chunk_k(word0, i), p.K, tok_ok);
-            if constexpr (GROUP) {
-                const int sn = s + 1;
-                if ((sn % p.spu == 0 || sn == p.n_steps) && row_ok)
-                    sg[u] = m.scales[(size_t)row * p.G + s / p.spu];
-            } else {
-                sg[u] = m.scales[p.scale_per_row && row_ok ? row : 0];
+            if (j < s_real && row_ok) {
+                const int64_t off = (int64_t)(s_begin + j) * SB + g * BPL;    // within the row
+                const int64_t rem = p.row_bytes - off;
+                const int valid = rem <= 0 ? 0 : (rem >= BPL ? BPL : (int)rem);
+                if (valid > 0) load_words<WPL>(c.w + (size_t)rl * (size_t)p.row_bytes + (size_t)j * SB + g * BPL,
+                                               valid, false, wv[u]);
+                if constexpr (GROUP) sg[u] = c.sc[ls_row + (uint32_t)(j / p.spu)];
+                else sg[u] = c.sc[ls_row];
             }
-            #pragma unroll
-            for (int r = 0; r < NR; ++r) sxs[u][r] = m.sx[min(4 * g + r, p.T - 1)];
+            if (j < s_real) {
+                const int8_t* qrow = c.q - (size_t)s_begin * KS + (size_t)(tok_ok ? rl : 0) * (size_t)p.K;
+                const int kbase = (s_begin + j) * KS + (KS / 4) * g;
+                #pragma unroll
+                for (int i = 0; i < NA; ++i) av[u][i] = load_a16<false>(qrow, kbase + 16 * i, p.K, tok_ok);
+            }
         }
+        #pragma unroll
+        for (int r = 0; r < NR; ++r) sxs[u][r] = c.sx[sxi[r]];
     };
 
     i32x4 C = {0, 0, 0, 0};
@@ -204,118 +220,116 @@ __global__ __launch_bounds__(256) void gemv_kernel(const GemvParams p) {
     #pragma unroll
     for (int r = 0; r < NR; ++r) yp[r] = 0.0f;
 
-    auto compute_slot = [&](int u, const Cursor& c) {
-        const int s = s_begin + c.j;
-        const bool live = s < s_end;             // c.it < n_iter holds here
-        const GemvMat& m = p.m[c.mi];
-        const int row = (c.tile - m.tile0) * 16 + rl;
-        const bool row_ok = c.tile < p.total_tiles && row < m.n;
-        if (live) {
-            if constexpr (FAST) {
-                // weights past the end of the row pair with clamped (garbage)
-                // activations: zero them (binary: after decoding, a zero word
-                // means +1 codes)
-                const bool wok = (int64_t)s * 4 * BPL + g * BPL < p.row_bytes;
-                if constexpr (FMT != FMT_BINARY) {
-                    #pragma unroll
-                    for (int i = 0; i < WPL; ++i) wv[u][i] = wok ? wv[u][i] : 0u;
-                } else {
-                    #pragma unroll
-                    for (int i = 0; i < NA; ++i) av[u][i] = wok ? av[u][i] : i32x4{0, 0, 0, 0};
-                }
-            }
-            step_mfma<FMT, WPL>(wv[u], av[u], C);
-            if constexpr (GROUP) {
-                const int sn = s + 1;
-                if (sn % p.spu == 0 || sn == p.n_steps) {        // a scale group is complete
-                    const int gi = s / p.spu;
-                    #pragma unroll
-                    for (int r = 0; r < NR; ++r) {
-                        const int32_t a = C[r] >> SHIFT;
-                        yp[r] = yp[r] + sg[u] * (float)a;
-                        if (m.acc) {
-                            const int t = 4 * g + r;
-                            if (t < p.T && row_ok) m.acc[((size_t)t * m.n + row) * p.G + gi] = a;
-                        }
-                    }
-                    C = i32x4{0, 0, 0, 0};
-                }
-            }
-        }
-        if (c.j == p.part_steps - 1) {           // end of this tile's k-range
-            if constexpr (GROUP) {
-                if (p.ksplit > 1) {
-                    #pragma unroll
-                    for (int r = 0; r < NR; ++r) red[wave][r][lane] = __float_as_int(yp[r]);
-                    __syncthreads();
-                    if (part == 0) {
-                        for (int q = 1; q < p.ksplit; ++q) {
-                            #pragma unroll
-                            for (int r = 0; r < NR; ++r) yp[r] = yp[r] + __int_as_float(red[wave + q][r][lane]);
-                        }
-                    }
-                    __syncthreads();
-                }
-                if (part == 0) {
-                    #pragma unroll
-                    for (int r = 0; r < NR; ++r) {
-                        const int t = 4 * g + r;
-                        if (t < p.T && row_ok) m.y[(size_t)t * m.n + row] = sxs[u][r] * yp[r];
-                    }
-                }
-            } else {
-                int32_t a[NR];
+    auto compute_slot = [&](int u, const TileCtx& c, int j) {
+        if (j >= s_real) return;                             // dead step (uniform)
+        if (GROUP && FAST && p.spu_shift == 0)               // one k-step per scale group
+            step_mfma<FMT, WPL, true>(wv[u], av[u], C);
+        else
+            step_mfma<FMT, WPL, false>(wv[u], av[u], C);
+        if constexpr (GROUP) {
+            const int sn = s_begin + j + 1;
+            bool group_end;
+            if constexpr (FAST) group_end = (sn & ((1 << p.spu_shift) - 1)) == 0 || sn == p.n_steps;
+            else group_end = sn % p.spu == 0 || sn == p.n_steps;
+            if (group_end) {
+                const int gi = FAST ? (s_begin + j) >> p.spu_shift : (s_begin + j) / p.spu;
+                const bool row_ok = rl < c.rows;
                 #pragma unroll
-                for (int r = 0; r < NR; ++r) a[r] = C[r] >> SHIFT;
-                if (p.ksplit > 1) {
-                    #pragma unroll
-                    for (int r = 0; r < NR; ++r) red[wave][r][lane] = a[r];
-                    __syncthreads();
-                    if (part == 0) {
-                        for (int q = 1; q < p.ksplit; ++q) {
-                            #pragma unroll
-                            for (int r = 0; r < NR; ++r) a[r] += red[wave + q][r][lane];
-                        }
-                    }
-                    __syncthreads();
-                }
-                if (part == 0 && row_ok) {
-                    #pragma unroll
-                    for (int r = 0; r < NR; ++r) {
+                for (int r = 0; r < NR; ++r) {
+                    const int32_t a = C[r] >> SHIFT;
+                    yp[r] = yp[r] + sg[u] * (float)a;
+                    if constexpr (ACC) {
                         const int t = 4 * g + r;
-                        if (t < p.T) {
-                            m.y[(size_t)t * m.n + row] = (float)a[r] * (sxs[u][r] * sg[u]);
-                            if (m.acc) m.acc[(size_t)t * m.n + row] = a[r];
-                        }
+                        if (c.acc && t < p.T && row_ok) c.acc[((size_t)t * c.n + rl) * p.G + gi] = a;
                     }
                 }
+                if (!(FAST && p.spu_shift == 0)) C = i32x4{0, 0, 0, 0};
             }
-            C = i32x4{0, 0, 0, 0};
-            #pragma unroll
-            for (int r = 0; r < NR; ++r) yp[r] = 0.0f;
         }
     };
 
-    Cursor pc, cc;
-    pc.mi = 0;
-    cc.mi = 0;
-    set_iter(pc, 0);
-    set_iter(cc, 0);
-    #pragma unroll
-    for (int u = 0; u < D; ++u) {
-        load_slot(u, pc);
-        advance(pc);
-    }
-    for (int f = 0; f < F; f += D) {
-        #pragma unroll
-        for (int u = 0; u < D; ++u) {
-            if (f + u < F) {
-                compute_slot(u, cc);
-                advance(cc);
-                load_slot(u, pc);
-                advance(pc);
+    float ep_sx[NR], ep_sw = 0.0f;                           // epilogue operands of the tile
+    auto tile_end = [&](const TileCtx& c) {
+        const bool row_ok = rl < c.rows;
+        if constexpr (GROUP) {
+            if (p.ksplit > 1) {
+                #pragma unroll
+                for (int r = 0; r < NR; ++r) red[wave][r][lane] = __float_as_int(yp[r]);
+                __syncthreads();
+                if (part == 0) {
+                    for (int q = 1; q < p.ksplit; ++q) {
+                        #pragma unroll
+                        for (int r = 0; r < NR; ++r) yp[r] = yp[r] + __int_as_float(red[wave + q][r][lane]);
+                    }
+                }
+                __syncthreads();
+            }
+            if (part == 0 && row_ok) {
+                #pragma unroll
+                for (int r = 0; r < NR; ++r) {
+                    const int t = 4 * g + r;
+                    if (t < p.T) c.y[(size_t)t * c.n + rl] = ep_sx[r] * yp[r];
+                }
+            }
+        } else {
+            int32_t a[NR];
+            #pragma unroll
+            for (int r = 0; r < NR; ++r) a[r] = C[r] >> SHIFT;
+            if (p.ksplit > 1) {
+                #pragma unroll
+                for (int r = 0; r < NR; ++r) red[wave][r][lane] = a[r];
+                __syncthreads();
+                if (part == 0) {
+                    for (int q = 1; q < p.ksplit; ++q) {
+                        #pragma unroll
+                        for (int r = 0; r < NR; ++r) a[r] += red[wave + q][r][lane];
+                    }
+                }
+                __syncthreads();
+            }
+            if (part == 0 && row_ok) {
+                #pragma unroll
+                for (int r = 0; r < NR; ++r) {
+                    const int t = 4 * g + r;
+                    if (t < p.T) {
+                        c.y[(size_t)t * c.n + rl] = (float)a[r] * (ep_sx[r] * ep_sw);
+                        if constexpr (ACC) {
+                            if (c.acc) c.acc[(size_t)t * c.n + rl] = a[r];
+                        }
+                    }
+                }
             }
         }
+        C = i32x4{0, 0, 0, 0};
+        #pragma unroll
+        for (int r = 0; r < NR; ++r) yp[r] = 0.0f;
+    };
+
+    int mi_cur = 0;
+    TileCtx cur = make_ctx(0, mi_cur);
+    int mi_nxt = mi_cur;
+    TileCtx nxt = make_ctx(1, mi_nxt);
+    #pragma unroll
+    for (int u = 0; u < D; ++u) load_slot(u, cur, u);         // S >= D: all in the first tile
+    for (int it = 0; it < n_iter; ++it) {
+        for (int j = 0; j < S; j += D) {
+            #pragma unroll
+            for (int u = 0; u < D; ++u) {
+                compute_slot(u, cur, j + u);
+                if (u == D - 1 && j + D == S) {                  // the tile's last step: keep its
+                    #pragma unroll                                // epilogue operands before the
+                    for (int r = 0; r < NR; ++r) ep_sx[r] = sxs[u][r];   // slot is refilled
+                    ep_sw = sg[u];
+                }
+                const int jn = j + u + D;                        // step this slot is refilled with
+                if (jn < S) load_slot(u, cur, jn);
+                else load_slot(u, nxt, jn - S);
+            }
+        }
+        tile_end(cur);
+        cur = nxt;
+        mi_cur = mi_nxt;
+        nxt = make_ctx(it + 2, mi_nxt);
     }
 }
 
@@ -324,23 +338,26 @@ __global__ __launch_bounds__(256) void gemv_kernel(const GemvParams p) {
 namespace {
 
 template <int FMT, int WPL, int NR, bool GROUP>
-void launch_t(const GemvParams& gp, int grid, bool fast, hipStream_t st) {
-    if (fast)
-        gemv_kernel<FMT, WPL, NR, GROUP, true><<<dim3(grid), dim3(256), 0, st>>>(gp);
-    else
-        gemv_kernel<FMT, WPL, NR, GROUP, false><<<dim3(grid), dim3(256), 0, st>>>(gp);
+void launch_t(const GemvParams& gp, int grid, bool fast, int d, bool acc, hipStream_t st) {
+    if (fast && !acc) {
+        if (d == 4) gemv_kernel<FMT, WPL, NR, GROUP, true, 4, false><<<dim3(grid), dim3(256), 0, st>>>(gp);
+        else gemv_kernel<FMT, WPL, NR, GROUP, true, 1, false><<<dim3(grid), dim3(256), 0, st>>>(gp);
+    } else if (fast) {
+        if (d == 4) gemv_kernel<FMT, WPL, NR, GROUP, true, 4, true><<<dim3(grid), dim3(256), 0, st>>>(gp);
+        else gemv_kernel<FMT, WPL, NR, GROUP, true, 1, true><<<dim3(grid), dim3(256), 0, st>>>(gp);
+    } else {
+        gemv_kernel<FMT, WPL, NR, GROUP, false, 1, true><<<dim3(grid), dim3(256), 0, st>>>(gp);
+    }
 }
 
 template <int FMT, int WPL>
-void launch_nr(const GemvParams& gp, int grid, int nr, bool group, bool fast, hipStream_t st) {
+void launch_nr(const GemvParams& gp, int grid, int nr, bool group, bool fast, int d, bool acc, hipStream_t st) {
     if (group) {
-        if (nr == 1) launch_t<FMT, WPL, 1, true>(gp, grid, fast, st);
-        else if (nr == 2) launch_t<FMT, WPL, 2, true>(gp, grid, fast, st);
-        else launch_t<FMT, WPL, 4, true>(gp, grid, fast, st);
+        if (nr == 1) launch_t<FMT, WPL, 1, true>(gp, grid, fast, d, acc, st);
+        else launch_t<FMT, WPL, 4, true>(gp, grid, fast, d, acc, st);
     } else {
-        if (nr == 1) launch_t<FMT, WPL, 1, false>(gp, grid, fast, st);
-        else if (nr == 2) launch_t<FMT, WPL, 2, false>(gp, grid, fast, st);
-        else launch_t<FMT, WPL, 4, false>(gp, grid, fast, st);
+        if (nr == 1) launch_t<FMT, WPL, 1, false>(gp, grid, fast, d, acc, st);
+        else launch_t<FMT, WPL, 4, false>(gp, grid, fast, d, acc, st);
     }
 }
 
@@ -357,6 +374,13 @@ int device_cu_count() {
     return cached[dev];
 }
 
+int log2_exact(int v) {   // log2 of a power of two, else -1
+    if (v <= 0 || (v & (v - 1)) != 0) return -1;
+    int l = 0;
+    while ((1 << l) < v) ++l;
+    return l;
+}
+
 }  // namespace
 
 // Launch one gemv over `count` matrices that share fmt, scale mode, group, k
@@ -365,21 +389,22 @@ hipError_t launch_gemv_group(const LinearArgs* mats, int count, hipStream_t stre
     const LinearArgs& a = mats[0];
     const int cpw = a.fmt == FMT_TERNARY ? 16 : (a.fmt == FMT_INT4 ? 8 : 32);
     const bool group = a.scale == LOWBIT_SCALE_GROUP;
-    const int min_bpl = a.fmt == FMT_INT4 ? 8 : 4;   // one int4 MFMA operand is 2 words
-    auto step_k = [&](int b) { return 4 * (b / 4) * cpw; };
-    // bytes per lane per k-step: the widest of 16/8/4 that keeps a scale
-    // group a whole number of steps and that the row length divides (else
-    // the byte-safe loader handles every step)
-    int bpl = 16;
-    if (group) {   // describe() guarantees group % 64 (128 binary) == 0, so min_bpl fits
-        while (bpl > min_bpl && (a.group % step_k(bpl)) != 0) bpl /= 2;
-    } else {
-        while (bpl > min_bpl && a.row_bytes % bpl != 0) bpl /= 2;
-    }
+    const int min_bpl = a.fmt == FMT_INT4 ? 8 : 4;           // one int4 MFMA operand is 2 words
+    auto step_k = [&](int b) { return b * cpw; };            // k per k-step = 4 lanes x b bytes
+    auto group_ok = [&](int b) { return !group || a.group % step_k(b) == 0; };
+    // bytes per lane per k-step: the widest of 16/8/4 whose k-step tiles the
+    // scale groups and the row exactly (FAST path); failing the row, the
+    // widest that tiles the groups (byte-safe path)
+    int bpl = 0;
+    for (int b = 16; b >= min_bpl; b /= 2)
+        if (group_ok(b) && a.row_bytes % (4 * b) == 0) { bpl = b; break; }
+    const bool rows_whole = bpl != 0;
+    if (!rows_whole)
+        for (int b = 16; b >= min_bpl; b /= 2)
+            if (group_ok(b)) { bpl = b; break; }
     const int wpl = bpl / 4;
     const int64_t step_bytes = 4 * (int64_t)bpl;
     const int n_steps = (int)((a.row_bytes + step_bytes - 1) / step_bytes);
-    bool w_aligned = a.row_bytes % bpl == 0;
 
     GemvParams gp;
     gp.n_mats = count;
@@ -388,9 +413,10 @@ hipError_t launch_gemv_group(const LinearArgs* mats, int count, hipStream_t stre
     gp.row_bytes = a.row_bytes;
     gp.n_steps = n_steps;
     gp.spu = group ? a.group / step_k(bpl) : 1;
+    gp.spu_shift = std::max(0, log2_exact(gp.spu));
     gp.G = group ? a.n_groups : 1;
     gp.scale_per_row = a.scale == LOWBIT_SCALE_ROW;
-    gp.q_aligned = a.k % 16 == 0;
+    bool fast = rows_whole && a.k % 16 == 0 && log2_exact(gp.spu) >= 0;
     int tiles = 0;
     for (int i = 0; i < count; ++i) {
         const LinearArgs& b = mats[i];
@@ -399,11 +425,11 @@ hipError_t launch_gemv_group(const LinearArgs* mats, int count, hipStream_t stre
         m.n = b.n;
         m.tile0 = tiles;
         tiles += (b.n + 15) / 16;
-        w_aligned = w_aligned && ((uintptr_t)b.packed % 16 == 0);
-        gp.q_aligned = gp.q_aligned && ((uintptr_t)b.q % 16 == 0);
+        fast = fast && ((uintptr_t)b.packed % 16 == 0) && ((uintptr_t)b.q % 16 == 0);
     }
     gp.total_tiles = tiles;
-    const bool fast = w_aligned && gp.q_aligned;
+    bool any_acc = false;
+    for (int i = 0; i < count; ++i) any_acc = any_acc || mats[i].acc != nullptr;
 
     // k-split: enough wavefronts to fill the chip, whole scale groups per part
     const int cus = device_cu_count();
@@ -413,26 +439,27 @@ hipError_t launch_gemv_group(const LinearArgs* mats, int count, hipStream_t stre
     if (tiles < 2 * cus && units >= 8) ksplit = 4;
     gp.ksplit = ksplit;
     gp.tpw = 4 / ksplit;
-    const int upp = (units + ksplit - 1) / ksplit;
-    gp.part_steps = upp * gp.spu;
+    gp.part_len = ((units + ksplit - 1) / ksplit) * gp.spu;
+    const int d = fast && gp.part_len >= 4 ? 4 : 1;
+    gp.loop_steps = (gp.part_len + d - 1) / d * d;
     gp.n_tile_groups = (tiles + gp.tpw - 1) / gp.tpw;
     const int grid = std::min(gp.n_tile_groups, cus * 8);
-    const int nr = a.t == 1 ? 1 : (a.t == 2 ? 2 : 4);
+    const int nr = a.t == 1 ? 1 : 4;
 
     switch (a.fmt) {
         case FMT_TERNARY:
-            if (wpl == 4) launch_nr<FMT_TERNARY, 4>(gp, grid, nr, group, fast, stream);
-            else if (wpl == 2) launch_nr<FMT_TERNARY, 2>(gp, grid, nr, group, fast, stream);
-            else launch_nr<FMT_TERNARY, 1>(gp, grid, nr, group, fast, stream);
+            if (wpl == 4) launch_nr<FMT_TERNARY, 4>(gp, grid, nr, group, fast, d, any_acc, stream);
+            else if (wpl == 2) launch_nr<FMT_TERNARY, 2>(gp, grid, nr, group, fast, d, any_acc, stream);
+            else launch_nr<FMT_TERNARY, 1>(gp, grid, nr, group, fast, d, any_acc, stream);
             break;
         case FMT_INT4:
-            if (wpl == 4) launch_nr<FMT_INT4, 4>(gp, grid, nr, group, fast, stream);
-            else launch_nr<FMT_INT4, 2>(gp, grid, nr, group, fast, stream);
+            if (wpl == 4) launch_nr<FMT_INT4, 4>(gp, grid, nr, group, fast, d, any_acc, stream);
+            else launch_nr<FMT_INT4, 2>(gp, grid, nr, group, fast, d, any_acc, stream);
             break;
         default:
-            if (wpl == 4) launch_nr<FMT_BINARY, 4>(gp, grid, nr, group, fast, stream);
-            else if (wpl == 2) launch_nr<FMT_BINARY, 2>(gp, grid, nr, group, fast, stream);
-            else launch_nr<FMT_BINARY, 1>(gp, grid, nr, group, fast, stream);
+            if (wpl == 4) launch_nr<FMT_BINARY, 4>(gp, grid, nr, group, fast, d, any_acc, stream);
+            else if (wpl == 2) launch_nr<FMT_BINARY, 2>(gp, grid, nr, group, fast, d, any_acc, stream);
+            else launch_nr<FMT_BINARY, 1>(gp, grid, nr, group, fast, d, any_acc, stream);
             break;
     }
     return hipGetLastError();

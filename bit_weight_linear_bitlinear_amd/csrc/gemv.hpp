@@ -28,12 +28,13 @@ struct GemvParams {
     int G;               // scale groups per row (group mode)
     int scale_per_row;   // tensor/row mode: 1 = scales[n], 0 = scales[0]
     int q_aligned;       // K % 16 == 0 and every q 16-byte aligned
+    int spu_shift;       // log2(spu) when spu is a power of two
     int ksplit;          // wavefronts sharing one tile's k-range (1, 2, 4)
     int tpw;             // tiles per workgroup = 4 / ksplit
-    int part_steps;      // k-steps per part (the last part may run short)
+    int part_len;        // k-steps per part (the last part may run short)
+    int loop_steps;      // part_len rounded up to the prefetch depth
     int total_tiles;
     int n_tile_groups;   // ceil(total_tiles / tpw)
-    int pad_;
     int64_t row_bytes;
     GemvMat m[kGemvMaxMats];
 };
