@@ -45,13 +45,17 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(
-            os.path.join(_HERE, "oracle.c")):
+    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < max(
+            os.path.getmtime(os.path.join(_HERE, f)) for f in ("oracle.c", "oracle.h")):
         _build.build()
     lib = ctypes.CDLL(_LIB_PATH)
     i64, i32, p = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
-    lib.orc_row_bytes.argtypes = [i32, i64]; lib.orc_row_bytes.restype = i64
+    pi32, pi64 = ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int64)
+    lib.orc_layout.argtypes = [i32, i64, i64, pi32, pi64, pi64, pi64]
     lib.orc_n_groups.argtypes = [i32, i64, i64]; lib.orc_n_groups.restype = i64
+    lib.orc_n_scales.argtypes = [i32, i64, i64, i64]; lib.orc_n_scales.restype = i64
+    lib.orc_pack_scales.argtypes = [i32, i64, i64, i64, p, p]
+    lib.orc_unpack_scales.argtypes = [i32, i64, i64, i64, p, p]
     lib.orc_weight_codes.argtypes = [i32, i32, i64, i32, i64, i64, p, p, p]
     lib.orc_pack.argtypes = [i32, i64, i64, p, p]
     lib.orc_unpack.argtypes = [i32, i64, i64, p, p]
@@ -78,16 +82,24 @@ def num_threads() -> int:
     return int(_load().orc_num_threads())
 
 
-def row_bytes(fmt: str, k: int) -> int:
-    return int(_load().orc_row_bytes(FMT[fmt], k))
+def layout(fmt: str, n: int, k: int) -> dict:
+    """Sizes of the tiled packed layout of an [n, k] matrix."""
+    w, st, sk, nb = ctypes.c_int(), ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    _check(_load().orc_layout(FMT[fmt], n, k, ctypes.byref(w), ctypes.byref(st), ctypes.byref(sk),
+                              ctypes.byref(nb)), "layout")
+    return {"wpl": w.value, "n_steps": st.value, "step_k": sk.value, "packed_bytes": nb.value}
 
 
 def n_groups(scale: str, k: int, group: int) -> int:
     return int(_load().orc_n_groups(SCALE[scale], k, group))
 
 
+def n_scales(scale: str, n: int, k: int, group: int) -> int:
+    return int(_load().orc_n_scales(SCALE[scale], n, k, group))
+
+
 def weight_codes(w: np.ndarray, fmt: str, scale: str, group: int = 0, tanh_premap: bool = False):
-    """Latent fp32 W[n, k] -> (codes int8 [n, k], scales fp32 [1] | [n] | [n, G])."""
+    """Latent fp32 W[n, k] -> (codes int8 [n, k], scales fp32 [1] | [n] | [n, G] in natural order)."""
     w = np.ascontiguousarray(w, dtype=np.float32)
     n, k = w.shape
     codes = np.empty((n, k), np.int8)
@@ -103,21 +115,37 @@ def weight_codes(w: np.ndarray, fmt: str, scale: str, group: int = 0, tanh_prema
 
 
 def pack(codes: np.ndarray, fmt: str) -> np.ndarray:
+    """codes int8 [n, k] -> packed uint8 [packed_bytes] (tiled layout)."""
     codes = np.ascontiguousarray(codes, dtype=np.int8)
     n, k = codes.shape
-    out = np.empty((n, row_bytes(fmt, k)), np.uint8)
+    out = np.empty((layout(fmt, n, k)["packed_bytes"],), np.uint8)
     _check(_load().orc_pack(FMT[fmt], n, k, _ptr(codes), _ptr(out)), "pack")
     return out
 
 
-def unpack(packed: np.ndarray, fmt: str, k: int) -> np.ndarray:
-    packed = np.ascontiguousarray(packed, dtype=np.uint8)
-    n = packed.shape[0]
-    if packed.ndim != 2 or packed.shape[1] != row_bytes(fmt, k):
+def unpack(packed: np.ndarray, fmt: str, n: int, k: int) -> np.ndarray:
+    packed = np.ascontiguousarray(packed, dtype=np.uint8).ravel()
+    if packed.size != layout(fmt, n, k)["packed_bytes"]:
         raise OracleError(-1, "unpack extent")
     codes = np.empty((n, k), np.int8)
     _check(_load().orc_unpack(FMT[fmt], n, k, _ptr(packed), _ptr(codes)), "unpack")
     return codes
+
+
+def pack_scales(scales: np.ndarray, scale: str, n: int, k: int, group: int = 0) -> np.ndarray:
+    """Natural-order scales -> the packed artifact's order (group scales tiled)."""
+    nat = np.ascontiguousarray(scales, dtype=np.float32).ravel()
+    out = np.empty((n_scales(scale, n, k, group),), np.float32)
+    _check(_load().orc_pack_scales(SCALE[scale], n, k, group, _ptr(nat), _ptr(out)), "pack_scales")
+    return out
+
+
+def unpack_scales(packed: np.ndarray, scale: str, n: int, k: int, group: int = 0) -> np.ndarray:
+    pk = np.ascontiguousarray(packed, dtype=np.float32).ravel()
+    G = n_groups(scale, k, group) if scale == "group" else 1
+    out = np.empty(((n, G) if scale == "group" else ((n,) if scale == "row" else (1,))), np.float32)
+    _check(_load().orc_unpack_scales(SCALE[scale], n, k, group, _ptr(pk), _ptr(out)), "unpack_scales")
+    return out
 
 
 def act_quant(x: np.ndarray):
@@ -157,16 +185,15 @@ def epilogue(acc: np.ndarray, sx: np.ndarray, scales: np.ndarray, scale: str):
     return y32, y64
 
 
-def linear(packed: np.ndarray, scales: np.ndarray, fmt: str, scale: str, group: int, k: int,
+def linear(packed: np.ndarray, scales: np.ndarray, fmt: str, scale: str, group: int, n: int, k: int,
            q: np.ndarray, sx: np.ndarray):
-    """Whole layer from packed bytes: returns (y32 [t, n], y64 [t, n], acc int64 [t, n, G])."""
-    packed = np.ascontiguousarray(packed, dtype=np.uint8)
-    sc = np.ascontiguousarray(scales, dtype=np.float32)
+    """Whole layer from packed bytes and packed scales: returns (y32 [t, n], y64 [t, n], acc int64 [t, n, G])."""
+    packed = np.ascontiguousarray(packed, dtype=np.uint8).ravel()
+    sc = np.ascontiguousarray(scales, dtype=np.float32).ravel()
     q = np.ascontiguousarray(q, dtype=np.int8)
     sx = np.ascontiguousarray(sx, dtype=np.float32)
-    n = packed.shape[0]
     t = q.shape[0]
-    if q.shape[1] != k:
+    if q.shape[1] != k or packed.size != layout(fmt, n, k)["packed_bytes"] or sc.size != n_scales(scale, n, k, group):
         raise OracleError(-1, "linear shapes")
     G = n_groups(scale, k, group) if scale == "group" else 1
     y32 = np.empty((t, n), np.float32)
@@ -182,5 +209,7 @@ def acc_bound_ok(fmt: str, k: int) -> bool:
 
 
 def quantize_and_pack(w: np.ndarray, fmt: str, scale: str, group: int = 0, tanh_premap: bool = False):
+    """-> (packed bytes, packed scales, codes [n, k], natural-order scales)."""
     codes, scales = weight_codes(w, fmt, scale, group, tanh_premap)
-    return pack(codes, fmt), scales, codes
+    n, k = codes.shape
+    return pack(codes, fmt), pack_scales(scales, scale, n, k, group), codes, scales

@@ -36,22 +36,56 @@ int orc_num_threads(void) {
 /* ------------------------------------------------------------------ layout */
 
 /*
- * Packed row sizes.
- *  binary : [NBT] 0x06E binary pack reference - bit = (1 - s) / 2, packed
- *           little-bit-first along K, ceil(K / 8) bytes per row.
- *  ternary: READING - 2-bit two's-complement fields ([NBT] 0x01A: fixed-width
- *           ternary takes two physical bits; [A1B]: four codes per byte),
- *           grouped in 32-bit words of 16 codes, so rows are whole words.
- *  int4   : READING - 4-bit two's-complement fields, 8 codes per 32-bit word.
+ * Packed layout.  The pages fix the code alphabets and their physical width -
+ * [NBT] 0x06E: binary bit = (1 - s) / 2, packed little-bit-first; [NBT] 0x01A:
+ * two physical bits per ternary code; [A1B]: four ternary codes per byte;
+ * [T4NT]: 15 levels, i.e. 4-bit codes - and leave the arrangement of fields
+ * to the implementation ([NBT] 0x07D: "not one universal physical
+ * representation").  READING (this library's arrangement):
+ *
+ *  field  ternary: 2-bit two's complement (+1 = 01, 0 = 00, -1 = 11, 10 reserved)
+ *         int4   : 4-bit two's complement (-7..+7, 1000 reserved)
+ *         binary : 1 bit, (1 - s) / 2
+ *  word   32 bits holding CPW codes (ternary 16, int4 8, binary 32):
+ *         ternary code j in byte j%4 at bit 2*(j/4); int4 code j in byte j%4,
+ *         low nibble if j < 4 else high; binary code j in byte j/8, bit j%8.
+ *  block  KB consecutive k (ternary, int4 64; binary 128) split in four
+ *         quarters of KB/4 codes, quarter g held by "lane group" g as WB
+ *         words (ternary 1, int4 2, binary 1).
+ *  step   wpl words per (lane group, row) = wpl/WB consecutive blocks,
+ *         SK = 4 * wpl * CPW consecutive k.
+ *  tile   16 consecutive rows.
+ *  order  byte offset of word w of (tile t, step s, lane group g, row r of the
+ *         tile): ((((t * n_steps + s) * 4 + g) * 16 + r) * wpl + w) * 4, where
+ *         word w covers block w / WB, codes (w % WB) * CPW .. of the quarter.
+ *  wpl    the largest of 4, 2, 1 (int4: 4, 2) whose step pads k no further
+ *         than the smallest step does.
+ *  padding rows n >= N of the last tile and codes k >= K are zero fields.
  */
-int64_t orc_row_bytes(int fmt, int64_t k) {
-    if (k < 1) return -1;
-    switch (fmt) {
-        case ORC_TERNARY: return 4 * ((k + 15) / 16);
-        case ORC_BINARY:  return (k + 7) / 8;
-        case ORC_INT4:    return 4 * ((k + 7) / 8);
-        default:          return -1;
+static int fmt_ok(int fmt) { return fmt == ORC_TERNARY || fmt == ORC_BINARY || fmt == ORC_INT4; }
+static int cpw_of(int fmt) { return fmt == ORC_TERNARY ? 16 : (fmt == ORC_INT4 ? 8 : 32); }
+static int kb_of(int fmt) { return fmt == ORC_BINARY ? 128 : 64; }
+static int field_bits(int fmt) { return fmt == ORC_TERNARY ? 2 : (fmt == ORC_INT4 ? 4 : 1); }
+
+int orc_layout(int fmt, int64_t n, int64_t k, int* wpl, int64_t* n_steps, int64_t* step_k,
+               int64_t* packed_bytes) {
+    if (!fmt_ok(fmt) || n < 1 || k < 1) return ORC_E_ARG;
+    const int wmin = fmt == ORC_INT4 ? 2 : 1;
+    const int64_t sk_min = 4 * wmin * cpw_of(fmt);
+    const int64_t padded_min = (k + sk_min - 1) / sk_min * sk_min;
+    int w = 4;
+    for (; w > wmin; w /= 2) {
+        const int64_t sk = 4 * (int64_t)w * cpw_of(fmt);
+        if ((k + sk - 1) / sk * sk == padded_min) break;
     }
+    const int64_t sk = 4 * (int64_t)w * cpw_of(fmt);
+    const int64_t steps = (k + sk - 1) / sk;
+    const int64_t tiles = (n + 15) / 16;
+    if (wpl) *wpl = w;
+    if (n_steps) *n_steps = steps;
+    if (step_k) *step_k = sk;
+    if (packed_bytes) *packed_bytes = tiles * steps * 4 * 16 * w * 4;
+    return 0;
 }
 
 int64_t orc_n_groups(int scale_mode, int64_t k, int64_t group) {
@@ -60,27 +94,60 @@ int64_t orc_n_groups(int scale_mode, int64_t k, int64_t group) {
     return (k + group - 1) / group;
 }
 
-static int fmt_ok(int fmt) { return fmt == ORC_TERNARY || fmt == ORC_BINARY || fmt == ORC_INT4; }
-
-/*
- * Where code k of a row lives.
- *  ternary: word w = k / 16, j = k % 16; byte 4w + (j % 4); bits 2 (j / 4) .. +1.
- *  int4   : word w = k / 8,  j = k % 8;  byte 4w + (j % 4); nibble j / 4 (0 = low).
- *  binary : byte k / 8, bit k % 8.
- */
-static void code_position(int fmt, int64_t k, int64_t* byte, int* shift) {
-    if (fmt == ORC_TERNARY) {
-        int64_t w = k / 16; int j = (int)(k % 16);
-        *byte = 4 * w + (j % 4); *shift = 2 * (j / 4);
-    } else if (fmt == ORC_INT4) {
-        int64_t w = k / 8; int j = (int)(k % 8);
-        *byte = 4 * w + (j % 4); *shift = 4 * (j / 4);
-    } else {
-        *byte = k / 8; *shift = (int)(k % 8);
-    }
+/* group scales are stored [tile][group][16 rows]; tensor [1]; row [n] */
+int64_t orc_n_scales(int scale_mode, int64_t n, int64_t k, int64_t group) {
+    if (scale_mode == ORC_SCALE_TENSOR) return 1;
+    if (scale_mode == ORC_SCALE_ROW) return n;
+    return (n + 15) / 16 * orc_n_groups(scale_mode, k, group) * 16;
 }
 
-static int field_bits(int fmt) { return fmt == ORC_TERNARY ? 2 : (fmt == ORC_INT4 ? 4 : 1); }
+int orc_pack_scales(int scale_mode, int64_t n, int64_t k, int64_t group, const float* natural, float* packed) {
+    const int64_t ns = orc_n_scales(scale_mode, n, k, group);
+    if (ns < 1 || !natural || !packed) return ORC_E_ARG;
+    if (scale_mode != ORC_SCALE_GROUP) {
+        memcpy(packed, natural, (size_t)ns * sizeof(float));
+        return 0;
+    }
+    const int64_t G = orc_n_groups(scale_mode, k, group);
+    memset(packed, 0, (size_t)ns * sizeof(float));
+    for (int64_t r = 0; r < n; ++r)
+        for (int64_t gi = 0; gi < G; ++gi)
+            packed[((r / 16) * G + gi) * 16 + r % 16] = natural[r * G + gi];
+    return 0;
+}
+
+int orc_unpack_scales(int scale_mode, int64_t n, int64_t k, int64_t group, const float* packed, float* natural) {
+    const int64_t ns = orc_n_scales(scale_mode, n, k, group);
+    if (ns < 1 || !natural || !packed) return ORC_E_ARG;
+    if (scale_mode != ORC_SCALE_GROUP) {
+        memcpy(natural, packed, (size_t)ns * sizeof(float));
+        return 0;
+    }
+    const int64_t G = orc_n_groups(scale_mode, k, group);
+    for (int64_t r = 0; r < n; ++r)
+        for (int64_t gi = 0; gi < G; ++gi)
+            natural[r * G + gi] = packed[((r / 16) * G + gi) * 16 + r % 16];
+    return 0;
+}
+
+/* byte offset (from the start of the packed matrix) and bit shift of the
+ * field of code (row, k) */
+static void code_position(int fmt, int wpl, int64_t n_steps, int64_t row, int64_t k, int64_t* byte, int* shift) {
+    const int cpw = cpw_of(fmt), kb = kb_of(fmt), wb = kb / 4 / cpw;
+    const int64_t sk = 4 * (int64_t)wpl * cpw;
+    const int64_t t = row / 16, r = row % 16, s = k / sk, kk = k % sk;
+    const int64_t b = kk / kb, q = kk % kb, g = q / (kb / 4), qq = q % (kb / 4);
+    const int64_t h = qq / cpw, j = qq % cpw;
+    const int64_t w = b * wb + h;
+    const int64_t word = (((t * n_steps + s) * 4 + g) * 16 + r) * wpl + w;
+    if (fmt == ORC_BINARY) {
+        *byte = word * 4 + j / 8;
+        *shift = (int)(j % 8);
+    } else {
+        *byte = word * 4 + j % 4;
+        *shift = (int)(field_bits(fmt) * (j / 4));
+    }
+}
 
 /* code -> field value.  binary: bit = (1 - s) / 2 ([NBT] 0x06E).
  * ternary/int4: the code's two's-complement low bits. */
@@ -102,45 +169,45 @@ static int decode_field(int fmt, int f) {
 
 int orc_pack(int fmt, int64_t n, int64_t k, const int8_t* codes, uint8_t* packed) {
     if (!fmt_ok(fmt) || n < 1 || k < 1 || !codes || !packed) return ORC_E_ARG;
-    const int64_t rb = orc_row_bytes(fmt, k);
-    const int lo = fmt == ORC_TERNARY ? -1 : (fmt == ORC_INT4 ? -7 : -1);
-    const int hi = fmt == ORC_TERNARY ? 1 : (fmt == ORC_INT4 ? 7 : 1);
+    int wpl; int64_t steps, sk, nbytes;
+    orc_layout(fmt, n, k, &wpl, &steps, &sk, &nbytes);
+    const int lo = fmt == ORC_INT4 ? -7 : -1, hi = fmt == ORC_INT4 ? 7 : 1;
     for (int64_t i = 0; i < n * k; ++i) {
         int c = codes[i];
         if (c < lo || c > hi || (fmt == ORC_BINARY && c == 0)) return ORC_E_FORMAT;
     }
-    memset(packed, 0, (size_t)(n * rb));   /* fields past k stay zero */
-    for (int64_t r = 0; r < n; ++r) {
+    memset(packed, 0, (size_t)nbytes);       /* padding fields stay zero */
+    for (int64_t r = 0; r < n; ++r)
         for (int64_t c = 0; c < k; ++c) {
             int64_t byte; int shift;
-            code_position(fmt, c, &byte, &shift);
-            packed[r * rb + byte] |= (uint8_t)(encode_field(fmt, codes[r * k + c]) << shift);
+            code_position(fmt, wpl, steps, r, c, &byte, &shift);
+            packed[byte] |= (uint8_t)(encode_field(fmt, codes[r * k + c]) << shift);
         }
-    }
     return 0;
 }
 
 /* [NBT] 0x06E binary unpack reference and 0x0BB "reserved patterns reject":
- * checks the extent, rejects reserved fields and any nonzero field past k. */
+ * every field slot of every padded row is visited; reserved fields and any
+ * nonzero field outside the logical extent are rejected. */
 int orc_unpack(int fmt, int64_t n, int64_t k, const uint8_t* packed, int8_t* codes) {
     if (!fmt_ok(fmt) || n < 1 || k < 1 || !codes || !packed) return ORC_E_ARG;
-    const int64_t rb = orc_row_bytes(fmt, k);
+    int wpl; int64_t steps, sk, nbytes;
+    orc_layout(fmt, n, k, &wpl, &steps, &sk, &nbytes);
     const int bits = field_bits(fmt);
-    const int64_t slots = rb * 8 / bits;    /* every field slot of a row */
-    for (int64_t r = 0; r < n; ++r) {
-        for (int64_t c = 0; c < slots; ++c) {
+    const int64_t rows = (n + 15) / 16 * 16, cols = steps * sk;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c) {
             int64_t byte; int shift;
-            code_position(fmt, c, &byte, &shift);
-            int f = (packed[r * rb + byte] >> shift) & ((1 << bits) - 1);
-            if (c >= k) {
-                if (f != 0) return ORC_E_FORMAT;        /* noncanonical padding */
+            code_position(fmt, wpl, steps, r, c, &byte, &shift);
+            int f = (packed[byte] >> shift) & ((1 << bits) - 1);
+            if (r >= n || c >= k) {
+                if (f != 0) return ORC_E_FORMAT;      /* noncanonical padding */
                 continue;
             }
             int v = decode_field(fmt, f);
-            if (v == 99) return ORC_E_FORMAT;           /* reserved pattern */
+            if (v == 99) return ORC_E_FORMAT;          /* reserved pattern */
             codes[r * k + c] = (int8_t)v;
         }
-    }
     return 0;
 }
 
@@ -360,12 +427,15 @@ int orc_linear(int fmt, int scale_mode, int64_t group, int64_t n, int64_t k,
     const int64_t G = orc_n_groups(scale_mode, k, group);
     if (G < 1) return ORC_E_ARG;
     int8_t* codes = (int8_t*)malloc((size_t)(n * k));
-    if (!codes) return ORC_E_ARG;
-    int rc = orc_unpack(fmt, n, k, packed, codes);
+    float* nat = (float*)malloc((size_t)(scale_mode == ORC_SCALE_GROUP ? n * G : (scale_mode == ORC_SCALE_ROW ? n : 1)) * sizeof(float));
+    int rc = (!codes || !nat) ? ORC_E_ARG : 0;
+    if (rc == 0) rc = orc_unpack(fmt, n, k, packed, codes);
+    if (rc == 0) rc = orc_unpack_scales(scale_mode, n, k, group, scales, nat);
     if (rc == 0)
         rc = orc_int_matmul(t, n, k, scale_mode == ORC_SCALE_GROUP ? group : 0, q, codes, acc);
     if (rc == 0)
-        rc = orc_epilogue(scale_mode, t, n, G, acc, sx, scales, y32, y64);
+        rc = orc_epilogue(scale_mode, t, n, G, acc, sx, nat, y32, y64);
     free(codes);
+    free(nat);
     return rc;
 }

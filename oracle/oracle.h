@@ -9,7 +9,8 @@
  * Conventions (all arrays row-major, caller-owned):
  *   W latent  float [n, k]         codes int8 [n, k]
  *   x         float [t, k]         q     int8 [t, k]      sx float [t]
- *   scales    float [1] | [n] | [n, G] with G = ceil(k / group)
+ *   scales    float [1] | [n] | [n, G] with G = ceil(k / group)  ("natural" order;
+ *             the packed artifact stores group scales tiled, orc_pack_scales)
  *   acc       int64 [t, n, G]  (G = 1 unless group scales)
  *   y         float [t, n] and double [t, n]
  *
@@ -41,15 +42,21 @@ extern "C" {
 #define ORC_ROW_NONFINITE 1
 #define ORC_ROW_OVERFLOW  2
 
-/* bytes per packed row (the layout each format defines) */
-int64_t orc_row_bytes(int fmt, int64_t k);
+/* Tiled packed layout: rows in tiles of 16, k in steps of `wpl` 32-bit words
+ * per (lane group, row); see oracle.c.  Returns 0 and fills the sizes. */
+int orc_layout(int fmt, int64_t n, int64_t k, int* wpl, int64_t* n_steps, int64_t* step_k,
+               int64_t* packed_bytes);
 int64_t orc_n_groups(int scale_mode, int64_t k, int64_t group);
+/* scale array sizes and the tiled order of group scales */
+int64_t orc_n_scales(int scale_mode, int64_t n, int64_t k, int64_t group);
+int orc_pack_scales(int scale_mode, int64_t n, int64_t k, int64_t group, const float* natural, float* packed);
+int orc_unpack_scales(int scale_mode, int64_t n, int64_t k, int64_t group, const float* packed, float* natural);
 
 /* latent weights -> codes + fp32 scales (premap: 1 = w -> 3 tanh(w/3) first) */
 int orc_weight_codes(int fmt, int scale_mode, int64_t group, int premap,
                      int64_t n, int64_t k, const float* w, int8_t* codes, float* scales);
 
-/* codes <-> packed bytes */
+/* codes <-> packed bytes (tiled layout) */
 int orc_pack(int fmt, int64_t n, int64_t k, const int8_t* codes, uint8_t* packed);
 int orc_unpack(int fmt, int64_t n, int64_t k, const uint8_t* packed, int8_t* codes);
 
@@ -67,7 +74,8 @@ int orc_epilogue(int scale_mode, int64_t t, int64_t n, int64_t n_groups,
                  const int64_t* acc, const float* sx, const float* scales,
                  float* y32, double* y64);
 
-/* whole linear from packed bytes: unpack, integer product, epilogue */
+/* whole linear from packed bytes and packed (tiled) scales: unpack, integer
+ * product, epilogue */
 int orc_linear(int fmt, int scale_mode, int64_t group, int64_t n, int64_t k,
                const uint8_t* packed, const float* scales,
                int64_t t, const int8_t* q, const float* sx,

@@ -116,25 +116,51 @@ def test_binary_total_sign_rule():
     assert s[0] == np.float32(float(sum(Fraction(abs(float(v))) for v in w[0]) / 8))
 
 
+def _words_to_row_stream(packed, fmt, n, k):
+    """Gather the packed words back into per-row order by the documented
+    offset rule (the word order is this library's own; the test only needs the
+    bit order *within* words, which the page fixes)."""
+    lay = oracle.layout(fmt, n, k)
+    wpl, steps, sk = lay["wpl"], lay["n_steps"], lay["step_k"]
+    cpw = 32
+    kb = 128
+    words = packed.view(np.uint32)
+    out = np.zeros((n, steps * sk // 32), np.uint32)
+    for r in range(n):
+        for s in range(steps):
+            for g in range(4):
+                for w in range(wpl):
+                    src = (((r // 16 * steps + s) * 4 + g) * 16 + r % 16) * wpl + w
+                    kpos = s * sk + w * kb + g * (kb // 4)
+                    out[r, kpos // cpw] = words[src]
+    return out.view(np.uint8)
+
+
 def test_binary_pack_matches_page_reference_packer():
-    """M8.8 0x06E: bits = (1 - s) / 2 packed with numpy.packbits(axis=1,
-    bitorder='little'); unused tail bits zero."""
+    """M8.8 0x06E: bits = (1 - s) / 2 packed little-bit-first (numpy.packbits
+    with bitorder='little'); unused tail bits zero.  Within each 32-bit word
+    the packed artifact keeps exactly that bit order."""
     rng = np.random.default_rng(1)
-    for k in (1, 7, 8, 9, 63, 192, 200):
-        s = rng.choice(np.array([-1, 1], np.int8), size=(5, k))
+    for n, k in ((5, 1), (5, 7), (3, 8), (17, 9), (2, 63), (4, 192), (3, 200), (1, 300)):
+        s = rng.choice(np.array([-1, 1], np.int8), size=(n, k))
         ref = np.packbits(((1 - s.astype(np.int8)) // 2).astype(np.uint8), axis=1, bitorder="little")
         got = oracle.pack(s, "binary")
-        assert got.shape == ref.shape and (got == ref).all()
-        back = oracle.unpack(got, "binary", k)
-        assert (back == s).all()
+        stream = _words_to_row_stream(got, "binary", n, k)
+        assert (stream[:, :ref.shape[1]] == ref).all()
+        assert (stream[:, ref.shape[1]:] == 0).all()
+        assert (oracle.unpack(got, "binary", n, k) == s).all()
 
 
 def test_binary_unpack_rejects_noncanonical_padding():
     s = np.ones((2, 9), np.int8)
     p = oracle.pack(s, "binary")
-    p[1, 1] |= 0x80                   # a tail bit past k = 9
+    p[1] |= 0x80                      # a tail bit past k = 9
     with pytest.raises(oracle.OracleError):
-        oracle.unpack(p, "binary", 9)
+        oracle.unpack(p, "binary", 2, 9)
+    p2 = oracle.pack(s, "binary")
+    p2[2 * 4] |= 0x01                 # row 2 of the tile is padding (n = 2)
+    with pytest.raises(oracle.OracleError):
+        oracle.unpack(p2, "binary", 2, 9)
     with pytest.raises(oracle.OracleError):
         oracle.pack(np.zeros((1, 4), np.int8), "binary")   # zero is not binary
 
@@ -180,47 +206,78 @@ def test_int4_ties_round_half_even():
 # ------------------------------------------------------------ layouts / pack
 
 def test_layout_golden_bytes():
-    for case in _golden("layout_examples.json")["cases"]:
-        k = case["k"]
-        if case["fmt"] == "binary":
-            codes = np.array([case["signs"]], np.int8)
+    g = _golden("layout_examples.json")
+    for case in g["cases"]:
+        n, k, fmt = case["n"], case["k"], case["fmt"]
+        lay = oracle.layout(fmt, n, k)
+        assert (lay["wpl"], lay["n_steps"], lay["packed_bytes"]) == (case["wpl"], case["n_steps"], case["packed_bytes"])
+        if fmt == "binary":
+            codes = np.ones((n, k), np.int8)
+            for r, c in case["minus_ones"]:
+                codes[r, c] = -1
         else:
-            codes = np.zeros((1, k), np.int8)
-            for key, v in case["nonzero_codes"].items():
-                codes[0, int(key)] = v
-        p = oracle.pack(codes, case["fmt"])
-        assert p[0].tolist() == case["bytes"], case["fmt"]
-        assert (oracle.unpack(p, case["fmt"], k) == codes).all()
+            codes = np.zeros((n, k), np.int8)
+            for r, c, v in case["codes"]:
+                codes[r, c] = v
+        p = oracle.pack(codes, fmt)
+        expect = np.zeros(case["packed_bytes"], np.uint8)
+        for off, v in case["bytes"].items():
+            expect[int(off)] = v
+        assert (p == expect).all(), fmt
+        assert (oracle.unpack(p, fmt, n, k) == codes).all()
+    sc = g["scales"]
+    nat = np.zeros((sc["n"], sc["groups"]), np.float32)
+    nat[sc["row"], sc["group"]] = 5.0
+    packed = oracle.pack_scales(nat, "group", sc["n"], sc["groups"] * 64, 64)
+    assert packed.size == sc["size"] and packed[sc["index"]] == 5.0 and packed.sum() == 5.0
+    assert (oracle.unpack_scales(packed, "group", sc["n"], sc["groups"] * 64, 64) == nat).all()
 
 
 @pytest.mark.parametrize("fmt,lo,hi", [("ternary", -1, 1), ("int4", -7, 7), ("binary", -1, 1)])
 def test_pack_roundtrip_random(fmt, lo, hi):
     rng = np.random.default_rng(3)
-    for k in (1, 3, 15, 16, 17, 33, 100, 257):
-        c = rng.integers(lo, hi + 1, size=(4, k)).astype(np.int8)
+    for n, k in ((1, 1), (4, 3), (17, 15), (3, 16), (33, 17), (5, 100), (2, 257), (16, 1024), (20, 1300)):
+        c = rng.integers(lo, hi + 1, size=(n, k)).astype(np.int8)
         if fmt == "binary":
             c[c == 0] = 1
         p = oracle.pack(c, fmt)
-        assert p.shape == (4, oracle.row_bytes(fmt, k))
-        assert (oracle.unpack(p, fmt, k) == c).all()
+        assert p.size == oracle.layout(fmt, n, k)["packed_bytes"]
+        assert (oracle.unpack(p, fmt, n, k) == c).all()
+        # every code occupies its own field: flipping one code changes the packing
+        c2 = c.copy()
+        c2[n // 2, k // 2] = -c2[n // 2, k // 2] if c2[n // 2, k // 2] != 0 else 1
+        assert (oracle.pack(c2, fmt) != p).sum() >= 1
+
+
+def test_layout_step_choice():
+    """wpl is the widest step that adds no padding beyond the smallest step."""
+    assert oracle.layout("ternary", 1, 2560)["wpl"] == 4       # 2560 = 10 x 256
+    assert oracle.layout("ternary", 1, 192)["wpl"] == 1        # 192 = 3 x 64, not a multiple of 128
+    assert oracle.layout("ternary", 1, 9728)["wpl"] == 4
+    assert oracle.layout("binary", 1, 192)["wpl"] == 2         # both 128 and 256 pad 192 to 256
+    assert oracle.layout("binary", 1, 768)["wpl"] == 2
+    assert oracle.layout("int4", 1, 1280)["wpl"] == 4
+    assert oracle.layout("int4", 1, 20)["wpl"] == 2
+    for fmt, bits in (("ternary", 2), ("int4", 4), ("binary", 1)):
+        lay = oracle.layout(fmt, 32, 4096)
+        assert lay["packed_bytes"] * 8 == 32 * 4096 * bits      # no padding when shapes align
 
 
 def test_reserved_patterns_and_tails_rejected():
     """M8.8 0x0BB: pack/unpack preserves valid symbols, reserved patterns reject."""
     c = np.zeros((1, 16), np.int8)
     p = oracle.pack(c, "ternary")
-    p[0, 2] = 0b10                        # ternary field 10 is reserved
+    p[2] = 0b10                           # ternary field 10 is reserved
     with pytest.raises(oracle.OracleError):
-        oracle.unpack(p, "ternary", 16)
-    c4 = np.zeros((1, 8), np.int8)
-    p4 = oracle.pack(c4, "int4")
-    p4[0, 1] = 0x80                       # int4 nibble 1000 (-8) is reserved
+        oracle.unpack(p, "ternary", 1, 16)
+    p4 = oracle.pack(np.zeros((1, 8), np.int8), "int4")
+    p4[1] = 0x08                          # int4 nibble 1000 (-8) is reserved
     with pytest.raises(oracle.OracleError):
-        oracle.unpack(p4, "int4", 8)
+        oracle.unpack(p4, "int4", 1, 8)
     pt = oracle.pack(np.ones((1, 5), np.int8), "ternary")
-    pt[0, 3] |= 0x40                      # field of k = 15 > 5: noncanonical tail
+    pt[3] |= 0x40                         # field of k = 15 > 5: noncanonical tail
     with pytest.raises(oracle.OracleError):
-        oracle.unpack(pt, "ternary", 5)
+        oracle.unpack(pt, "ternary", 1, 5)
     with pytest.raises(oracle.OracleError):
         oracle.pack(np.full((1, 4), 2, np.int8), "ternary")
     with pytest.raises(oracle.OracleError):
@@ -367,9 +424,9 @@ def test_acc_bound():
     assert oracle.acc_bound_ok("ternary", kmax_t) and not oracle.acc_bound_ok("ternary", kmax_t + 1)
     kmax_4 = (2**31 - 1) // (127 * 7)
     assert oracle.acc_bound_ok("int4", kmax_4) and not oracle.acc_bound_ok("int4", kmax_4 + 1)
-    big = np.zeros((1, 1), np.uint8)
+    big = np.zeros(oracle.layout("int4", 1, kmax_4 + 1)["packed_bytes"], np.uint8)
     with pytest.raises(oracle.OracleError):
-        oracle.linear(big, np.ones(1, np.float32), "int4", "tensor", 0, kmax_4 + 1,
+        oracle.linear(big, np.ones(1, np.float32), "int4", "tensor", 0, 1, kmax_4 + 1,
                       np.zeros((1, kmax_4 + 1), np.int8), np.ones(1, np.float32))
 
 
@@ -403,9 +460,9 @@ def test_linear_matches_dense_fp64_reconstruction():
     for fmt, scale, group, pre in [("ternary", "tensor", 0, False), ("ternary", "group", 128, False),
                                    ("binary", "row", 0, False), ("int4", "row", 0, True),
                                    ("int4", "group", 64, False), ("binary", "group", 128, False)]:
-        packed, sc, codes = oracle.quantize_and_pack(w, fmt, scale, group, pre)
+        packed, psc, codes, sc = oracle.quantize_and_pack(w, fmt, scale, group, pre)
         q, sx, _ = oracle.act_quant(x)
-        y32, y64, acc = oracle.linear(packed, sc, fmt, scale, group, 300, q, sx)
+        y32, y64, acc = oracle.linear(packed, psc, fmt, scale, group, 37, 300, q, sx)
         if scale == "group":
             G = sc.shape[1]
             wdq = (codes.astype(np.float64).reshape(37, -1) *
