@@ -279,10 +279,10 @@ def sampled_check(p: Pass, picks, rows_per=48, seed=0):
         w = workloads.latent_weights(wl.index, layer, mi, m.n, m.k)[rows]
         if wl.scale == "tensor":
             raise RuntimeError("sampled rows need row-local scales")
-        pk, sc, _ = oracle.quantize_and_pack(w, wl.fmt, wl.scale, wl.group, wl.tanh_premap)
+        pk, sc, _, _ = oracle.quantize_and_pack(w, wl.fmt, wl.scale, wl.group, wl.tanh_premap)
         q_ref, sx_ref, _ = oracle.act_quant(p.xs[i])
         assert (q.cpu().numpy() == q_ref).all(), "activation codes differ"
-        y32, y64, acc_ref = oracle.linear(pk, sc, wl.fmt, wl.scale, wl.group, m.k, q_ref, sx_ref)
+        y32, y64, acc_ref = oracle.linear(pk, sc, wl.fmt, wl.scale, wl.group, len(rows), m.k, q_ref, sx_ref)
         a = acc.cpu().numpy()[:, rows]
         assert (a == acc_ref).all(), f"matrix {i}: accumulators differ"
         yy = y.cpu().numpy()[:, rows].astype(np.float64)
@@ -308,7 +308,7 @@ def cpu_baseline(wl, tokens, budget_s=12.0, sample_layers=4):
     def prep(item):
         layer, mi, m = item
         w = workloads.latent_weights(wl.index, layer, mi, m.n, m.k)
-        pk, sc, _ = oracle.quantize_and_pack(w, wl.fmt, wl.scale, wl.group, wl.tanh_premap)
+        pk, sc, _, _ = oracle.quantize_and_pack(w, wl.fmt, wl.scale, wl.group, wl.tanh_premap)
         x = workloads.workload_activations(wl, layer, mi, tokens, m.k)
         return m, pk, sc, x
 
@@ -319,7 +319,7 @@ def cpu_baseline(wl, tokens, budget_s=12.0, sample_layers=4):
         for m, pk, sc, x in prepped:
             t0 = time.perf_counter()
             q, sx, _ = oracle.act_quant(x)
-            oracle.linear(pk, sc, wl.fmt, wl.scale, wl.group, m.k, q, sx)
+            oracle.linear(pk, sc, wl.fmt, wl.scale, wl.group, m.n, m.k, q, sx)
             spent += time.perf_counter() - t0
             nbytes += (pk.size + 4 * sc.size + tokens * m.k + 4 * tokens + 4 * tokens * m.n
                        + tokens * (5 * m.k + 4))

@@ -46,12 +46,13 @@ _lib = ctypes.CDLL(LIB_PATH)
 class lowbit_desc(ctypes.Structure):
     _fields_ = [("format", ctypes.c_int32), ("scale", ctypes.c_int32), ("n", ctypes.c_int32),
                 ("k", ctypes.c_int32), ("group", ctypes.c_int32), ("flags", ctypes.c_int32),
-                ("row_bytes", ctypes.c_int64), ("packed_bytes", ctypes.c_int64),
-                ("n_groups", ctypes.c_int64), ("n_scales", ctypes.c_int64)]
+                ("wpl", ctypes.c_int32), ("step_k", ctypes.c_int32), ("n_steps", ctypes.c_int64),
+                ("packed_bytes", ctypes.c_int64), ("n_groups", ctypes.c_int64), ("n_scales", ctypes.c_int64)]
 
     def __repr__(self):
         return (f"lowbit_desc(format={self.format}, scale={self.scale}, n={self.n}, k={self.k}, "
-                f"group={self.group}, flags={self.flags}, row_bytes={self.row_bytes}, "
+                f"group={self.group}, flags={self.flags}, wpl={self.wpl}, step_k={self.step_k}, "
+                f"n_steps={self.n_steps}, "
                 f"packed_bytes={self.packed_bytes}, n_groups={self.n_groups}, n_scales={self.n_scales})")
 
 

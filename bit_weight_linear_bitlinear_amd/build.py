@@ -19,7 +19,8 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "liblowbit.so")
 ARCH = os.environ.get("LOWBIT_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["act_quant.hip", "gemv.hip", "gemm.hip", "lowbit_host.cpp"]
+SOURCES = ["act_quant.hip", "gemv.hip", "gemv_ternary.hip", "gemv_int4.hip", "gemv_binary.hip", "gemm.hip",
+           "lowbit_host.cpp"]
 
 COMMON = ["-std=c++17", "-O3", "-fPIC", "-ffp-contract=off", "-fno-fast-math",
           "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-function"]

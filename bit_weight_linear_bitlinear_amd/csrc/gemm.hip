@@ -29,14 +29,15 @@ struct GemmArgs {
     const float* sx;
     float* y;
     int32_t* acc;
-    int64_t row_bytes;
+    int wpl;            // packed layout: words per (lane group, row) per layout k-step
+    int lay_steps;      // packed layout: k-steps per row
+    int n_rows_pad;     // 16 * ceil(N / 16): rows present in the packed buffer
     int T, N, K;
     int n_steps;        // ceil(K / 128)
     int group;          // group mode: columns per group
     int G;              // group mode: groups per row (else 1)
     int scale_per_row;
     int q_aligned;      // K % 16 == 0 and q 16-byte aligned
-    int w_aligned;      // row_bytes % 16 == 0 and packed 16-byte aligned
 };
 
 constexpr int BM = 128, BN = 128, BK = 128;
@@ -61,14 +62,18 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     const int g = lane >> 4, rl = lane & 15;
     const int wm = wave >> 1, wn = wave & 1;
     const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
-    const bool q_aligned = a.q_aligned != 0, w_aligned = a.w_aligned != 0;
+    const bool q_aligned = a.q_aligned != 0;
 
     // ---- global -> register staging: 4 x 16 B of activations per thread
-    // (binary: 2 x 32 B chunks), and the packed weight tile in 16 B pieces.
-    constexpr int B_CHUNKS = BN * WB / 16;                 // 16 B pieces in the weight tile
-    constexpr int B_PER_THREAD = (B_CHUNKS + 255) / 256;
+    // (binary: 2 x 32 B chunks), and the weight tile's packed words gathered
+    // from the tiled layout into per-row order (word i of a row's 128-k slice:
+    // block i / (4 * WB), lane-group quarter, half).
+    constexpr int B_WORDS = BN * WB / 4;                   // words in the weight tile
+    constexpr int B_PER_THREAD = B_WORDS / 256;
+    constexpr int KBLK = FMT == FMT_BINARY ? 128 : 64;     // k per layout block
+    constexpr int WBW = FMT == FMT_INT4 ? 2 : 1;           // words per lane group per block
     i32x4 ra[4];
-    i32x4 rb[B_PER_THREAD];
+    uint32_t rb[B_PER_THREAD];
 
     // activation pieces: 16 B (ternary, int4) or 32 B (binary, so one thread
     // can permute a whole 32-code word's worth of activations)
@@ -103,27 +108,19 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
         }
     };
     auto load_b = [&](int step) {
+        const int nb_step = a.wpl / WBW;                   // layout blocks per layout k-step
         #pragma unroll
         for (int i = 0; i < B_PER_THREAD; ++i) {
             const int c = tid + 256 * i;
-            i32x4 v = {0, 0, 0, 0};
-            if (c < B_CHUNKS) {
-                const int r = c / (WB / 16), off = (c % (WB / 16)) * 16;
-                const int n = n0 + r;
-                const int64_t boff = (int64_t)step * WB + off;
-                if (n < a.N && boff < a.row_bytes) {
-                    const uint8_t* p = a.packed + (size_t)n * a.row_bytes + boff;
-                    const int64_t rem = a.row_bytes - boff;
-                    if (w_aligned) {
-                        v = *reinterpret_cast<const i32x4*>(p);
-                    } else {
-                        #pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const int64_t vj = rem - 4 * j;
-                            v[j] = vj <= 0 ? 0 : (int32_t)load_u32_partial(p + 4 * j, vj < 4 ? (int)vj : 4);
-                        }
-                    }
-                }
+            const int r = c / (WB / 4), wi = c % (WB / 4);
+            const int b = wi / (4 * WBW), gq = (wi / WBW) % 4, h = wi % WBW;
+            const int blk = step * (BK / KBLK) + b;          // layout block along k
+            const int ls = blk / nb_step, w = (blk % nb_step) * WBW + h;
+            const int n = n0 + r;
+            uint32_t v = 0;
+            if (n < a.n_rows_pad && ls < a.lay_steps) {
+                const size_t off = ((((size_t)(n >> 4) * a.lay_steps + ls) * 4 + gq) * 16 + (n & 15)) * a.wpl + w;
+                v = reinterpret_cast<const uint32_t*>(a.packed)[off];
             }
             rb[i] = v;
         }
@@ -150,12 +147,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
         #pragma unroll
         for (int i = 0; i < B_PER_THREAD; ++i) {
             const int c = tid + 256 * i;
-            if (c < B_CHUNKS) {
-                const int r = c / (WB / 16), off = (c % (WB / 16)) * 16;
-                u32x2* d = reinterpret_cast<u32x2*>(Bs + r * BS + off);
-                d[0] = u32x2{(uint32_t)rb[i][0], (uint32_t)rb[i][1]};
-                d[1] = u32x2{(uint32_t)rb[i][2], (uint32_t)rb[i][3]};
-            }
+            const int r = c / (WB / 4), wi = c % (WB / 4);
+            *reinterpret_cast<uint32_t*>(Bs + r * BS + 4 * wi) = rb[i];
         }
     };
 
@@ -180,7 +173,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
         #pragma unroll
         for (int tj = 0; tj < 4; ++tj) {
             const int n = n0 + wn * 64 + tj * 16 + rl;
-            const float sg = n < a.N ? a.scales[(size_t)n * a.G + gi] : 0.0f;
+            const float sg = n < a.N ? a.scales[((size_t)(n >> 4) * a.G + gi) * 16 + (n & 15)] : 0.0f;   // tiled
             #pragma unroll
             for (int ti = 0; ti < 4; ++ti) {
                 #pragma unroll
@@ -284,13 +277,13 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
 hipError_t launch_gemm(const LinearArgs& a, hipStream_t stream) {
     GemmArgs ga;
     ga.packed = a.packed; ga.scales = a.scales; ga.q = a.q; ga.sx = a.sx; ga.y = a.y; ga.acc = a.acc;
-    ga.row_bytes = a.row_bytes; ga.T = a.t; ga.N = a.n; ga.K = a.k;
+    ga.wpl = a.wpl; ga.lay_steps = a.n_steps; ga.n_rows_pad = (a.n + 15) / 16 * 16;
+    ga.T = a.t; ga.N = a.n; ga.K = a.k;
     ga.n_steps = (a.k + BK - 1) / BK;
     ga.group = a.scale == LOWBIT_SCALE_GROUP ? a.group : 0;
     ga.G = a.scale == LOWBIT_SCALE_GROUP ? a.n_groups : 1;
     ga.scale_per_row = a.scale == LOWBIT_SCALE_ROW;
     ga.q_aligned = (a.k % 16 == 0) && ((uintptr_t)a.q % 16 == 0);
-    ga.w_aligned = (a.row_bytes % 16 == 0) && ((uintptr_t)a.packed % 16 == 0);
     dim3 grid((unsigned)((a.n + BN - 1) / BN), (unsigned)((a.t + BM - 1) / BM));
     const bool group = a.scale == LOWBIT_SCALE_GROUP;
     switch (a.fmt) {

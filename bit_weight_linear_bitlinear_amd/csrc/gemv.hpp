@@ -2,11 +2,13 @@
 // weight matrices of equal k, format, scale mode and token count).
 #pragma once
 
+#include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace lowbit {
 
-constexpr int kGemvMaxMats = 40;   // matrices per launch (kernel-argument space)
+constexpr int kGemvMaxMats = 40;     // matrices per launch (kernel-argument space)
+constexpr int kGemvLdsA = 56 * 1024; // activation bytes a workgroup may stage in LDS
 
 struct GemvMat {
     const uint8_t* packed;
@@ -16,27 +18,44 @@ struct GemvMat {
     float* y;
     int32_t* acc;        // nullable
     int n;               // rows
-    int tile0;           // first global 16-row tile of this matrix
+    int n_tiles;         // ceil(n / 16)
 };
 
 struct GemvParams {
     int n_mats;
     int K;
     int T;               // tokens, 1..16
-    int n_steps;         // k-steps per row
-    int spu;             // k-steps per scale group (1 unless group mode)
+    int n_steps;         // k-steps per row (packed layout)
     int G;               // scale groups per row (group mode)
+    int upg;             // group mode: scale units per group
+    int upg_shift;       // log2(upg), or -1 when upg is not a power of two
+    uint32_t upg_magic;  // ceil(2^32 / upg): x / upg = umulhi(x, magic) for the small x used
     int scale_per_row;   // tensor/row mode: 1 = scales[n], 0 = scales[0]
-    int q_aligned;       // K % 16 == 0 and every q 16-byte aligned
-    int spu_shift;       // log2(spu) when spu is a power of two
     int ksplit;          // wavefronts sharing one tile's k-range (1, 2, 4)
-    int tpw;             // tiles per workgroup = 4 / ksplit
+    int ksplit_log;
     int part_len;        // k-steps per part (the last part may run short)
-    int loop_steps;      // part_len rounded up to the prefetch depth
-    int total_tiles;
-    int n_tile_groups;   // ceil(total_tiles / tpw)
-    int64_t row_bytes;
+    int tiles_per_wg;    // 4 / ksplit
+    int stride;          // LDS bytes per staged token row (k padded + 16)
+    int q_vec;           // k % 16 == 0 and every q 16-byte aligned
+    int lds_a_bytes;     // T * stride when activations are staged in LDS, else 0
+    int wg_start[kGemvMaxMats + 1];   // first workgroup of each matrix (ascending)
     GemvMat m[kGemvMaxMats];
 };
+
+// Launch configuration chosen on the host.
+struct GemvCfg {
+    int wpl;             // packed words per lane per k-step
+    int nr;              // C registers per lane holding live tokens: 1 (t = 1) or 4
+    int sps;             // group mode: scale units per k-step (1, 2, 4); 0 = tensor/row scales
+    bool lds_a;          // activations staged in LDS (else read from global memory)
+    bool acc;            // some matrix wants the integer products
+    int grid;
+    size_t lds_bytes;
+};
+
+// Per-format launchers (gemv_ternary.hip, gemv_int4.hip, gemv_binary.hip).
+hipError_t gemv_launch_ternary(const GemvParams& p, const GemvCfg& c, hipStream_t stream);
+hipError_t gemv_launch_int4(const GemvParams& p, const GemvCfg& c, hipStream_t stream);
+hipError_t gemv_launch_binary(const GemvParams& p, const GemvCfg& c, hipStream_t stream);
 
 }  // namespace lowbit

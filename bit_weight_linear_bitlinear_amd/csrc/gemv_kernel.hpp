@@ -1,0 +1,331 @@
+// gemv_kernel.hpp - decode-shaped low-bit product: t <= 16 tokens per launch,
+// one or many weight matrices of equal k per launch.
+//
+// What it computes (M8.8 "Native Binary and Ternary Transformers", 0x02D,
+// 0x05D, 0x09C):  acc[t, n] = sum_k q[t, k] * code[n, k] exactly in int32,
+// then y = fp32 rescale (tensor/row scales) or a sum of per-group rescaled
+// partials (group scales).
+//
+// Why this shape: decode streams each packed weight byte once (decode has a
+// small token dimension and re-reads large weight matrices every token,
+// 0x09B), so the kernel is HBM-bound and the work per packed byte must stay
+// small.  Per 16 codes it spends 7 VALU ops (shift + mask decode) and hands
+// the multiply-accumulate to one quarter of an i8 MFMA; the token dimension
+// (<= 16) rides in the MFMA's M side, so t = 1 and t = 16 stream the same
+// weight bytes.
+//
+// Mapping.  A 16-row tile of W is one MFMA column block: lane l holds weight
+// row (l % 16) and lane group (l / 16) holds a quarter of every block, which
+// is exactly how the packed layout orders a (tile, k-step) - so a wavefront
+// reads one k-step of its tile as ONE contiguous 256 * wpl-byte block, one
+// 4 * wpl-byte load per lane (1 KB per wavefront for wpl = 4).  Each
+// wavefront keeps the loads of the next D k-steps in flight (a register ring,
+// refilled right after each step is consumed).  The activation codes (the
+// MFMA A operand: tokens x k) are staged once per workgroup in LDS, zero
+// padded to whole k-steps, and read from there; binary activations are staged
+// already permuted to the packbits code order.  When t * k is too large for
+// LDS they ride in the register ring instead, read from L2.
+//
+// A workgroup is 4 wavefronts on 4 / ksplit consecutive tiles of ONE matrix;
+// `ksplit` wavefronts share a tile's k-range and add their partials in LDS in
+// a fixed order.  Group scales are applied per scale unit (a whole number of
+// MFMA blocks inside one group): at a group's last unit the int32 partial is
+// converted and accumulated in fp32 with the group's scale.
+#pragma once
+
+#include "device_common.hpp"
+#include "gemv.hpp"
+
+namespace lowbit {
+
+constexpr int kGemvD = 4;   // k-steps of weight loads in flight per wavefront
+
+template <int FMT, int WPL> struct GemvShape {
+    static constexpr int kKB = FMT == FMT_BINARY ? 128 : 64;    // k per block (one MFMA k-extent per quarter)
+    static constexpr int kWB = FMT == FMT_INT4 ? 2 : 1;         // words per lane per block
+    static constexpr int kNB = WPL / kWB;                        // blocks per k-step
+    static constexpr int kSK = 4 * WPL * Fmt<FMT>::kCodesPerWord;  // k per k-step
+    static constexpr int kMPB = FMT == FMT_BINARY ? 2 : 1;      // MFMAs per block
+    static constexpr int kStepBytes = 256 * WPL;                 // bytes of one (tile, k-step)
+};
+
+// 16 activation bytes q[k0 .. k0 + 16) of one token row, zero past K.
+__device__ __forceinline__ i32x4 load_q16(const int8_t* qrow, int k0, int K, bool vec) {
+    i32x4 v = {0, 0, 0, 0};
+    if (k0 < K) {
+        if (vec) {
+            v = *reinterpret_cast<const i32x4*>(qrow + k0);
+        } else {
+            const uint8_t* p = reinterpret_cast<const uint8_t*>(qrow + k0);
+            const int valid = K - k0;
+            #pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int vi = valid - 4 * i;
+                v[i] = vi <= 0 ? 0 : (int32_t)load_u32_partial(p + 4 * i, vi < 4 ? vi : 4);
+            }
+        }
+    }
+    return v;
+}
+
+// NR: C registers per lane holding live tokens (token = 4 * lane group + r).
+// SPS: group mode: scale units per k-step; 0 = tensor/row scales.
+// LDSA: activations staged in LDS.  ACC: also write the integer products
+// (kept out of the streaming instantiations: optional stores inside the
+// k-loop make the compiler's wait counting conservative).
+template <int FMT, int WPL, int NR, int SPS, bool LDSA, bool ACC>
+__global__ __launch_bounds__(256) void gemv_kernel(const GemvParams p) {
+    using S = GemvShape<FMT, WPL>;
+    constexpr int D = kGemvD;
+    constexpr int NB = S::kNB, KB = S::kKB, SK = S::kSK, MPB = S::kMPB;
+    constexpr int STEP = S::kStepBytes;
+    constexpr bool GROUP = SPS > 0;
+    constexpr int NU = GROUP ? SPS : 1;                      // scale loads per k-step
+    constexpr int BPU = GROUP ? NB / SPS : NB;               // blocks per scale unit
+    constexpr int NA = LDSA ? 1 : NB * MPB;                  // ring-held activation operands
+    constexpr int SHIFT = Fmt<FMT>::kShift;
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
+    // the wavefront index is uniform; saying so keeps every value derived
+    // from it (tile, part, k-range) in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4;                                 // lane group
+    const int rl = lane & 15;                                // weight row in the tile / token of A
+
+    int mi = 0;                                              // matrix of this workgroup
+    for (int hi = p.n_mats - 1; mi < hi;) {
+        const int mid = (mi + hi + 1) >> 1;
+        if ((int)blockIdx.x >= p.wg_start[mid]) mi = mid; else hi = mid - 1;
+    }
+    const GemvMat& M = p.m[mi];
+    const int part = wave & (p.ksplit - 1);
+    const int tile_raw = ((int)blockIdx.x - p.wg_start[mi]) * p.tiles_per_wg + (wave >> p.ksplit_log);
+    const bool live = tile_raw < M.n_tiles;                  // uniform
+    const int tile = live ? tile_raw : M.n_tiles - 1;
+    const int s0 = part * p.part_len;
+    const int s_cnt = live ? min(p.n_steps - s0, p.part_len) : 0;
+    const int s_loop = (s_cnt + D - 1) / D * D;
+    const int K = p.K, T = p.T;
+    const int tok = min(rl, T - 1);                          // A row; rows >= t are never stored
+
+    // per-tile operands, loaded once (before the ring, so in-order completion
+    // makes them ready by the first step)
+    const int row = tile * 16 + rl;
+    const int row_c = min(row, M.n - 1);
+    float sw = 0.0f;
+    if constexpr (!GROUP) sw = M.scales[p.scale_per_row ? row_c : 0];
+    float sxv[NR];
+    #pragma unroll
+    for (int r = 0; r < NR; ++r) sxv[r] = M.sx[min(4 * g + r, T - 1)];
+
+    const uint8_t* wp = M.packed + ((size_t)tile * p.n_steps + s0) * STEP + lane * (4 * WPL);
+    const float* scp = M.scales + (size_t)tile * p.G * 16 + rl;            // group mode
+    const int8_t* qrow = M.q + (size_t)tok * K;                            // global activations
+
+    uint32_t wv[D][WPL];
+    float sg[D][NU];
+    i32x4 av[D][NA];
+
+    auto div_upg = [&](int x) -> int {                       // x / upg
+        return p.upg_shift >= 0 ? (x >> p.upg_shift) : (int)__umulhi((uint32_t)x, p.upg_magic);
+    };
+    auto unit_group = [&](int U) -> int { return min(div_upg(U), p.G - 1); };   // scale group of unit U
+    auto load_slot = [&](int u, int j) {
+        // Unconditional loads (a dead step past the part re-reads its last
+        // step, never consumed): the compiler's wait counting then keeps all
+        // D steps in flight.
+        const int jj = j < s_cnt ? j : s_cnt - 1;
+        load_words<WPL>(wp + (size_t)jj * STEP, 4 * WPL, true, wv[u]);
+        if constexpr (GROUP) {
+            #pragma unroll
+            for (int v = 0; v < NU; ++v) sg[u][v] = scp[unit_group((s0 + jj) * SPS + v) * 16];
+        }
+        if constexpr (!LDSA) {
+            #pragma unroll
+            for (int b = 0; b < NB; ++b)
+                #pragma unroll
+                for (int m = 0; m < MPB; ++m) {
+                    const int k0 = (s0 + jj) * SK + b * KB + g * (KB / 4) + 16 * m;
+                    if (p.q_vec) av[u][b * MPB + m] = *reinterpret_cast<const i32x4*>(qrow + (k0 < K ? k0 : 0));
+                    else av[u][b * MPB + m] = load_q16(qrow, k0, K, false);
+                }
+        }
+    };
+
+    // ---- ring prologue, then the activation stage
+    if (s_cnt > 0) {
+        #pragma unroll
+        for (int u = 0; u < D; ++u) load_slot(u, u);
+    }
+    const int8_t* lds_a = reinterpret_cast<const int8_t*>(smem) + (size_t)tok * p.stride + g * (KB / 4);
+    if constexpr (LDSA) {
+        const int kpad = p.n_steps * SK;
+        const int8_t* q = M.q;
+        for (int t = 0; t < T; ++t) {
+            uint8_t* dst = smem + (size_t)t * p.stride;
+            if constexpr (FMT == FMT_BINARY) {
+                // 32-code chunks permuted to the order decode_binary yields
+                for (int c = threadIdx.x; c < kpad / 32; c += 256) {
+                    const i32x4 lo = load_q16(q + (size_t)t * K, 32 * c, K, p.q_vec);
+                    const i32x4 hi = load_q16(q + (size_t)t * K, 32 * c + 16, K, p.q_vec);
+                    const uint32_t X[8] = {(uint32_t)lo[0], (uint32_t)lo[1], (uint32_t)lo[2], (uint32_t)lo[3],
+                                           (uint32_t)hi[0], (uint32_t)hi[1], (uint32_t)hi[2], (uint32_t)hi[3]};
+                    i32x4 a0, a1;
+                    perm_binary_a(X, a0, a1);
+                    *reinterpret_cast<i32x4*>(dst + 32 * c) = a0;
+                    *reinterpret_cast<i32x4*>(dst + 32 * c + 16) = a1;
+                }
+            } else {
+                for (int c = threadIdx.x; c < kpad / 16; c += 256)
+                    *reinterpret_cast<i32x4*>(dst + 16 * c) = load_q16(q + (size_t)t * K, 16 * c, K, p.q_vec);
+            }
+        }
+        __syncthreads();
+    }
+
+    i32x4 C = {0, 0, 0, 0};
+    float yp[NR];
+    #pragma unroll
+    for (int r = 0; r < NR; ++r) yp[r] = 0.0f;
+
+    auto compute_slot = [&](int u, int j) {
+        if (j >= s_cnt) return;                              // dead step (uniform)
+        const int s = s0 + j;
+        #pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            i32x4 A[MPB];
+            if constexpr (LDSA) {
+                #pragma unroll
+                for (int m = 0; m < MPB; ++m)
+                    A[m] = *reinterpret_cast<const i32x4*>(lds_a + s * SK + b * KB + 16 * m);
+            } else if constexpr (FMT == FMT_BINARY) {
+                // binary padding codes decode as +1: activations past K must be zero
+                const int k0 = s * SK + b * KB + g * (KB / 4);
+                i32x4 lo = av[u][2 * b], hi = av[u][2 * b + 1];
+                if (k0 >= K) lo = i32x4{0, 0, 0, 0};
+                if (k0 + 16 >= K) hi = i32x4{0, 0, 0, 0};
+                const uint32_t X[8] = {(uint32_t)lo[0], (uint32_t)lo[1], (uint32_t)lo[2], (uint32_t)lo[3],
+                                       (uint32_t)hi[0], (uint32_t)hi[1], (uint32_t)hi[2], (uint32_t)hi[3]};
+                perm_binary_a(X, A[0], A[1]);
+            } else {
+                A[0] = av[u][b];                             // padding codes are 0: any A is fine
+            }
+            if constexpr (FMT == FMT_TERNARY) {
+                C = mfma16(A[0], decode_ternary(wv[u][b]), C);
+            } else if constexpr (FMT == FMT_INT4) {
+                C = mfma16(A[0], decode_int4(wv[u][2 * b], wv[u][2 * b + 1]), C);
+            } else {
+                i32x4 b0, b1;
+                decode_binary(wv[u][b], b0, b1);
+                C = mfma16(A[0], b0, C);
+                C = mfma16(A[1], b1, C);
+            }
+            if constexpr (GROUP) {
+                if (b % BPU == BPU - 1) {
+                    const int v = b / BPU;
+                    const int U = s * SPS + v;
+                    const int uk = SK / SPS;
+                    const bool group_last = div_upg(U + 1) * p.upg == U + 1;
+                    if (U * uk < K && (group_last || (U + 1) * uk >= K)) {   // uniform
+                        #pragma unroll
+                        for (int r = 0; r < NR; ++r) {
+                            const int32_t a = C[r] >> SHIFT;
+                            yp[r] = yp[r] + sg[u][v] * (float)a;
+                            if constexpr (ACC) {
+                                const int t = 4 * g + r;
+                                if (M.acc && live && t < T && row < M.n)
+                                    M.acc[((size_t)t * M.n + row) * p.G + unit_group(U)] = a;
+                            }
+                        }
+                        C = i32x4{0, 0, 0, 0};
+                    }
+                }
+            }
+        }
+    };
+
+    // steady state: consume a step, refill its slot D steps ahead; then the
+    // last D steps without refills
+    int j = 0;
+    for (; j + D < s_loop; j += D) {
+        #pragma unroll
+        for (int u = 0; u < D; ++u) {
+            compute_slot(u, j + u);
+            load_slot(u, j + u + D);
+        }
+    }
+    if (s_loop > 0) {
+        #pragma unroll
+        for (int u = 0; u < D; ++u) compute_slot(u, j + u);
+    }
+
+    // ---- combine k-split partials (fixed order), rescale, store
+    int32_t ai[NR];
+    #pragma unroll
+    for (int r = 0; r < NR; ++r) ai[r] = C[r] >> SHIFT;
+    if (p.ksplit > 1) {
+        int32_t* red = reinterpret_cast<int32_t*>(smem + p.lds_a_bytes);   // [4 waves][NR][64], after A
+        #pragma unroll
+        for (int r = 0; r < NR; ++r)
+            red[(wave * NR + r) * 64 + lane] = GROUP ? __float_as_int(yp[r]) : ai[r];
+        __syncthreads();
+        if (part == 0) {
+            for (int q = 1; q < p.ksplit; ++q) {
+                #pragma unroll
+                for (int r = 0; r < NR; ++r) {
+                    const int32_t o = red[((wave + q) * NR + r) * 64 + lane];
+                    if constexpr (GROUP) yp[r] = yp[r] + __int_as_float(o);
+                    else ai[r] += o;
+                }
+            }
+        }
+    }
+    if (part == 0 && live && row < M.n) {
+        #pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            const int t = 4 * g + r;
+            if (t < T) {
+                if constexpr (GROUP) {
+                    M.y[(size_t)t * M.n + row] = sxv[r] * yp[r];
+                } else {
+                    M.y[(size_t)t * M.n + row] = (float)ai[r] * (sxv[r] * sw);
+                    if constexpr (ACC) {
+                        if (M.acc) M.acc[(size_t)t * M.n + row] = ai[r];
+                    }
+                }
+            }
+        }
+    }
+}
+
+template <int FMT, int WPL, int NR, int SPS>
+void gemv_launch_lds(const GemvParams& p, const GemvCfg& c, hipStream_t st) {
+    const dim3 grid((unsigned)c.grid), block(256);
+    if (c.lds_a) {
+        if (c.acc) gemv_kernel<FMT, WPL, NR, SPS, true, true><<<grid, block, c.lds_bytes, st>>>(p);
+        else gemv_kernel<FMT, WPL, NR, SPS, true, false><<<grid, block, c.lds_bytes, st>>>(p);
+    } else {
+        // activations from L2: the large-t*k fallback, always 4 token registers
+        if (c.acc) gemv_kernel<FMT, WPL, 4, SPS, false, true><<<grid, block, c.lds_bytes, st>>>(p);
+        else gemv_kernel<FMT, WPL, 4, SPS, false, false><<<grid, block, c.lds_bytes, st>>>(p);
+    }
+}
+
+template <int FMT, int WPL>
+void gemv_launch_wpl(const GemvParams& p, const GemvCfg& c, hipStream_t st) {
+    constexpr int NB = GemvShape<FMT, WPL>::kNB;
+    auto by_nr = [&](auto sps_tag) {
+        constexpr int SPS = decltype(sps_tag)::value;
+        if (c.nr == 1 && c.lds_a) gemv_launch_lds<FMT, WPL, 1, SPS>(p, c, st);
+        else gemv_launch_lds<FMT, WPL, 4, SPS>(p, c, st);
+    };
+    switch (c.sps) {
+        case 0: by_nr(std::integral_constant<int, 0>{}); break;
+        case 1: by_nr(std::integral_constant<int, 1>{}); break;
+        case 2: if constexpr (NB >= 2) by_nr(std::integral_constant<int, 2>{}); break;
+        default: if constexpr (NB >= 4) by_nr(std::integral_constant<int, 4>{}); break;
+    }
+}
+
+}  // namespace lowbit

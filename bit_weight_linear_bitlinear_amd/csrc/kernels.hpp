@@ -15,7 +15,9 @@ struct LinearArgs {
     int group;           // group mode: columns per group
     int n_groups;        // group mode: ceil(k / group), else 1
     int n, k, t;
-    int64_t row_bytes;
+    int wpl;             // packed words per (lane group, row) per k-step
+    int step_k;          // codes per k-step
+    int n_steps;         // k-steps per row
     const uint8_t* packed;
     const float* scales;
     const int8_t* q;

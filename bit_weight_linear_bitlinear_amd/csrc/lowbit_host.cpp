@@ -18,16 +18,11 @@
 
 namespace {
 
-constexpr int32_t kAbiVersion = 1;
+constexpr int32_t kAbiVersion = 2;
 
-int64_t packed_row_bytes(int32_t fmt, int64_t k) {
-    switch (fmt) {
-        case LOWBIT_TERNARY2: return ((k + 15) / 16) * 4;   // whole 16-code words
-        case LOWBIT_INT4:     return ((k + 7) / 8) * 4;     // whole 8-code words
-        case LOWBIT_BINARY1:  return (k + 7) / 8;           // packbits rows
-        default:              return -1;
-    }
-}
+// Field geometry of the packed formats (the layout comment of lowbit.h).
+int codes_per_word(int32_t fmt) { return fmt == LOWBIT_TERNARY2 ? 16 : (fmt == LOWBIT_INT4 ? 8 : 32); }
+int block_k(int32_t fmt) { return fmt == LOWBIT_BINARY1 ? 128 : 64; }   // k of one matrix-core step
 
 int32_t max_k_of(int32_t fmt) {
     // int32 sums of (scaled code) x (activation code): |sum| <= k * 127 * qmax * scale
@@ -47,18 +42,28 @@ lowbit_status fill_desc(int32_t format, int32_t scale, int32_t n, int32_t k, int
     if (n < 1 || k < 1) return LOWBIT_E_ARG;
     if ((flags & ~LOWBIT_FLAG_TANH3) != 0) return LOWBIT_E_ARG;
     if (scale == LOWBIT_SCALE_GROUP) {
-        const int32_t step = format == LOWBIT_BINARY1 ? 128 : 64;
+        const int32_t step = block_k(format);
         if (group < step || group % step != 0) return LOWBIT_E_ARG;
     } else if (group != 0) {
         return LOWBIT_E_ARG;
     }
     if (k > max_k_of(format)) return LOWBIT_E_RANGE;
+    // k-step: the widest of 4, 2, 1 words per lane (int4: 4, 2 - one int4
+    // operand is two words) that pads k no further than the narrowest does
+    const int cpw = codes_per_word(format);
+    const int wmin = format == LOWBIT_INT4 ? 2 : 1;
+    auto padded = [&](int w) { const int64_t sk = 4LL * w * cpw; return (k + sk - 1) / sk * sk; };
+    int wpl = 4;
+    while (wpl > wmin && padded(wpl) != padded(wmin)) wpl /= 2;
     lowbit_desc d;
     d.format = format; d.scale = scale; d.n = n; d.k = k; d.group = group; d.flags = flags;
-    d.row_bytes = packed_row_bytes(format, k);
-    d.packed_bytes = d.row_bytes * (int64_t)n;
+    d.wpl = wpl;
+    d.step_k = 4 * wpl * cpw;
+    d.n_steps = (k + d.step_k - 1) / d.step_k;
+    d.packed_bytes = ((int64_t)n + 15) / 16 * d.n_steps * 256 * wpl;
     d.n_groups = scale == LOWBIT_SCALE_GROUP ? ((int64_t)k + group - 1) / group : 1;
-    d.n_scales = scale == LOWBIT_SCALE_TENSOR ? 1 : (scale == LOWBIT_SCALE_ROW ? n : (int64_t)n * d.n_groups);
+    d.n_scales = scale == LOWBIT_SCALE_TENSOR ? 1
+               : (scale == LOWBIT_SCALE_ROW ? n : ((int64_t)n + 15) / 16 * 16 * d.n_groups);
     *out = d;
     return LOWBIT_OK;
 }
@@ -69,8 +74,8 @@ lowbit_status check_desc(const lowbit_desc* d) {
     lowbit_desc ref;
     lowbit_status st = fill_desc(d->format, d->scale, d->n, d->k, d->group, d->flags, &ref);
     if (st != LOWBIT_OK) return st;
-    if (ref.row_bytes != d->row_bytes || ref.packed_bytes != d->packed_bytes || ref.n_groups != d->n_groups ||
-        ref.n_scales != d->n_scales)
+    if (ref.wpl != d->wpl || ref.step_k != d->step_k || ref.n_steps != d->n_steps ||
+        ref.packed_bytes != d->packed_bytes || ref.n_groups != d->n_groups || ref.n_scales != d->n_scales)
         return LOWBIT_E_ARG;
     return LOWBIT_OK;
 }
@@ -129,40 +134,43 @@ struct RowPacker {
                 float s = tensor_scale;
                 if (d.scale != LOWBIT_SCALE_TENSOR) {
                     s = domain_scale(d.format, c1 - c0, [&](int64_t i) { return row[(size_t)(c0 + i)]; });
-                    scales[d.scale == LOWBIT_SCALE_ROW ? r : r * d.n_groups + gi] = s;
+                    if (d.scale == LOWBIT_SCALE_ROW) scales[r] = s;
+                    else scales[((r / 16) * d.n_groups + gi) * 16 + r % 16] = s;   // [tile][group][16]
                 }
                 for (int64_t c = c0; c < c1; ++c) codes[(size_t)c] = (int8_t)code_of(d.format, row[(size_t)c], s);
             }
-            emit_row(codes.data(), packed + r * d.row_bytes);
+            emit_row(r, codes.data());
         }
     }
 
-    // write one row of codes in the packed layout of lowbit.h
-    void emit_row(const int8_t* c, uint8_t* out) const {
+    // Scatter one row of codes into its words of the tiled layout (lowbit.h).
+    // Each word belongs to exactly one row, so rows can be packed concurrently;
+    // the buffer was zeroed beforehand (padding rows and k stay zero).
+    void emit_row(int64_t row, const int8_t* c) const {
         const int64_t K = d.k;
-        std::memset(out, 0, (size_t)d.row_bytes);
-        if (d.format == LOWBIT_BINARY1) {
-            for (int64_t b = 0; b * 8 < K; ++b) {
-                uint32_t byte = 0;
-                for (int j = 0; j < 8 && b * 8 + j < K; ++j) byte |= (uint32_t)(c[b * 8 + j] < 0) << j;
-                out[b] = (uint8_t)byte;
-            }
-            return;
-        }
-        const int per_word = d.format == LOWBIT_TERNARY2 ? 16 : 8;
-        const int bits = d.format == LOWBIT_TERNARY2 ? 2 : 4;
+        const int cpw = codes_per_word(d.format), kb = block_k(d.format), wb = kb / 4 / cpw;
+        const int bits = d.format == LOWBIT_TERNARY2 ? 2 : (d.format == LOWBIT_INT4 ? 4 : 1);
         const uint32_t mask = (1u << bits) - 1u;
-        for (int64_t wi = 0; wi * per_word < K; ++wi) {
-            uint32_t word = 0;
-            for (int j = 0; j < per_word && wi * per_word + j < K; ++j) {
-                const uint32_t field = (uint32_t)c[wi * per_word + j] & mask;   // two's complement
-                word |= field << (8 * (j % 4) + bits * (j / 4));
-            }
-            out[4 * wi + 0] = (uint8_t)(word);
-            out[4 * wi + 1] = (uint8_t)(word >> 8);
-            out[4 * wi + 2] = (uint8_t)(word >> 16);
-            out[4 * wi + 3] = (uint8_t)(word >> 24);
-        }
+        const int64_t t = row / 16, rr = row % 16;
+        for (int64_t s = 0; s < d.n_steps; ++s)
+            for (int g = 0; g < 4; ++g)
+                for (int w = 0; w < d.wpl; ++w) {
+                    const int64_t k0 = s * d.step_k + (w / wb) * kb + g * (kb / 4) + (w % wb) * cpw;
+                    if (k0 >= K) continue;
+                    uint32_t word = 0;
+                    for (int j = 0; j < cpw && k0 + j < K; ++j) {
+                        const int8_t v = c[k0 + j];
+                        if (d.format == LOWBIT_BINARY1)
+                            word |= (uint32_t)(v < 0) << j;                        // byte j/8, bit j%8
+                        else
+                            word |= ((uint32_t)v & mask) << (8 * (j % 4) + bits * (j / 4));
+                    }
+                    const int64_t off = ((((t * d.n_steps + s) * 4 + g) * 16 + rr) * d.wpl + w) * 4;
+                    packed[off + 0] = (uint8_t)(word);
+                    packed[off + 1] = (uint8_t)(word >> 8);
+                    packed[off + 2] = (uint8_t)(word >> 16);
+                    packed[off + 3] = (uint8_t)(word >> 24);
+                }
     }
 };
 
@@ -184,9 +192,13 @@ lowbit_status linear_common(const lowbit_desc* d, const uint8_t* packed, const f
     lowbit_status st = check_desc(d);
     if (st != LOWBIT_OK) return st;
     if (!packed || !scales || !q || !sx || !y || t < 1) return LOWBIT_E_ARG;
+    if ((uintptr_t)packed % 16 != 0 || (uintptr_t)scales % 4 != 0 || (uintptr_t)sx % 4 != 0 ||
+        (uintptr_t)y % 4 != 0 || (uintptr_t)acc % 4 != 0)
+        return LOWBIT_E_ARG;
     lowbit::LinearArgs a;
     a.fmt = d->format; a.scale = d->scale; a.group = d->group; a.n_groups = (int)d->n_groups;
-    a.n = d->n; a.k = d->k; a.t = t; a.row_bytes = d->row_bytes;
+    a.n = d->n; a.k = d->k; a.t = t;
+    a.wpl = d->wpl; a.step_k = d->step_k; a.n_steps = (int)d->n_steps;
     a.packed = packed; a.scales = scales; a.q = q; a.sx = sx; a.y = y; a.acc = acc;
     *out = a;
     return LOWBIT_OK;
@@ -215,6 +227,9 @@ lowbit_status lowbit_pack(const lowbit_desc* d, const float* w, uint8_t* packed,
         tensor_scale = domain_scale(d->format, N * K, [&](int64_t i) { return premapped(w[i], tanh3); });
         scales[0] = tensor_scale;
     }
+
+    std::memset(packed, 0, (size_t)d->packed_bytes);
+    if (d->scale == LOWBIT_SCALE_GROUP) std::memset(scales, 0, (size_t)d->n_scales * sizeof(float));
 
     std::atomic<int> bad{0};
     RowPacker job{*d, w, packed, scales, tensor_scale, &bad};

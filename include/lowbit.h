@@ -10,34 +10,50 @@
  * product is accumulated exactly in int32, and an fp32 epilogue rescales it.
  *
  * Conventions
- *  - Every matrix is row-major.  W is [n, k] (k contiguous), x and q are
- *    [t, k], y is [t, n].
+ *  - W is [n, k] (k contiguous) before packing; x and q are [t, k], y is
+ *    [t, n], all row-major.
  *  - Host pointers are plain CPU memory.  Device pointers are HIP device
  *    memory on the current device (e.g. torch tensor data pointers).
- *  - The caller owns every buffer.  The library allocates nothing and keeps no
- *    state between calls; all entry points are reentrant and thread-safe.
+ *  - The caller owns every buffer; the library allocates nothing.  Its only
+ *    state is a per-device cache of the compute-unit count, filled on first
+ *    use; all entry points are reentrant and thread-safe.
  *  - Device calls are asynchronous on `hip_stream` (a hipStream_t, NULL = the
  *    null stream); their outputs are valid once the stream has synchronised.
  *  - No entry point reads device memory on the host.  Argument checks are
  *    synchronous and happen before any launch; a rejected call launches
  *    nothing.  No exception crosses this interface.
  *
- * Packed weight layout (bytes per row = lowbit_desc.row_bytes, rows back to
- * back, fields past k are zero):
- *  - LOWBIT_BINARY1: one bit per code, bit = (1 - s) / 2, little-bit-first
- *    along k, ceil(k / 8) bytes per row (the binary export reference of M8.8
- *    section 0x06E).
- *  - LOWBIT_TERNARY2: 2-bit two's-complement fields (+1 = 01, 0 = 00,
- *    -1 = 11, 10 reserved) - the two physical bits per ternary code of M8.8
- *    section 0x01A, four codes per byte.  Codes are grouped in 32-bit
- *    little-endian words of 16: code j of a word sits in byte (j mod 4), bits
- *    2*(j div 4).  Rows are whole words: 4 * ceil(k / 16) bytes.
- *  - LOWBIT_INT4: 4-bit two's-complement fields for the symmetric levels
- *    -7..+7 of the T4NT model card (1000 reserved), two codes per byte, 8 per
- *    32-bit word: code j of a word sits in byte (j mod 4), nibble (j div 4)
- *    (0 = low).  Rows are whole words: 4 * ceil(k / 8) bytes.
- * Scales are fp32 arrays: [1] (tensor), [n] (row) or [n, n_groups] (group of
- * `group` consecutive columns of a row, the last one possibly shorter).
+ * Packed weight layout.  The code alphabets and their widths follow the pages;
+ * the arrangement of the fields is this library's own (M8.8 section 0x07D
+ * leaves the physical representation of a ternary matrix open), chosen so
+ * that one 16-row tile of one k-step is a single contiguous block that a
+ * wavefront reads with one 16-byte load per lane.
+ *  - Fields.  LOWBIT_BINARY1: one bit per code, bit = (1 - s) / 2 (the binary
+ *    export reference of M8.8 section 0x06E).  LOWBIT_TERNARY2: 2-bit two's
+ *    complement, +1 = 01, 0 = 00, -1 = 11, 10 reserved (two physical bits per
+ *    ternary code, M8.8 section 0x01A; four codes per byte).  LOWBIT_INT4:
+ *    4-bit two's complement for the symmetric levels -7..+7 of the T4NT model
+ *    card, 1000 reserved.
+ *  - Words.  A little-endian 32-bit word holds CPW codes (ternary 16, int4 8,
+ *    binary 32).  Ternary code j sits in byte j % 4 at bit 2 * (j / 4); int4
+ *    code j in byte j % 4, low nibble for j < 4; binary code j in byte j / 8
+ *    at bit j % 8 (little-bit-first, as numpy.packbits(bitorder="little")).
+ *  - Blocks.  KB consecutive k (ternary and int4 64, binary 128) split into
+ *    four quarters; quarter g is "lane group" g's, held as WB words (ternary
+ *    1, int4 2, binary 1) of consecutive codes.
+ *  - Steps.  wpl words per (lane group, row) = wpl / WB consecutive blocks =
+ *    step_k = 4 * wpl * CPW consecutive k.  wpl is the widest of 4, 2, 1
+ *    (int4: 4, 2) whose step pads k no further than the narrowest step does.
+ *  - Tiles.  16 consecutive rows.
+ *  - Order.  Word w of (tile t, step s, lane group g, row r of the tile) is at
+ *    byte ((((t * n_steps + s) * 4 + g) * 16 + r) * wpl + w) * 4; it covers
+ *    block w / WB of the step, codes (w % WB) * CPW onwards of quarter g.
+ *  - Padding.  Rows n.. of the last tile and codes k.. are zero fields.
+ *    packed_bytes = ceil(n / 16) * n_steps * 256 * wpl.
+ * Scales are fp32 arrays: [1] (tensor), [n] (row), or, for groups of `group`
+ * consecutive columns (the last one possibly shorter), tiled like the codes:
+ * scale (row r, group j) at ((r / 16) * n_groups + j) * 16 + r % 16, padding
+ * rows zero, n_scales = ceil(n / 16) * 16 * n_groups.
  */
 #ifndef LOWBIT_H
 #define LOWBIT_H
@@ -85,10 +101,12 @@ typedef struct lowbit_desc {
     int32_t k;               /* input columns, >= 1 */
     int32_t group;           /* group mode: columns per group; else 0 */
     int32_t flags;           /* LOWBIT_FLAG_* */
-    int64_t row_bytes;       /* packed bytes per row */
-    int64_t packed_bytes;    /* n * row_bytes */
+    int32_t wpl;             /* packed words per (lane group, row) per k-step: 1, 2 or 4 */
+    int32_t step_k;          /* codes per k-step: 4 * wpl * codes per word */
+    int64_t n_steps;         /* ceil(k / step_k) */
+    int64_t packed_bytes;    /* ceil(n / 16) * n_steps * 256 * wpl */
     int64_t n_groups;        /* ceil(k / group) in group mode, else 1 */
-    int64_t n_scales;        /* 1, n, or n * n_groups */
+    int64_t n_scales;        /* 1, n, or ceil(n / 16) * 16 * n_groups */
 } lowbit_desc;
 
 /*
@@ -106,8 +124,8 @@ lowbit_status lowbit_describe(int32_t format, int32_t scale, int32_t n, int32_t 
 /*
  * lowbit_pack - quantise latent fp32 weights and pack them (host, offline).
  *   w      host float [n, k]           latent weights
- *   packed host uint8  [packed_bytes]  out: codes in the layout above
- *   scales host float  [n_scales]      out: fp32 scales
+ *   packed host uint8  [packed_bytes]  out: codes in the tiled layout above
+ *   scales host float  [n_scales]      out: fp32 scales (group scales tiled)
  * Per scale domain (M8.8 0x05A, 0x06E; T4NT model card):
  *   ternary: s = mean |w| (binary64 sum in ascending index order / count,
  *            rounded once to fp32); code = clip(rint(w / s), -1, 1) in fp32

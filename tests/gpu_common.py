@@ -78,9 +78,9 @@ def run_layer(w, x, fmt, scale, group, tanh, entries=("gemv", "gemm"), token_sam
     say(f"[case] {label} fmt={fmt} scale={scale} group={group} tanh={tanh} W={w.shape} x={x.shape} "
         f"entries={entries}")
     d, packed, scales, ph, sh = pack_upload(w, fmt, scale, group, tanh)
-    p_ref, s_ref, _ = oracle.quantize_and_pack(w, fmt, scale, group, tanh)
-    assert (ph.reshape(p_ref.shape) == p_ref).all(), f"{label}: packed bytes differ"
-    assert (sh.view(np.uint32) == s_ref.ravel().view(np.uint32)).all(), f"{label}: scales differ"
+    p_ref, s_ref, _, _ = oracle.quantize_and_pack(w, fmt, scale, group, tanh)
+    assert (ph == p_ref).all(), f"{label}: packed bytes differ"
+    assert (sh.view(np.uint32) == s_ref.view(np.uint32)).all(), f"{label}: scales differ"
 
     x_dev = to_dev(x)
     q, sx, st = act_quant_dev(x_dev)
@@ -94,7 +94,7 @@ def run_layer(w, x, fmt, scale, group, tanh, entries=("gemv", "gemm"), token_sam
     assert (sx_h[sel].view(np.uint32) == sx_ref.view(np.uint32)).all(), f"{label}: activation scales differ"
     assert int(st.cpu()[0]) == 0
 
-    y32, y64, acc_ref = oracle.linear(p_ref, s_ref, fmt, scale, group, w.shape[1], q_ref, sx_ref)
+    y32, y64, acc_ref = oracle.linear(p_ref, s_ref, fmt, scale, group, w.shape[0], w.shape[1], q_ref, sx_ref)
     out = {}
     for entry in entries:
         y, acc = linear_dev(entry, d, packed, scales, q, sx)

@@ -32,23 +32,29 @@ def test_exports_every_declared_symbol():
     lib = ctypes.CDLL(lb.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
-    assert lb.lowbit_abi_version() == 1
+    assert lb.lowbit_abi_version() == 2
 
 
 def test_describe_sizes():
     d = lb.lowbit_describe(lb.TERNARY2, lb.SCALE_GROUP, 9728, 2560, 128)
-    assert (d.row_bytes, d.packed_bytes, d.n_groups, d.n_scales) == (640, 9728 * 640, 20, 9728 * 20)
+    assert (d.wpl, d.step_k, d.n_steps) == (4, 256, 10)
+    assert (d.packed_bytes, d.n_groups, d.n_scales) == (9728 * 640, 20, 9728 * 20)
     d = lb.lowbit_describe(lb.BINARY1, lb.SCALE_ROW, 96, 192)
-    assert (d.row_bytes, d.n_scales, d.n_groups) == (24, 96, 1)
+    assert (d.wpl, d.step_k, d.n_steps, d.packed_bytes, d.n_scales) == (2, 256, 1, 6 * 512, 96)
     d = lb.lowbit_describe(lb.INT4, lb.SCALE_ROW, 3840, 1280, 0, lb.FLAG_TANH3)
-    assert d.row_bytes == 640 and d.flags == 1
+    assert (d.wpl, d.step_k, d.packed_bytes, d.flags) == (4, 128, 3840 * 640, 1)
     d = lb.lowbit_describe(lb.TERNARY2, lb.SCALE_TENSOR, 5, 17)
-    assert d.row_bytes == 8 and d.n_scales == 1
+    assert (d.wpl, d.packed_bytes, d.n_scales) == (1, 256, 1)
     d = lb.lowbit_describe(lb.INT4, lb.SCALE_GROUP, 3, 200, 64)
-    assert d.row_bytes == 4 * 25 and d.n_groups == 4
+    assert d.n_groups == 4 and d.n_scales == 16 * 4
     for fmt in ("ternary", "binary", "int4"):
-        for k in (1, 7, 16, 100, 2560):
-            assert lb.lowbit_describe(FMT[fmt], 0, 1, k).row_bytes == oracle.row_bytes(fmt, k)
+        for n, k in ((1, 1), (17, 7), (3, 16), (40, 100), (16, 2560), (2, 9728), (5, 4100)):
+            d = lb.lowbit_describe(FMT[fmt], 0, n, k)
+            lay = oracle.layout(fmt, n, k)
+            assert (d.wpl, d.n_steps, d.step_k, d.packed_bytes) == \
+                (lay["wpl"], lay["n_steps"], lay["step_k"], lay["packed_bytes"]), (fmt, n, k)
+            dg = lb.lowbit_describe(FMT[fmt], 2, n, k, 128)
+            assert dg.n_scales == oracle.n_scales("group", n, k, 128)
 
 
 @pytest.mark.parametrize("args", [
@@ -89,9 +95,12 @@ def test_device_calls_reject_bad_arguments_before_launch():
     assert lib.lowbit_linear(ctypes.byref(d), one, one, one, one, 0, one, None, None) == 1
     assert lib.lowbit_linear(ctypes.byref(d), None, one, one, one, 1, one, None, None) == 1
     assert lib.lowbit_linear_batched(ctypes.byref(d), one, one, None, one, 1, one, None, None) == 1
-    bad = lb.lowbit_describe(lb.TERNARY2, lb.SCALE_TENSOR, 16, 64)
-    bad.row_bytes += 4
-    assert lib.lowbit_linear(ctypes.byref(bad), one, one, one, one, 1, one, None, None) == 1
+    for field, delta in (("wpl", 1), ("step_k", 64), ("n_steps", 1), ("packed_bytes", 256), ("n_scales", 1)):
+        bad = lb.lowbit_describe(lb.TERNARY2, lb.SCALE_TENSOR, 16, 64)
+        setattr(bad, field, getattr(bad, field) + delta)
+        assert lib.lowbit_linear(ctypes.byref(bad), one, one, one, one, 1, one, None, None) == 1, field
+    odd = ctypes.c_void_p(24)    # packed must be 16-byte aligned
+    assert lib.lowbit_linear(ctypes.byref(d), odd, one, one, one, 1, one, None, None) == 1
     assert lib.lowbit_linear_batched(None, one, one, one, one, 1, one, None, None) == 1
 
 
@@ -101,12 +110,12 @@ def _pack_lib(w, fmt, scale, group=0, tanh=False):
     packed = np.empty(d.packed_bytes, np.uint8)
     scales = np.empty(d.n_scales, np.float32)
     lb.lowbit_pack(d, np.ascontiguousarray(w), packed, scales)
-    return packed.reshape(n, d.row_bytes), scales
+    return packed, scales
 
 
 def _pack_oracle(w, fmt, scale, group=0, tanh=False):
-    p, s, _ = oracle.quantize_and_pack(w, fmt, scale, group, tanh)
-    return p, s.ravel()
+    p, s, _, _ = oracle.quantize_and_pack(w, fmt, scale, group, tanh)
+    return p, s
 
 
 @pytest.mark.parametrize("wl", workloads.WORKLOADS, ids=lambda w: w.name)
@@ -142,7 +151,7 @@ def test_host_pack_ties_and_zero_domains():
     g = np.array([[0.25, -0.75, 0.75, -0.25, 0.5, -0.5, 0.0, 1.0]], np.float32)
     p, s = _pack_lib(g, "ternary", "tensor")
     assert s[0] == 0.5
-    assert (oracle.unpack(p, "ternary", 8)[0] == np.array([0, -1, 1, 0, 1, -1, 0, 1])).all()
+    assert (oracle.unpack(p, "ternary", 1, 8)[0] == np.array([0, -1, 1, 0, 1, -1, 0, 1])).all()
     z = np.zeros((2, 130), np.float32)
     z[1, 129] = 1.0
     for fmt, scale, group in (("ternary", "group", 64), ("int4", "row", 0), ("binary", "group", 128)):

@@ -77,8 +77,11 @@ def test_int4_t4nt_layer0_sampled_tokens():
 
 # ------------------------------------------------------- ragged / random
 
+# (n, k, t): tails in n and k, t above 16 (several launches), t * k too large
+# for the LDS activation stage (k = 4100, 4112 at t = 16), few tiles with many
+# k-steps (split k-ranges)
 RAGGED = [(1, 1, 1), (16, 64, 1), (17, 100, 3), (5, 257, 2), (33, 1000, 17), (130, 520, 5), (64, 4100, 16),
-          (40, 384, 130)]
+          (40, 384, 130), (48, 4112, 16)]
 
 
 @pytest.mark.parametrize("fmt", ["ternary", "binary", "int4"])
@@ -88,6 +91,20 @@ def test_ragged_shapes(fmt, scale):
         group = (128 if fmt == "binary" else 64) * (1 + i % 2) if scale == "group" else 0
         w, x = workloads.random_case(100 + i, n, k, t)
         run_layer(w, x, fmt, scale, group, fmt == "int4", label=f"ragged {i}")
+
+
+@pytest.mark.parametrize("fmt,k,groups", [
+    ("ternary", 2560, (64, 128, 192, 256, 512, 640, 2560)),
+    ("int4", 1280, (64, 128, 192, 256, 1280)),
+    ("binary", 1536, (128, 256, 384, 512, 1024)),
+])
+def test_group_sizes(fmt, k, groups):
+    """Scale groups smaller than, equal to, larger than and not aligned with a
+    packed k-step, including a last group cut short by k."""
+    for gi, group in enumerate(groups):
+        for t in (1, 5):
+            w, x = workloads.random_case(300 + gi, 200, k, t)
+            run_layer(w, x, fmt, "group", group, fmt == "int4", label=f"group {group} t={t}")
 
 
 def test_act_quant_edge_rows():
@@ -155,8 +172,8 @@ def test_entry_points_agree_on_random_large():
     torch.cuda.synchronize()
     assert torch.equal(a0, a1)
     q_ref, sx_ref, _ = oracle.act_quant(x)
-    p_ref, s_ref, _ = oracle.quantize_and_pack(w, "ternary", "group", 128)
-    y32, y64, acc_ref = oracle.linear(p_ref, s_ref, "ternary", "group", 128, 2048, q_ref, sx_ref)
+    p_ref, s_ref, _, _ = oracle.quantize_and_pack(w, "ternary", "group", 128)
+    y32, y64, acc_ref = oracle.linear(p_ref, s_ref, "ternary", "group", 128, w.shape[0], 2048, q_ref, sx_ref)
     assert (a0.cpu().numpy() == acc_ref).all()
     check_y(y0.cpu().numpy(), y32, y64, "gemv")
     check_y(y1.cpu().numpy(), y32, y64, "gemm")
@@ -195,8 +212,8 @@ def test_grouped_matches_single_and_oracle(fmt, scale, group, t):
             assert torch.equal(accs[i], a1), i
     for i in (0, 17, 44):
         w, x = refs[i]
-        p_ref, s_ref, _ = oracle.quantize_and_pack(w, fmt, scale, group, fmt == "int4")
+        p_ref, s_ref, _, _ = oracle.quantize_and_pack(w, fmt, scale, group, fmt == "int4")
         q_ref, sx_ref, _ = oracle.act_quant(x)
-        y32, y64, acc_ref = oracle.linear(p_ref, s_ref, fmt, scale, group, k, q_ref, sx_ref)
+        y32, y64, acc_ref = oracle.linear(p_ref, s_ref, fmt, scale, group, w.shape[0], k, q_ref, sx_ref)
         assert (accs[i].cpu().numpy() == acc_ref).all()
         check_y(ys[i].cpu().numpy(), y32, y64, f"grouped {i}")
