@@ -26,6 +26,9 @@ COMMON = ["-std=c++17", "-O3", "-fPIC", "-ffp-contract=off", "-fno-fast-math",
           "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-function"]
 DEVICE = [f"--offload-arch={ARCH}", "-fno-gpu-flush-denormals-to-zero",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# the decode GEMV keeps its MFMA accumulators in ordinary VGPRs (its group
+# epilogue reads them every few MFMAs; no accumulation-register copies)
+EXTRA = {f"gemv_{f}.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"] for f in ("ternary", "int4", "binary")}
 
 
 def _hipcc():
@@ -37,7 +40,7 @@ def _hipcc():
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *COMMON, *DEVICE, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *COMMON, *DEVICE, *EXTRA.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

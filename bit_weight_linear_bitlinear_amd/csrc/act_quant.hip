@@ -10,10 +10,11 @@
 // once and the file is built with -ffp-contract=off, and rintf maps to
 // v_rndne_f32.  Denormals are kept (no flush-to-zero).
 //
-// HBM-bound stream (4 bytes read, 1 byte written per element): one wavefront
-// per row, 16-byte loads, the row max reduced across the wave with lane
-// shuffles, then a second pass over the row (served from L2) writes 4 codes
-// per 32-bit store.
+// HBM-bound stream (4 bytes read, 1 byte written per element).  Aligned rows
+// of up to 16384 elements are read once into registers by a wavefront (k <=
+// 2048) or a whole workgroup, reduced, and quantised from the registers;
+// longer or unaligned rows take a two-pass loop (one wavefront per row, the
+// second pass served from L2).
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -94,14 +95,91 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const float* __restrict_
     }
 }
 
+// Register-resident variant for rows of up to TPR * 4 * R floats (16-byte
+// aligned, k % 4 == 0): TPR threads (a wavefront, or a whole 256-thread
+// workgroup) share one row, every element is read from HBM exactly once into
+// registers, the row max is reduced with lane shuffles (and LDS across the
+// workgroup's wavefronts), and the codes are written from the same registers.
+// All loads of a thread are issued before any is consumed.
+template <int TPR, int R>
+__global__ __launch_bounds__(256) void act_quant_reg_kernel(const float* __restrict__ x, int t, int k,
+                                                            int8_t* __restrict__ q, float* __restrict__ sx,
+                                                            int32_t* __restrict__ status) {
+    constexpr int RPW = 256 / TPR;                           // rows per workgroup
+    __shared__ float red_m[4];
+    __shared__ int red_bad[4];
+    const int row = blockIdx.x * RPW + (int)threadIdx.x / TPR;
+    const int sub = threadIdx.x % TPR;
+    const int lane = threadIdx.x & 63;
+    if (TPR == 64 && row >= t) return;                       // whole wavefronts exit together
+    const int k4 = k >> 2;
+    const float4* x4 = reinterpret_cast<const float4*>(x + (size_t)row * k);
+    float4 v[R];
+    #pragma unroll
+    for (int i = 0; i < R; ++i) {
+        const int idx = sub + i * TPR;
+        v[i] = idx < k4 ? x4[idx] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
+    float m = 0.0f;
+    int bad = 0;
+    #pragma unroll
+    for (int i = 0; i < R; ++i) {
+        bad |= !(isfinite(v[i].x) && isfinite(v[i].y) && isfinite(v[i].z) && isfinite(v[i].w));
+        const float a0 = fabsf(v[i].x), a1 = fabsf(v[i].y), a2 = fabsf(v[i].z), a3 = fabsf(v[i].w);
+        m = a0 > m ? a0 : m; m = a1 > m ? a1 : m; m = a2 > m ? a2 : m; m = a3 > m ? a3 : m;
+    }
+    m = wave_max(m);
+    bad = wave_or(bad);
+    if constexpr (TPR == 256) {
+        const int w = threadIdx.x >> 6;
+        if (lane == 0) { red_m[w] = m; red_bad[w] = bad; }
+        __syncthreads();
+        #pragma unroll
+        for (int i = 0; i < 4; ++i) { m = red_m[i] > m ? red_m[i] : m; bad |= red_bad[i]; }
+    }
+    float r = 0.0f;
+    int flag = 0;
+    if (bad) {
+        flag = LOWBIT_ACT_NONFINITE;
+    } else if (m > 0.0f) {
+        r = 127.0f / m;
+        if (!isfinite(r)) flag = LOWBIT_ACT_OVERFLOW;
+    }
+    uint32_t* q4 = reinterpret_cast<uint32_t*>(q + (size_t)row * k);
+    #pragma unroll
+    for (int i = 0; i < R; ++i) {
+        const int idx = sub + i * TPR;
+        if (idx < k4) {
+            uint32_t p = 0u;   // a rejected row gets zero codes
+            if (!flag)
+                p = (uint32_t)(uint8_t)quant1(v[i].x, r) | ((uint32_t)(uint8_t)quant1(v[i].y, r) << 8) |
+                    ((uint32_t)(uint8_t)quant1(v[i].z, r) << 16) | ((uint32_t)(uint8_t)quant1(v[i].w, r) << 24);
+            q4[idx] = p;
+        }
+    }
+    if (sub == 0) {
+        sx[row] = flag ? __builtin_nanf("") : m / 127.0f;
+        if (flag && status) atomicOr(status, flag);
+    }
+}
+
 hipError_t launch_act_quant(const float* x, int t, int k, int8_t* q, float* sx, int32_t* status,
                             hipStream_t stream) {
-    dim3 grid((unsigned)((t + kActWaves - 1) / kActWaves)), block(256);
     const bool vec = (k % 4 == 0) && ((uintptr_t)x % 16 == 0) && ((uintptr_t)q % 4 == 0);
-    if (vec)
-        act_quant_kernel<true><<<grid, block, 0, stream>>>(x, t, k, q, sx, status);
-    else
-        act_quant_kernel<false><<<grid, block, 0, stream>>>(x, t, k, q, sx, status);
+    const int k4 = k / 4;
+    if (vec && k4 <= 64 * 8) {
+        act_quant_reg_kernel<64, 8><<<dim3((unsigned)((t + 3) / 4)), dim3(256), 0, stream>>>(x, t, k, q, sx, status);
+    } else if (vec && k4 <= 256 * 4) {
+        act_quant_reg_kernel<256, 4><<<dim3((unsigned)t), dim3(256), 0, stream>>>(x, t, k, q, sx, status);
+    } else if (vec && k4 <= 256 * 16) {
+        act_quant_reg_kernel<256, 16><<<dim3((unsigned)t), dim3(256), 0, stream>>>(x, t, k, q, sx, status);
+    } else {
+        dim3 grid((unsigned)((t + kActWaves - 1) / kActWaves)), block(256);
+        if (vec)
+            act_quant_kernel<true><<<grid, block, 0, stream>>>(x, t, k, q, sx, status);
+        else
+            act_quant_kernel<false><<<grid, block, 0, stream>>>(x, t, k, q, sx, status);
+    }
     return hipGetLastError();
 }
 

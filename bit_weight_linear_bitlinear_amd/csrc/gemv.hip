@@ -60,7 +60,6 @@ hipError_t launch_gemv_group(const LinearArgs* mats, int count, hipStream_t stre
         cfg.sps = sps;
         gp.upg = a.group / (SK / sps);
         gp.upg_shift = log2_exact(gp.upg);
-        gp.upg_magic = (uint32_t)((((uint64_t)1 << 32) + (uint64_t)gp.upg - 1) / (uint64_t)gp.upg);
     }
     gp.stride = n_steps * SK + 16;
     cfg.lds_a = (int64_t)a.t * gp.stride <= kGemvLdsA;

@@ -29,7 +29,6 @@ struct GemvParams {
     int G;               // scale groups per row (group mode)
     int upg;             // group mode: scale units per group
     int upg_shift;       // log2(upg), or -1 when upg is not a power of two
-    uint32_t upg_magic;  // ceil(2^32 / upg): x / upg = umulhi(x, magic) for the small x used
     int scale_per_row;   // tensor/row mode: 1 = scales[n], 0 = scales[0]
     int ksplit;          // wavefronts sharing one tile's k-range (1, 2, 4)
     int ksplit_log;

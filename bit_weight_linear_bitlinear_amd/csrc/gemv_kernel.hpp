@@ -70,10 +70,11 @@ __device__ __forceinline__ i32x4 load_q16(const int8_t* qrow, int k0, int K, boo
 
 // NR: C registers per lane holding live tokens (token = 4 * lane group + r).
 // SPS: group mode: scale units per k-step; 0 = tensor/row scales.
+// UPG1: group mode: every scale unit is a whole group.
 // LDSA: activations staged in LDS.  ACC: also write the integer products
 // (kept out of the streaming instantiations: optional stores inside the
 // k-loop make the compiler's wait counting conservative).
-template <int FMT, int WPL, int NR, int SPS, bool LDSA, bool ACC>
+template <int FMT, int WPL, int NR, int SPS, bool UPG1, bool LDSA, bool ACC>
 __global__ __launch_bounds__(256) void gemv_kernel(const GemvParams p) {
     using S = GemvShape<FMT, WPL>;
     constexpr int D = kGemvD;
@@ -127,10 +128,12 @@ __global__ __launch_bounds__(256) void gemv_kernel(const GemvParams p) {
     float sg[D][NU];
     i32x4 av[D][NA];
 
-    auto div_upg = [&](int x) -> int {                       // x / upg
-        return p.upg_shift >= 0 ? (x >> p.upg_shift) : (int)__umulhi((uint32_t)x, p.upg_magic);
-    };
-    auto unit_group = [&](int U) -> int { return min(div_upg(U), p.G - 1); };   // scale group of unit U
+    // Scale units run in order on both sides of the ring, so the group of a
+    // unit is tracked with running counters (a part always starts at a group
+    // boundary): lu/lg for the loads, cu/cg for the compute.
+    const int unit0 = s0 * NU;
+    const int g0 = UPG1 ? unit0 : (p.upg_shift >= 0 ? unit0 >> p.upg_shift : unit0 / p.upg);
+    int lu = 0, lg = g0;                                     // load side: unit within group, group
     auto load_slot = [&](int u, int j) {
         // Unconditional loads (a dead step past the part re-reads its last
         // step, never consumed): the compiler's wait counting then keeps all
@@ -139,7 +142,15 @@ __global__ __launch_bounds__(256) void gemv_kernel(const GemvParams p) {
         load_words<WPL>(wp + (size_t)jj * STEP, 4 * WPL, true, wv[u]);
         if constexpr (GROUP) {
             #pragma unroll
-            for (int v = 0; v < NU; ++v) sg[u][v] = scp[unit_group((s0 + jj) * SPS + v) * 16];
+            for (int v = 0; v < NU; ++v) {
+                sg[u][v] = scp[min(lg, p.G - 1) * 16];
+                if constexpr (UPG1) {
+                    ++lg;
+                } else {
+                    lu = lu + 1 == p.upg ? 0 : lu + 1;
+                    lg = lu == 0 ? lg + 1 : lg;
+                }
+            }
         }
         if constexpr (!LDSA) {
             #pragma unroll
@@ -184,63 +195,90 @@ __global__ __launch_bounds__(256) void gemv_kernel(const GemvParams p) {
         __syncthreads();
     }
 
-    i32x4 C = {0, 0, 0, 0};
-    float yp[NR];
+    i32x4 C = {0, 0, 0, 0};                                  // tensor/row mode: the whole product
+    float yp[NR];                                            // group mode: rescaled partial sums
     #pragma unroll
     for (int r = 0; r < NR; ++r) yp[r] = 0.0f;
+
+    const int n_units = (K + SK / NU - 1) / (SK / NU);       // scale units holding real k
+    int cu = 0, cg = g0, cunit = unit0;                      // compute side: unit in group, group, unit
+    i32x4 Cg = {0, 0, 0, 0};                                 // group partial (groups of several units)
+
+    // MFMAs of block b of slot u into C
+    auto block_mfma = [&](int u, int s, int b, i32x4 C, bool fresh) -> i32x4 {
+        const i32x4 zero = {0, 0, 0, 0};
+        i32x4 A[MPB];
+        if constexpr (LDSA) {
+            #pragma unroll
+            for (int m = 0; m < MPB; ++m) A[m] = *reinterpret_cast<const i32x4*>(lds_a + s * SK + b * KB + 16 * m);
+        } else if constexpr (FMT == FMT_BINARY) {
+            // binary padding codes decode as +1: activations past K must be zero
+            const int k0 = s * SK + b * KB + g * (KB / 4);
+            i32x4 lo = av[u][2 * b], hi = av[u][2 * b + 1];
+            if (k0 >= K) lo = zero;
+            if (k0 + 16 >= K) hi = zero;
+            const uint32_t X[8] = {(uint32_t)lo[0], (uint32_t)lo[1], (uint32_t)lo[2], (uint32_t)lo[3],
+                                   (uint32_t)hi[0], (uint32_t)hi[1], (uint32_t)hi[2], (uint32_t)hi[3]};
+            perm_binary_a(X, A[0], A[1]);
+        } else {
+            A[0] = av[u][b];                                 // padding codes are 0: any A is fine
+        }
+        if constexpr (FMT == FMT_TERNARY) {
+            C = mfma16(A[0], decode_ternary(wv[u][b]), fresh ? zero : C);
+        } else if constexpr (FMT == FMT_INT4) {
+            C = mfma16(A[0], decode_int4(wv[u][2 * b], wv[u][2 * b + 1]), fresh ? zero : C);
+        } else {
+            i32x4 b0, b1;
+            decode_binary(wv[u][b], b0, b1);
+            C = mfma16(A[0], b0, fresh ? zero : C);
+            C = mfma16(A[1], b1, C);
+        }
+        return C;
+    };
+    // a group's integer partial is complete: rescale into yp (and record it)
+    auto close_group = [&](const i32x4& Cx, float sc, int gi) {
+        #pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            const int32_t a = Cx[r] >> SHIFT;
+            yp[r] = yp[r] + sc * (float)a;
+            if constexpr (ACC) {
+                const int t = 4 * g + r;
+                if (M.acc && live && t < T && row < M.n) M.acc[((size_t)t * M.n + row) * p.G + gi] = a;
+            }
+        }
+    };
 
     auto compute_slot = [&](int u, int j) {
         if (j >= s_cnt) return;                              // dead step (uniform)
         const int s = s0 + j;
-        #pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            i32x4 A[MPB];
-            if constexpr (LDSA) {
+        if constexpr (!GROUP) {
+            #pragma unroll
+            for (int b = 0; b < NB; ++b) C = block_mfma(u, s, b, C, false);
+        } else {
+            #pragma unroll
+            for (int v = 0; v < NU; ++v) {
+                i32x4 Cu = {0, 0, 0, 0};                     // this unit's partial: a fresh chain
                 #pragma unroll
-                for (int m = 0; m < MPB; ++m)
-                    A[m] = *reinterpret_cast<const i32x4*>(lds_a + s * SK + b * KB + 16 * m);
-            } else if constexpr (FMT == FMT_BINARY) {
-                // binary padding codes decode as +1: activations past K must be zero
-                const int k0 = s * SK + b * KB + g * (KB / 4);
-                i32x4 lo = av[u][2 * b], hi = av[u][2 * b + 1];
-                if (k0 >= K) lo = i32x4{0, 0, 0, 0};
-                if (k0 + 16 >= K) hi = i32x4{0, 0, 0, 0};
-                const uint32_t X[8] = {(uint32_t)lo[0], (uint32_t)lo[1], (uint32_t)lo[2], (uint32_t)lo[3],
-                                       (uint32_t)hi[0], (uint32_t)hi[1], (uint32_t)hi[2], (uint32_t)hi[3]};
-                perm_binary_a(X, A[0], A[1]);
-            } else {
-                A[0] = av[u][b];                             // padding codes are 0: any A is fine
-            }
-            if constexpr (FMT == FMT_TERNARY) {
-                C = mfma16(A[0], decode_ternary(wv[u][b]), C);
-            } else if constexpr (FMT == FMT_INT4) {
-                C = mfma16(A[0], decode_int4(wv[u][2 * b], wv[u][2 * b + 1]), C);
-            } else {
-                i32x4 b0, b1;
-                decode_binary(wv[u][b], b0, b1);
-                C = mfma16(A[0], b0, C);
-                C = mfma16(A[1], b1, C);
-            }
-            if constexpr (GROUP) {
-                if (b % BPU == BPU - 1) {
-                    const int v = b / BPU;
-                    const int U = s * SPS + v;
-                    const int uk = SK / SPS;
-                    const bool group_last = div_upg(U + 1) * p.upg == U + 1;
-                    if (U * uk < K && (group_last || (U + 1) * uk >= K)) {   // uniform
+                for (int bb = 0; bb < BPU; ++bb) Cu = block_mfma(u, s, v * BPU + bb, Cu, bb == 0);
+                const bool real = cunit < n_units;           // (uniform) units past k hold only padding
+                if constexpr (UPG1) {
+                    // padding units add exact zeros (and never record a partial)
+                    if constexpr (ACC) { if (real) close_group(Cu, sg[u][v], cg); }
+                    else close_group(Cu, sg[u][v], cg);
+                    ++cg;
+                } else {
+                    #pragma unroll
+                    for (int r = 0; r < NR; ++r) Cg[r] += Cu[r];
+                    const bool last = cu + 1 == p.upg || cunit + 1 == n_units;
+                    if (real && last) {                      // uniform
+                        close_group(Cg, sg[u][v], cg);
                         #pragma unroll
-                        for (int r = 0; r < NR; ++r) {
-                            const int32_t a = C[r] >> SHIFT;
-                            yp[r] = yp[r] + sg[u][v] * (float)a;
-                            if constexpr (ACC) {
-                                const int t = 4 * g + r;
-                                if (M.acc && live && t < T && row < M.n)
-                                    M.acc[((size_t)t * M.n + row) * p.G + unit_group(U)] = a;
-                            }
-                        }
-                        C = i32x4{0, 0, 0, 0};
+                        for (int r = 0; r < NR; ++r) Cg[r] = 0;
                     }
+                    cu = cu + 1 == p.upg ? 0 : cu + 1;
+                    cg = cu == 0 ? cg + 1 : cg;
                 }
+                ++cunit;
             }
         }
     };
@@ -299,16 +337,16 @@ __global__ __launch_bounds__(256) void gemv_kernel(const GemvParams p) {
     }
 }
 
-template <int FMT, int WPL, int NR, int SPS>
+template <int FMT, int WPL, int NR, int SPS, bool UPG1>
 void gemv_launch_lds(const GemvParams& p, const GemvCfg& c, hipStream_t st) {
     const dim3 grid((unsigned)c.grid), block(256);
     if (c.lds_a) {
-        if (c.acc) gemv_kernel<FMT, WPL, NR, SPS, true, true><<<grid, block, c.lds_bytes, st>>>(p);
-        else gemv_kernel<FMT, WPL, NR, SPS, true, false><<<grid, block, c.lds_bytes, st>>>(p);
+        if (c.acc) gemv_kernel<FMT, WPL, NR, SPS, UPG1, true, true><<<grid, block, c.lds_bytes, st>>>(p);
+        else gemv_kernel<FMT, WPL, NR, SPS, UPG1, true, false><<<grid, block, c.lds_bytes, st>>>(p);
     } else {
         // activations from L2: the large-t*k fallback, always 4 token registers
-        if (c.acc) gemv_kernel<FMT, WPL, 4, SPS, false, true><<<grid, block, c.lds_bytes, st>>>(p);
-        else gemv_kernel<FMT, WPL, 4, SPS, false, false><<<grid, block, c.lds_bytes, st>>>(p);
+        if (c.acc) gemv_kernel<FMT, WPL, 4, SPS, UPG1, false, true><<<grid, block, c.lds_bytes, st>>>(p);
+        else gemv_kernel<FMT, WPL, 4, SPS, UPG1, false, false><<<grid, block, c.lds_bytes, st>>>(p);
     }
 }
 
@@ -317,8 +355,16 @@ void gemv_launch_wpl(const GemvParams& p, const GemvCfg& c, hipStream_t st) {
     constexpr int NB = GemvShape<FMT, WPL>::kNB;
     auto by_nr = [&](auto sps_tag) {
         constexpr int SPS = decltype(sps_tag)::value;
-        if (c.nr == 1 && c.lds_a) gemv_launch_lds<FMT, WPL, 1, SPS>(p, c, st);
-        else gemv_launch_lds<FMT, WPL, 4, SPS>(p, c, st);
+        if constexpr (SPS == 0) {
+            if (c.nr == 1 && c.lds_a) gemv_launch_lds<FMT, WPL, 1, 0, false>(p, c, st);
+            else gemv_launch_lds<FMT, WPL, 4, 0, false>(p, c, st);
+        } else if (p.upg == 1) {
+            if (c.nr == 1 && c.lds_a) gemv_launch_lds<FMT, WPL, 1, SPS, true>(p, c, st);
+            else gemv_launch_lds<FMT, WPL, 4, SPS, true>(p, c, st);
+        } else {
+            if (c.nr == 1 && c.lds_a) gemv_launch_lds<FMT, WPL, 1, SPS, false>(p, c, st);
+            else gemv_launch_lds<FMT, WPL, 4, SPS, false>(p, c, st);
+        }
     };
     switch (c.sps) {
         case 0: by_nr(std::integral_constant<int, 0>{}); break;
