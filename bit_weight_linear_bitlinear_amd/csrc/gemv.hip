@@ -1,6 +1,7 @@
 // gemv.hip - host-side dispatch of the decode GEMV (the kernel itself is in
 // gemv_kernel.hpp, instantiated per format in gemv_{ternary,int4,binary}.hip).
 #include <algorithm>
+#include <climits>
 
 #include "device_common.hpp"
 #include "gemv.hpp"
@@ -109,7 +110,7 @@ hipError_t launch_gemv_group(const LinearArgs* mats, int count, hipStream_t stre
         gp.wg_start[i] = wgs;
         wgs += (gp.m[i].n_tiles + gp.tiles_per_wg - 1) / gp.tiles_per_wg;
     }
-    gp.wg_start[count] = wgs;
+    for (int i = count; i <= kGemvMaxMats; ++i) gp.wg_start[i] = 0x7fffffff;   // never reached
     cfg.grid = wgs;
     cfg.lds_bytes = (size_t)gp.lds_a_bytes + (ksplit > 1 ? (size_t)4 * cfg.nr * 64 * 4 : 0);
 

@@ -37,7 +37,7 @@ struct GemvParams {
     int stride;          // LDS bytes per staged token row (k padded + 16)
     int q_vec;           // k % 16 == 0 and every q 16-byte aligned
     int lds_a_bytes;     // T * stride when activations are staged in LDS, else 0
-    int wg_start[kGemvMaxMats + 1];   // first workgroup of each matrix (ascending)
+    int wg_start[kGemvMaxMats + 1];   // first workgroup of each matrix (ascending; INT_MAX past n_mats)
     GemvMat m[kGemvMaxMats];
 };
 

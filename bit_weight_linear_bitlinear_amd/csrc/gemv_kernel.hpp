@@ -94,11 +94,11 @@ __global__ __launch_bounds__(256) void gemv_kernel(const GemvParams p) {
     const int g = lane >> 4;                                 // lane group
     const int rl = lane & 15;                                // weight row in the tile / token of A
 
-    int mi = 0;                                              // matrix of this workgroup
-    for (int hi = p.n_mats - 1; mi < hi;) {
-        const int mid = (mi + hi + 1) >> 1;
-        if ((int)blockIdx.x >= p.wg_start[mid]) mi = mid; else hi = mid - 1;
-    }
+    // matrix of this workgroup: one batch of independent scalar loads and
+    // compares (no chain of dependent loads before the first weight load)
+    int mi = 0;
+    #pragma unroll
+    for (int i = 1; i < kGemvMaxMats; ++i) mi += (int)blockIdx.x >= p.wg_start[i] ? 1 : 0;
     const GemvMat& M = p.m[mi];
     const int part = wave & (p.ksplit - 1);
     const int tile_raw = ((int)blockIdx.x - p.wg_start[mi]) * p.tiles_per_wg + (wave >> p.ksplit_log);
@@ -110,15 +110,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const GemvParams p) {
     const int K = p.K, T = p.T;
     const int tok = min(rl, T - 1);                          // A row; rows >= t are never stored
 
-    // per-tile operands, loaded once (before the ring, so in-order completion
-    // makes them ready by the first step)
     const int row = tile * 16 + rl;
-    const int row_c = min(row, M.n - 1);
-    float sw = 0.0f;
-    if constexpr (!GROUP) sw = M.scales[p.scale_per_row ? row_c : 0];
-    float sxv[NR];
-    #pragma unroll
-    for (int r = 0; r < NR; ++r) sxv[r] = M.sx[min(4 * g + r, T - 1)];
 
     const uint8_t* wp = M.packed + ((size_t)tile * p.n_steps + s0) * STEP + lane * (4 * WPL);
     const float* scp = M.scales + (size_t)tile * p.G * 16 + rl;            // group mode
@@ -164,11 +156,16 @@ __global__ __launch_bounds__(256) void gemv_kernel(const GemvParams p) {
         }
     };
 
-    // ---- ring prologue, then the activation stage
+    // ---- ring prologue, the epilogue operands, then the activation stage
     if (s_cnt > 0) {
         #pragma unroll
         for (int u = 0; u < D; ++u) load_slot(u, u);
     }
+    float sw = 0.0f;
+    if constexpr (!GROUP) sw = M.scales[p.scale_per_row ? min(row, M.n - 1) : 0];
+    float sxv[NR];
+    #pragma unroll
+    for (int r = 0; r < NR; ++r) sxv[r] = M.sx[min(4 * g + r, T - 1)];
     const int8_t* lds_a = reinterpret_cast<const int8_t*>(smem) + (size_t)tok * p.stride + g * (KB / 4);
     if constexpr (LDSA) {
         const int kpad = p.n_steps * SK;

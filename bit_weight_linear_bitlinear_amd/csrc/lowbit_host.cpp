@@ -302,10 +302,13 @@ lowbit_status lowbit_linear_grouped(int32_t count, const lowbit_desc* descs, con
             a.y += (size_t)t0 * a.n;
             if (a.acc) a.acc += (size_t)t0 * a.n * a.n_groups;
         }
-        for (int32_t b = 0; b < count; b += lowbit::kGemvMaxMats) {
-            const int32_t c = std::min(count - b, lowbit::kGemvMaxMats);
-            lowbit_status st = hip_status(lowbit::launch_gemv_group(chunk.data() + b, c, stream));
+        // as few launches as the kernel-argument space allows, of near-equal size
+        const int32_t launches = (count + lowbit::kGemvMaxMats - 1) / lowbit::kGemvMaxMats;
+        for (int32_t li = 0, b = 0; li < launches; ++li) {
+            const int32_t e = (int32_t)((int64_t)count * (li + 1) / launches);
+            lowbit_status st = hip_status(lowbit::launch_gemv_group(chunk.data() + b, e - b, stream));
             if (st != LOWBIT_OK) return st;
+            b = e;
         }
     }
     return LOWBIT_OK;
