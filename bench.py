@@ -235,6 +235,40 @@ def per_launch(p: Pass, reps: int):
     return total / (n * reps), sum(p.linear_bytes) / n, sum(p.linear_ops) / n
 
 
+def gemm_profile(args):
+    """The int4 prefill pass alone, then each distinct GEMM shape timed on its
+    own (HIP events on the launching stream)."""
+    import torch
+    import workloads
+    wl4 = workloads.BY_NAME["int4_t4nt"]
+    p4 = Pass(wl4, wl4.tokens[0], "gemm", layers=args.layers)
+    run = (None if args.no_graph else capture(p4.step)) or p4.step
+    el, _ = time_steps(run, args.steps, args.warmup)
+    st = el / args.steps
+    log(f"[bench] gemm pass: {sum(p4.linear_ops) / st / 1e12:.1f} TOPS/step, {st * 1e3:.3f} ms/step")
+    p4.act_quant()
+    torch.cuda.synchronize()
+    seen = {}
+    for i, (layer, mi, m) in enumerate(p4.mats):
+        seen.setdefault((m.n, m.k), i)
+    for (n, k), i in seen.items():
+        q, sx = p4.views[i]
+        d = p4.desc[i]
+        for _ in range(2):
+            p4.fn(d, p4.packed[i], p4.scales[i], q, sx, p4.y[i])
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 10
+        e0.record()
+        for _ in range(reps):
+            p4.fn(d, p4.packed[i], p4.scales[i], q, sx, p4.y[i])
+        e1.record()
+        torch.cuda.synchronize()
+        dt = e0.elapsed_time(e1) / reps / 1e3
+        ops = 2.0 * p4.t * n * k
+        log(f"[bench] gemm N={n} K={k} T={p4.t}: {dt * 1e6:.1f} us, {ops / dt / 1e12:.1f} TOPS "
+            f"({100 * ops / dt / 1e12 / I8_PEAK_TOPS:.1f}% of peak)")
+
+
 def copy_calibration(nbytes=1 << 30, reps=5):
     """A plain copy of known size (torch's copy kernel): its rate is the
     practical streaming ceiling of this GPU, and its FETCH_SIZE / WRITE_SIZE
@@ -347,6 +381,8 @@ def main():
     ap.add_argument("--skip-check", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--quick", action="store_true", help="grouped schedule only")
+    ap.add_argument("--profile-gemm", action="store_true",
+                    help="batched GEMM pass only, with per-shape launch timings (for profiler runs)")
     ap.add_argument("--profile-pass", action="store_true",
                     help="copy calibration + grouped GEMV pass only (for profiler runs)")
     args = ap.parse_args()
@@ -364,6 +400,10 @@ def main():
         args.quick = args.skip_gemm = args.skip_cpu = args.skip_check = True
     calib = copy_calibration()
     log(f"[bench] copy calibration: {calib}")
+
+    if args.profile_gemm:
+        gemm_profile(args)
+        return
 
     # ---- GEMV line: ternary_4b decode pass
     wl = workloads.BY_NAME["ternary_4b"]

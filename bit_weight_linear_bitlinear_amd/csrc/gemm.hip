@@ -274,7 +274,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     }
 }
 
-hipError_t launch_gemm(const LinearArgs& a, hipStream_t stream) {
+// the general path: any k, any alignment (ragged tails read byte by byte)
+hipError_t launch_gemm_generic(const LinearArgs& a, hipStream_t stream) {
     GemmArgs ga;
     ga.packed = a.packed; ga.scales = a.scales; ga.q = a.q; ga.sx = a.sx; ga.y = a.y; ga.acc = a.acc;
     ga.wpl = a.wpl; ga.lay_steps = a.n_steps; ga.n_rows_pad = (a.n + 15) / 16 * 16;
@@ -301,6 +302,10 @@ hipError_t launch_gemm(const LinearArgs& a, hipStream_t stream) {
             break;
     }
     return hipGetLastError();
+}
+
+hipError_t launch_gemm(const LinearArgs& a, hipStream_t stream) {
+    return gemm_mfma_supported(a) ? launch_gemm_mfma(a, stream) : launch_gemm_generic(a, stream);
 }
 
 }  // namespace lowbit

@@ -103,6 +103,10 @@ def run_layer(w, x, fmt, scale, group, tanh, entries=("gemv", "gemm"), token_sam
         assert (acc_h == acc_ref).all(), (f"{label} {entry}: int32 accumulators differ in "
                                           f"{int((acc_h != acc_ref).sum())} places")
         check_y(y.cpu().numpy()[sel], y32, y64, f"{label} {entry}")
+        # the streaming kernels (no integer output) must give the same y bit for bit
+        y_stream, _ = linear_dev(entry, d, packed, scales, q, sx, with_acc=False)
+        torch.cuda.synchronize()
+        assert torch.equal(y_stream, y), f"{label} {entry}: y without acc differs from y with acc"
         out[entry] = (y, acc)
     if len(entries) == 2:
         a0, a1 = out["gemv"][1], out["gemm"][1]
