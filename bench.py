@@ -25,6 +25,7 @@ import argparse
 import json
 import math
 import os
+import re
 import sys
 import time
 from concurrent.futures import ThreadPoolExecutor
@@ -195,43 +196,74 @@ def time_steps(run, steps, warmup):
 
 
 def per_launch_grouped(p: Pass, calls, reps: int):
-    """Average duration of one gemv launch of a grouped schedule, from HIP
-    events recorded on the launching stream around every grouped call
-    (act-quant excluded); a call of c matrices issues ceil(c / 40) launches."""
+    """Average duration of one gemv launch of a grouped schedule: the gemv
+    launches alone (inputs quantised beforehand) captured in a HIP graph and
+    replayed `reps` times between two HIP events on the replaying stream; a
+    call of c matrices issues ceil(c / 40) launches."""
     import torch
     p.act_quant()
     torch.cuda.synchronize()
-    evs = []
-    for _ in range(reps):
+
+    def gemvs():
         for c in calls:
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
             c()
-            b.record()
-            evs.append((a, b))
+    run = capture(gemvs) or gemvs
+    run()
     torch.cuda.synchronize()
-    total = sum(a.elapsed_time(b) for a, b in evs) / 1e3
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    total = e0.elapsed_time(e1) / 1e3
     n_launch = p.launches(calls) * reps
     return total / n_launch, sum(p.linear_bytes) / p.launches(calls)
 
 
+def committed_traffic():
+    """HBM bytes per grouped gemv launch from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE scaled by a copy of known size), or None
+    when the GEMV sources have changed since those counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "gemv_ternary_4b_t1_traffic.md")
+    try:
+        text = open(path).read()
+    except OSError:
+        return None
+    vals = dict(re.findall(r"^(traffic_bytes_per_launch|kernel_source_sha256): (\S+)$", text, re.M))
+    h = hashlib.sha256()
+    for f in ("gemv_kernel.hpp", "gemv.hip", "gemv.hpp", "device_common.hpp"):
+        with open(os.path.join(ROOT, "bit_weight_linear_bitlinear_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if vals.get("kernel_source_sha256") != h.hexdigest() or "traffic_bytes_per_launch" not in vals:
+        return None
+    return float(vals["traffic_bytes_per_launch"])
+
+
 def per_launch(p: Pass, reps: int):
-    """Average duration of the product kernel, from HIP events recorded on the
-    launching stream around every launch (act-quant excluded)."""
+    """Average duration of the product kernel: every product of the pass
+    (inputs quantised beforehand) captured in a HIP graph and replayed `reps`
+    times between two HIP events on the replaying stream."""
     import torch
     p.act_quant()
     torch.cuda.synchronize()
-    n = len(p.desc)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n * reps)]
-    for r in range(reps):
+
+    def products():
         for i, d in enumerate(p.desc):
             q, sx = p.views[i]
-            a, b = evs[r * n + i]
-            a.record()
             p.fn(d, p.packed[i], p.scales[i], q, sx, p.y[i])
-            b.record()
+    run = capture(products) or products
+    run()
     torch.cuda.synchronize()
-    total = sum(a.elapsed_time(b) for a, b in evs) / 1e3
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    total = e0.elapsed_time(e1) / 1e3
+    n = len(p.desc)
     return total / (n * reps), sum(p.linear_bytes) / n, sum(p.linear_ops) / n
 
 
@@ -425,7 +457,7 @@ def main():
     head = schedules["grouped"]
     step_s = head["ms_per_step"] / 1e3
     value = p.step_bytes / step_s / 1e9
-    dur, bytes_per_launch = per_launch_grouped(p, p.grouped_calls, reps=5)
+    dur, bytes_per_launch = per_launch_grouped(p, p.grouped_calls, reps=10)
     achieved = bytes_per_launch / dur / 1e9
     check = None if args.skip_check else sampled_check(p, [0, 4, 6, len(p.mats) - 1])
 
@@ -439,7 +471,7 @@ def main():
                    "tokens": args.tokens, "matrices": len(p.mats), "bytes_per_step": p.step_bytes,
                    "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2), "schedules": schedules},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": committed_traffic(),
                      "kernel": "gemv_kernel (grouped schedule)", "avg_launch_us": round(dur * 1e6, 3),
                      "bytes_per_launch": round(bytes_per_launch)},
     })
@@ -456,14 +488,14 @@ def main():
         el4, _ = time_steps(r4, max(3, args.steps // 4), 1)
         st4 = el4 / max(3, args.steps // 4)
         ops4 = sum(p4.linear_ops)
-        d4, _, ops_per_launch = per_launch(p4, reps=1)
+        d4, _, ops_per_launch = per_launch(p4, reps=3)
         tops_launch = ops_per_launch / d4 / 1e12
         chk4 = None if args.skip_check else sampled_check(p4, [0, 1, 4], rows_per=32)
         out["gemm"] = {"workload": "int4_t4nt prefill pass: 100 int4 row-scale GEMMs, T=4096, act-quant included",
                        "tops_step": round(ops4 / st4 / 1e12, 2), "ms_per_step": round(st4 * 1e3, 4),
                        "tops_per_launch": round(tops_launch, 2),
                        "pct_mfma_peak": round(100 * tops_launch / I8_PEAK_TOPS, 2),
-                       "avg_launch_us": round(d4 * 1e6, 2), "kernel": "gemm_kernel", "check": chk4}
+                       "avg_launch_us": round(d4 * 1e6, 2), "kernel": "gemm_mfma_kernel", "check": chk4}
         log(f"[bench] gemm pass: {ops4 / st4 / 1e12:.1f} TOPS/step; per launch {tops_launch:.1f} TOPS")
         del p4
 
