@@ -129,6 +129,22 @@ __device__ __forceinline__ void load_words(const uint8_t* p, int valid, bool ali
     }
 }
 
+// NWORDS aligned words read with the non-temporal hint: data that is read
+// exactly once (the decode GEMV's weight stream) should not displace reused
+// lines in the caches.
+template <int NWORDS>
+__device__ __forceinline__ void load_words_stream(const uint8_t* p, uint32_t* out) {
+    if constexpr (NWORDS == 4) {
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+        out[0] = v[0]; out[1] = v[1]; out[2] = v[2]; out[3] = v[3];
+    } else if constexpr (NWORDS == 2) {
+        const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+        out[0] = v[0]; out[1] = v[1];
+    } else {
+        out[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+    }
+}
+
 __device__ __forceinline__ float wave_max(float v) {
     #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {

@@ -18,9 +18,11 @@
 // row (l % 16) and lane group (l / 16) holds a quarter of every block, which
 // is exactly how the packed layout orders a (tile, k-step) - so a wavefront
 // reads one k-step of its tile as ONE contiguous 256 * wpl-byte block, one
-// 4 * wpl-byte load per lane (1 KB per wavefront for wpl = 4).  Each
-// wavefront keeps the loads of the next D k-steps in flight (a register ring,
-// refilled right after each step is consumed).  The activation codes (the
+// 4 * wpl-byte load per lane (1 KB per wavefront for wpl = 4), with the
+// non-temporal hint (the stream is read once and must not evict the reused
+// activation and scale lines).  Each wavefront keeps the loads of the next D
+// k-steps in flight (a register ring, refilled right after each step is
+// consumed).  The activation codes (the
 // MFMA A operand: tokens x k) are staged once per workgroup in LDS, zero
 // padded to whole k-steps, and read from there; binary activations are staged
 // already permuted to the packbits code order.  When t * k is too large for
@@ -131,7 +133,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const GemvParams p) {
         // step, never consumed): the compiler's wait counting then keeps all
         // D steps in flight.
         const int jj = j < s_cnt ? j : s_cnt - 1;
-        load_words<WPL>(wp + (size_t)jj * STEP, 4 * WPL, true, wv[u]);
+        load_words_stream<WPL>(wp + (size_t)jj * STEP, wv[u]);      // each weight byte is read once
         if constexpr (GROUP) {
             #pragma unroll
             for (int v = 0; v < NU; ++v) {
