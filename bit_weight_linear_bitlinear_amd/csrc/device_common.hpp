@@ -76,6 +76,17 @@ __device__ __forceinline__ void decode_binary(uint32_t w, i32x4& o0, i32x4& o1) 
     o1[3] = (int32_t)((w & 0x80808080u) | 0x40404040u);
 }
 
+// one of the two operands of decode_binary (op 0: registers 0..3, op 1: 4..7)
+__device__ __forceinline__ i32x4 decode_binary_half(uint32_t w, int op) {
+    const int sh = op == 0 ? 7 : 3;
+    i32x4 o;
+    o[0] = (int32_t)(((w << sh) & 0x80808080u) | 0x40404040u);
+    o[1] = (int32_t)(((w << (sh - 1)) & 0x80808080u) | 0x40404040u);
+    o[2] = (int32_t)(((w << (sh - 2)) & 0x80808080u) | 0x40404040u);
+    o[3] = (int32_t)(((w << (sh - 3)) & 0x80808080u) | 0x40404040u);
+    return o;
+}
+
 // 4x4 byte transpose: out[j] byte i = in[i] byte j  (8 v_perm_b32)
 __device__ __forceinline__ void transpose4x4(uint32_t a, uint32_t b, uint32_t c, uint32_t d, i32x4& o) {
     // v_perm_b32(s0, s1, sel): byte i of the result = byte sel[i] of {s0:s1},

@@ -4,28 +4,31 @@
 // What it computes (M8.8 "Native Binary and Ternary Transformers", 0x02D,
 // 0x09C): acc[t, n] = sum_k q[t, k] * code[n, k] exactly in int32 (per scale
 // group in group mode), then the fp32 rescale.  Prefill is a dense contraction
-// (0x09B), so the work is v_mfma_i32_16x16x64_i8 with the packed codes decoded
+// (0x09B), so the work is v_mfma_i32_32x32x32_i8 with the packed codes decoded
 // in registers right before each MFMA.
 //
-// Tiling.  A 256-thread workgroup owns a 128-token x 128-row output tile; its
-// four wavefronts are a 2 x 2 grid of 64 x 64 sub-tiles (4 x 4 MFMA blocks).
-// k advances one packed-layout k-step (SK codes) at a time.  Each step's
-// operands are copied global -> LDS by the memory unit itself (16-byte
-// direct-to-LDS loads: no registers, no LDS write instructions), NS steps in
-// flight:
-//  - activations: 1 KB LDS pieces, one per (64-k chunk, 16-token block), laid
-//    out exactly as an MFMA A operand (lane l: token l % 16, bytes 16 (l / 16)
-//    .. of the chunk; binary chunks follow the quarter / half order of a
-//    128-code block), so every operand read is one contiguous, conflict-free
-//    1 KB ds_read_b128;
-//  - weights: the packed (16-row tile, k-step) blocks, copied as they are - the
-//    packed layout already is the per-lane B operand order.
-// The compiler does not track the LDS side of these loads, so the pipeline
-// waits with explicit vmcnt counts (every load of a step is unconditional)
-// followed by a workgroup barrier.  Tokens past t and rows past n read clamped
-// (valid) addresses; their results are never stored.  Binary activations past
-// k are zeroed in registers (binary padding codes decode as +1; ternary and
-// int4 padding codes are 0).
+// Tiling.  A 512-thread workgroup owns a 256-token x 256-row output tile; its
+// eight wavefronts (two per SIMD) are a 2 x 4 grid of 128 x 64 sub-tiles, i.e.
+// 4 x 2 blocks of 32 x 32.  (TILE 0: 128 x 128 with four wavefronts of 64 x 64,
+// two workgroups per CU.)  k advances one packed-layout k-step (SK codes) at a
+// time.  Each step's operands are copied global -> LDS by the memory unit itself
+// (16-byte direct-to-LDS loads: no registers, no LDS write instructions), NS
+// steps in flight:
+//  - activations: row-major [tile token][SK bytes], every copy reading whole
+//    128-byte lines (a copy of 1 KB covers 1024 / SK rows), the 16-byte chunks
+//    of a row XOR-swizzled with the row number so that the operand reads - 32
+//    rows at one k offset - hit 16 different bank groups;
+//  - weights: the packed (16-row tile, k-step) blocks as they are.
+// MFMA operand lanes: lane l holds token / row l % 32 and 16 k values of half
+// h = l / 32.  Half h takes the packed lane groups 2h and 2h + 1 of a 16-row
+// tile, i.e. k offsets 32h .. 32h + 31 of each 64-code chunk (binary: 64h ..
+// 64h + 63 of each 128-code chunk, bit order matched by perm_binary_a).
+// The compiler does not track the LDS side of the copies, so the pipeline waits
+// with explicit vmcnt counts (every copy of a step is unconditional) followed
+// by a workgroup barrier.  Tokens past t and rows past n read clamped (valid)
+// addresses; their results are never stored.  Binary activations past k are
+// zeroed in registers (binary padding codes decode as +1; ternary and int4
+// padding codes are 0).
 //
 // Workgroups are numbered so that each XCD (workgroup i runs on XCD i % 8)
 // owns a contiguous run of output tiles, token-block-major: the weight matrix
@@ -36,6 +39,8 @@
 #include "kernels.hpp"
 
 namespace lowbit {
+
+typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
 
 struct GemmFastArgs {
     const uint8_t* packed;
@@ -50,20 +55,16 @@ struct GemmFastArgs {
     int group;          // group mode: columns per group
     int G;              // group mode: groups per row
     int scale_per_row;
-    int mb, nb;         // token blocks, row blocks (of 128)
+    int mb, nb;         // token blocks, row blocks
 };
 
-// Workgroup tile configurations.  TILE 0: 2 x 2 wavefronts of 64 tokens x 64
-// rows (4 x 4 MFMA blocks), a 128 x 128 tile, two workgroups per CU.
-// TILE 1: 2 x 4 wavefronts of 128 tokens x 64 rows (8 x 4 blocks), a 256 x 256
-// tile - twice the MFMA work per staged byte - with eight wavefronts, i.e. two
-// per SIMD (one wavefront alone cannot issue i8 MFMAs back to back).
+// Workgroup tile configurations (blocks of 32 x 32 per wavefront).
 template <int TILE> struct TileCfg;
 template <> struct TileCfg<0> {
-    static constexpr int WAVES_M = 2, WAVES_N = 2, WMB = 4, WNB = 4, BUDGET = 73728;
+    static constexpr int WAVES_M = 2, WAVES_N = 2, WMB = 2, WNB = 2, BUDGET = 73728;
 };
 template <> struct TileCfg<1> {
-    static constexpr int WAVES_M = 2, WAVES_N = 4, WMB = 8, WNB = 4, BUDGET = 163840;
+    static constexpr int WAVES_M = 2, WAVES_N = 4, WMB = 4, WNB = 2, BUDGET = 163840;
 };
 
 template <int FMT, int WPL, int TILE> struct GemmShape {
@@ -72,9 +73,10 @@ template <int FMT, int WPL, int TILE> struct GemmShape {
     static constexpr int NW = WAVES_M * WAVES_N;             // wavefronts per workgroup
     static constexpr int CPW = Fmt<FMT>::kCodesPerWord;
     static constexpr int SK = 4 * WPL * CPW;                // k per packed-layout step
-    static constexpr int KC = SK / 64;                       // 64-k MFMA chunks per step
-    static constexpr int BM = 16 * WMB * WAVES_M, BN = 16 * WNB * WAVES_N;
-    static constexpr int TBLK = BM / 16, NTILE = BN / 16;    // 16-token blocks, 16-row tiles
+    static constexpr int CK = FMT == FMT_BINARY ? 128 : 64;  // k per chunk (one packed word per lane group)
+    static constexpr int KC = SK / CK;                       // chunks per step
+    static constexpr int BM = 32 * WMB * WAVES_M, BN = 32 * WNB * WAVES_N;
+    static constexpr int NTILE = BN / 16;                    // 16-row tiles
     static constexpr int A_BYTES = BM * SK;
     static constexpr int B_BYTES = NTILE * 256 * WPL;
     static constexpr int STAGE = A_BYTES + B_BYTES;
@@ -82,41 +84,36 @@ template <int FMT, int WPL, int TILE> struct GemmShape {
     static constexpr int A_PIECES = A_BYTES / 1024;          // 1 KB direct loads per step
     static constexpr int B_PIECES = B_BYTES / 1024;
     static constexpr bool FITS = NS * STAGE <= 163840;
+    static constexpr int CPR = SK / 16;                      // 16-byte chunks per activation row
+    static constexpr int RPP = 64 / CPR;                     // activation rows per 1 KB piece
+    // swizzle: chunk c of row r sits at chunk c ^ swz(r); 16 consecutive rows
+    // read at one chunk then fall on 16 distinct 16-byte bank groups
+    static constexpr int SW_DIV = CPR >= 16 ? 1 : 16 / CPR, SW_MOD = CPR >= 16 ? 16 : CPR;
+    static_assert(A_PIECES % NW == 0, "activation copies per wavefront");
 };
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    // the direct loads write LDS behind the compiler's back: wait explicitly,
+    // and keep every LDS access on its side of the wait
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 // one 1 KB direct-to-LDS copy: lane l's 16 bytes land at lds + 16 * l
 __device__ __forceinline__ void dma16(const void* src, void* lds) {
     __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
 }
 
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-    // the direct loads write LDS behind the compiler's back: wait explicitly,
-    // and keep every LDS access on its side of the wait
-    if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    else if constexpr (N == 1) asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
-    else if constexpr (N == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
-    else if constexpr (N == 3) asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
-    else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    else if constexpr (N == 5) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
-    else if constexpr (N == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-    else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    else if constexpr (N == 9) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-    else if constexpr (N == 10) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
-    else if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-    else if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-    else if constexpr (N == 17) asm volatile("s_waitcnt vmcnt(17)" ::: "memory");
-    else if constexpr (N == 18) asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
-    else if constexpr (N == 20) asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
-    else if constexpr (N == 34) asm volatile("s_waitcnt vmcnt(34)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // any other count: wait for everything
+__device__ __forceinline__ i32x16 mfma32(const i32x4& a, const i32x4& b, const i32x16& c) {
+    return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
 }
 
 template <int FMT, int WPL, int TILE, bool GROUP, bool ACC>
 __global__ __launch_bounds__(TILE == 0 ? 256 : 512) void gemm_mfma_kernel(const GemmFastArgs a) {
     using S = GemmShape<FMT, WPL, TILE>;
-    constexpr int SK = S::SK, KC = S::KC, NS = S::NS, STAGE = S::STAGE, A_BYTES = S::A_BYTES;
-    constexpr int BM = S::BM, BN = S::BN, TBLK = S::TBLK, NW = S::NW;
+    constexpr int SK = S::SK, CK = S::CK, KC = S::KC, NS = S::NS, STAGE = S::STAGE, A_BYTES = S::A_BYTES;
+    constexpr int BM = S::BM, BN = S::BN, NW = S::NW, CPR = S::CPR, RPP = S::RPP;
     constexpr int WMB = S::WMB, WNB = S::WNB;
     constexpr int SHIFT = Fmt<FMT>::kShift;
     // direct loads per wave per step: the fewest any wave issues (waits are
@@ -128,30 +125,31 @@ __global__ __launch_bounds__(TILE == 0 ? 256 : 512) void gemm_mfma_kernel(const 
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lane = tid & 63, g = lane >> 4, rl = lane & 15;
+    const int lane = tid & 63, h = lane >> 5, j = lane & 31;
     const int wm = wave / S::WAVES_N, wn = wave % S::WAVES_N;
 
     // XCD-aware tile order: XCD x runs a contiguous run of tiles
     const int total = a.mb * a.nb;
-    const int xcd = (int)blockIdx.x % 8, j = (int)blockIdx.x / 8;
-    const int logical = xcd * (total / 8) + min(xcd, total % 8) + j;
+    const int xcd = (int)blockIdx.x % 8, jx = (int)blockIdx.x / 8;
+    const int logical = xcd * (total / 8) + min(xcd, total % 8) + jx;
     const int tb_m = logical / a.nb, tb_n = logical % a.nb;
     const int m0 = tb_m * BM, n0 = tb_n * BN;
     const int K = a.K, T = a.T;
+    auto swz = [](int r) { return (r / S::SW_DIV) % S::SW_MOD; };
 
-    // ---- per-lane source addresses of this workgroup's direct loads
-    // activation pieces: piece kc * TBLK + tb holds 64-k chunk kc of token
-    // block tb; wave w issues the token blocks w, w + NW, ... of every chunk,
-    // lane (g, tok) reading 16 bytes of its row
-    constexpr int TBW = TBLK / NW;                           // token blocks per wave
-    const int8_t* arow[TBW];
+    // ---- per-lane sources of this workgroup's direct loads
+    // activation piece p: rows p * RPP .. of the tile, lane i reading chunk
+    // (i % CPR) ^ swz(row) of row p * RPP + i / CPR, which lands at LDS byte
+    // p * 1024 + 16 i = row * SK + 16 * ((i % CPR)): the swizzled position
+    const int8_t* const qt = a.q + (size_t)m0 * K;
+    int aoff[LA], akc[LA];                                   // row offset in the tile, chunk byte offset
     #pragma unroll
-    for (int ii = 0; ii < TBW; ++ii)
-        arow[ii] = a.q + (size_t)min(m0 + (wave + NW * ii) * 16 + rl, T - 1) * K;
-    auto a_off = [&](int kc) -> int {                        // k offset of chunk kc within a step
-        if constexpr (FMT == FMT_BINARY) return (kc / 2) * 128 + 32 * g + 16 * (kc % 2);
-        else return kc * 64 + 16 * g;
-    };
+    for (int ii = 0; ii < LA; ++ii) {
+        const int p = wave + NW * ii;
+        const int r = p * RPP + lane / CPR;
+        aoff[ii] = (min(m0 + r, T - 1) - m0) * K;
+        akc[ii] = 16 * ((lane % CPR) ^ swz(r));
+    }
     // weight piece p: 16-byte chunk c = 64 p + lane of the stage's row tiles
     constexpr int LBW = LB > 0 ? LB : 1;
     const uint8_t* b_src[LBW];
@@ -165,14 +163,13 @@ __global__ __launch_bounds__(TILE == 0 ? 256 : 512) void gemm_mfma_kernel(const 
     }
 
     // The direct loads of one step, numbered 0 .. NDMA-1 for this wave:
-    // activation pieces first (chunk kc, token block ii), then weight pieces.
+    // activation pieces first, then weight pieces.
     constexpr int NDMA = LA + (LB > 0 ? LB : 1);
     auto issue_one = [&](int s, int d) {
         uint8_t* st = smem + (s % NS) * STAGE;
         if (d < LA) {
-            const int kc = d / TBW, ii = d % TBW;
-            const int k = s * SK + a_off(kc);
-            dma16(arow[ii] + (k < K ? k : 0), st + (kc * TBLK + wave + NW * ii) * 1024);
+            const int k = s * SK + akc[d];
+            dma16(qt + aoff[d] + (k < K ? k : 0), st + (wave + NW * d) * 1024);
         } else if constexpr (LB > 0) {
             const int i = d - LA;
             dma16(b_src[i] + (size_t)s * (256 * WPL), st + A_BYTES + (wave + NW * i) * 1024);
@@ -185,41 +182,45 @@ __global__ __launch_bounds__(TILE == 0 ? 256 : 512) void gemm_mfma_kernel(const 
         for (int d = 0; d < NDMA; ++d) issue_one(s, d);
     };
 
-    i32x4 C[WMB][WNB];
+    // this lane's activation rows (one per 32-token block) and their swizzle
+    const int sw = swz(j);                                   // rows are 32 apart between blocks: same swizzle
+    const int arow0 = (wm * (32 * WMB) + j) * SK;
+
+    i32x16 C[WMB][WNB];
     #pragma unroll
     for (int i = 0; i < WMB; ++i)
         #pragma unroll
-        for (int jj = 0; jj < WNB; ++jj) C[i][jj] = i32x4{0, 0, 0, 0};
-    float yp[GROUP ? WMB : 1][GROUP ? WNB : 1][4];
+        for (int jb = 0; jb < WNB; ++jb) C[i][jb] = i32x16{};
+    float yp[GROUP ? WMB : 1][GROUP ? WNB : 1][16];
     if constexpr (GROUP) {
         #pragma unroll
         for (int i = 0; i < WMB; ++i)
             #pragma unroll
-            for (int jj = 0; jj < WNB; ++jj)
+            for (int jb = 0; jb < WNB; ++jb)
                 #pragma unroll
-                for (int r = 0; r < 4; ++r) yp[i][jj][r] = 0.0f;
+                for (int r = 0; r < 16; ++r) yp[i][jb][r] = 0.0f;
     }
 
-    // group mode: the k-chunks ending at kend close a group
+    // group mode: the chunks ending at kend close a group
     auto close_groups = [&](int kend) {
         const int gi = (min(kend, K) - 1) / a.group;
         #pragma unroll
-        for (int jj = 0; jj < WNB; ++jj) {
-            const int n = n0 + wn * (16 * WNB) + jj * 16 + rl;
+        for (int jb = 0; jb < WNB; ++jb) {
+            const int n = n0 + wn * (32 * WNB) + jb * 32 + j;
             const int nc = min(n, a.N - 1);
             const float sg = a.scales[((size_t)(nc >> 4) * a.G + gi) * 16 + (nc & 15)];
             #pragma unroll
             for (int i = 0; i < WMB; ++i) {
                 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int32_t v = C[i][jj][r] >> SHIFT;
-                    yp[i][jj][r] = yp[i][jj][r] + sg * (float)v;
+                for (int r = 0; r < 16; ++r) {
+                    const int32_t v = C[i][jb][r] >> SHIFT;
+                    yp[i][jb][r] = yp[i][jb][r] + sg * (float)v;
                     if constexpr (ACC) {
-                        const int t = m0 + wm * (16 * WMB) + i * 16 + 4 * g + r;
+                        const int t = m0 + wm * (32 * WMB) + i * 32 + 8 * (r / 4) + 4 * h + (r % 4);
                         if (a.acc && t < T && n < a.N) a.acc[((size_t)t * a.N + n) * a.G + gi] = v;
                     }
                 }
-                C[i][jj] = i32x4{0, 0, 0, 0};
+                C[i][jb] = i32x16{};
             }
         }
     };
@@ -255,79 +256,112 @@ __global__ __launch_bounds__(TILE == 0 ? 256 : 512) void gemm_mfma_kernel(const 
 
         const uint8_t* st = smem + (s % NS) * STAGE;
         const uint8_t* bs = st + A_BYTES;
-        uint32_t bw[WNB][WPL];                               // this lane's packed words of the step
+        // this lane's packed words of the step: groups 2h, 2h + 1 of row
+        // j % 16 in tile 2 jb + j / 16 of the wave's rows
+        uint32_t bw[WNB][2][WPL];
         #pragma unroll
-        for (int jj = 0; jj < WNB; ++jj) {
-            const uint8_t* p = bs + (wn * WNB + jj) * (256 * WPL) + lane * (4 * WPL);
-            if constexpr (WPL == 4) {
-                const u32x4 v = *reinterpret_cast<const u32x4*>(p);
-                bw[jj][0] = v[0]; bw[jj][1] = v[1]; bw[jj][2] = v[2]; bw[jj][3] = v[3];
-            } else if constexpr (WPL == 2) {
-                const u32x2 v = *reinterpret_cast<const u32x2*>(p);
-                bw[jj][0] = v[0]; bw[jj][1] = v[1];
-            } else {
-                bw[jj][0] = *reinterpret_cast<const uint32_t*>(p);
+        for (int jb = 0; jb < WNB; ++jb) {
+            #pragma unroll
+            for (int gg = 0; gg < 2; ++gg) {
+                const uint8_t* p = bs + (wn * (2 * WNB) + 2 * jb + (j >> 4)) * (256 * WPL) +
+                                   (((2 * h + gg) * 16 + (j & 15)) * WPL) * 4;
+                if constexpr (WPL == 4) {
+                    const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+                    bw[jb][gg][0] = v[0]; bw[jb][gg][1] = v[1]; bw[jb][gg][2] = v[2]; bw[jb][gg][3] = v[3];
+                } else if constexpr (WPL == 2) {
+                    const u32x2 v = *reinterpret_cast<const u32x2*>(p);
+                    bw[jb][gg][0] = v[0]; bw[jb][gg][1] = v[1];
+                } else {
+                    bw[jb][gg][0] = *reinterpret_cast<const uint32_t*>(p);
+                }
             }
         }
         const bool tail = (s + 1) * SK > K;                  // uniform: the step holds padding k
         #pragma unroll
-        for (int kc = 0; kc < KC; kc += (FMT == FMT_BINARY ? 2 : 1)) {
-            i32x4 Aop[WMB][FMT == FMT_BINARY ? 2 : 1];
-            #pragma unroll
-            for (int i = 0; i < WMB; ++i) {
-                const uint8_t* ap = st + (kc * TBLK + wm * WMB + i) * 1024 + lane * 16;
-                Aop[i][0] = *reinterpret_cast<const i32x4*>(ap);
-                if constexpr (FMT == FMT_BINARY) {
-                    i32x4 lo = Aop[i][0];
-                    i32x4 hi = *reinterpret_cast<const i32x4*>(ap + TBLK * 1024);
-                    if (tail) {
-                        const int k0 = s * SK + (kc / 2) * 128 + 32 * g;
-                        if (k0 >= K) lo = i32x4{0, 0, 0, 0};
-                        if (k0 + 16 >= K) hi = i32x4{0, 0, 0, 0};
+        for (int cc = 0; cc < KC; ++cc) {
+            if constexpr (FMT == FMT_BINARY) {
+                // lane half h: the 64 activations at 64h of the chunk, as the
+                // operands of lane groups 2h (gg 0) and 2h + 1 (gg 1)
+                i32x4 Ap[WMB][2][2];
+                #pragma unroll
+                for (int i = 0; i < WMB; ++i) {
+                    i32x4 X[4];
+                    #pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int c = 8 * cc + 4 * h + e;    // logical 16-byte chunk of the row
+                        X[e] = *reinterpret_cast<const i32x4*>(st + arow0 + i * 32 * SK + 16 * (c ^ sw));
+                        if (tail && s * SK + 16 * c >= K) X[e] = i32x4{0, 0, 0, 0};
                     }
-                    const uint32_t X[8] = {(uint32_t)lo[0], (uint32_t)lo[1], (uint32_t)lo[2], (uint32_t)lo[3],
-                                           (uint32_t)hi[0], (uint32_t)hi[1], (uint32_t)hi[2], (uint32_t)hi[3]};
-                    perm_binary_a(X, Aop[i][0], Aop[i][1]);
-                }
-            }
-            #pragma unroll
-            for (int jj = 0; jj < WNB; ++jj) {
-                if constexpr (FMT == FMT_TERNARY) {
-                    const i32x4 B = decode_ternary(bw[jj][kc]);
                     #pragma unroll
-                    for (int i = 0; i < WMB; ++i) C[i][jj] = mfma16(Aop[i][0], B, C[i][jj]);
-                } else if constexpr (FMT == FMT_INT4) {
-                    const i32x4 B = decode_int4(bw[jj][2 * kc], bw[jj][2 * kc + 1]);
-                    #pragma unroll
-                    for (int i = 0; i < WMB; ++i) C[i][jj] = mfma16(Aop[i][0], B, C[i][jj]);
-                } else {
-                    i32x4 b0, b1;
-                    decode_binary(bw[jj][kc / 2], b0, b1);
-                    #pragma unroll
-                    for (int i = 0; i < WMB; ++i) {
-                        C[i][jj] = mfma16(Aop[i][0], b0, C[i][jj]);
-                        C[i][jj] = mfma16(Aop[i][1], b1, C[i][jj]);
+                    for (int gg = 0; gg < 2; ++gg) {
+                        const uint32_t Xw[8] = {(uint32_t)X[2 * gg][0], (uint32_t)X[2 * gg][1],
+                                                (uint32_t)X[2 * gg][2], (uint32_t)X[2 * gg][3],
+                                                (uint32_t)X[2 * gg + 1][0], (uint32_t)X[2 * gg + 1][1],
+                                                (uint32_t)X[2 * gg + 1][2], (uint32_t)X[2 * gg + 1][3]};
+                        perm_binary_a(Xw, Ap[i][gg][0], Ap[i][gg][1]);
                     }
                 }
+                #pragma unroll
+                for (int gg = 0; gg < 2; ++gg) {
+                    #pragma unroll
+                    for (int op = 0; op < 2; ++op) {
+                        #pragma unroll
+                        for (int jb = 0; jb < WNB; ++jb) {
+                            const i32x4 B = decode_binary_half(bw[jb][gg][cc], op);
+                            #pragma unroll
+                            for (int i = 0; i < WMB; ++i) C[i][jb] = mfma32(Ap[i][gg][op], B, C[i][jb]);
+                        }
+                    }
+                }
+            } else {
+                i32x4 A[WMB][2];
+                #pragma unroll
+                for (int i = 0; i < WMB; ++i) {
+                    #pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        const int c = 4 * cc + 2 * h + e;    // logical 16-byte chunk of the row
+                        A[i][e] = *reinterpret_cast<const i32x4*>(st + arow0 + i * 32 * SK + 16 * (c ^ sw));
+                    }
+                }
+                #pragma unroll
+                for (int gg = 0; gg < 2; ++gg) {
+                    #pragma unroll
+                    for (int jb = 0; jb < WNB; ++jb) {
+                        i32x4 B;
+                        if constexpr (FMT == FMT_TERNARY) B = decode_ternary(bw[jb][gg][cc]);
+                        else B = decode_int4(bw[jb][gg][2 * cc], bw[jb][gg][2 * cc + 1]);
+                        #pragma unroll
+                        for (int i = 0; i < WMB; ++i) C[i][jb] = mfma32(A[i][gg], B, C[i][jb]);
+                        // this group's share of the next loads
+                        const int d = (cc * 2 + gg) * WNB + jb;
+                        if constexpr (FETCH) {
+                            if (d < NDMA) {
+                                issue_one(sf, d);
+                                __builtin_amdgcn_sched_barrier(0);   // keep it after this group
+                            }
+                        }
+                    }
+                }
             }
-            #pragma unroll
-            for (int jj = 0; jj < WNB; ++jj) {               // this chunk's share of the next loads
-                const int d = (FMT == FMT_BINARY ? kc / 2 : kc) * WNB + jj;
-                if constexpr (FETCH) {
-                    if (d < NDMA) {
-                        issue_one(sf, d);
-                        __builtin_amdgcn_sched_barrier(0);     // keep it after this group
+            if constexpr (FMT == FMT_BINARY) {
+                #pragma unroll
+                for (int jb = 0; jb < WNB; ++jb) {
+                    const int d = cc * WNB + jb;
+                    if constexpr (FETCH) {
+                        if (d < NDMA) {
+                            issue_one(sf, d);
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
                     }
                 }
             }
             if constexpr (GROUP) {
-                const int kw = FMT == FMT_BINARY ? 128 : 64;
-                const int kbeg = s * SK + (FMT == FMT_BINARY ? kc / 2 * 128 : kc * 64);
-                const int kend = kbeg + kw;
+                const int kbeg = s * SK + cc * CK;
+                const int kend = kbeg + CK;
                 if (kbeg < K && (kend % a.group == 0 || kend >= K)) close_groups(kend);   // uniform
             }
         }
-        constexpr int SLOTS = (FMT == FMT_BINARY ? KC / 2 : KC) * WNB;
+        constexpr int SLOTS = FMT == FMT_BINARY ? KC * WNB : KC * 2 * WNB;
         #pragma unroll
         for (int d = SLOTS; d < NDMA; ++d)                   // loads beyond the MFMA groups
             if constexpr (FETCH) issue_one(sf, d);
@@ -337,27 +371,30 @@ __global__ __launch_bounds__(TILE == 0 ? 256 : 512) void gemm_mfma_kernel(const 
     for (; s < n_steps; ++s) k_step(s, std::false_type{});
 
     // ---- epilogue (every scale is loaded before the first store: the
-    // compiler cannot tell y from sx and would otherwise wait per element)
-    float sxv[WMB][4], swv[WNB];
+    // compiler cannot tell y from sx and would otherwise wait per element).
+    // Accumulator register r of block (i, jb) is token 32 i + 8 (r / 4) +
+    // 4 h + r % 4 and row 32 jb + j of the wave's sub-tile.
+    float sxv[WMB][16], swv[WNB];
     #pragma unroll
     for (int i = 0; i < WMB; ++i)
         #pragma unroll
-        for (int r = 0; r < 4; ++r) sxv[i][r] = a.sx[min(m0 + wm * (16 * WMB) + i * 16 + 4 * g + r, T - 1)];
+        for (int r = 0; r < 16; ++r)
+            sxv[i][r] = a.sx[min(m0 + wm * (32 * WMB) + i * 32 + 8 * (r / 4) + 4 * h + (r % 4), T - 1)];
     #pragma unroll
-    for (int jj = 0; jj < WNB; ++jj) {
-        const int nc = min(n0 + wn * (16 * WNB) + jj * 16 + rl, a.N - 1);
-        swv[jj] = GROUP ? 0.0f : a.scales[a.scale_per_row ? nc : 0];
+    for (int jb = 0; jb < WNB; ++jb) {
+        const int nc = min(n0 + wn * (32 * WNB) + jb * 32 + j, a.N - 1);
+        swv[jb] = GROUP ? 0.0f : a.scales[a.scale_per_row ? nc : 0];
     }
     if constexpr (GROUP) {
         #pragma unroll
-        for (int jj = 0; jj < WNB; ++jj) {
-            const int n = n0 + wn * (16 * WNB) + jj * 16 + rl;
+        for (int jb = 0; jb < WNB; ++jb) {
+            const int n = n0 + wn * (32 * WNB) + jb * 32 + j;
             #pragma unroll
             for (int i = 0; i < WMB; ++i)
                 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = m0 + wm * (16 * WMB) + i * 16 + 4 * g + r;
-                    if (t < T && n < a.N) a.y[(size_t)t * a.N + n] = sxv[i][r] * yp[i][jj][r];
+                for (int r = 0; r < 16; ++r) {
+                    const int t = m0 + wm * (32 * WMB) + i * 32 + 8 * (r / 4) + 4 * h + (r % 4);
+                    if (t < T && n < a.N) a.y[(size_t)t * a.N + n] = sxv[i][r] * yp[i][jb][r];
                 }
         }
     } else {
@@ -365,6 +402,7 @@ __global__ __launch_bounds__(TILE == 0 ? 256 : 512) void gemm_mfma_kernel(const 
         // workgroup's valid rows drop every out-of-range element in hardware
         // (columns past n get an offset past the end).  With a branch per
         // element the compiler would wait for all earlier stores before each.
+        // Each store writes 32 consecutive columns of two token rows.
         const int rows_here = min(BM, T - m0);
         const __amdgpu_buffer_rsrc_t ry =
             __builtin_amdgcn_make_buffer_rsrc(a.y + (size_t)m0 * a.N, 0, rows_here * a.N * 4, 0x00020000);
@@ -375,60 +413,24 @@ __global__ __launch_bounds__(TILE == 0 ? 256 : 512) void gemm_mfma_kernel(const 
         // size here (rows * n * 4 <= 256 * 2^20 * 4)
         int col[WNB];
         #pragma unroll
-        for (int jj = 0; jj < WNB; ++jj) {
-            const int n = n0 + wn * (16 * WNB) + jj * 16 + rl;
-            col[jj] = n < a.N ? 4 * n : (1 << 30);
+        for (int jb = 0; jb < WNB; ++jb) {
+            const int n = n0 + wn * (32 * WNB) + jb * 32 + j;
+            col[jb] = n < a.N ? 4 * n : (1 << 30);
         }
         const int row_bytes = 4 * a.N;
-        if (ACC || (a.N & 3) != 0) {
-            // one element per store (and the integer products when asked for)
+        #pragma unroll
+        for (int i = 0; i < WMB; ++i) {
             #pragma unroll
-            for (int jj = 0; jj < WNB; ++jj) {
+            for (int jb = 0; jb < WNB; ++jb) {
                 #pragma unroll
-                for (int i = 0; i < WMB; ++i) {
-                    #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int tl = wm * (16 * WMB) + i * 16 + 4 * g + r;      // row within the tile
-                        const int off = tl * row_bytes + col[jj];
-                        const int32_t v = C[i][jj][r] >> SHIFT;
-                        const float yv = (float)v * (sxv[i][r] * swv[jj]);
-                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(yv), ry, off, 0, 0);
-                        if constexpr (ACC) __builtin_amdgcn_raw_buffer_store_b32((uint32_t)v, ra, off, 0, 0);
-                    }
+                for (int r = 0; r < 16; ++r) {
+                    const int tl = wm * (32 * WMB) + i * 32 + 8 * (r / 4) + 4 * h + (r % 4);   // row within the tile
+                    const int off = tl * row_bytes + col[jb];
+                    const int32_t v = C[i][jb][r] >> SHIFT;
+                    const float yv = (float)v * (sxv[i][r] * swv[jb]);
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(yv), ry, off, 0, 0);
+                    if constexpr (ACC) __builtin_amdgcn_raw_buffer_store_b32((uint32_t)v, ra, off, 0, 0);
                 }
-            }
-        } else {
-            // Through LDS, one 16-token block row at a time: the MFMA layout
-            // gives each lane 4 rows x 1 column per block, i.e. 64-byte row
-            // pieces; re-read row-major, every store is 16 bytes per lane and
-            // covers whole 64 * WB-byte row segments.
-            constexpr int WC = 16 * WNB;                     // columns of the wave's tile
-            constexpr int LD = WC + 4;                       // LDS row stride in floats (16-byte aligned)
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            __builtin_amdgcn_s_barrier();                    // every wave is done with the pipeline buffers
-            asm volatile("" ::: "memory");
-            float* ws = reinterpret_cast<float*>(smem) + wave * (16 * LD);
-            #pragma unroll
-            for (int i = 0; i < WMB; ++i) {
-                #pragma unroll
-                for (int jj = 0; jj < WNB; ++jj)
-                    #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int32_t v = C[i][jj][r] >> SHIFT;
-                        ws[(4 * g + r) * LD + jj * 16 + rl] = (float)v * (sxv[i][r] * swv[jj]);
-                    }
-                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // (the wave's own region only)
-                #pragma unroll
-                for (int it = 0; it < 16 * WC / 4 / 64; ++it) {
-                    const int c = it * 64 + lane;             // 16-byte chunk of the block row
-                    const int rr = c / (WC / 4), c4 = c % (WC / 4);
-                    const u32x4 v = *reinterpret_cast<const u32x4*>(ws + rr * LD + 4 * c4);
-                    const int n = n0 + wn * WC + 4 * c4;
-                    const int tl = wm * (16 * WMB) + i * 16 + rr;
-                    const int off = tl * row_bytes + (n < a.N ? 4 * n : (1 << 30));
-                    __builtin_amdgcn_raw_buffer_store_b128(v, ry, off, 0, 0);
-                }
-                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads done before the next block row
             }
         }
     }
