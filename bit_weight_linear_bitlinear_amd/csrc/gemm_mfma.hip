@@ -10,7 +10,7 @@
 // Tiling.  A 512-thread workgroup owns a 256-token x 256-row output tile; its
 // eight wavefronts (two per SIMD) are a 2 x 4 grid of 128 x 64 sub-tiles, i.e.
 // 4 x 2 blocks of 32 x 32.  (TILE 0: 128 x 128 with four wavefronts of 64 x 64,
-// two workgroups per CU.)  k advances one packed-layout k-step (SK codes) at a
+// two workgroups per CU; TILE 2: 128 x 192 with four of 64 x 96.)  k advances one packed-layout k-step (SK codes) at a
 // time.  Each step's operands are copied global -> LDS by the memory unit itself
 // (16-byte direct-to-LDS loads: no registers, no LDS write instructions), NS
 // steps in flight:
@@ -66,6 +66,12 @@ template <> struct TileCfg<0> {
 template <> struct TileCfg<1> {
     static constexpr int WAVES_M = 2, WAVES_N = 4, WMB = 4, WNB = 2, BUDGET = 163840;
 };
+// TILE 2: 128 x 192 with four wavefronts of 64 x 96, one workgroup per CU (a
+// whole number of rounds for row counts such as 1280 where 256-wide tiles
+// leave CUs idle)
+template <> struct TileCfg<2> {
+    static constexpr int WAVES_M = 2, WAVES_N = 2, WMB = 2, WNB = 3, BUDGET = 163840;
+};
 
 template <int FMT, int WPL, int TILE> struct GemmShape {
     using TC = TileCfg<TILE>;
@@ -110,7 +116,7 @@ __device__ __forceinline__ i32x16 mfma32(const i32x4& a, const i32x4& b, const i
 }
 
 template <int FMT, int WPL, int TILE, bool GROUP, bool ACC>
-__global__ __launch_bounds__(TILE == 0 ? 256 : 512) void gemm_mfma_kernel(const GemmFastArgs a) {
+__global__ __launch_bounds__(TILE == 1 ? 512 : 256) void gemm_mfma_kernel(const GemmFastArgs a) {
     using S = GemmShape<FMT, WPL, TILE>;
     constexpr int SK = S::SK, CK = S::CK, KC = S::KC, NS = S::NS, STAGE = S::STAGE, A_BYTES = S::A_BYTES;
     constexpr int BM = S::BM, BN = S::BN, NW = S::NW, CPR = S::CPR, RPP = S::RPP;
@@ -119,7 +125,7 @@ __global__ __launch_bounds__(TILE == 0 ? 256 : 512) void gemm_mfma_kernel(const 
     // direct loads per wave per step: the fewest any wave issues (waits are
     // then exact or conservative for every wave)
     constexpr int LA = S::A_PIECES / NW;
-    constexpr int LB = S::B_PIECES / NW;                     // 0: waves 0 .. B_PIECES-1 issue one
+    constexpr int LB = (S::B_PIECES + NW - 1) / NW;          // past the last piece: a copy of it again
     constexpr int L = LA + LB;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
 
@@ -150,12 +156,15 @@ __global__ __launch_bounds__(TILE == 0 ? 256 : 512) void gemm_mfma_kernel(const 
         aoff[ii] = (min(m0 + r, T - 1) - m0) * K;
         akc[ii] = 16 * ((lane % CPR) ^ swz(r));
     }
-    // weight piece p: 16-byte chunk c = 64 p + lane of the stage's row tiles
-    constexpr int LBW = LB > 0 ? LB : 1;
-    const uint8_t* b_src[LBW];
+    // weight piece p: 16-byte chunk c = 64 p + lane of the stage's row tiles;
+    // every wave issues LB pieces, those past the last one repeat it (same
+    // bytes to the same place), so all waves wait for the same counts
+    const uint8_t* b_src[LB];
+    int b_dst[LB];
     #pragma unroll
-    for (int i = 0; i < LBW; ++i) {
-        const int p = LB > 0 ? wave + NW * i : wave;
+    for (int i = 0; i < LB; ++i) {
+        const int p = min(wave + NW * i, S::B_PIECES - 1);
+        b_dst[i] = A_BYTES + p * 1024;
         const int c = 64 * p + lane;
         const int tt = c / (16 * WPL), cc = c % (16 * WPL);
         const int tile = min(tb_n * S::NTILE + tt, a.n_tiles - 1);
@@ -164,17 +173,15 @@ __global__ __launch_bounds__(TILE == 0 ? 256 : 512) void gemm_mfma_kernel(const 
 
     // The direct loads of one step, numbered 0 .. NDMA-1 for this wave:
     // activation pieces first, then weight pieces.
-    constexpr int NDMA = LA + (LB > 0 ? LB : 1);
+    constexpr int NDMA = LA + LB;
     auto issue_one = [&](int s, int d) {
         uint8_t* st = smem + (s % NS) * STAGE;
         if (d < LA) {
             const int k = s * SK + akc[d];
             dma16(qt + aoff[d] + (k < K ? k : 0), st + (wave + NW * d) * 1024);
-        } else if constexpr (LB > 0) {
-            const int i = d - LA;
-            dma16(b_src[i] + (size_t)s * (256 * WPL), st + A_BYTES + (wave + NW * i) * 1024);
         } else {
-            if (wave < S::B_PIECES) dma16(b_src[0] + (size_t)s * (256 * WPL), st + A_BYTES + wave * 1024);
+            const int i = d - LA;
+            dma16(b_src[i] + (size_t)s * (256 * WPL), st + b_dst[i]);
         }
     };
     auto issue = [&](int s) {                                // all direct loads of step s
@@ -450,17 +457,31 @@ void gemm_mfma_launch_tile(const GemmFastArgs& ga, bool group, bool acc, hipStre
     }
 }
 
-// Tile choice: the 256 x 256 tile whenever it still gives most CUs a
-// workgroup; else 128 x 128 (two workgroups per CU).
+// Tile choice: the least work on the busiest CU, rounds of tiles per CU times
+// the tile's area, weighted by how close each tile shape runs to the matrix
+// cores' rate (the 256 x 256 tile best: two wavefronts per SIMD and the most
+// MFMA work per staged byte).  Group mode runs the 128 x 128 tile only.
 template <int FMT, int WPL>
 void gemm_mfma_launch(GemmFastArgs ga, bool group, bool acc, hipStream_t st) {
     using Big = GemmShape<FMT, WPL, 1>;
+    using Mid = GemmShape<FMT, WPL, 2>;
     using Small = GemmShape<FMT, WPL, 0>;
-    const int big_tiles = ((ga.T + Big::BM - 1) / Big::BM) * ((ga.N + Big::BN - 1) / Big::BN);
-    if (Big::FITS && !group && big_tiles >= 192) {
+    const long cus = device_cu_count();
+    auto cost = [&](int bm, int bn, double eff) {
+        const long tiles = (long)((ga.T + bm - 1) / bm) * ((ga.N + bn - 1) / bn);
+        return (double)((tiles + cus - 1) / cus) * bm * bn / eff;
+    };
+    const double c_big = Big::FITS && !group ? cost(Big::BM, Big::BN, 1.0) : 1e300;
+    const double c_mid = Mid::FITS && !group ? cost(Mid::BM, Mid::BN, 0.9) : 1e300;
+    const double c_small = cost(Small::BM, Small::BN, 0.8);
+    if (c_big <= c_mid && c_big <= c_small) {
         ga.mb = (ga.T + Big::BM - 1) / Big::BM;
         ga.nb = (ga.N + Big::BN - 1) / Big::BN;
         if constexpr (Big::FITS) gemm_mfma_launch_tile<FMT, WPL, 1>(ga, false, acc, st);
+    } else if (c_mid <= c_small) {
+        ga.mb = (ga.T + Mid::BM - 1) / Mid::BM;
+        ga.nb = (ga.N + Mid::BN - 1) / Mid::BN;
+        if constexpr (Mid::FITS) gemm_mfma_launch_tile<FMT, WPL, 2>(ga, false, acc, st);
     } else {
         ga.mb = (ga.T + Small::BM - 1) / Small::BM;
         ga.nb = (ga.N + Small::BN - 1) / Small::BN;

@@ -9,8 +9,6 @@
 
 namespace lowbit {
 
-namespace {
-
 int device_cu_count() {
     static int cached[64] = {0};
     int dev = 0;
@@ -23,6 +21,8 @@ int device_cu_count() {
     }
     return cached[dev];
 }
+
+namespace {
 
 int log2_exact(int v) {   // log2 of a power of two, else -1
     if (v <= 0 || (v & (v - 1)) != 0) return -1;

@@ -36,5 +36,7 @@ hipError_t launch_gemm(const LinearArgs& a, hipStream_t stream);
 bool gemm_mfma_supported(const LinearArgs& a);
 hipError_t launch_gemm_mfma(const LinearArgs& a, hipStream_t stream);
 hipError_t launch_gemm_generic(const LinearArgs& a, hipStream_t stream);
+// compute units of the current device (cached per device)
+int device_cu_count();
 
 }  // namespace lowbit

@@ -217,3 +217,17 @@ def test_grouped_matches_single_and_oracle(fmt, scale, group, t):
         y32, y64, acc_ref = oracle.linear(p_ref, s_ref, fmt, scale, group, w.shape[0], k, q_ref, sx_ref)
         assert (accs[i].cpu().numpy() == acc_ref).all()
         check_y(ys[i].cpu().numpy(), y32, y64, f"grouped {i}")
+
+
+@pytest.mark.parametrize("fmt", ["ternary", "binary", "int4"])
+def test_gemm_tile_shapes(fmt):
+    """Prefill shapes that select each workgroup tile of the batched kernel
+    (256 x 256, 128 x 192, 128 x 128 at 256 CUs), ragged in tokens, rows and k,
+    checked on sampled tokens including the first and the last."""
+    rng = np.random.default_rng(11)
+    for i, (n, k, t) in enumerate([(3800, 272, 4000), (1250, 272, 4000), (500, 272, 300)]):
+        w, x = workloads.random_case(700 + i, n, k, t)
+        sample = np.sort(rng.choice(t, size=min(t, 96), replace=False))
+        sample[0], sample[-1] = 0, t - 1
+        run_layer(w, x, fmt, "row", 0, fmt == "int4", entries=("gemm",), token_sample=sample,
+                  label=f"tile shapes n={n} k={k} t={t}")
