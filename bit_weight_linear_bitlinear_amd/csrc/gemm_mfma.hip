@@ -8,8 +8,9 @@
 // in registers right before each MFMA.
 //
 // Tiling.  A 512-thread workgroup owns a 256-token x 256-row output tile; its
-// eight wavefronts (two per SIMD) are a 2 x 4 grid of 128 x 64 sub-tiles, i.e.
-// 4 x 2 blocks of 32 x 32.  (TILE 0: 128 x 128 with four wavefronts of 64 x 64,
+// eight wavefronts (two per SIMD) are a 4 x 2 grid of 64 x 128 sub-tiles, i.e.
+// 2 x 4 blocks of 32 x 32 (each staged activation byte is read by two
+// wavefronts, each packed weight byte by four).  (TILE 0: 128 x 128 with four wavefronts of 64 x 64,
 // two workgroups per CU; TILE 2: 128 x 192 with four of 64 x 96.)  k advances one packed-layout k-step (SK codes) at a
 // time.  Each step's operands are copied global -> LDS by the memory unit itself
 // (16-byte direct-to-LDS loads: no registers, no LDS write instructions), NS
@@ -64,7 +65,7 @@ template <> struct TileCfg<0> {
     static constexpr int WAVES_M = 2, WAVES_N = 2, WMB = 2, WNB = 2, BUDGET = 73728;
 };
 template <> struct TileCfg<1> {
-    static constexpr int WAVES_M = 2, WAVES_N = 4, WMB = 4, WNB = 2, BUDGET = 163840;
+    static constexpr int WAVES_M = 4, WAVES_N = 2, WMB = 2, WNB = 4, BUDGET = 163840;
 };
 // TILE 2: 128 x 192 with four wavefronts of 64 x 96, one workgroup per CU (a
 // whole number of rounds for row counts such as 1280 where 256-wide tiles
@@ -257,8 +258,8 @@ __global__ __launch_bounds__(TILE == 1 ? 512 : 256) void gemm_mfma_kernel(const 
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");                       // (the direct loads below stay after the barrier)
         // Step s+NS-1 goes into the buffer step s-1 used.  Its loads are
-        // spread over this step's MFMA groups, one after each group: issued
-        // all at once, every wave would stall behind the others' requests.
+        // spread over this step's MFMA groups: issued all at once, every wave
+        // would stall behind the others' requests.
         const int sf = s + NS - 1;
 
         const uint8_t* st = smem + (s % NS) * STAGE;
@@ -344,7 +345,6 @@ __global__ __launch_bounds__(TILE == 1 ? 512 : 256) void gemm_mfma_kernel(const 
                         if constexpr (FETCH) {
                             if (d < NDMA) {
                                 issue_one(sf, d);
-                                __builtin_amdgcn_sched_barrier(0);   // keep it after this group
                             }
                         }
                     }
@@ -357,7 +357,6 @@ __global__ __launch_bounds__(TILE == 1 ? 512 : 256) void gemm_mfma_kernel(const 
                     if constexpr (FETCH) {
                         if (d < NDMA) {
                             issue_one(sf, d);
-                            __builtin_amdgcn_sched_barrier(0);
                         }
                     }
                 }
