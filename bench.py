@@ -491,11 +491,23 @@ def main():
         d4, _, ops_per_launch = per_launch(p4, reps=3)
         tops_launch = ops_per_launch / d4 / 1e12
         chk4 = None if args.skip_check else sampled_check(p4, [0, 1, 4], rows_per=32)
+        # the second roofline of a prefill product: its HBM bytes (fp32 y
+        # dominates) at peak bandwidth; the larger of the two floors bounds it
+        bytes4 = sum(p4.linear_bytes)
+        floor_mfma = ops4 / (I8_PEAK_TOPS * 1e12)
+        floor_hbm = bytes4 / (HBM_PEAK_GBS * 1e9)
+        n4 = len(p4.linear_ops)
         out["gemm"] = {"workload": "int4_t4nt prefill pass: 100 int4 row-scale GEMMs, T=4096, act-quant included",
                        "tops_step": round(ops4 / st4 / 1e12, 2), "ms_per_step": round(st4 * 1e3, 4),
                        "tops_per_launch": round(tops_launch, 2),
                        "pct_mfma_peak": round(100 * tops_launch / I8_PEAK_TOPS, 2),
-                       "avg_launch_us": round(d4 * 1e6, 2), "kernel": "gemm_mfma_kernel", "check": chk4}
+                       "avg_launch_us": round(d4 * 1e6, 2), "kernel": "gemm_mfma_kernel",
+                       "roofline": {"bound": "mfma", "achieved": round(tops_launch, 2), "peak": I8_PEAK_TOPS,
+                                    "unit": "TOPS", "frac": round(tops_launch / I8_PEAK_TOPS, 4),
+                                    "mfma_floor_us_per_launch": round(floor_mfma / n4 * 1e6, 2),
+                                    "hbm_floor_us_per_launch": round(floor_hbm / n4 * 1e6, 2),
+                                    "frac_of_larger_floor": round(max(floor_mfma, floor_hbm) / n4 / d4, 4)},
+                       "check": chk4}
         log(f"[bench] gemm pass: {ops4 / st4 / 1e12:.1f} TOPS/step; per launch {tops_launch:.1f} TOPS")
         del p4
 
