@@ -92,6 +92,10 @@ class Pass:
             self.kgroups.setdefault(m.k, []).append(i)
         self.x, self.q, self.sx = {}, {}, {}
         self.views = [None] * len(self.mats)
+        self.pos = {}                                    # matrix -> (k, position in its k-stack)
+        for k, idx in self.kgroups.items():
+            for j, i in enumerate(idx):
+                self.pos[i] = (k, j)
         for k, idx in self.kgroups.items():
             rows = len(idx) * tokens
             self.x[k] = torch.from_numpy(np.concatenate([xs[i] for i in idx], axis=0)).cuda()
@@ -100,6 +104,11 @@ class Pass:
             for j, i in enumerate(idx):
                 self.views[i] = (self.q[k][j * tokens:(j + 1) * tokens], self.sx[k][j * tokens:(j + 1) * tokens])
         self.y = [torch.empty((tokens, m.n), dtype=torch.float32, device="cuda") for _, _, m in self.mats]
+        self.xv = [None] * len(self.mats)
+        for k, idx in self.kgroups.items():
+            for j, i in enumerate(idx):
+                self.xv[i] = self.x[k][j * tokens:(j + 1) * tokens]
+        self.status = torch.zeros(1, dtype=torch.int32, device="cuda")
         self.xs = xs
         self.fn = lb.lowbit_linear if entry == "gemv" else lb.lowbit_linear_batched
 
@@ -107,7 +116,11 @@ class Pass:
         self.linear_bytes = [d.packed_bytes + 4 * d.n_scales + tokens * d.k + 4 * tokens + 4 * tokens * d.n
                              for d in self.desc]
         self.linear_ops = [2 * tokens * d.n * d.k for d in self.desc]
-        self.aq_bytes = sum(len(idx) * tokens * (5 * k + 4) for k, idx in self.kgroups.items())
+        # what one pass must move at least: fp32 x read, codes and scales of x
+        # written, packed weights and scales read, fp32 y written (the separate
+        # schedules also read the codes back: that re-read is their overhead)
+        self.pass_bytes = [d.packed_bytes + 4 * d.n_scales + 5 * tokens * d.k + 4 * tokens + 4 * tokens * d.n
+                           for d in self.desc]
 
     def act_quant(self):
         for k in self.kgroups:
@@ -123,13 +136,35 @@ class Pass:
                                    [self.scales[i] for i in idx], [self.views[i][0] for i in idx],
                                    [self.views[i][1] for i in idx], [self.y[i] for i in idx])
 
+    def _grouped_fused(self, idx):
+        return self.lb.GroupedFusedCall([self.desc[i] for i in idx], [self.packed[i] for i in idx],
+                                        [self.scales[i] for i in idx], [self.xv[i] for i in idx],
+                                        [self.views[i][0] for i in idx], [self.views[i][1] for i in idx],
+                                        [self.y[i] for i in idx], self.status)
+
+    def _quant_rows(self, idx):
+        """act-quant of the inputs of matrices idx (adjacent in one k-stack)
+        as one call"""
+        k, j0 = self.pos[idx[0]]
+        assert all(self.pos[i] == (k, j0 + n) for n, i in enumerate(idx))
+        r0, r1 = j0 * self.t, (j0 + len(idx)) * self.t
+        x, q, sx = self.x[k][r0:r1], self.q[k][r0:r1], self.sx[k][r0:r1]
+        return lambda: self.lb.lowbit_act_quant(x, q, sx)
+
     def build_schedules(self):
-        """grouped: every matrix of equal k in one call (the pass as one weight
-        stream of independent products); layer: the calls a decoder layer's
-        data dependencies allow - q/k/v together, o, gate/up together, down."""
+        """grouped: every matrix of equal k in one call, on inputs quantised
+        beforehand by the act-quant kernel (one launch per k); grouped_fused:
+        the same calls from fp32 inputs, the quantiser run in the product
+        kernel's prologue.  The layer schedules issue the calls a decoder
+        layer's data dependencies allow - q/k/v together, o, gate/up together,
+        down: layer quantises every input up front (one launch per k),
+        layer_dep quantises each call's inputs right before it (what a model
+        whose next input is the previous output must do), layer_fused does that
+        inside the product kernel."""
+        self.fused_calls = [self._grouped_fused(idx) for idx in self.kgroups.values()]
         self.grouped_calls = [self._grouped(idx) for idx in self.kgroups.values()]
         names = [m.name for _, _, m in self.mats]
-        self.layer_calls = []
+        self.layer_calls, self.layer_fused_calls, self.layer_dep_calls = [], [], []
         by_layer = {}
         for i, (layer, _, _) in enumerate(self.mats):
             by_layer.setdefault(layer, []).append(i)
@@ -138,12 +173,23 @@ class Pass:
                     [i for i in idx if names[i] == "attn3"],
                     [i for i in idx if names[i] in ("gate", "up")],
                     [i for i in idx if names[i] == "down"]]
-            self.layer_calls += [self._grouped(s_) for s_ in sets if s_]
+            for s_ in sets:
+                if not s_:
+                    continue
+                self.layer_calls.append(self._grouped(s_))
+                self.layer_fused_calls.append(self._grouped_fused(s_))
+                self.layer_dep_calls += [self._quant_rows(s_), self.layer_calls[-1]]
 
     def launches(self, calls):
         return sum((c.count + 39) // 40 * ((c.t + 15) // 16) for c in calls)
 
     def step(self, schedule="per_matrix"):
+        if schedule in ("grouped_fused", "layer_fused", "layer_dep"):
+            calls = {"grouped_fused": self.fused_calls, "layer_fused": self.layer_fused_calls,
+                     "layer_dep": self.layer_dep_calls}[schedule]
+            for c in calls:
+                c()
+            return
         self.act_quant()
         if schedule == "grouped":
             for c in self.grouped_calls:
@@ -156,7 +202,7 @@ class Pass:
 
     @property
     def step_bytes(self):
-        return sum(self.linear_bytes) + self.aq_bytes
+        return sum(self.pass_bytes)
 
 
 def capture(fn):
@@ -195,13 +241,15 @@ def time_steps(run, steps, warmup):
     return e0.elapsed_time(e1) / 1e3, wall
 
 
-def per_launch_grouped(p: Pass, calls, reps: int):
+def per_launch_grouped(p: Pass, calls, reps: int, fused: bool):
     """Average duration of one gemv launch of a grouped schedule: the gemv
-    launches alone (inputs quantised beforehand) captured in a HIP graph and
-    replayed `reps` times between two HIP events on the replaying stream; a
-    call of c matrices issues ceil(c / 40) launches."""
+    launches alone (for the unfused calls, inputs quantised beforehand)
+    captured in a HIP graph and replayed `reps` times between two HIP events on
+    the replaying stream; a call of c matrices issues ceil(c / 40) launches.
+    Returns (seconds, algorithmic bytes) per launch."""
     import torch
-    p.act_quant()
+    if not fused:
+        p.act_quant()
     torch.cuda.synchronize()
 
     def gemvs():
@@ -218,7 +266,8 @@ def per_launch_grouped(p: Pass, calls, reps: int):
     torch.cuda.synchronize()
     total = e0.elapsed_time(e1) / 1e3
     n_launch = p.launches(calls) * reps
-    return total / n_launch, sum(p.linear_bytes) / p.launches(calls)
+    per_pass = sum(p.pass_bytes) if fused else sum(p.linear_bytes)
+    return total / n_launch, per_pass / p.launches(calls)
 
 
 def committed_traffic():
@@ -354,8 +403,17 @@ def sampled_check(p: Pass, picks, rows_per=48, seed=0):
         yy = y.cpu().numpy()[:, rows].astype(np.float64)
         err = np.abs(yy - y32)
         assert (err <= 1e-6 + 1e-5 * np.abs(y32)).all(), f"matrix {i}: y out of tolerance"
+        if p.entry == "gemv":
+            # the fused entry on the same fp32 input: codes, scales and y equal
+            # to the separate path's bit for bit
+            qf, sxf, yf = torch.empty_like(q), torch.empty_like(sx), torch.empty_like(y)
+            p.lb.lowbit_linear_fused(d, p.packed[i], p.scales[i], p.xv[i], qf, sxf, yf)
+            torch.cuda.synchronize()
+            assert (qf.cpu().numpy() == q_ref).all(), f"matrix {i}: fused activation codes differ"
+            assert torch.equal(sxf, sx) and torch.equal(yf, y), f"matrix {i}: fused path differs"
         worst = max(worst, float((err / (1e-6 + 1e-5 * np.abs(y32))).max()))
     return {"matrices": len(picks), "rows_each": rows_per, "acc_bit_exact": True,
+            "fused_equals_separate": p.entry == "gemv",
             "y_worst_frac_of_tol": round(worst, 4)}
 
 
@@ -453,12 +511,32 @@ def extra_views(args):
     el, _ = time_steps(run, 50, 5)
     st = el / 50
     dur, bpl, _ = per_launch(p1, reps=20)
+
+    # the same 31 products as a model runs them, each input quantised right
+    # before its product: the quantiser kernel + product per call, or the
+    # fused entry (one launch per call)
+    def dep_separate():
+        for i, d in enumerate(p1.desc):
+            q, sx = p1.views[i]
+            lb.lowbit_act_quant(p1.xv[i], q, sx)
+            lb.lowbit_linear(d, p1.packed[i], p1.scales[i], q, sx, p1.y[i])
+
+    def dep_fused():
+        for i, d in enumerate(p1.desc):
+            q, sx = p1.views[i]
+            lb.lowbit_linear_fused(d, p1.packed[i], p1.scales[i], p1.xv[i], q, sx, p1.y[i])
+    dep = {}
+    for name, fn in (("separate", dep_separate), ("fused", dep_fused)):
+        el_d, _ = time_steps(capture(fn) or fn, 50, 5)
+        dep[name] = round(el_d / 50 * 1e6, 2)
     views["decode_stack_t1"] = {
         "what": "the 256-d 6-layer ternary decode stack (31 GEMVs + 2 act-quant per step), t = 1; "
                 "1.9 MB of weights, cache-resident: launch- and latency-bound, not an HBM figure",
         "us_per_step": round(st * 1e6, 2), "gemv_calls": len(p1.mats), "us_per_gemv_call": round(dur * 1e6, 2),
-        "effective_GBps_not_hbm": round(p1.step_bytes / st / 1e9, 1)}
-    log(f"[bench] decode stack t=1: {st * 1e6:.1f} us/step, {dur * 1e6:.2f} us per GEMV call")
+        "effective_GBps_not_hbm": round(p1.step_bytes / st / 1e9, 1),
+        "dependent_us_per_step": {"what": "each input quantised right before its product (31 calls)", **dep}}
+    log(f"[bench] decode stack t=1: {st * 1e6:.1f} us/step, {dur * 1e6:.2f} us per GEMV call; "
+        f"dependent calls: {dep}")
     del p1
 
     # the binary 8192-token GEMM pass
@@ -523,23 +601,38 @@ def main():
     p = Pass(wl, args.tokens, "gemv", layers=args.layers)
     p.build_schedules()
     schedules = {}
-    order = ["grouped"] if args.quick else ["grouped", "layer", "per_matrix"]
+    # untimed: about half a second of the headline step first, so that the
+    # first schedule timed does not meet the device still at idle clocks
+    warm = capture(lambda: p.step("grouped")) or (lambda: p.step("grouped"))
+    t_end = time.perf_counter() + 0.5
+    while time.perf_counter() < t_end:
+        for _ in range(20):
+            warm()
+        torch.cuda.synchronize()
+    order = (["grouped"] if args.quick else
+             ["grouped", "grouped_fused", "layer", "layer_dep", "layer_fused", "per_matrix"])
     for sched in order:
         fn = (lambda sc=sched: p.step(sc))
         run = None if args.no_graph else capture(fn)
         elapsed, wall = time_steps(run or fn, args.steps, args.warmup)
         st = elapsed / args.steps
-        n_l = (p.launches(p.grouped_calls) if sched == "grouped" else
-               p.launches(p.layer_calls) if sched == "layer" else len(p.mats))
+        n_l = {"grouped": p.launches(p.grouped_calls), "grouped_fused": p.launches(p.fused_calls),
+               "layer": p.launches(p.layer_calls), "layer_dep": p.launches(p.layer_calls),
+               "layer_fused": p.launches(p.layer_fused_calls), "per_matrix": len(p.mats)}[sched]
+        n_aq = {"grouped_fused": 0, "layer_fused": 0, "layer_dep": len(p.layer_calls)}.get(sched, len(p.kgroups))
         schedules[sched] = {"GBps": round(p.step_bytes / st / 1e9, 2), "ms_per_step": round(st * 1e3, 4),
-                            "gemv_launches": n_l, "act_quant_launches": len(p.kgroups),
+                            "gemv_launches": n_l, "act_quant_launches": n_aq,
                             "graph": run is not None, "wall_s": round(wall, 3)}
         log(f"[bench] gemv {sched}: {p.step_bytes / st / 1e9:.1f} GB/s, {st * 1e3:.3f} ms/step, {n_l} launches")
     head = schedules["grouped"]
     step_s = head["ms_per_step"] / 1e3
     value = p.step_bytes / step_s / 1e9
-    dur, bytes_per_launch = per_launch_grouped(p, p.grouped_calls, reps=10)
+    dur, bytes_per_launch = per_launch_grouped(p, p.grouped_calls, reps=10, fused=False)
     achieved = bytes_per_launch / dur / 1e9
+    if not args.quick:
+        dur_f, bytes_f = per_launch_grouped(p, p.fused_calls, reps=10, fused=True)
+        schedules["grouped_fused"]["per_launch"] = {"avg_launch_us": round(dur_f * 1e6, 3),
+                                                    "GBps": round(bytes_f / dur_f / 1e9, 2)}
     check = None if args.skip_check else sampled_check(p, [0, 4, 6, len(p.mats) - 1])
 
     out.update({
@@ -547,8 +640,9 @@ def main():
         "ms_per_step": round(step_s * 1e3, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "int8", "data": "synthetic",
         "config": {"workload": f"ternary_4b decode pass: {len(p.mats)} ternary group-128 GEMVs "
-                               f"(K=2560/9728, N=2560/9728), T={args.tokens}, per-token act-quant of every input "
-                               f"included; equal-k products issued as grouped launches",
+                               f"(K=2560/9728, N=2560/9728), T={args.tokens}, from fp32 inputs: per-token "
+                               f"act-quant of every input included (one launch per k); equal-k products "
+                               f"issued as grouped launches",
                    "tokens": args.tokens, "matrices": len(p.mats), "bytes_per_step": p.step_bytes,
                    "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2), "schedules": schedules},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",

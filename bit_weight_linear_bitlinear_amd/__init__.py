@@ -67,6 +67,10 @@ _lib.lowbit_linear_batched.argtypes = [_D, _P, _P, _P, _P, _i32, _P, _P, _P]
 _PP = ctypes.POINTER(ctypes.c_void_p)
 _lib.lowbit_linear_grouped.argtypes = [_i32, _D, _PP, _PP, _PP, _PP, _i32, _PP, _PP, _P]
 _lib.lowbit_linear_grouped.restype = _i32
+_lib.lowbit_linear_fused.argtypes = [_D, _P, _P, _P, _i32, _P, _P, _P, _P, _P]
+_lib.lowbit_linear_fused.restype = _i32
+_lib.lowbit_linear_grouped_fused.argtypes = [_i32, _D, _PP, _PP, _PP, _PP, _PP, _i32, _PP, _P, _P]
+_lib.lowbit_linear_grouped_fused.restype = _i32
 _lib.lowbit_max_k.argtypes = [_i32]
 _lib.lowbit_max_k.restype = _i32
 _lib.lowbit_status_string.argtypes = [_i32]
@@ -77,7 +81,7 @@ for _f in ("lowbit_describe", "lowbit_pack", "lowbit_act_quant", "lowbit_linear"
     getattr(_lib, _f).restype = _i32
 
 EXPORTS = ("lowbit_describe", "lowbit_pack", "lowbit_act_quant", "lowbit_linear", "lowbit_linear_batched",
-           "lowbit_linear_grouped",
+           "lowbit_linear_grouped", "lowbit_linear_fused", "lowbit_linear_grouped_fused",
            "lowbit_max_k", "lowbit_status_string", "lowbit_abi_version", "lowbit_last_hip_error")
 
 
@@ -196,6 +200,57 @@ class GroupedCall:
 def lowbit_linear_grouped(descs, packed, scales, q, sx, y, acc=None, stream=None) -> None:
     """Device: several independent GEMVs of equal k in one launch."""
     GroupedCall(descs, packed, scales, q, sx, y, acc)(stream)
+
+
+def _fused_ptrs(d, packed, scales, x, q, sx, y):
+    t = x.shape[0]
+    if x.dim() != 2 or x.shape[1] != d.k or tuple(q.shape) != (t, d.k):
+        raise ValueError(f"x, q: expected [t, {d.k}], got {tuple(x.shape)}, {tuple(q.shape)}")
+    return (_dev(packed, "packed", d.packed_bytes), _dev(scales, "scales", 4 * d.n_scales),
+            _dev(x, "x", 4 * t * d.k), t, _dev(q, "q", t * d.k), _dev(sx, "sx", 4 * t),
+            _dev(y, "y", 4 * t * d.n))
+
+
+def lowbit_linear_fused(d: lowbit_desc, packed, scales, x, q, sx, y, status=None, stream=None) -> None:
+    """Device GEMV from fp32 x: the activation quantiser runs inside the product;
+    q int8[t, k] and sx fp32[t] receive the codes and scales as by-products."""
+    _check(_lib.lowbit_linear_fused(ctypes.byref(d), *_fused_ptrs(d, packed, scales, x, q, sx, y),
+                                    _dev(status, "status", 4), _stream(stream)), "lowbit_linear_fused")
+
+
+class GroupedFusedCall:
+    """Marshalled arguments of one lowbit_linear_grouped_fused call."""
+
+    def __init__(self, descs, packed, scales, x, q, sx, y, status=None):
+        n = len(descs)
+        if not (n == len(packed) == len(scales) == len(x) == len(q) == len(sx) == len(y)) or n < 1:
+            raise ValueError("lowbit_linear_grouped_fused: argument lists differ in length")
+        cols = [_fused_ptrs(d, pk, sc, xx, qq, ss, yy) for d, pk, sc, xx, qq, ss, yy in
+                zip(descs, packed, scales, x, q, sx, y)]
+        t = cols[0][3]
+        if any(c[3] != t for c in cols):
+            raise ValueError("lowbit_linear_grouped_fused: every x must have the same token count")
+        arr = lambda ptrs: (ctypes.c_void_p * n)(*[p.value for p in ptrs])
+        self.count, self.t = n, t
+        self.descs = (lowbit_desc * n)(*descs)
+        self.packed = arr([c[0] for c in cols])
+        self.scales = arr([c[1] for c in cols])
+        self.x = arr([c[2] for c in cols])
+        self.q = arr([c[4] for c in cols])
+        self.sx = arr([c[5] for c in cols])
+        self.y = arr([c[6] for c in cols])
+        self.status = _dev(status, "status", 4)
+        self._keep = (packed, scales, x, q, sx, y, status)
+
+    def __call__(self, stream=None):
+        _check(_lib.lowbit_linear_grouped_fused(self.count, self.descs, self.packed, self.scales, self.x, self.q,
+                                                self.sx, self.t, self.y, self.status, _stream(stream)),
+               "lowbit_linear_grouped_fused")
+
+
+def lowbit_linear_grouped_fused(descs, packed, scales, x, q, sx, y, status=None, stream=None) -> None:
+    """Device: several independent GEMVs of equal k from fp32 inputs, quantiser fused."""
+    GroupedFusedCall(descs, packed, scales, x, q, sx, y, status)(stream)
 
 
 def lowbit_max_k(format: int) -> int:

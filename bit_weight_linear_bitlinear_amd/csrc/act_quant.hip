@@ -22,13 +22,6 @@ namespace lowbit {
 
 constexpr int kActWaves = 4;   // rows per 256-thread workgroup
 
-__device__ __forceinline__ int8_t quant1(float v, float r) {
-    float p = v * r;
-    float c = rintf(p);
-    c = c < -127.0f ? -127.0f : (c > 127.0f ? 127.0f : c);
-    return (int8_t)(int)c;
-}
-
 template <bool VEC>
 __global__ __launch_bounds__(256) void act_quant_kernel(const float* __restrict__ x, int t, int k,
                                                         int8_t* __restrict__ q, float* __restrict__ sx,

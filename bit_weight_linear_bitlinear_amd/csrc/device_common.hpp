@@ -156,6 +156,16 @@ __device__ __forceinline__ void load_words_stream(const uint8_t* p, uint32_t* ou
     }
 }
 
+// One activation code (M8.8 0x02C, 0x05C): clip(rint(v * r), -127, 127) with
+// r = 127 / max|x| of the token row; one fp32 multiply (files are built without
+// contraction), rintf rounds half to even.
+__device__ __forceinline__ int8_t quant1(float v, float r) {
+    float p = v * r;
+    float c = rintf(p);
+    c = c < -127.0f ? -127.0f : (c > 127.0f ? 127.0f : c);
+    return (int8_t)(int)c;
+}
+
 __device__ __forceinline__ float wave_max(float v) {
     #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {

@@ -67,6 +67,26 @@ hipError_t launch_gemv_group(const LinearArgs* mats, int count, hipStream_t stre
     gp.lds_a_bytes = cfg.lds_a ? a.t * gp.stride : 0;
     cfg.nr = (cfg.lds_a && a.t == 1) ? 1 : 4;
 
+    // The quantiser runs in the product kernel's prologue for one token (every
+    // workgroup redoes the row; for a single token that is cheaper than a
+    // launch), with the LDS stage and whole 16-byte x words (k % 4 == 0, every
+    // x 16-byte aligned).  Otherwise the quantiser kernel produces the codes
+    // first, into the given q / sx, one launch per matrix.
+    const bool fused_in = a.x != nullptr;
+    bool x_vec = a.k % 4 == 0;
+    for (int i = 0; fused_in && i < count; ++i) x_vec = x_vec && (uintptr_t)mats[i].x % 16 == 0;
+    cfg.fuse = fused_in && cfg.lds_a && x_vec && a.t == 1;
+    if (fused_in && !cfg.fuse) {
+        for (int i = 0; i < count; ++i) {
+            const LinearArgs& b = mats[i];
+            hipError_t e = launch_act_quant(b.x, b.t, b.k, const_cast<int8_t*>(b.q), const_cast<float*>(b.sx),
+                                            b.status, stream);
+            if (e != hipSuccess) return e;
+        }
+    }
+    gp.status = cfg.fuse ? a.status : nullptr;
+    bool q_word = a.k % 4 == 0;
+
     bool q_vec = a.k % 16 == 0;
     int tiles = 0;
     bool any_acc = false;
@@ -74,6 +94,8 @@ hipError_t launch_gemv_group(const LinearArgs* mats, int count, hipStream_t stre
         const LinearArgs& b = mats[i];
         gp.m[i].packed = b.packed; gp.m[i].scales = b.scales; gp.m[i].q = b.q; gp.m[i].sx = b.sx;
         gp.m[i].y = b.y; gp.m[i].acc = b.acc;
+        gp.m[i].x = cfg.fuse ? b.x : nullptr;
+        q_word = q_word && (uintptr_t)b.q % 4 == 0;
         gp.m[i].n = b.n;
         gp.m[i].n_tiles = (b.n + 15) / 16;
         tiles += gp.m[i].n_tiles;
@@ -81,7 +103,8 @@ hipError_t launch_gemv_group(const LinearArgs* mats, int count, hipStream_t stre
         any_acc = any_acc || b.acc != nullptr;
     }
     gp.q_vec = q_vec;
-    cfg.acc = any_acc;
+    gp.q_word = q_word;
+    cfg.acc = any_acc && !cfg.fuse;
 
     // k-split: enough wavefronts to fill the chip; in group mode every part
     // holds whole groups
@@ -130,6 +153,7 @@ hipError_t launch_gemv(const LinearArgs& a, hipStream_t stream) {
         c.sx = a.sx + t0;
         c.y = a.y + (size_t)t0 * a.n;
         c.acc = a.acc ? a.acc + (size_t)t0 * a.n * a.n_groups : nullptr;
+        c.x = a.x ? a.x + (size_t)t0 * a.k : nullptr;
         hipError_t e = launch_gemv_group(&c, 1, stream);
         if (e != hipSuccess) return e;
     }

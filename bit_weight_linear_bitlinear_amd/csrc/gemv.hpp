@@ -13,8 +13,9 @@ constexpr int kGemvLdsA = 56 * 1024; // activation bytes a workgroup may stage i
 struct GemvMat {
     const uint8_t* packed;
     const float* scales;
-    const int8_t* q;
-    const float* sx;
+    const int8_t* q;     // fused launches: written (the codes of x) by the matrix's first workgroup
+    const float* sx;     // fused launches: written likewise
+    const float* x;      // fused launches: fp32 activations [T, K]; else unused
     float* y;
     int32_t* acc;        // nullable
     int n;               // rows
@@ -37,6 +38,8 @@ struct GemvParams {
     int stride;          // LDS bytes per staged token row (k padded + 16)
     int q_vec;           // k % 16 == 0 and every q 16-byte aligned
     int lds_a_bytes;     // T * stride when activations are staged in LDS, else 0
+    int q_word;          // fused: k % 4 == 0 and every q 4-byte aligned
+    int32_t* status;     // fused: LOWBIT_ACT_* bits of rejected rows (nullable)
     int wg_start[kGemvMaxMats + 1];   // first workgroup of each matrix (ascending; INT_MAX past n_mats)
     GemvMat m[kGemvMaxMats];
 };
@@ -48,6 +51,7 @@ struct GemvCfg {
     int sps;             // group mode: scale units per k-step (1, 2, 4); 0 = tensor/row scales
     bool lds_a;          // activations staged in LDS (else read from global memory)
     bool acc;            // some matrix wants the integer products
+    bool fuse;           // activations quantised in the kernel's prologue (needs lds_a)
     int grid;
     size_t lds_bytes;
 };

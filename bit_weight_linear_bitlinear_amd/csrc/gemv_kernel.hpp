@@ -37,6 +37,7 @@
 
 #include "device_common.hpp"
 #include "gemv.hpp"
+#include "lowbit.h"
 
 namespace lowbit {
 
@@ -70,13 +71,28 @@ __device__ __forceinline__ i32x4 load_q16(const int8_t* qrow, int k0, int K, boo
     return v;
 }
 
+// The codes of four consecutive activations v (scale factor r), packed
+// little first; the elements from `valid` on are past K and give 0.
+__device__ __forceinline__ uint32_t quant_word(const float4 v, float r, int valid) {
+    const float e[4] = {v.x, v.y, v.z, v.w};
+    uint32_t w = 0;
+    #pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (i < valid) w |= (uint32_t)(uint8_t)quant1(e[i], r) << (8 * i);
+    return w;
+}
+
 // NR: C registers per lane holding live tokens (token = 4 * lane group + r).
 // SPS: group mode: scale units per k-step; 0 = tensor/row scales.
 // UPG1: group mode: every scale unit is a whole group.
 // LDSA: activations staged in LDS.  ACC: also write the integer products
 // (kept out of the streaming instantiations: optional stores inside the
 // k-loop make the compiler's wait counting conservative).
-template <int FMT, int WPL, int NR, int SPS, bool UPG1, bool LDSA, bool ACC>
+// FUSE (with LDSA, one token): the stage is filled from fp32 x by the
+// per-token absmax quantiser itself (M8.8 0x02C, 0x05C: m = max|x|,
+// r = 127 / m, codes clip(rint(x r)), s_x = m / 127), every workgroup for its
+// own stage; the matrix's first workgroup also writes the codes and scale out.
+template <int FMT, int WPL, int NR, int SPS, bool UPG1, bool LDSA, bool ACC, bool FUSE>
 __global__ __launch_bounds__(256) void gemv_kernel(const GemvParams p) {
     using S = GemvShape<FMT, WPL>;
     constexpr int D = kGemvD;
@@ -88,6 +104,9 @@ __global__ __launch_bounds__(256) void gemv_kernel(const GemvParams p) {
     constexpr int NA = LDSA ? 1 : NB * MPB;                  // ring-held activation operands
     constexpr int SHIFT = Fmt<FMT>::kShift;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    static_assert(!FUSE || LDSA, "the fused quantiser fills the LDS stage");
+    __shared__ float fz_m[4];                                // fused: per-wave max |x|
+    __shared__ int fz_bad[4];                                // fused: per-wave non-finite flag
 
     // the wavefront index is uniform; saying so keeps every value derived
     // from it (tile, part, k-range) in scalar registers
@@ -114,7 +133,10 @@ __global__ __launch_bounds__(256) void gemv_kernel(const GemvParams p) {
 
     const int row = tile * 16 + rl;
 
-    const uint8_t* wp = M.packed + ((size_t)tile * p.n_steps + s0) * STEP + lane * (4 * WPL);
+    // (a fused launch issues its ring unconditionally; a wave without steps
+    // then reads its tile's first step, never consumed)
+    const uint8_t* wp = M.packed + ((size_t)tile * p.n_steps + (FUSE && s_cnt <= 0 ? 0 : s0)) * STEP +
+                        lane * (4 * WPL);
     const float* scp = M.scales + (size_t)tile * p.G * 16 + rl;            // group mode
     const int8_t* qrow = M.q + (size_t)tok * K;                            // global activations
 
@@ -132,7 +154,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const GemvParams p) {
         // Unconditional loads (a dead step past the part re-reads its last
         // step, never consumed): the compiler's wait counting then keeps all
         // D steps in flight.
-        const int jj = j < s_cnt ? j : s_cnt - 1;
+        const int jj = j < s_cnt ? j : max(s_cnt - 1, 0);
         load_words_stream<WPL>(wp + (size_t)jj * STEP, wv[u]);      // each weight byte is read once
         if constexpr (GROUP) {
             #pragma unroll
@@ -158,18 +180,132 @@ __global__ __launch_bounds__(256) void gemv_kernel(const GemvParams p) {
         }
     };
 
+    // fused: the first round of x is issued ahead of the weight
+    // ring, so the quantiser's reduction waits for x alone (the loads are
+    // counted in order) and runs while the ring's HBM loads are in flight
+    constexpr int FR = 3;                                    // words (4 k) per thread per round
+    const int nword = (K + 3) >> 2;                          // words holding real k
+    const int tid = threadIdx.x;
+    float4 xv[FR];
+    auto load_round = [&](const float* xr, int base) {      // fused launches have k % 4 == 0, x 16-byte aligned
+        #pragma unroll
+        for (int j = 0; j < FR; ++j)
+            xv[j] = reinterpret_cast<const float4*>(xr)[min(base + tid + 256 * j, nword - 1)];
+    };
+    if constexpr (FUSE) {
+        load_round(M.x, 0);
+        __builtin_amdgcn_sched_barrier(0);                   // keep these loads ahead of the ring's
+    }
+
     // ---- ring prologue, the epilogue operands, then the activation stage
-    if (s_cnt > 0) {
+    if (FUSE || s_cnt > 0) {
         #pragma unroll
         for (int u = 0; u < D; ++u) load_slot(u, u);
+    }
+    if constexpr (FUSE) {
+        // ... and the quantiser's use of x after them: an empty asm that
+        // takes the values (and orders memory) pins that point
+        #pragma unroll
+        for (int j = 0; j < FR; ++j)
+            asm volatile("" : "+v"(xv[j].x), "+v"(xv[j].y), "+v"(xv[j].z), "+v"(xv[j].w) :: "memory");
     }
     float sw = 0.0f;
     if constexpr (!GROUP) sw = M.scales[p.scale_per_row ? min(row, M.n - 1) : 0];
     float sxv[NR];
-    #pragma unroll
-    for (int r = 0; r < NR; ++r) sxv[r] = M.sx[min(4 * g + r, T - 1)];
+    if constexpr (!FUSE) {
+        #pragma unroll
+        for (int r = 0; r < NR; ++r) sxv[r] = M.sx[min(4 * g + r, T - 1)];
+    }
     const int8_t* lds_a = reinterpret_cast<const int8_t*>(smem) + (size_t)tok * p.stride + g * (KB / 4);
-    if constexpr (LDSA) {
+    if constexpr (FUSE) {
+        // fp32 x -> int8 codes in the stage (one token).  Thread tid owns the
+        // words (4 consecutive k) tid + 256 j and issues their loads in rounds
+        // of FR before using any of them, so a round costs one memory round
+        // trip; the loads are unconditional at clamped addresses (an element
+        // read twice changes neither max |x| nor finiteness).  Pass 1 reduces
+        // max |x| (wavefront shuffles, then LDS over the 4 wavefronts); pass 2
+        // quantises, from pass 1's registers when the row fits one round,
+        // else re-reading the row (L1/L2).  The first round sits outside every
+        // loop so that its wait counts the ring's loads as younger (a loop
+        // header would merge that away).
+        const bool writer = (int)blockIdx.x == p.wg_start[mi];
+        const int npad = (p.n_steps * SK) >> 2;              // words of the stage row
+        const bool one_round = nword <= 256 * FR;
+        float m = 0.0f;
+        int bad = 0;
+        auto reduce_round = [&]() {
+            #pragma unroll
+            for (int j = 0; j < FR; ++j) {
+                const float4 v = xv[j];
+                bad |= !(isfinite(v.x) && isfinite(v.y) && isfinite(v.z) && isfinite(v.w));
+                const float a0 = fabsf(v.x), a1 = fabsf(v.y), a2 = fabsf(v.z), a3 = fabsf(v.w);
+                m = a0 > m ? a0 : m; m = a1 > m ? a1 : m; m = a2 > m ? a2 : m; m = a3 > m ? a3 : m;
+            }
+        };
+        reduce_round();                                      // round 0: already in flight
+        #pragma unroll 1
+        for (int base = 256 * FR; base < nword; base += 256 * FR) {
+            load_round(M.x, base);
+            reduce_round();
+        }
+        m = wave_max(m);
+        bad = wave_or(bad);
+        if (lane == 0) { fz_m[wave] = m; fz_bad[wave] = bad; }
+        __syncthreads();
+        m = fz_m[0];
+        bad = fz_bad[0];
+        #pragma unroll
+        for (int w = 1; w < 4; ++w) {
+            m = fz_m[w] > m ? fz_m[w] : m;
+            bad |= fz_bad[w];
+        }
+        float r = 0.0f;
+        int flag = 0;
+        if (bad) {
+            flag = LOWBIT_ACT_NONFINITE;
+        } else if (m > 0.0f) {
+            r = 127.0f / m;
+            if (!isfinite(r)) flag = LOWBIT_ACT_OVERFLOW;
+        }
+        const float st = flag ? __builtin_nanf("") : m / 127.0f;
+        if (writer && threadIdx.x == 0) {
+            const_cast<float*>(M.sx)[0] = st;
+            if (flag && p.status) atomicOr(p.status, flag);
+        }
+        int8_t* qo = const_cast<int8_t*>(M.q);
+        #pragma unroll 1
+        for (int base = 0; base < npad; base += 256 * FR) {
+            if (!(one_round && base == 0)) load_round(M.x, base);
+            #pragma unroll
+            for (int j = 0; j < FR; ++j) {
+                const int w = base + tid + 256 * j;
+                if (w >= npad) continue;
+                const int valid = K - 4 * w;                 // codes of this word that exist
+                const uint32_t X = flag || valid <= 0 ? 0u : quant_word(xv[j], r, valid);
+                if constexpr (FMT == FMT_BINARY) {
+                    // word w of a 32-code chunk holds k = 8b + 4a + e (a = w & 1,
+                    // b = (w & 7) >> 1); decode_binary wants it in operand a,
+                    // register e, byte b
+                    uint8_t* o = smem + 32 * (w >> 3) + 16 * (w & 1) + ((w & 7) >> 1);
+                    #pragma unroll
+                    for (int e = 0; e < 4; ++e) o[4 * e] = (uint8_t)(X >> (8 * e));
+                } else {
+                    *reinterpret_cast<uint32_t*>(smem + 4 * w) = X;
+                }
+                if (writer && valid > 0) {                   // natural-order codes to q (k % 4 == 0)
+                    if (p.q_word) {
+                        *reinterpret_cast<uint32_t*>(qo + 4 * w) = X;
+                    } else {
+                        #pragma unroll
+                        for (int e = 0; e < 4; ++e) qo[4 * w + e] = (int8_t)(X >> (8 * e));
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        #pragma unroll
+        for (int r = 0; r < NR; ++r) sxv[r] = st;
+    } else if constexpr (LDSA) {
         const int kpad = p.n_steps * SK;
         const int8_t* q = M.q;
         for (int t = 0; t < T; ++t) {
@@ -340,12 +476,18 @@ template <int FMT, int WPL, int NR, int SPS, bool UPG1>
 void gemv_launch_lds(const GemvParams& p, const GemvCfg& c, hipStream_t st) {
     const dim3 grid((unsigned)c.grid), block(256);
     if (c.lds_a) {
-        if (c.acc) gemv_kernel<FMT, WPL, NR, SPS, UPG1, true, true><<<grid, block, c.lds_bytes, st>>>(p);
-        else gemv_kernel<FMT, WPL, NR, SPS, UPG1, true, false><<<grid, block, c.lds_bytes, st>>>(p);
+        if constexpr (NR == 1) {   // fused launches have one token
+            if (c.fuse) {
+                gemv_kernel<FMT, WPL, 1, SPS, UPG1, true, false, true><<<grid, block, c.lds_bytes, st>>>(p);
+                return;
+            }
+        }
+        if (c.acc) gemv_kernel<FMT, WPL, NR, SPS, UPG1, true, true, false><<<grid, block, c.lds_bytes, st>>>(p);
+        else gemv_kernel<FMT, WPL, NR, SPS, UPG1, true, false, false><<<grid, block, c.lds_bytes, st>>>(p);
     } else {
         // activations from L2: the large-t*k fallback, always 4 token registers
-        if (c.acc) gemv_kernel<FMT, WPL, 4, SPS, UPG1, false, true><<<grid, block, c.lds_bytes, st>>>(p);
-        else gemv_kernel<FMT, WPL, 4, SPS, UPG1, false, false><<<grid, block, c.lds_bytes, st>>>(p);
+        if (c.acc) gemv_kernel<FMT, WPL, 4, SPS, UPG1, false, true, false><<<grid, block, c.lds_bytes, st>>>(p);
+        else gemv_kernel<FMT, WPL, 4, SPS, UPG1, false, false, false><<<grid, block, c.lds_bytes, st>>>(p);
     }
 }
 

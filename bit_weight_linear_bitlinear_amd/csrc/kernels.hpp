@@ -24,6 +24,11 @@ struct LinearArgs {
     const float* sx;
     float* y;
     int32_t* acc;        // nullable
+    // fused activation quantisation (decode path only): x fp32 [t, k] is
+    // quantised inside the product, and q / sx above are then outputs (the
+    // codes and scales lowbit_act_quant would write); nullptr = q / sx given
+    const float* x = nullptr;
+    int32_t* status = nullptr;   // nullable: LOWBIT_ACT_* bits of rejected rows
 };
 
 hipError_t launch_act_quant(const float* x, int t, int k, int8_t* q, float* sx, int32_t* status,

@@ -18,7 +18,7 @@
 
 namespace {
 
-constexpr int32_t kAbiVersion = 2;
+constexpr int32_t kAbiVersion = 3;
 
 // Field geometry of the packed formats (the layout comment of lowbit.h).
 int codes_per_word(int32_t fmt) { return fmt == LOWBIT_TERNARY2 ? 16 : (fmt == LOWBIT_INT4 ? 8 : 32); }
@@ -204,6 +204,55 @@ lowbit_status linear_common(const lowbit_desc* d, const uint8_t* packed, const f
     return LOWBIT_OK;
 }
 
+// The grouped entry points: every matrix validated, then 16 tokens and at
+// most kGemvMaxMats matrices per launch.  x == nullptr: q / sx are inputs;
+// else x is quantised into q / sx (fused).
+lowbit_status grouped_common(int32_t count, const lowbit_desc* descs, const uint8_t* const* packed,
+                             const float* const* scales, const int8_t* const* q, const float* const* sx,
+                             const float* const* x, int32_t* status, int32_t t, float* const* y,
+                             int32_t* const* acc, void* hip_stream) {
+    if (count < 1 || !descs || !packed || !scales || !q || !sx || !y || t < 1) return LOWBIT_E_ARG;
+    std::vector<lowbit::LinearArgs> args((size_t)count);
+    for (int32_t i = 0; i < count; ++i) {
+        const lowbit_desc& d0 = descs[0];
+        const lowbit_desc& d = descs[i];
+        if (d.format != d0.format || d.scale != d0.scale || d.group != d0.group || d.flags != d0.flags ||
+            d.k != d0.k)
+            return LOWBIT_E_ARG;
+        lowbit_status st = linear_common(&d, packed[i], scales[i], q[i], sx[i], t, y[i], acc ? acc[i] : nullptr,
+                                         &args[(size_t)i]);
+        if (st != LOWBIT_OK) return st;
+        if (x) {
+            if (!x[i] || (uintptr_t)x[i] % 4 != 0) return LOWBIT_E_ARG;
+            args[(size_t)i].x = x[i];
+            args[(size_t)i].status = status;
+        }
+    }
+    clear_hip_error();
+    const hipStream_t stream = (hipStream_t)hip_stream;
+    for (int32_t t0 = 0; t0 < t; t0 += 16) {              // 16 tokens per launch
+        const int32_t tc = std::min(16, t - t0);
+        std::vector<lowbit::LinearArgs> chunk(args);
+        for (auto& a : chunk) {
+            a.t = tc;
+            a.q += (size_t)t0 * a.k;
+            a.sx += t0;
+            a.y += (size_t)t0 * a.n;
+            if (a.acc) a.acc += (size_t)t0 * a.n * a.n_groups;
+            if (a.x) a.x += (size_t)t0 * a.k;
+        }
+        // as few launches as the kernel-argument space allows, of near-equal size
+        const int32_t launches = (count + lowbit::kGemvMaxMats - 1) / lowbit::kGemvMaxMats;
+        for (int32_t li = 0, b = 0; li < launches; ++li) {
+            const int32_t e = (int32_t)((int64_t)count * (li + 1) / launches);
+            lowbit_status st = hip_status(lowbit::launch_gemv_group(chunk.data() + b, e - b, stream));
+            if (st != LOWBIT_OK) return st;
+            b = e;
+        }
+    }
+    return LOWBIT_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -275,43 +324,31 @@ lowbit_status lowbit_linear_batched(const lowbit_desc* d, const uint8_t* packed,
     return hip_status(lowbit::launch_gemm(a, (hipStream_t)hip_stream));
 }
 
+lowbit_status lowbit_linear_fused(const lowbit_desc* d, const uint8_t* packed, const float* scales, const float* x,
+                                  int32_t t, int8_t* q, float* sx, float* y, int32_t* status, void* hip_stream) {
+    lowbit::LinearArgs a;
+    lowbit_status st = linear_common(d, packed, scales, q, sx, t, y, nullptr, &a);
+    if (st != LOWBIT_OK) return st;
+    if (!x || (uintptr_t)x % 4 != 0 || (uintptr_t)status % 4 != 0) return LOWBIT_E_ARG;
+    a.x = x;
+    a.status = status;
+    clear_hip_error();
+    return hip_status(lowbit::launch_gemv(a, (hipStream_t)hip_stream));
+}
+
 lowbit_status lowbit_linear_grouped(int32_t count, const lowbit_desc* descs, const uint8_t* const* packed,
                                     const float* const* scales, const int8_t* const* q, const float* const* sx,
                                     int32_t t, float* const* y, int32_t* const* acc, void* hip_stream) {
-    if (count < 1 || !descs || !packed || !scales || !q || !sx || !y || t < 1) return LOWBIT_E_ARG;
-    std::vector<lowbit::LinearArgs> args((size_t)count);
-    for (int32_t i = 0; i < count; ++i) {
-        const lowbit_desc& d0 = descs[0];
-        const lowbit_desc& d = descs[i];
-        if (d.format != d0.format || d.scale != d0.scale || d.group != d0.group || d.flags != d0.flags ||
-            d.k != d0.k)
-            return LOWBIT_E_ARG;
-        lowbit_status st = linear_common(&d, packed[i], scales[i], q[i], sx[i], t, y[i], acc ? acc[i] : nullptr,
-                                         &args[(size_t)i]);
-        if (st != LOWBIT_OK) return st;
-    }
-    clear_hip_error();
-    const hipStream_t stream = (hipStream_t)hip_stream;
-    for (int32_t t0 = 0; t0 < t; t0 += 16) {              // 16 tokens per launch
-        const int32_t tc = std::min(16, t - t0);
-        std::vector<lowbit::LinearArgs> chunk(args);
-        for (auto& a : chunk) {
-            a.t = tc;
-            a.q += (size_t)t0 * a.k;
-            a.sx += t0;
-            a.y += (size_t)t0 * a.n;
-            if (a.acc) a.acc += (size_t)t0 * a.n * a.n_groups;
-        }
-        // as few launches as the kernel-argument space allows, of near-equal size
-        const int32_t launches = (count + lowbit::kGemvMaxMats - 1) / lowbit::kGemvMaxMats;
-        for (int32_t li = 0, b = 0; li < launches; ++li) {
-            const int32_t e = (int32_t)((int64_t)count * (li + 1) / launches);
-            lowbit_status st = hip_status(lowbit::launch_gemv_group(chunk.data() + b, e - b, stream));
-            if (st != LOWBIT_OK) return st;
-            b = e;
-        }
-    }
-    return LOWBIT_OK;
+    return grouped_common(count, descs, packed, scales, q, sx, nullptr, nullptr, t, y, acc, hip_stream);
+}
+
+lowbit_status lowbit_linear_grouped_fused(int32_t count, const lowbit_desc* descs, const uint8_t* const* packed,
+                                          const float* const* scales, const float* const* x, int8_t* const* q,
+                                          float* const* sx, int32_t t, float* const* y, int32_t* status,
+                                          void* hip_stream) {
+    if (!x || (uintptr_t)status % 4 != 0) return LOWBIT_E_ARG;
+    return grouped_common(count, descs, packed, scales, reinterpret_cast<const int8_t* const*>(q),
+                          reinterpret_cast<const float* const*>(sx), x, status, t, y, nullptr, hip_stream);
 }
 
 int32_t lowbit_max_k(int32_t format) { return max_k_of(format); }

@@ -207,6 +207,42 @@ lowbit_status lowbit_linear_grouped(int32_t count, const lowbit_desc* descs, con
                                     const float* const* sx, int32_t t, float* const* y,
                                     int32_t* const* acc, void* hip_stream);
 
+/*
+ * lowbit_linear_fused - the decode product with the activation quantiser fused
+ * into it (M8.8 "Native Binary and Ternary Transformers" 0x02C / 0x05C
+ * quantiser, 0x02D product): what lowbit_act_quant(x, t, k, q, sx, status)
+ * followed by lowbit_linear(d, packed, scales, q, sx, t, y, NULL) computes,
+ * bit for bit, from fp32 x, in one call.  For one token (t = 1) with
+ * k % 4 == 0, x 16-byte aligned and the row within the product's LDS stage,
+ * every workgroup of the product quantises the row into its own stage (one
+ * launch, the codes never read back; one workgroup per matrix still writes
+ * q and sx).  Otherwise the quantiser kernel runs first and the product reads
+ * its codes: redoing a row per workgroup costs more than that launch once
+ * there are several token rows.
+ *   x       device float [t, k]
+ *   q, sx   device int8 [t, k], device float [t]   out (as lowbit_act_quant)
+ *   status  device int32 [1] or NULL: LOWBIT_ACT_* bits ORed in, as lowbit_act_quant
+ *   other arguments and y as lowbit_linear (no integer output)
+ * Errors: as lowbit_linear.
+ */
+lowbit_status lowbit_linear_fused(const lowbit_desc* d, const uint8_t* packed, const float* scales,
+                                  const float* x, int32_t t, int8_t* q, float* sx, float* y,
+                                  int32_t* status, void* hip_stream);
+
+/*
+ * lowbit_linear_grouped_fused - lowbit_linear_grouped with the quantiser fused
+ * as in lowbit_linear_fused: matrix i quantises x[i] (device float [t, k])
+ * into q[i], sx[i] and computes y[i].  One status word for all matrices.
+ * Where the quantiser does not run in the product's prologue it is launched
+ * once per matrix; callers with many matrices and several tokens do better
+ * with one lowbit_act_quant over stacked inputs and lowbit_linear_grouped.
+ * Errors: as lowbit_linear_grouped.
+ */
+lowbit_status lowbit_linear_grouped_fused(int32_t count, const lowbit_desc* descs, const uint8_t* const* packed,
+                                          const float* const* scales, const float* const* x, int8_t* const* q,
+                                          float* const* sx, int32_t t, float* const* y, int32_t* status,
+                                          void* hip_stream);
+
 /* Largest k the kernels accept for a format.  The operator's own bound
  * (M8.8 0x09C) is k * 127 * qmax < 2^31; the kernels hold each code scaled
  * by 64 (ternary, binary) or 16 (int4) in int8 lanes, so their int32 sums need

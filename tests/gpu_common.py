@@ -58,6 +58,19 @@ def linear_dev(entry, d, packed, scales, q, sx, with_acc=True):
     return y, acc
 
 
+def linear_fused_dev(d, packed, scales, x_dev):
+    """lowbit_linear_fused on fresh (poisoned) output buffers."""
+    import torch
+    lb = lib()
+    t = x_dev.shape[0]
+    y = torch.full((t, d.n), float("nan"), dtype=torch.float32, device="cuda")
+    q = torch.full((t, d.k), 99, dtype=torch.int8, device="cuda")
+    sx = torch.full((t,), -1.0, dtype=torch.float32, device="cuda")
+    st = torch.zeros((1,), dtype=torch.int32, device="cuda")
+    lb.lowbit_linear_fused(d, packed, scales, x_dev, q, sx, y, st)
+    return y, q, sx, st
+
+
 def check_y(y_gpu, y32, y64, what):
     y_gpu = np.asarray(y_gpu, np.float32)
     err = np.abs(y_gpu.astype(np.float64) - y32.astype(np.float64))
@@ -107,6 +120,14 @@ def run_layer(w, x, fmt, scale, group, tanh, entries=("gemv", "gemm"), token_sam
         y_stream, _ = linear_dev(entry, d, packed, scales, q, sx, with_acc=False)
         torch.cuda.synchronize()
         assert torch.equal(y_stream, y), f"{label} {entry}: y without acc differs from y with acc"
+        if entry == "gemv":
+            # the quantiser fused into the product: the same codes, scales and y
+            yf, qf, sxf, stf = linear_fused_dev(d, packed, scales, x_dev)
+            torch.cuda.synchronize()
+            assert torch.equal(qf, q), f"{label}: fused codes differ from lowbit_act_quant's"
+            assert torch.equal(sxf.view(torch.int32), sx.view(torch.int32)), f"{label}: fused scales differ"
+            assert int(stf.cpu()[0]) == 0
+            assert torch.equal(yf, y), f"{label}: fused y differs from act-quant + product"
         out[entry] = (y, acc)
     if len(entries) == 2:
         a0, a1 = out["gemv"][1], out["gemm"][1]

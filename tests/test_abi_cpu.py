@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol():
     lib = ctypes.CDLL(lb.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
-    assert lb.lowbit_abi_version() == 2
+    assert lb.lowbit_abi_version() == 3
 
 
 def test_describe_sizes():

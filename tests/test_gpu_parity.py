@@ -7,7 +7,8 @@ import pytest
 
 import oracle
 import workloads
-from tests.gpu_common import act_quant_dev, check_y, linear_dev, pack_upload, run_layer, say, to_dev
+from tests.gpu_common import (act_quant_dev, check_y, linear_dev, linear_fused_dev, pack_upload, run_layer, say,
+                               to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -231,3 +232,90 @@ def test_gemm_tile_shapes(fmt):
         sample[0], sample[-1] = 0, t - 1
         run_layer(w, x, fmt, "row", 0, fmt == "int4", entries=("gemm",), token_sample=sample,
                   label=f"tile shapes n={n} k={k} t={t}")
+
+
+@pytest.mark.parametrize("fmt", ["ternary", "binary", "int4"])
+def test_fused_quantiser_edges(fmt):
+    """The fused entry against the quantiser kernel + product.  One token (the
+    quantiser runs in the product kernel's prologue): rows that are ordinary,
+    with NaN, with Inf, all zero, and whose 127 / max overflows, at k from one
+    word round to several (64, 1000 - ending inside a k-step -, 3072 = exactly
+    one round, 4100, 9728), and rows the prologue does not take (k % 4 != 0, an
+    x not 16-byte aligned).  Several tokens (the quantiser kernel runs first):
+    the same edge rows, 17 tokens (two launches), t * k too large for the LDS
+    stage.  Then the grouped call."""
+    import torch
+    lb = pytest.importorskip("bit_weight_linear_bitlinear_amd")
+    scale = "group" if fmt == "ternary" else "row"
+    group = 128 if fmt != "binary" else 0
+
+    def compare(d, packed, scales, x, x_dev, expect_status):
+        q, sx, st = act_quant_dev(x_dev)
+        y, _ = linear_dev("gemv", d, packed, scales, q, sx, with_acc=False)
+        yf, qf, sxf, stf = linear_fused_dev(d, packed, scales, x_dev)
+        torch.cuda.synchronize()
+        assert int(st.cpu()[0]) == expect_status and int(stf.cpu()[0]) == expect_status
+        assert torch.equal(qf, q)
+        assert torch.equal(sxf.view(torch.int32), sx.view(torch.int32))
+        assert torch.equal(yf.isnan(), y.isnan())
+        ok = ~y.isnan()
+        assert torch.equal(yf[ok], y[ok])
+        q_ref, sx_ref, rs = oracle.act_quant(x)
+        good = rs == 0
+        assert (qf.cpu().numpy()[good] == q_ref[good]).all()
+        assert (sxf.cpu().numpy()[good].view(np.uint32) == sx_ref[good].view(np.uint32)).all()
+        return yf
+
+    def edge_rows(x):
+        x[1, 7] = np.nan
+        x[2, 3] = np.inf
+        x[3, :] = 0.0
+        x[4, :] = np.float32(1e-39)           # 127 / max overflows fp32
+        return x
+
+    # one token
+    for (n, k, misalign) in [(40, 64, False), (48, 1000, False), (24, 3072, False), (33, 4100, False),
+                             (20, 9728, False), (40, 1003, False), (20, 512, True)]:
+        say(f"[case] fused quantiser t=1 fmt={fmt} n={n} k={k} misaligned_x={misalign}")
+        w, x5 = workloads.random_case(900 + k, n, k, 5)
+        x5[0, ::97] *= 40.0                   # outliers in the ordinary row
+        edge_rows(x5)
+        d, packed, scales, _, _ = pack_upload(w, fmt, scale, group if scale == "group" else 0, fmt == "int4")
+        for row, status in ((0, 0), (1, 1), (2, 1), (3, 0), (4, 2)):
+            x = np.ascontiguousarray(x5[row:row + 1])
+            x_dev = to_dev(x)
+            if misalign:                      # same values, 4 bytes past a 16-byte boundary
+                x_dev = torch.empty(k + 4, device="cuda")[1:1 + k].view(1, k).copy_(x_dev)
+            yf = compare(d, packed, scales, x, x_dev, status)
+            assert bool(yf.isnan().all()) == (status != 0)
+
+    # several tokens
+    for (n, k, t) in [(48, 1000, 6), (40, 1003, 17), (33, 4100, 16)]:
+        say(f"[case] fused quantiser fmt={fmt} n={n} k={k} t={t}")
+        w, x = workloads.random_case(900 + k, n, k, t)
+        edge_rows(x)
+        d, packed, scales, _, _ = pack_upload(w, fmt, scale, group if scale == "group" else 0, fmt == "int4")
+        yf = compare(d, packed, scales, x, to_dev(x), 3)
+        assert bool(yf.isnan()[1].all()) and bool(yf.isnan()[4].all())
+
+    # grouped: 5 matrices of one k, mixed n, against the separate grouped call
+    # (one token: the prologue quantiser; three: the quantiser kernel first)
+    k = 2560
+    for t in (1, 3):
+        say(f"[case] grouped fused fmt={fmt} t={t}")
+        descs, pk, sc, xs, qs, sxs, ys, yfs, qfs, sxfs = [], [], [], [], [], [], [], [], [], []
+        for i, n in enumerate([2560, 64, 9728 // 8, 16, 520]):
+            w, x = workloads.random_case(950 + i, n, k, t)
+            d, packed, scales, _, _ = pack_upload(w, fmt, scale, group if scale == "group" else 0, fmt == "int4")
+            descs.append(d); pk.append(packed); sc.append(scales); xs.append(to_dev(x))
+            q, sx, _ = act_quant_dev(xs[-1])
+            qs.append(q); sxs.append(sx)
+            ys.append(torch.empty((t, n), device="cuda")); yfs.append(torch.full((t, n), float("nan"), device="cuda"))
+            qfs.append(torch.zeros((t, k), dtype=torch.int8, device="cuda")); sxfs.append(torch.zeros(t, device="cuda"))
+        lb.lowbit_linear_grouped(descs, pk, sc, qs, sxs, ys)
+        st = torch.zeros(1, dtype=torch.int32, device="cuda")
+        lb.lowbit_linear_grouped_fused(descs, pk, sc, xs, qfs, sxfs, yfs, st)
+        torch.cuda.synchronize()
+        assert int(st.cpu()[0]) == 0
+        for i in range(len(descs)):
+            assert torch.equal(qfs[i], qs[i]) and torch.equal(sxfs[i], sxs[i]) and torch.equal(yfs[i], ys[i]), i
