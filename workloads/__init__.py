@@ -40,7 +40,7 @@ TERNARY, BINARY, INT4 = "ternary", "binary", "int4"
 TENSOR, ROW, GROUP = "tensor", "row", "group"
 
 WEIGHT_STD = np.float32(0.02)
-KIND_W, KIND_X, KIND_OUTLIER = 0, 1, 2
+KIND_W, KIND_X, KIND_OUTLIER, KIND_EMBED, KIND_NORM, KIND_TOKENS = 0, 1, 2, 3, 4, 5
 
 
 @dataclass(frozen=True)
@@ -139,3 +139,28 @@ def random_case(seed: int, n: int, k: int, t: int, scale: float = 0.02) -> Tuple
     w = g.standard_normal((n, k), dtype=np.float32) * np.float32(scale)
     x = g.standard_normal((t, k), dtype=np.float32)
     return w, x
+
+
+# ---------------------------------------------------------------- decode model
+# The 256-d decoder the decode-stack matrices belong to, as a whole model:
+# the add/sub-only engine's quick-start configuration (256-d, 6 layers, 4
+# heads, 4096-entry vocabulary, 128-token context) with the stack's gated FFN.
+DECODE_MODEL = dict(d=256, layers=6, heads=4, d_ff=1024, vocab=4096, context=128)
+
+
+def decode_model_embedding(vocab: int, d: int) -> np.ndarray:
+    """Token embedding table [vocab, d] = N(0, 1) fp32 (kept in fp32, as the
+    engine's README keeps it)."""
+    return _rng(1, 0, 0, KIND_EMBED).standard_normal((vocab, d), dtype=np.float32)
+
+
+def decode_model_norms(layers: int, d: int) -> np.ndarray:
+    """RMSNorm gains [2 * layers + 1, d] = 1 + 0.1 N(0, 1) fp32 (attention and
+    FFN norm of each layer, then the final norm)."""
+    g = _rng(1, 0, 0, KIND_NORM).standard_normal((2 * layers + 1, d), dtype=np.float32)
+    return (np.float32(1.0) + np.float32(0.1) * g).astype(np.float32)
+
+
+def decode_model_tokens(n: int, vocab: int, seed: int = 0) -> np.ndarray:
+    """n seeded token ids in [0, vocab)."""
+    return _rng(1, seed, 0, KIND_TOKENS).integers(0, vocab, size=n, dtype=np.int64).astype(np.int32)
