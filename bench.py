@@ -449,15 +449,171 @@ def cpu_baseline(wl, tokens, budget_s=12.0, sample_layers=4):
                        + tokens * (5 * m.k + 4))
             nops += 2 * tokens * m.n * m.k
         passes += 1
-    return {"value": round(nbytes / spent / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": f"{len(items)} matrices ({min(sample_layers, wl.layers)} of {wl.layers} layer-equivalents) "
-                      f"x {passes} passes, T={tokens}: act-quant + unpack + int64 product + fp32 epilogue, "
-                      f"{spent:.1f}s timed",
-            "gops": round(nops / spent / 1e9, 3)}
+    out = {"value": round(nbytes / spent / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
+           "kind": "oracle",
+           "sample": f"{len(items)} matrices ({min(sample_layers, wl.layers)} of {wl.layers} layer-equivalents) "
+                     f"x {passes} passes, T={tokens}: act-quant + unpack + int64 product + fp32 epilogue, "
+                     f"{spent:.1f}s timed",
+           "gops": round(nops / spent / 1e9, 3)}
+    out["single_thread"] = single_thread_baselines()
+    return out
+
+
+def single_thread_baselines(min_s=1.0):
+    """The oracle on one host thread, the comparable of a single-thread CPU
+    engine: the single ternary projection (768 x 192, 256 tokens), one pass
+    of the 256-d decode stack at t = 1 (31 products, each input quantised),
+    and decode steps of the 256-d model (binary64 float steps, exact
+    products); each repeated for at least min_s seconds."""
+    import oracle
+    import workloads
+    from oracle import model as om
+    n_before = oracle.num_threads()
+    oracle.set_threads(1)
+    try:
+        def timed(fn):
+            n, t0 = 0, time.perf_counter()
+            while True:
+                fn()
+                n += 1
+                dt = time.perf_counter() - t0
+                if dt >= min_s:
+                    return dt / n
+        res = {}
+        wl0 = workloads.BY_NAME["single_ternary"]
+        m0 = wl0.matrices[0]
+        pk0, sc0, _, _ = oracle.quantize_and_pack(workloads.latent_weights(wl0.index, 0, 0, m0.n, m0.k), "ternary",
+                                                  "tensor")
+        x0 = workloads.workload_activations(wl0, 0, 0, wl0.tokens[0], m0.k)
+
+        def call0():
+            q, sx, _ = oracle.act_quant(x0)
+            oracle.linear(pk0, sc0, "ternary", "tensor", 0, m0.n, m0.k, q, sx)
+        res["single_ternary_ms_per_call"] = round(timed(call0) * 1e3, 3)
+        wl1 = workloads.BY_NAME["decode_stack"]
+        mats = []
+        for layer in range(wl1.layers):
+            for mi, m in enumerate(wl1.matrices):
+                if layer < m.count:
+                    pk, sc, _, _ = oracle.quantize_and_pack(workloads.latent_weights(wl1.index, layer, mi, m.n, m.k),
+                                                            "ternary", "tensor")
+                    mats.append((m, pk, sc, workloads.workload_activations(wl1, layer, mi, 1, m.k)))
+
+        def pass1():
+            for m, pk, sc, x in mats:
+                q, sx, _ = oracle.act_quant(x)
+                oracle.linear(pk, sc, "ternary", "tensor", 0, m.n, m.k, q, sx)
+        res["decode_stack_ms_per_pass"] = round(timed(pass1) * 1e3, 3)
+        cfg = workloads.DECODE_MODEL
+        d, L, H, ff, V, C = (cfg[k] for k in ("d", "layers", "heads", "d_ff", "vocab", "context"))
+        order = {0: 0, 1: 1, 2: 3, 3: 2, 4: 4}
+        shapes = [(3 * d, d), (d, d), (ff, d), (ff, d), (d, ff)]
+        packed, scales = [], []
+        for layer in range(L):
+            for slot in range(5):
+                n, k = shapes[slot]
+                pk, sc, _, _ = oracle.quantize_and_pack(
+                    workloads.latent_weights(wl1.index, layer, order[slot], n, k), "ternary", "tensor")
+                packed.append(pk)
+                scales.append(sc)
+        pk, sc, _, _ = oracle.quantize_and_pack(workloads.latent_weights(wl1.index, 0, 5, V, d), "ternary", "tensor")
+        packed.append(pk)
+        scales.append(sc)
+        model = om.Model(d, L, H, ff, V, C, workloads.decode_model_embedding(V, d),
+                         workloads.decode_model_norms(L, d), packed, scales)
+        kc, vc = np.zeros((L, C, d)), np.zeros((L, C, d))
+        state = {"tok": int(workloads.decode_model_tokens(1, V, seed=3)[0]), "pos": 0}
+
+        def step():
+            if state["pos"] >= C:
+                state["pos"] = 0
+            _, state["tok"], _ = om.decode_step(model, state["tok"], state["pos"], kc, vc)
+            state["pos"] += 1
+        res["decode_model_tokens_per_s"] = round(1.0 / timed(step), 1)
+        res["threads"] = 1
+        return res
+    finally:
+        oracle.set_threads(n_before)
 
 
 # ------------------------------------------------------------------- main
+
+def build_decode_model(lb):
+    """The 256-d ternary decoder (quick-start shape of the add/sub-only engine,
+    the decode stack's projections) from the seeded latent weights, packed by
+    the library: (DecodeModel, config)."""
+    import torch
+    import workloads
+    cfg = workloads.DECODE_MODEL
+    d, L, H, ff, V, C = (cfg[k] for k in ("d", "layers", "heads", "d_ff", "vocab", "context"))
+    shapes = [(3 * d, d), (d, d), (ff, d), (ff, d), (d, ff), (V, d)]
+    descs = [lb.lowbit_describe(lb.TERNARY2, lb.SCALE_TENSOR, n, k) for n, k in shapes]
+    mi = {0: 0, 1: 1, 2: 3, 3: 2, 4: 4, 5: 5}                 # decode_stack matrix of each slot
+    wl = workloads.BY_NAME["decode_stack"]
+    packed, scales = [], []
+    for layer in range(L + 1):
+        for slot in (range(5) if layer < L else [5]):
+            n, k = shapes[slot]
+            w = workloads.latent_weights(wl.index, layer if slot < 5 else 0, mi[slot], n, k)
+            pk = np.empty(descs[slot].packed_bytes, np.uint8)
+            sc = np.empty(descs[slot].n_scales, np.float32)
+            lb.lowbit_pack(descs[slot], w, pk, sc)
+            packed.append(torch.from_numpy(pk).cuda())
+            scales.append(torch.from_numpy(sc).cuda())
+    embed = torch.from_numpy(workloads.decode_model_embedding(V, d)).cuda()
+    norms = torch.from_numpy(workloads.decode_model_norms(L, d)).cuda()
+    return lb.DecodeModel(d, L, H, ff, V, C, descs, embed, norms, packed, scales), cfg
+
+
+def decode_model_view():
+    """Greedy generation with the 256-d ternary decoder at batch 1: one step
+    captured in a HIP graph and replayed across the whole 128-token context
+    (each replay reads the token and position the previous one left on the
+    device), timed with events; the eager step beside it."""
+    import torch
+    import workloads
+    lb = __import__("bit_weight_linear_bitlinear_amd")
+    gm, cfg = build_decode_model(lb)
+    V, C = cfg["vocab"], cfg["context"]
+    start = int(workloads.decode_model_tokens(1, V, seed=3)[0])
+    st = torch.tensor([start, 0, 0, 0], dtype=torch.int32, device="cuda")
+    logits = torch.empty(V, device="cuda")
+    toks = torch.zeros(C, dtype=torch.int32, device="cuda")
+
+    def reset():
+        st.copy_(torch.tensor([start, 0, 0, 0], dtype=torch.int32))
+        gm.k_cache.zero_()
+        gm.v_cache.zero_()
+
+    step = lambda: gm.step(st, logits, tokens=toks)
+    run = capture(step)
+    steps = C - 1
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    res = {}
+    for name, fn in (("graph", run), ("eager", step)):
+        if fn is None:
+            continue
+        for rep in range(2):                                 # the second pass is timed
+            reset()
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(steps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+        dt = e0.elapsed_time(e1) / 1e3
+        res[name] = {"tokens_per_s": round(steps / dt, 1), "us_per_token": round(dt / steps * 1e6, 2)}
+    s = st.cpu().tolist()
+    L = cfg["layers"]
+    out = {"what": "greedy decode, batch 1, of the 256-d 6-layer ternary decoder (4 heads, 4096 vocabulary, "
+                   "128-token context; RMSNorm, rotary attention over an fp32 KV cache, SwiGLU, ternary head), "
+                   f"{steps} tokens per timed run from position 0; 3 + 8 * {L} launches per token",
+           "launches_per_token": 3 + 8 * L, "final_state": s, **res,
+           "context_not_target": "the engine's README quotes ~170-185 tokens/s for this configuration on one "
+                                 "Apple M-series CPU thread without a KV cache"}
+    log(f"[bench] decode model: {res}")
+    return out
+
 
 def extra_views(args):
     """The other timing views: (iii) the streaming ceiling on one large cold
@@ -538,6 +694,8 @@ def extra_views(args):
     log(f"[bench] decode stack t=1: {st * 1e6:.1f} us/step, {dur * 1e6:.2f} us per GEMV call; "
         f"dependent calls: {dep}")
     del p1
+
+    views["decode_model_t1"] = decode_model_view()
 
     # the binary 8192-token GEMM pass
     wl2 = workloads.BY_NAME["binary_gqa"]

@@ -71,6 +71,30 @@ _lib.lowbit_linear_fused.argtypes = [_D, _P, _P, _P, _i32, _P, _P, _P, _P, _P]
 _lib.lowbit_linear_fused.restype = _i32
 _lib.lowbit_linear_grouped_fused.argtypes = [_i32, _D, _PP, _PP, _PP, _PP, _PP, _i32, _PP, _P, _P]
 _lib.lowbit_linear_grouped_fused.restype = _i32
+
+
+class lowbit_model(ctypes.Structure):
+    """Mirror of the C struct lowbit_model (one decode step's model)."""
+    _fields_ = [("d_model", ctypes.c_int32), ("n_layers", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+                ("d_ff", ctypes.c_int32), ("vocab", ctypes.c_int32), ("context", ctypes.c_int32),
+                ("norm_eps", ctypes.c_float), ("rope_base", ctypes.c_float), ("proj", lowbit_desc * 6),
+                ("embed", _P), ("norms", _P), ("packed", _PP), ("scales", _PP), ("k_cache", _P),
+                ("v_cache", _P), ("work", _P)]
+
+
+_M = ctypes.POINTER(lowbit_model)
+_lib.lowbit_model_work_bytes.argtypes = [_M]
+_lib.lowbit_model_work_bytes.restype = ctypes.c_int64
+_lib.lowbit_model_trace_floats.argtypes = [_M]
+_lib.lowbit_model_trace_floats.restype = ctypes.c_int64
+_lib.lowbit_decode_step.argtypes = [_M, _P, _P, _P, _P, _P]
+_lib.lowbit_decode_step.restype = _i32
+_lib.lowbit_rmsnorm.argtypes = [_P, _P, _P, _P, _i32, _i32, ctypes.c_float, _P, _P]
+_lib.lowbit_rmsnorm.restype = _i32
+_lib.lowbit_rope_attention.argtypes = [_P, _i32, _i32, _i32, ctypes.c_float, _P, _P, _P, _P]
+_lib.lowbit_rope_attention.restype = _i32
+_lib.lowbit_swiglu.argtypes = [_P, _P, ctypes.c_int64, _P, _P]
+_lib.lowbit_swiglu.restype = _i32
 _lib.lowbit_max_k.argtypes = [_i32]
 _lib.lowbit_max_k.restype = _i32
 _lib.lowbit_status_string.argtypes = [_i32]
@@ -82,7 +106,13 @@ for _f in ("lowbit_describe", "lowbit_pack", "lowbit_act_quant", "lowbit_linear"
 
 EXPORTS = ("lowbit_describe", "lowbit_pack", "lowbit_act_quant", "lowbit_linear", "lowbit_linear_batched",
            "lowbit_linear_grouped", "lowbit_linear_fused", "lowbit_linear_grouped_fused",
+           "lowbit_model_work_bytes", "lowbit_model_trace_floats", "lowbit_decode_step",
+           "lowbit_rmsnorm", "lowbit_rope_attention", "lowbit_swiglu",
            "lowbit_max_k", "lowbit_status_string", "lowbit_abi_version", "lowbit_last_hip_error")
+
+# projection slots (lowbit_model.proj and the per-layer weight lists)
+PROJ_QKV, PROJ_O, PROJ_GATE, PROJ_UP, PROJ_DOWN, PROJ_HEAD = range(6)
+STEP_POSITION, STEP_TOKEN = 1, 2
 
 
 class LowbitError(RuntimeError):
@@ -251,6 +281,88 @@ class GroupedFusedCall:
 def lowbit_linear_grouped_fused(descs, packed, scales, x, q, sx, y, status=None, stream=None) -> None:
     """Device: several independent GEMVs of equal k from fp32 inputs, quantiser fused."""
     GroupedFusedCall(descs, packed, scales, x, q, sx, y, status)(stream)
+
+
+def _f32(t, name):
+    if t is not None and t.dtype != __import__("torch").float32:
+        raise ValueError(f"{name}: expected float32")
+
+
+def lowbit_rmsnorm(x, g, h, eps=1e-6, r=None, x_out=None, stream=None) -> None:
+    """Device: h = RMSNorm(x + r; g) per row (r optional), x_out = x + r."""
+    t, d = x.shape
+    for v, nm in ((x, "x"), (g, "g"), (h, "h"), (r, "r"), (x_out, "x_out")):
+        _f32(v, nm)
+    _check(_lib.lowbit_rmsnorm(_dev(x, "x", 4 * t * d), _dev(r, "r", 4 * t * d), _dev(x_out, "x_out", 4 * t * d),
+                               _dev(g, "g", 4 * d), t, d, eps, _dev(h, "h", 4 * t * d), _stream(stream)),
+           "lowbit_rmsnorm")
+
+
+def lowbit_rope_attention(qkv, pos, k_cache, v_cache, attn, rope_base=10000.0, stream=None) -> None:
+    """Device: one token's rotary attention at position pos over one layer's
+    caches [context, d] (writes row pos of both)."""
+    context, d = k_cache.shape
+    for v, nm in ((qkv, "qkv"), (k_cache, "k_cache"), (v_cache, "v_cache"), (attn, "attn")):
+        _f32(v, nm)
+    if d % 64 or tuple(v_cache.shape) != (context, d):
+        raise ValueError("lowbit_rope_attention: caches must be [context, 64 * n_heads]")
+    _check(_lib.lowbit_rope_attention(_dev(qkv, "qkv", 12 * d), d // 64, pos, context, rope_base,
+                                      _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(attn, "attn", 4 * d),
+                                      _stream(stream)), "lowbit_rope_attention")
+
+
+def lowbit_swiglu(gate, up, a, stream=None) -> None:
+    """Device: a = SiLU(gate) * up elementwise."""
+    n = gate.numel()
+    for v, nm in ((gate, "gate"), (up, "up"), (a, "a")):
+        _f32(v, nm)
+    _check(_lib.lowbit_swiglu(_dev(gate, "gate"), _dev(up, "up", 4 * n), n, _dev(a, "a", 4 * n), _stream(stream)),
+           "lowbit_swiglu")
+
+
+class DecodeModel:
+    """Marshalled arguments of lowbit_decode_step: the model struct over device
+    tensors the caller provides (embedding, norm gains, packed weights and
+    scales in the C struct's order), with the key/value caches and the
+    workspace allocated here as torch tensors."""
+
+    def __init__(self, d_model, n_layers, n_heads, d_ff, vocab, context, descs, embed, norms, packed, scales,
+                 norm_eps=1e-6, rope_base=10000.0):
+        import torch
+        if len(descs) != 6 or len(packed) != 5 * n_layers + 1 or len(scales) != len(packed):
+            raise ValueError("DecodeModel: 6 descriptors and 5 * n_layers + 1 weight / scale tensors expected")
+        m = lowbit_model()
+        m.d_model, m.n_layers, m.n_heads, m.d_ff, m.vocab, m.context = d_model, n_layers, n_heads, d_ff, vocab, context
+        m.norm_eps, m.rope_base = norm_eps, rope_base
+        for i, d in enumerate(descs):
+            m.proj[i] = d
+        m.embed = _dev(embed, "embed", 4 * vocab * d_model).value
+        m.norms = _dev(norms, "norms", 4 * (2 * n_layers + 1) * d_model).value
+        slot_desc = [descs[i % 5] for i in range(5 * n_layers)] + [descs[5]]
+        self._packed = (ctypes.c_void_p * len(packed))(
+            *[_dev(p, "packed", d.packed_bytes).value for p, d in zip(packed, slot_desc)])
+        self._scales = (ctypes.c_void_p * len(scales))(
+            *[_dev(s, "scales", 4 * d.n_scales).value for s, d in zip(scales, slot_desc)])
+        m.packed = ctypes.cast(self._packed, _PP)
+        m.scales = ctypes.cast(self._scales, _PP)
+        self.k_cache = torch.zeros((n_layers, context, d_model), dtype=torch.float32, device="cuda")
+        self.v_cache = torch.zeros_like(self.k_cache)
+        m.k_cache, m.v_cache = self.k_cache.data_ptr(), self.v_cache.data_ptr()
+        wb = int(_lib.lowbit_model_work_bytes(ctypes.byref(m)))
+        if wb < 0:
+            raise ValueError("DecodeModel: invalid model sizes or descriptors")
+        self.work = torch.empty(wb, dtype=torch.uint8, device="cuda")
+        m.work = self.work.data_ptr()
+        self.trace_floats = int(_lib.lowbit_model_trace_floats(ctypes.byref(m)))
+        self.model = m
+        self._keep = (embed, norms, list(packed), list(scales))
+
+    def step(self, state, logits, tokens=None, trace=None, stream=None) -> None:
+        m = self.model
+        _check(_lib.lowbit_decode_step(ctypes.byref(m), _dev(state, "state", 16), _dev(logits, "logits", 4 * m.vocab),
+                                       _dev(tokens, "tokens", 4 * m.context),
+                                       _dev(trace, "trace", 4 * self.trace_floats), _stream(stream)),
+               "lowbit_decode_step")
 
 
 def lowbit_max_k(format: int) -> int:

@@ -20,6 +20,7 @@ LIB = os.path.join(HERE, "liblowbit.so")
 ARCH = os.environ.get("LOWBIT_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["act_quant.hip", "gemv.hip", "gemv_ternary.hip", "gemv_int4.hip", "gemv_binary.hip", "gemm.hip",
+           "decode_model.hip",
            "gemm_mfma.hip", "lowbit_host.cpp"]
 
 COMMON = ["-std=c++17", "-O3", "-fPIC", "-ffp-contract=off", "-fno-fast-math",

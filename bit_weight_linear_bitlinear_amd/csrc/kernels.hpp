@@ -44,4 +44,18 @@ hipError_t launch_gemm_generic(const LinearArgs& a, hipStream_t stream);
 // compute units of the current device (cached per device)
 int device_cu_count();
 
+// the small kernels of a decode step (decode_model.hip); state = int32[4],
+// or nullptr outside a step (then the position is `pos` and nothing is skipped)
+hipError_t launch_embed_norm(const float* embed, int vocab, int d, const float* g, float eps, int32_t* state,
+                             int context, float* x, float* h, hipStream_t st);
+hipError_t launch_add_norm(const float* xs, const float* r, float* xd, int rows, int d, const float* g,
+                           float eps, const int32_t* state, int context, float* h, hipStream_t st);
+hipError_t launch_rope_attn(const float* qkv, int d, int heads, double base, const int32_t* state, int pos,
+                            int context, float* kc, float* vc, float* attn, float* q_trace, float* k_trace,
+                            hipStream_t st);
+hipError_t launch_swiglu(const float* gate, const float* up, float* a, int64_t n, const int32_t* state,
+                         int context, hipStream_t st);
+hipError_t launch_argmax_advance(const float* logits, int vocab, int32_t* state, int context, int32_t* tokens,
+                                 hipStream_t st);
+
 }  // namespace lowbit

@@ -18,7 +18,7 @@
 
 namespace {
 
-constexpr int32_t kAbiVersion = 3;
+constexpr int32_t kAbiVersion = 4;
 
 // Field geometry of the packed formats (the layout comment of lowbit.h).
 int codes_per_word(int32_t fmt) { return fmt == LOWBIT_TERNARY2 ? 16 : (fmt == LOWBIT_INT4 ? 8 : 32); }
@@ -253,9 +253,186 @@ lowbit_status grouped_common(int32_t count, const lowbit_desc* descs, const uint
     return LOWBIT_OK;
 }
 
+// ---- decode step of a BitLinear decoder
+
+bool desc_is(const lowbit_desc& d, int64_t n, int64_t k) {
+    return check_desc(&d) == LOWBIT_OK && d.n == n && d.k == k;
+}
+
+// Sizes valid?  (Pointers are checked by the step itself.)
+bool model_sizes_ok(const lowbit_model* m) {
+    if (!m) return false;
+    const int64_t d = m->d_model, ff = m->d_ff;
+    if (m->n_heads < 1 || d != 64LL * m->n_heads || d > 4096 || m->n_layers < 1 || ff < 1 || m->vocab < 1 ||
+        m->context < 1 || m->context > 8192 || !(m->norm_eps >= 0.0f) || !(m->rope_base > 0.0f) ||
+        !std::isfinite(m->norm_eps) || !std::isfinite(m->rope_base))
+        return false;
+    return desc_is(m->proj[LOWBIT_PROJ_QKV], 3 * d, d) && desc_is(m->proj[LOWBIT_PROJ_O], d, d) &&
+           desc_is(m->proj[LOWBIT_PROJ_GATE], ff, d) && desc_is(m->proj[LOWBIT_PROJ_UP], ff, d) &&
+           desc_is(m->proj[LOWBIT_PROJ_DOWN], d, ff) && desc_is(m->proj[LOWBIT_PROJ_HEAD], m->vocab, d);
+}
+
+inline int64_t up16(int64_t b) { return (b + 15) / 16 * 16; }
+
+// Workspace: the float intermediates, then the codes and token scales the
+// fused products write (gate and up get separate code buffers).
+struct WorkLayout {
+    int64_t x, h, qkv, attn, o, gate, up, a, dn, sx, q0, q1, total;
+};
+
+WorkLayout work_layout(const lowbit_model* m) {
+    const int64_t d = m->d_model, ff = m->d_ff;
+    WorkLayout w;
+    int64_t o = 0;
+    auto take = [&](int64_t bytes) { const int64_t at = o; o += up16(bytes); return at; };
+    w.x = take(4 * d); w.h = take(4 * d); w.qkv = take(12 * d); w.attn = take(4 * d); w.o = take(4 * d);
+    w.gate = take(4 * ff); w.up = take(4 * ff); w.a = take(4 * ff); w.dn = take(4 * d); w.sx = take(16);
+    w.q0 = take(std::max(d, ff)); w.q1 = take(ff);
+    w.total = o;
+    return w;
+}
+
+int64_t trace_floats(const lowbit_model* m) {
+    const int64_t d = m->d_model, ff = m->d_ff;
+    return d + (int64_t)m->n_layers * (12 * d + 3 * ff) + d;
+}
+
 }  // namespace
 
 extern "C" {
+
+lowbit_status lowbit_rmsnorm(const float* x, const float* r, float* x_out, const float* g, int32_t t, int32_t d,
+                             float eps, float* h, void* hip_stream) {
+    if (!x || !g || !h || t < 1 || d < 1 || d > 4096 || !(eps >= 0.0f) || !std::isfinite(eps)) return LOWBIT_E_ARG;
+    if ((uintptr_t)x % 4 || (uintptr_t)r % 4 || (uintptr_t)x_out % 4 || (uintptr_t)g % 4 || (uintptr_t)h % 4)
+        return LOWBIT_E_ARG;
+    clear_hip_error();
+    return hip_status(lowbit::launch_add_norm(x, r, x_out, t, d, g, eps, nullptr, 0, h, (hipStream_t)hip_stream));
+}
+
+lowbit_status lowbit_rope_attention(const float* qkv, int32_t n_heads, int32_t pos, int32_t context, float rope_base,
+                                    float* k_cache, float* v_cache, float* attn, void* hip_stream) {
+    if (!qkv || !k_cache || !v_cache || !attn || n_heads < 1 || n_heads > 64 || context < 1 || context > 8192 ||
+        pos < 0 || pos >= context || !(rope_base > 0.0f) || !std::isfinite(rope_base))
+        return LOWBIT_E_ARG;
+    if ((uintptr_t)qkv % 4 || (uintptr_t)k_cache % 16 || (uintptr_t)v_cache % 4 || (uintptr_t)attn % 4)
+        return LOWBIT_E_ARG;
+    clear_hip_error();
+    return hip_status(lowbit::launch_rope_attn(qkv, 64 * n_heads, n_heads, (double)rope_base, nullptr, pos, context,
+                                               k_cache, v_cache, attn, nullptr, nullptr, (hipStream_t)hip_stream));
+}
+
+lowbit_status lowbit_swiglu(const float* gate, const float* up, int64_t n, float* a, void* hip_stream) {
+    if (!gate || !up || !a || n < 1 || n > (int64_t)256 * 0x7fffffff) return LOWBIT_E_ARG;
+    if ((uintptr_t)gate % 4 || (uintptr_t)up % 4 || (uintptr_t)a % 4) return LOWBIT_E_ARG;
+    clear_hip_error();
+    return hip_status(lowbit::launch_swiglu(gate, up, a, n, nullptr, 0, (hipStream_t)hip_stream));
+}
+
+int64_t lowbit_model_work_bytes(const lowbit_model* m) { return model_sizes_ok(m) ? work_layout(m).total : -1; }
+
+int64_t lowbit_model_trace_floats(const lowbit_model* m) { return model_sizes_ok(m) ? trace_floats(m) : -1; }
+
+lowbit_status lowbit_decode_step(const lowbit_model* m, int32_t* state, float* logits, int32_t* tokens,
+                                 float* trace, void* hip_stream) {
+    if (!model_sizes_ok(m)) return LOWBIT_E_ARG;
+    const int L = m->n_layers;
+    if (!m->embed || !m->norms || !m->packed || !m->scales || !m->k_cache || !m->v_cache || !m->work || !state ||
+        !logits)
+        return LOWBIT_E_ARG;
+    if ((uintptr_t)m->work % 16 != 0 || (uintptr_t)trace % 16 != 0 || (uintptr_t)state % 4 != 0 ||
+        (uintptr_t)logits % 4 != 0 || (uintptr_t)tokens % 4 != 0 || (uintptr_t)m->embed % 4 != 0 ||
+        (uintptr_t)m->norms % 4 != 0 || (uintptr_t)m->k_cache % 16 != 0 || (uintptr_t)m->v_cache % 4 != 0)
+        return LOWBIT_E_ARG;
+    for (int i = 0; i < 5 * L + 1; ++i)
+        if (!m->packed[i] || !m->scales[i]) return LOWBIT_E_ARG;
+
+    const int d = m->d_model, ff = m->d_ff, ctx = m->context;
+    const hipStream_t st = (hipStream_t)hip_stream;
+    const WorkLayout wl = work_layout(m);
+    uint8_t* wb = static_cast<uint8_t*>(m->work);
+    auto wf = [&](int64_t off) { return reinterpret_cast<float*>(wb + off); };
+    float* sx = wf(wl.sx);
+    int8_t* q0 = reinterpret_cast<int8_t*>(wb + wl.q0);
+    int8_t* q1 = reinterpret_cast<int8_t*>(wb + wl.q1);
+    int32_t* act_status = state + 2;
+
+    // one fused BitLinear on one token
+    auto product = [&](int slot, int layer, const float* x, int8_t* q, float* sxp, float* y,
+                       lowbit::LinearArgs* out) -> lowbit_status {
+        const int i = layer < L ? 5 * layer + slot : 5 * L;
+        lowbit_status s = linear_common(&m->proj[slot], m->packed[i], m->scales[i], q, sxp, 1, y, nullptr, out);
+        out->x = x;
+        out->status = act_status;
+        return s;
+    };
+    lowbit_status s = LOWBIT_OK;
+    auto run = [&](hipError_t e) { if (s == LOWBIT_OK && e != hipSuccess) s = hip_status(e); };
+    auto single = [&](int slot, int layer, const float* x, float* y) {
+        lowbit::LinearArgs a;
+        if (s != LOWBIT_OK) return;
+        s = product(slot, layer, x, q0, sx, y, &a);
+        if (s == LOWBIT_OK) run(lowbit::launch_gemv(a, st));
+    };
+
+    // intermediates: trace slots, or the workspace (x updated in place)
+    const int64_t ls = 12LL * d + 3LL * ff;                  // trace floats per layer
+    auto tl = [&](int layer, int64_t off) { return trace + d + layer * ls + off; };
+    float* x = trace ? trace : wf(wl.x);
+    float* h = trace ? tl(0, 0) : wf(wl.h);
+    const float eps = m->norm_eps;
+
+    clear_hip_error();
+    run(lowbit::launch_embed_norm(m->embed, m->vocab, d, m->norms, eps, state, ctx, x, h, st));
+    for (int l = 0; l < L && s == LOWBIT_OK; ++l) {
+        float* qkv = trace ? tl(l, d) : wf(wl.qkv);
+        float* qrot = trace ? tl(l, 4LL * d) : nullptr;
+        float* krot = trace ? tl(l, 5LL * d) : nullptr;
+        float* attn = trace ? tl(l, 6LL * d) : wf(wl.attn);
+        float* o = trace ? tl(l, 7LL * d) : wf(wl.o);
+        float* xmid = trace ? tl(l, 8LL * d) : x;
+        float* h2 = trace ? tl(l, 9LL * d) : wf(wl.h);
+        float* gate = trace ? tl(l, 10LL * d) : wf(wl.gate);
+        float* up = trace ? tl(l, 10LL * d + ff) : wf(wl.up);
+        float* a = trace ? tl(l, 10LL * d + 2LL * ff) : wf(wl.a);
+        float* dn = trace ? tl(l, 10LL * d + 3LL * ff) : wf(wl.dn);
+        float* xout = trace ? tl(l, 11LL * d + 3LL * ff) : x;
+        float* hnext = trace ? (l + 1 < L ? tl(l + 1, 0) : trace + d + L * ls) : wf(wl.h);
+        const size_t cache_off = (size_t)l * ctx * d;
+
+        single(LOWBIT_PROJ_QKV, l, h, qkv);
+        if (s != LOWBIT_OK) break;
+        run(lowbit::launch_rope_attn(qkv, d, m->n_heads, (double)m->rope_base, state, 0, ctx,
+                                     m->k_cache + cache_off, m->v_cache + cache_off, attn, qrot, krot, st));
+        single(LOWBIT_PROJ_O, l, attn, o);
+        if (s != LOWBIT_OK) break;
+        run(lowbit::launch_add_norm(x, o, xmid, 1, d, m->norms + (size_t)(2 * l + 1) * d, eps, state, ctx, h2,
+                                    st));
+        // gate and up share their input: one launch when their formats allow
+        lowbit::LinearArgs gu[2];
+        s = product(LOWBIT_PROJ_GATE, l, h2, q0, sx + 1, gate, &gu[0]);
+        if (s == LOWBIT_OK) s = product(LOWBIT_PROJ_UP, l, h2, q1, sx + 2, up, &gu[1]);
+        if (s != LOWBIT_OK) break;
+        const lowbit_desc& dg = m->proj[LOWBIT_PROJ_GATE];
+        const lowbit_desc& du = m->proj[LOWBIT_PROJ_UP];
+        if (dg.format == du.format && dg.scale == du.scale && dg.group == du.group && dg.flags == du.flags) {
+            run(lowbit::launch_gemv_group(gu, 2, st));
+        } else {
+            run(lowbit::launch_gemv(gu[0], st));
+            run(lowbit::launch_gemv(gu[1], st));
+        }
+        run(lowbit::launch_swiglu(gate, up, a, ff, state, ctx, st));
+        single(LOWBIT_PROJ_DOWN, l, a, dn);
+        if (s != LOWBIT_OK) break;
+        const float* gnext = m->norms + (size_t)(2 * l + 2) * d;   // next layer's attention norm, or the final one
+        run(lowbit::launch_add_norm(xmid, dn, xout, 1, d, gnext, eps, state, ctx, hnext, st));
+        x = xout;
+        h = hnext;
+    }
+    single(LOWBIT_PROJ_HEAD, L, h, logits);
+    if (s == LOWBIT_OK) run(lowbit::launch_argmax_advance(logits, m->vocab, state, ctx, tokens, st));
+    return s;
+}
 
 lowbit_status lowbit_describe(int32_t format, int32_t scale, int32_t n, int32_t k, int32_t group, int32_t flags,
                               lowbit_desc* out) {

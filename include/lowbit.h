@@ -243,6 +243,110 @@ lowbit_status lowbit_linear_grouped_fused(int32_t count, const lowbit_desc* desc
                                           float* const* sx, int32_t t, float* const* y, int32_t* status,
                                           void* hip_stream);
 
+/* ---------------------------------------------------------------------------
+ * One decode step of a BitLinear decoder.
+ *
+ * The block is the LLaMA-like recipe of the b1.58 models (M8.8 "Native Binary
+ * and Ternary Transformers", the b1.58 section): pre-norm RMSNorm, attention
+ * with rotary position embeddings over a key/value cache, a SwiGLU FFN,
+ * residual adds, a final RMSNorm and a head; every projection a BitLinear
+ * (lowbit_linear_fused: per-token int8 codes of its input, exact integer
+ * product, fp32 rescale).  Its shape follows the add/sub-only engine's
+ * quick-start model (Atomic-1Bit README: 256-d, 6 layers, 4 heads, 4096
+ * vocabulary, 128-token context, fp32 token embedding).
+ *   RMSNorm(x; g) = x / sqrt(mean(x^2) + norm_eps) * g
+ *   rotary: head dimension i < 32 paired with i + 32, angle pos * base^(-i/32)
+ *   attention: per head, softmax over cached positions 0 .. pos of
+ *              q . k_j / sqrt(64), output sum_j p_j v_j
+ *   SwiGLU: a = SiLU(x W_gate) * (x W_up), SiLU(z) = z / (1 + e^-z)
+ *   next token: argmax of the logits (lowest index among equal maxima)
+ * ------------------------------------------------------------------------- */
+
+#define LOWBIT_STEP_POSITION 1   /* position outside [0, context): nothing computed */
+#define LOWBIT_STEP_TOKEN 2      /* token outside [0, vocab): clamped into it */
+
+/* Projection slots of lowbit_model.proj and of the per-layer weight arrays. */
+enum { LOWBIT_PROJ_QKV = 0, LOWBIT_PROJ_O = 1, LOWBIT_PROJ_GATE = 2, LOWBIT_PROJ_UP = 3, LOWBIT_PROJ_DOWN = 4,
+       LOWBIT_PROJ_HEAD = 5 };
+
+typedef struct lowbit_model {
+    int32_t d_model;         /* n_heads * 64 (head dimension 64), <= 4096 */
+    int32_t n_layers;        /* >= 1 */
+    int32_t n_heads;         /* >= 1 */
+    int32_t d_ff;            /* FFN width, >= 1 */
+    int32_t vocab;           /* >= 1 */
+    int32_t context;         /* positions the caches hold, 1 .. 8192 */
+    float norm_eps;          /* RMSNorm epsilon, >= 0 */
+    float rope_base;         /* rotary base, > 0 */
+    /* shapes of every layer's projections and of the head: qkv [3 d_model,
+     * d_model] (rows: q, k, v), o [d_model, d_model], gate and up [d_ff,
+     * d_model], down [d_model, d_ff], head [vocab, d_model]; any format and
+     * scale mode (lowbit_describe) */
+    lowbit_desc proj[6];
+    const float* embed;               /* device [vocab, d_model] fp32 */
+    const float* norms;               /* device [2 n_layers + 1, d_model]: attention, FFN gain per layer, then final */
+    const uint8_t* const* packed;     /* host array [5 n_layers + 1] of device pointers: per layer qkv, o, gate,
+                                         up, down; then the head (lowbit_pack output, 16-byte aligned) */
+    const float* const* scales;       /* host array, same indexing */
+    float* k_cache;                   /* device [n_layers, context, d_model] fp32 (rotated keys), 16-byte aligned */
+    float* v_cache;                   /* device [n_layers, context, d_model] fp32 */
+    void* work;                       /* device workspace, lowbit_model_work_bytes() bytes, 16-byte aligned */
+} lowbit_model;
+
+/* The step's building blocks on their own (the same kernels).
+ *
+ * lowbit_rmsnorm - per row of t: v = x + r (r NULL: v = x), x_out = v (when
+ *   not NULL; may equal x), h = v / sqrt(mean(v^2) + eps) * g.  fp32 sums.
+ *   x, r, x_out, h device float [t, d]; g device float [d]; 1 <= d <= 4096.
+ * lowbit_rope_attention - one layer's attention for one token at position
+ *   pos (0 <= pos < context <= 8192): the query and key of qkv (device
+ *   float [3 * 64 * n_heads]: q, k, v blocks) rotated by pos, key and value
+ *   stored at row pos of k_cache / v_cache (device float [context, 64 *
+ *   n_heads]; k_cache 16-byte aligned), attn (device float [64 * n_heads]) =
+ *   per-head softmax attention over rows 0 .. pos.  Rows above pos are not
+ *   read.
+ * lowbit_swiglu - a = SiLU(gate) * up elementwise, n >= 1 elements.
+ * Errors: LOWBIT_E_ARG for null / misaligned pointers or sizes out of range;
+ *         LOWBIT_E_HIP. */
+lowbit_status lowbit_rmsnorm(const float* x, const float* r, float* x_out, const float* g, int32_t t, int32_t d,
+                             float eps, float* h, void* hip_stream);
+lowbit_status lowbit_rope_attention(const float* qkv, int32_t n_heads, int32_t pos, int32_t context, float rope_base,
+                                    float* k_cache, float* v_cache, float* attn, void* hip_stream);
+lowbit_status lowbit_swiglu(const float* gate, const float* up, int64_t n, float* a, void* hip_stream);
+
+/* Bytes of lowbit_model.work for this model (the intermediates of one step),
+ * or -1 when the model's sizes are invalid. */
+int64_t lowbit_model_work_bytes(const lowbit_model* m);
+
+/* Floats of the optional trace buffer of lowbit_decode_step: x0 [d] (the
+ * embedding row), then per layer h [d], qkv [3d], q rotated [d], k rotated
+ * [d], attention output [d], o [d], x after attention [d], h2 [d], gate [ff],
+ * up [ff], SwiGLU output [ff], down [d], x after the FFN [d], and last the
+ * final norm's output [d]; -1 when the model's sizes are invalid. */
+int64_t lowbit_model_trace_floats(const lowbit_model* m);
+
+/*
+ * lowbit_decode_step - one token through the model, on the device.
+ *   state   device int32[4]: [0] the token (in), replaced by the greedy next
+ *           token; [1] its position, advanced by one; [2] LOWBIT_ACT_* bits
+ *           ORed in by the products (a rejected activation row); [3]
+ *           LOWBIT_STEP_* bits ORed in.  Token and position are read on the
+ *           device, so a captured graph of this call replays step after step.
+ *           A position outside [0, context) leaves caches, state [0..1],
+ *           tokens and trace untouched (logits are then unspecified).
+ *   logits  device float [vocab], out
+ *   tokens  device int32 [context] or NULL: tokens[pos + 1] = next token
+ *           when pos + 1 < context
+ *   trace   device float [lowbit_model_trace_floats(m)] or NULL (16-byte
+ *           aligned): every intermediate of the step, for tests
+ * The caches receive this position's rotated key and value per layer.  All
+ * launches go to hip_stream in order; nothing is allocated.
+ * Errors: LOWBIT_E_ARG (invalid model, descriptor shape mismatch, null or
+ *         misaligned pointer), LOWBIT_E_RANGE, LOWBIT_E_HIP.
+ */
+lowbit_status lowbit_decode_step(const lowbit_model* m, int32_t* state, float* logits, int32_t* tokens,
+                                 float* trace, void* hip_stream);
+
 /* Largest k the kernels accept for a format.  The operator's own bound
  * (M8.8 0x09C) is k * 127 * qmax < 2^31; the kernels hold each code scaled
  * by 64 (ternary, binary) or 16 (int4) in int8 lanes, so their int32 sums need

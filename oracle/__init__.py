@@ -65,6 +65,8 @@ def _load():
     lib.orc_linear.argtypes = [i32, i32, i64, i64, i64, p, p, i64, p, p, p, p, p]
     lib.orc_acc_bound_ok.argtypes = [i32, i64]
     lib.orc_num_threads.argtypes = []
+    lib.orc_set_threads.argtypes = [i32]
+    lib.orc_set_threads.restype = None
     _lib = lib
     return lib
 
@@ -80,6 +82,11 @@ def _check(rc: int, what: str):
 
 def num_threads() -> int:
     return int(_load().orc_num_threads())
+
+
+def set_threads(n: int) -> None:
+    """Threads of the oracle's parallel loops from now on (timing only)."""
+    _load().orc_set_threads(int(n))
 
 
 def layout(fmt: str, n: int, k: int) -> dict:

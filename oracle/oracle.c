@@ -33,6 +33,15 @@ int orc_num_threads(void) {
 #endif
 }
 
+/* Threads the parallel loops use from now on (n >= 1); a timing knob only. */
+void orc_set_threads(int n) {
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* ------------------------------------------------------------------ layout */
 
 /*

@@ -85,6 +85,7 @@ int orc_linear(int fmt, int scale_mode, int64_t group, int64_t n, int64_t k,
 int orc_acc_bound_ok(int fmt, int64_t k);
 
 int orc_num_threads(void);
+void orc_set_threads(int n);
 
 #ifdef __cplusplus
 }

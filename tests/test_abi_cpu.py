@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol():
     lib = ctypes.CDLL(lb.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
-    assert lb.lowbit_abi_version() == 3
+    assert lb.lowbit_abi_version() == 4
 
 
 def test_describe_sizes():
@@ -180,3 +180,53 @@ def test_single_hip_runtime_in_process():
     with open("/proc/self/maps") as f:
         paths = set(re.findall(r"\S*libamdhip64\S*", f.read()))
     assert len(paths) == 1, paths
+
+
+# ------------------------------------------------------------- decode model
+
+def _model_struct(d=256, layers=6, heads=4, ff=1024, vocab=4096, context=128):
+    m = lb.lowbit_model()
+    m.d_model, m.n_layers, m.n_heads, m.d_ff, m.vocab, m.context = d, layers, heads, ff, vocab, context
+    m.norm_eps, m.rope_base = 1e-6, 10000.0
+    shapes = [(3 * d, d), (d, d), (ff, d), (ff, d), (d, ff), (vocab, d)]
+    for i, (n, k) in enumerate(shapes):
+        m.proj[i] = lb.lowbit_describe(lb.TERNARY2, lb.SCALE_TENSOR, n, k)
+    return m
+
+
+def test_model_sizes():
+    """Workspace and trace sizes of the 256-d model follow the documented
+    layouts; invalid sizes report -1."""
+    lib = lb.raw_library()
+    m = _model_struct()
+    d, ff, L = 256, 1024, 6
+    up16 = lambda b: (b + 15) // 16 * 16
+    want = sum(up16(b) for b in (4 * d, 4 * d, 12 * d, 4 * d, 4 * d, 4 * ff, 4 * ff, 4 * ff, 4 * d, 16,
+                                 max(d, ff), ff))
+    assert lib.lowbit_model_work_bytes(ctypes.byref(m)) == want
+    assert lib.lowbit_model_trace_floats(ctypes.byref(m)) == d + L * (12 * d + 3 * ff) + d
+    for field, bad in (("n_heads", 3), ("d_model", 250), ("context", 0), ("context", 8193), ("vocab", 0),
+                       ("n_layers", 0), ("rope_base", 0.0), ("norm_eps", -1.0)):
+        mb = _model_struct()
+        setattr(mb, field, bad)
+        assert lib.lowbit_model_work_bytes(ctypes.byref(mb)) == -1, field
+    mb = _model_struct()
+    mb.proj[lb.PROJ_DOWN] = lb.lowbit_describe(lb.TERNARY2, lb.SCALE_TENSOR, 256, 512)   # wrong k
+    assert lib.lowbit_model_trace_floats(ctypes.byref(mb)) == -1
+
+
+def test_decode_step_rejects_bad_arguments_on_the_host():
+    """Every check happens before any launch: no GPU is touched."""
+    lib = lb.raw_library()
+    m = _model_struct()
+    fake = ctypes.c_void_p(1 << 20)                          # never dereferenced: the checks fail first
+    assert lib.lowbit_decode_step(ctypes.byref(m), fake, fake, None, None, None) == 1
+    m.embed = m.norms = m.k_cache = m.v_cache = 1 << 20
+    m.work = (1 << 20) + 8                                   # misaligned workspace
+    arr = (ctypes.c_void_p * 31)(*([1 << 20] * 31))
+    m.packed = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
+    m.scales = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
+    assert lib.lowbit_decode_step(ctypes.byref(m), fake, fake, None, None, None) == 1
+    m.work = 1 << 20
+    arr[7] = None                                            # a missing weight pointer
+    assert lib.lowbit_decode_step(ctypes.byref(m), fake, fake, None, None, None) == 1
