@@ -15,6 +15,8 @@
 // 2048) or a whole workgroup, reduced, and quantised from the registers;
 // longer or unaligned rows take a two-pass loop (one wavefront per row, the
 // second pass served from L2).
+#include <algorithm>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -22,10 +24,23 @@ namespace lowbit {
 
 constexpr int kActWaves = 4;   // rows per 256-thread workgroup
 
+// The inputs of one launch: up to kActQuantMaxSrc matrices [t, k] of equal
+// shape (blockIdx.y picks one), so that several products' inputs are
+// quantised by one launch.
+struct ActQuantTable {
+    int t;
+    const float* x[kActQuantMaxSrc];
+    int8_t* q[kActQuantMaxSrc];
+    float* sx[kActQuantMaxSrc];
+};
+
 template <bool VEC>
-__global__ __launch_bounds__(256) void act_quant_kernel(const float* __restrict__ x, int t, int k,
-                                                        int8_t* __restrict__ q, float* __restrict__ sx,
+__global__ __launch_bounds__(256) void act_quant_kernel(const ActQuantTable tab, int k,
                                                         int32_t* __restrict__ status) {
+    const float* __restrict__ x = tab.x[blockIdx.y];
+    int8_t* __restrict__ q = tab.q[blockIdx.y];
+    float* __restrict__ sx = tab.sx[blockIdx.y];
+    const int t = tab.t;
     const int row = blockIdx.x * kActWaves + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (row >= t) return;   // whole wavefronts exit together
@@ -95,9 +110,12 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const float* __restrict_
 // workgroup's wavefronts), and the codes are written from the same registers.
 // All loads of a thread are issued before any is consumed.
 template <int TPR, int R>
-__global__ __launch_bounds__(256) void act_quant_reg_kernel(const float* __restrict__ x, int t, int k,
-                                                            int8_t* __restrict__ q, float* __restrict__ sx,
+__global__ __launch_bounds__(256) void act_quant_reg_kernel(const ActQuantTable tab, int k,
                                                             int32_t* __restrict__ status) {
+    const float* __restrict__ x = tab.x[blockIdx.y];
+    int8_t* __restrict__ q = tab.q[blockIdx.y];
+    float* __restrict__ sx = tab.sx[blockIdx.y];
+    const int t = tab.t;
     constexpr int RPW = 256 / TPR;                           // rows per workgroup
     __shared__ float red_m[4];
     __shared__ int red_bad[4];
@@ -156,24 +174,42 @@ __global__ __launch_bounds__(256) void act_quant_reg_kernel(const float* __restr
     }
 }
 
+hipError_t launch_act_quant_group(const float* const* x, int8_t* const* q, float* const* sx, int count, int t,
+                                  int k, int32_t* status, hipStream_t stream) {
+    for (int b = 0; b < count; b += kActQuantMaxSrc) {
+        const int n = std::min(kActQuantMaxSrc, count - b);
+        ActQuantTable tab{};
+        tab.t = t;
+        bool vec = k % 4 == 0;
+        for (int i = 0; i < n; ++i) {
+            tab.x[i] = x[b + i];
+            tab.q[i] = q[b + i];
+            tab.sx[i] = sx[b + i];
+            vec = vec && (uintptr_t)x[b + i] % 16 == 0 && (uintptr_t)q[b + i] % 4 == 0;
+        }
+        const int k4 = k / 4;
+        if (vec && k4 <= 64 * 8) {
+            act_quant_reg_kernel<64, 8><<<dim3((unsigned)((t + 3) / 4), n), dim3(256), 0, stream>>>(tab, k, status);
+        } else if (vec && k4 <= 256 * 4) {
+            act_quant_reg_kernel<256, 4><<<dim3((unsigned)t, n), dim3(256), 0, stream>>>(tab, k, status);
+        } else if (vec && k4 <= 256 * 16) {
+            act_quant_reg_kernel<256, 16><<<dim3((unsigned)t, n), dim3(256), 0, stream>>>(tab, k, status);
+        } else {
+            dim3 grid((unsigned)((t + kActWaves - 1) / kActWaves), n), block(256);
+            if (vec)
+                act_quant_kernel<true><<<grid, block, 0, stream>>>(tab, k, status);
+            else
+                act_quant_kernel<false><<<grid, block, 0, stream>>>(tab, k, status);
+        }
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 hipError_t launch_act_quant(const float* x, int t, int k, int8_t* q, float* sx, int32_t* status,
                             hipStream_t stream) {
-    const bool vec = (k % 4 == 0) && ((uintptr_t)x % 16 == 0) && ((uintptr_t)q % 4 == 0);
-    const int k4 = k / 4;
-    if (vec && k4 <= 64 * 8) {
-        act_quant_reg_kernel<64, 8><<<dim3((unsigned)((t + 3) / 4)), dim3(256), 0, stream>>>(x, t, k, q, sx, status);
-    } else if (vec && k4 <= 256 * 4) {
-        act_quant_reg_kernel<256, 4><<<dim3((unsigned)t), dim3(256), 0, stream>>>(x, t, k, q, sx, status);
-    } else if (vec && k4 <= 256 * 16) {
-        act_quant_reg_kernel<256, 16><<<dim3((unsigned)t), dim3(256), 0, stream>>>(x, t, k, q, sx, status);
-    } else {
-        dim3 grid((unsigned)((t + kActWaves - 1) / kActWaves)), block(256);
-        if (vec)
-            act_quant_kernel<true><<<grid, block, 0, stream>>>(x, t, k, q, sx, status);
-        else
-            act_quant_kernel<false><<<grid, block, 0, stream>>>(x, t, k, q, sx, status);
-    }
-    return hipGetLastError();
+    return launch_act_quant_group(&x, &q, &sx, 1, t, k, status, stream);
 }
 
 }  // namespace lowbit

@@ -63,26 +63,30 @@ hipError_t launch_gemv_group(const LinearArgs* mats, int count, hipStream_t stre
         gp.upg_shift = log2_exact(gp.upg);
     }
     gp.stride = n_steps * SK + 16;
-    cfg.lds_a = (int64_t)a.t * gp.stride <= kGemvLdsA;
-    gp.lds_a_bytes = cfg.lds_a ? a.t * gp.stride : 0;
-    cfg.nr = (cfg.lds_a && a.t == 1) ? 1 : 4;
+    const int64_t stage = (int64_t)a.t * gp.stride;          // LDS bytes of the staged activations
+    const bool small_stage = stage <= kGemvLdsA;
+    cfg.nr = (small_stage && a.t == 1) ? 1 : 4;
 
     // The quantiser runs in the product kernel's prologue for one token (every
     // workgroup redoes the row; for a single token that is cheaper than a
     // launch), with the LDS stage and whole 16-byte x words (k % 4 == 0, every
     // x 16-byte aligned).  Otherwise the quantiser kernel produces the codes
-    // first, into the given q / sx, one launch per matrix.
+    // first, into the given q / sx (one launch for all the matrices).
     const bool fused_in = a.x != nullptr;
     bool x_vec = a.k % 4 == 0;
     for (int i = 0; fused_in && i < count; ++i) x_vec = x_vec && (uintptr_t)mats[i].x % 16 == 0;
-    cfg.fuse = fused_in && cfg.lds_a && x_vec && a.t == 1;
-    if (fused_in && !cfg.fuse) {
+    cfg.fuse = fused_in && small_stage && x_vec && a.t == 1;
+    if (fused_in && !cfg.fuse) {                             // every matrix's input in one launch
+        const float* xs[kGemvMaxMats];
+        int8_t* qs[kGemvMaxMats];
+        float* sxs[kGemvMaxMats];
         for (int i = 0; i < count; ++i) {
-            const LinearArgs& b = mats[i];
-            hipError_t e = launch_act_quant(b.x, b.t, b.k, const_cast<int8_t*>(b.q), const_cast<float*>(b.sx),
-                                            b.status, stream);
-            if (e != hipSuccess) return e;
+            xs[i] = mats[i].x;
+            qs[i] = const_cast<int8_t*>(mats[i].q);
+            sxs[i] = const_cast<float*>(mats[i].sx);
         }
+        hipError_t e = launch_act_quant_group(xs, qs, sxs, count, a.t, a.k, a.status, stream);
+        if (e != hipSuccess) return e;
     }
     gp.status = cfg.fuse ? a.status : nullptr;
     bool q_word = a.k % 4 == 0;
@@ -126,7 +130,22 @@ hipError_t launch_gemv_group(const LinearArgs* mats, int count, hipStream_t stre
     gp.ksplit = ksplit;
     gp.ksplit_log = ksplit == 4 ? 2 : (ksplit == 2 ? 1 : 0);
     gp.part_len = part_len;
-    gp.tiles_per_wg = 4 / ksplit;
+
+    // Where the activations live.  Several tokens make the LDS stage large
+    // (t * k bytes): above kGemvLdsWide four-wavefront workgroups would leave
+    // the CU short of wavefronts streaming weights, so 16-wavefront workgroups
+    // share one stage, which may then take the whole LDS.  Otherwise the
+    // activations ride in the register ring from L2.
+    const int64_t red16 = ksplit > 1 ? (int64_t)16 * cfg.nr * 64 * 4 : 0;
+    cfg.waves = 4;
+    if (!cfg.fuse && a.t > 1 && stage > kGemvLdsWide && stage + red16 <= kGemvLdsMax) {
+        cfg.lds_a = true;
+        cfg.waves = 16;
+    } else {
+        cfg.lds_a = small_stage;
+    }
+    gp.lds_a_bytes = cfg.lds_a ? (int)stage : 0;
+    gp.tiles_per_wg = cfg.waves / ksplit;
 
     int wgs = 0;
     for (int i = 0; i < count; ++i) {
@@ -135,7 +154,7 @@ hipError_t launch_gemv_group(const LinearArgs* mats, int count, hipStream_t stre
     }
     for (int i = count; i <= kGemvMaxMats; ++i) gp.wg_start[i] = 0x7fffffff;   // never reached
     cfg.grid = wgs;
-    cfg.lds_bytes = (size_t)gp.lds_a_bytes + (ksplit > 1 ? (size_t)4 * cfg.nr * 64 * 4 : 0);
+    cfg.lds_bytes = (size_t)gp.lds_a_bytes + (ksplit > 1 ? (size_t)cfg.waves * cfg.nr * 64 * 4 : 0);
 
     switch (a.fmt) {
         case FMT_TERNARY: return gemv_launch_ternary(gp, cfg, stream);

@@ -8,7 +8,9 @@
 namespace lowbit {
 
 constexpr int kGemvMaxMats = 40;     // matrices per launch (kernel-argument space)
-constexpr int kGemvLdsA = 56 * 1024; // activation bytes a workgroup may stage in LDS
+constexpr int kGemvLdsA = 56 * 1024; // activation bytes a 4-wavefront workgroup may stage in LDS
+constexpr int kGemvLdsWide = 20 * 1024;   // above this stage, 16-wavefront workgroups share it (t > 1)
+constexpr int kGemvLdsMax = 160 * 1024;   // LDS of a CU
 
 struct GemvMat {
     const uint8_t* packed;
@@ -34,7 +36,7 @@ struct GemvParams {
     int ksplit;          // wavefronts sharing one tile's k-range (1, 2, 4)
     int ksplit_log;
     int part_len;        // k-steps per part (the last part may run short)
-    int tiles_per_wg;    // 4 / ksplit
+    int tiles_per_wg;    // waves per workgroup / ksplit
     int stride;          // LDS bytes per staged token row (k padded + 16)
     int q_vec;           // k % 16 == 0 and every q 16-byte aligned
     int lds_a_bytes;     // T * stride when activations are staged in LDS, else 0
@@ -51,7 +53,8 @@ struct GemvCfg {
     int sps;             // group mode: scale units per k-step (1, 2, 4); 0 = tensor/row scales
     bool lds_a;          // activations staged in LDS (else read from global memory)
     bool acc;            // some matrix wants the integer products
-    bool fuse;           // activations quantised in the kernel's prologue (needs lds_a)
+    bool fuse;           // activations quantised in the kernel's prologue (needs lds_a, 4 waves)
+    int waves;           // wavefronts per workgroup: 4, or 16 with a large LDS stage
     int grid;
     size_t lds_bytes;
 };

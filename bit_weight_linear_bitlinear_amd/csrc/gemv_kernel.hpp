@@ -28,7 +28,8 @@
 // already permuted to the packbits code order.  When t * k is too large for
 // LDS they ride in the register ring instead, read from L2.
 //
-// A workgroup is 4 wavefronts on 4 / ksplit consecutive tiles of ONE matrix;
+// A workgroup is WV wavefronts (4, or 16 sharing a large LDS stage) on
+// WV / ksplit consecutive tiles of ONE matrix;
 // `ksplit` wavefronts share a tile's k-range and add their partials in LDS in
 // a fixed order.  Group scales are applied per scale unit (a whole number of
 // MFMA blocks inside one group): at a group's last unit the int32 partial is
@@ -88,12 +89,13 @@ __device__ __forceinline__ uint32_t quant_word(const float4 v, float r, int vali
 // LDSA: activations staged in LDS.  ACC: also write the integer products
 // (kept out of the streaming instantiations: optional stores inside the
 // k-loop make the compiler's wait counting conservative).
+// WV: wavefronts per workgroup (4; 16 only for LDSA without FUSE).
 // FUSE (with LDSA, one token): the stage is filled from fp32 x by the
 // per-token absmax quantiser itself (M8.8 0x02C, 0x05C: m = max|x|,
 // r = 127 / m, codes clip(rint(x r)), s_x = m / 127), every workgroup for its
 // own stage; the matrix's first workgroup also writes the codes and scale out.
-template <int FMT, int WPL, int NR, int SPS, bool UPG1, bool LDSA, bool ACC, bool FUSE>
-__global__ __launch_bounds__(256) void gemv_kernel(const GemvParams p) {
+template <int FMT, int WPL, int NR, int SPS, bool UPG1, bool LDSA, bool ACC, bool FUSE, int WV>
+__global__ __launch_bounds__(64 * WV) void gemv_kernel(const GemvParams p) {
     using S = GemvShape<FMT, WPL>;
     constexpr int D = kGemvD;
     constexpr int NB = S::kNB, KB = S::kKB, SK = S::kSK, MPB = S::kMPB;
@@ -105,6 +107,8 @@ __global__ __launch_bounds__(256) void gemv_kernel(const GemvParams p) {
     constexpr int SHIFT = Fmt<FMT>::kShift;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     static_assert(!FUSE || LDSA, "the fused quantiser fills the LDS stage");
+    static_assert(WV == 4 || (WV == 16 && LDSA && !FUSE), "16-wavefront workgroups share an LDS stage");
+    constexpr int NT = 64 * WV;                              // threads per workgroup
     __shared__ float fz_m[4];                                // fused: per-wave max |x|
     __shared__ int fz_bad[4];                                // fused: per-wave non-finite flag
 
@@ -312,7 +316,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const GemvParams p) {
             uint8_t* dst = smem + (size_t)t * p.stride;
             if constexpr (FMT == FMT_BINARY) {
                 // 32-code chunks permuted to the order decode_binary yields
-                for (int c = threadIdx.x; c < kpad / 32; c += 256) {
+                for (int c = threadIdx.x; c < kpad / 32; c += NT) {
                     const i32x4 lo = load_q16(q + (size_t)t * K, 32 * c, K, p.q_vec);
                     const i32x4 hi = load_q16(q + (size_t)t * K, 32 * c + 16, K, p.q_vec);
                     const uint32_t X[8] = {(uint32_t)lo[0], (uint32_t)lo[1], (uint32_t)lo[2], (uint32_t)lo[3],
@@ -323,7 +327,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const GemvParams p) {
                     *reinterpret_cast<i32x4*>(dst + 32 * c + 16) = a1;
                 }
             } else {
-                for (int c = threadIdx.x; c < kpad / 16; c += 256)
+                for (int c = threadIdx.x; c < kpad / 16; c += NT)
                     *reinterpret_cast<i32x4*>(dst + 16 * c) = load_q16(q + (size_t)t * K, 16 * c, K, p.q_vec);
             }
         }
@@ -438,7 +442,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const GemvParams p) {
     #pragma unroll
     for (int r = 0; r < NR; ++r) ai[r] = C[r] >> SHIFT;
     if (p.ksplit > 1) {
-        int32_t* red = reinterpret_cast<int32_t*>(smem + p.lds_a_bytes);   // [4 waves][NR][64], after A
+        int32_t* red = reinterpret_cast<int32_t*>(smem + p.lds_a_bytes);   // [WV waves][NR][64], after A
         #pragma unroll
         for (int r = 0; r < NR; ++r)
             red[(wave * NR + r) * 64 + lane] = GROUP ? __float_as_int(yp[r]) : ai[r];
@@ -474,20 +478,27 @@ __global__ __launch_bounds__(256) void gemv_kernel(const GemvParams p) {
 
 template <int FMT, int WPL, int NR, int SPS, bool UPG1>
 void gemv_launch_lds(const GemvParams& p, const GemvCfg& c, hipStream_t st) {
-    const dim3 grid((unsigned)c.grid), block(256);
+    const dim3 grid((unsigned)c.grid), block(64 * c.waves);
     if (c.lds_a) {
         if constexpr (NR == 1) {   // fused launches have one token
             if (c.fuse) {
-                gemv_kernel<FMT, WPL, 1, SPS, UPG1, true, false, true><<<grid, block, c.lds_bytes, st>>>(p);
+                gemv_kernel<FMT, WPL, 1, SPS, UPG1, true, false, true, 4><<<grid, block, c.lds_bytes, st>>>(p);
                 return;
             }
         }
-        if (c.acc) gemv_kernel<FMT, WPL, NR, SPS, UPG1, true, true, false><<<grid, block, c.lds_bytes, st>>>(p);
-        else gemv_kernel<FMT, WPL, NR, SPS, UPG1, true, false, false><<<grid, block, c.lds_bytes, st>>>(p);
+        if constexpr (NR == 4) {   // a large stage shared by 16 wavefronts (several tokens)
+            if (c.waves == 16) {
+                if (c.acc) gemv_kernel<FMT, WPL, 4, SPS, UPG1, true, true, false, 16><<<grid, block, c.lds_bytes, st>>>(p);
+                else gemv_kernel<FMT, WPL, 4, SPS, UPG1, true, false, false, 16><<<grid, block, c.lds_bytes, st>>>(p);
+                return;
+            }
+        }
+        if (c.acc) gemv_kernel<FMT, WPL, NR, SPS, UPG1, true, true, false, 4><<<grid, block, c.lds_bytes, st>>>(p);
+        else gemv_kernel<FMT, WPL, NR, SPS, UPG1, true, false, false, 4><<<grid, block, c.lds_bytes, st>>>(p);
     } else {
-        // activations from L2: the large-t*k fallback, always 4 token registers
-        if (c.acc) gemv_kernel<FMT, WPL, 4, SPS, UPG1, false, true, false><<<grid, block, c.lds_bytes, st>>>(p);
-        else gemv_kernel<FMT, WPL, 4, SPS, UPG1, false, false, false><<<grid, block, c.lds_bytes, st>>>(p);
+        // activations from L2: the fallback for stages too large for LDS, always 4 token registers
+        if (c.acc) gemv_kernel<FMT, WPL, 4, SPS, UPG1, false, true, false, 4><<<grid, block, c.lds_bytes, st>>>(p);
+        else gemv_kernel<FMT, WPL, 4, SPS, UPG1, false, false, false, 4><<<grid, block, c.lds_bytes, st>>>(p);
     }
 }
 

@@ -33,6 +33,10 @@ struct LinearArgs {
 
 hipError_t launch_act_quant(const float* x, int t, int k, int8_t* q, float* sx, int32_t* status,
                             hipStream_t stream);
+// the inputs of `count` matrices of equal [t, k] in as few launches as possible
+constexpr int kActQuantMaxSrc = 40;
+hipError_t launch_act_quant_group(const float* const* x, int8_t* const* q, float* const* sx, int count, int t,
+                                  int k, int32_t* status, hipStream_t stream);
 hipError_t launch_gemv(const LinearArgs& a, hipStream_t stream);
 // several matrices of equal fmt / scale mode / group / k and t <= 16 in one launch
 hipError_t launch_gemv_group(const LinearArgs* mats, int count, hipStream_t stream);

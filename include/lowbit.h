@@ -233,9 +233,8 @@ lowbit_status lowbit_linear_fused(const lowbit_desc* d, const uint8_t* packed, c
  * lowbit_linear_grouped_fused - lowbit_linear_grouped with the quantiser fused
  * as in lowbit_linear_fused: matrix i quantises x[i] (device float [t, k])
  * into q[i], sx[i] and computes y[i].  One status word for all matrices.
- * Where the quantiser does not run in the product's prologue it is launched
- * once per matrix; callers with many matrices and several tokens do better
- * with one lowbit_act_quant over stacked inputs and lowbit_linear_grouped.
+ * Where the quantiser does not run in the product's prologue, one quantiser
+ * launch covers the inputs of up to 40 matrices before the products.
  * Errors: as lowbit_linear_grouped.
  */
 lowbit_status lowbit_linear_grouped_fused(int32_t count, const lowbit_desc* descs, const uint8_t* const* packed,
