@@ -134,7 +134,8 @@ class Pass:
     def _grouped(self, idx):
         return self.lb.GroupedCall([self.desc[i] for i in idx], [self.packed[i] for i in idx],
                                    [self.scales[i] for i in idx], [self.views[i][0] for i in idx],
-                                   [self.views[i][1] for i in idx], [self.y[i] for i in idx])
+                                   [self.views[i][1] for i in idx], [self.y[i] for i in idx],
+                                   batched=self.entry == "gemm")
 
     def _grouped_fused(self, idx):
         return self.lb.GroupedFusedCall([self.desc[i] for i in idx], [self.packed[i] for i in idx],
@@ -160,9 +161,12 @@ class Pass:
         down: layer quantises every input up front (one launch per k),
         layer_dep quantises each call's inputs right before it (what a model
         whose next input is the previous output must do), layer_fused does that
-        inside the product kernel."""
-        self.fused_calls = [self._grouped_fused(idx) for idx in self.kgroups.values()]
+        inside the product kernel.  A prefill pass has the grouped schedule
+        only (lowbit_linear_batched_grouped, 24 products per launch)."""
         self.grouped_calls = [self._grouped(idx) for idx in self.kgroups.values()]
+        if self.entry == "gemm":
+            return
+        self.fused_calls = [self._grouped_fused(idx) for idx in self.kgroups.values()]
         names = [m.name for _, _, m in self.mats]
         self.layer_calls, self.layer_fused_calls, self.layer_dep_calls = [], [], []
         by_layer = {}
@@ -181,6 +185,8 @@ class Pass:
                 self.layer_dep_calls += [self._quant_rows(s_), self.layer_calls[-1]]
 
     def launches(self, calls):
+        if self.entry == "gemm":
+            return sum((c.count + 23) // 24 for c in calls)
         return sum((c.count + 39) // 40 * ((c.t + 15) // 16) for c in calls)
 
     def step(self, schedule="per_matrix"):
@@ -290,6 +296,40 @@ def committed_traffic():
     return float(vals["traffic_bytes_per_launch"])
 
 
+def gemm_pass(p: Pass, steps: int, no_graph: bool = False):
+    """A prefill pass both ways: every product as its own launch, and equal-k
+    products as grouped launches; seconds per step of each.  Then the
+    average grouped launch (inputs quantised beforehand), timed like
+    per_launch_grouped: (seconds, bytes, ops) per launch."""
+    import torch
+    p.build_schedules()
+    res = {}
+    for sched in ("per_matrix", "grouped"):
+        fn = (lambda sc=sched: p.step(sc))
+        run = None if no_graph else capture(fn)
+        el, _ = time_steps(run or fn, steps, 1)
+        res[sched] = el / steps
+    p.act_quant()
+    torch.cuda.synchronize()
+
+    def prods():
+        for c in p.grouped_calls:
+            c()
+    run = capture(prods) or prods
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 3
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    n = p.launches(p.grouped_calls)
+    dur = e0.elapsed_time(e1) / 1e3 / (reps * n)
+    return res, (dur, sum(p.linear_bytes) / n, sum(p.linear_ops) / n)
+
+
 def per_launch(p: Pass, reps: int):
     """Average duration of the product kernel: every product of the pass
     (inputs quantised beforehand) captured in a HIP graph and replayed `reps`
@@ -317,16 +357,20 @@ def per_launch(p: Pass, reps: int):
 
 
 def gemm_profile(args):
-    """The int4 prefill pass alone, then each distinct GEMM shape timed on its
-    own (HIP events on the launching stream)."""
+    """The int4 prefill pass alone as the bench runs it (one act-quant launch
+    per k, equal-k products as grouped launches), then each distinct GEMM
+    shape timed on its own (HIP events on the launching stream)."""
     import torch
     import workloads
     wl4 = workloads.BY_NAME["int4_t4nt"]
     p4 = Pass(wl4, wl4.tokens[0], "gemm", layers=args.layers)
-    run = (None if args.no_graph else capture(p4.step)) or p4.step
+    p4.build_schedules()
+    fn = lambda: p4.step("grouped")
+    run = (None if args.no_graph else capture(fn)) or fn
     el, _ = time_steps(run, args.steps, args.warmup)
     st = el / args.steps
-    log(f"[bench] gemm pass: {sum(p4.linear_ops) / st / 1e12:.1f} TOPS/step, {st * 1e3:.3f} ms/step")
+    log(f"[bench] gemm pass: {sum(p4.linear_ops) / st / 1e12:.1f} TOPS/step, {st * 1e3:.3f} ms/step, "
+        f"{p4.launches(p4.grouped_calls)} grouped launches")
     p4.act_quant()
     torch.cuda.synchronize()
     seen = {}
@@ -700,18 +744,18 @@ def extra_views(args):
     # the binary 8192-token GEMM pass
     wl2 = workloads.BY_NAME["binary_gqa"]
     p2 = Pass(wl2, wl2.tokens[0], "gemm")
-    run = capture(p2.step) or p2.step
-    el, _ = time_steps(run, 5, 1)
-    st = el / 5
-    dur, bpl, opl = per_launch(p2, reps=3)
+    sched, (dur, bpl, opl) = gemm_pass(p2, 5)
+    st = sched["grouped"]
     ops = sum(p2.linear_ops)
     views["binary_gqa_gemm"] = {
-        "what": "the binary d=192 8-layer model's 56 products at 8192 tokens, act-quant included; "
-                "bound by the fp32 output (HBM), not by the matrix cores",
+        "what": "the binary d=192 8-layer model's 56 products at 8192 tokens, act-quant included, equal-k "
+                "products as grouped launches; bound by the fp32 output (HBM), not by the matrix cores",
         "ms_per_step": round(st * 1e3, 4), "TOPS_step": round(ops / st / 1e12, 2),
         "GBps_step": round(p2.step_bytes / st / 1e9, 1),
         "pct_hbm_peak_step": round(100 * p2.step_bytes / st / 1e9 / HBM_PEAK_GBS, 2),
-        "GBps_per_launch": round(bpl / dur / 1e9, 1), "TOPS_per_launch": round(opl / dur / 1e12, 2)}
+        "ms_per_step_one_launch_per_product": round(sched["per_matrix"] * 1e3, 4),
+        "grouped_launches": p2.launches(p2.grouped_calls),
+        "GBps_per_grouped_launch": round(bpl / dur / 1e9, 1), "TOPS_per_grouped_launch": round(opl / dur / 1e12, 2)}
     log(f"[bench] binary gqa gemm: {ops / st / 1e12:.1f} TOPS/step, {p2.step_bytes / st / 1e9:.1f} GB/s/step")
     del p2
     return views
@@ -818,11 +862,11 @@ def main():
     if not args.skip_gemm:
         wl4 = workloads.BY_NAME["int4_t4nt"]
         p4 = Pass(wl4, wl4.tokens[0], "gemm")
-        r4 = (None if args.no_graph else capture(p4.step)) or p4.step
-        el4, _ = time_steps(r4, max(3, args.steps // 4), 1)
-        st4 = el4 / max(3, args.steps // 4)
+        sched4, (dg, _, opg) = gemm_pass(p4, max(3, args.steps // 4), args.no_graph)
+        st4 = min(sched4.values())
         ops4 = sum(p4.linear_ops)
-        d4, _, ops_per_launch = per_launch(p4, reps=3)
+        d1, _, ops_single = per_launch(p4, reps=3)             # each product as its own launch
+        d4, ops_per_launch = dg, opg                           # the launches the pass runs (grouped)
         tops_launch = ops_per_launch / d4 / 1e12
         chk4 = None if args.skip_check else sampled_check(p4, [0, 1, 4], rows_per=32)
         # the second roofline of a prefill product: its HBM bytes (fp32 y
@@ -830,12 +874,17 @@ def main():
         bytes4 = sum(p4.linear_bytes)
         floor_mfma = ops4 / (I8_PEAK_TOPS * 1e12)
         floor_hbm = bytes4 / (HBM_PEAK_GBS * 1e9)
-        n4 = len(p4.linear_ops)
-        out["gemm"] = {"workload": "int4_t4nt prefill pass: 100 int4 row-scale GEMMs, T=4096, act-quant included",
+        n4 = p4.launches(p4.grouped_calls)
+        out["gemm"] = {"workload": "int4_t4nt prefill pass: 100 int4 row-scale GEMMs, T=4096, act-quant included; "
+                                   "equal-k products as grouped launches (24 per launch)",
                        "tops_step": round(ops4 / st4 / 1e12, 2), "ms_per_step": round(st4 * 1e3, 4),
+                       "schedules_ms_per_step": {k: round(v * 1e3, 4) for k, v in sched4.items()},
+                       "single_product_launch": {"avg_us": round(d1 * 1e6, 2),
+                                                 "TOPS": round(ops_single / d1 / 1e12, 2)},
                        "tops_per_launch": round(tops_launch, 2),
                        "pct_mfma_peak": round(100 * tops_launch / I8_PEAK_TOPS, 2),
-                       "avg_launch_us": round(d4 * 1e6, 2), "kernel": "gemm_mfma_kernel",
+                       "avg_launch_us": round(d4 * 1e6, 2), "launches": n4,
+                       "kernel": "gemm_mfma_kernel (grouped launches)",
                        "roofline": {"bound": "mfma", "achieved": round(tops_launch, 2), "peak": I8_PEAK_TOPS,
                                     "unit": "TOPS", "frac": round(tops_launch / I8_PEAK_TOPS, 4),
                                     "mfma_floor_us_per_launch": round(floor_mfma / n4 * 1e6, 2),

@@ -67,6 +67,8 @@ _lib.lowbit_linear_batched.argtypes = [_D, _P, _P, _P, _P, _i32, _P, _P, _P]
 _PP = ctypes.POINTER(ctypes.c_void_p)
 _lib.lowbit_linear_grouped.argtypes = [_i32, _D, _PP, _PP, _PP, _PP, _i32, _PP, _PP, _P]
 _lib.lowbit_linear_grouped.restype = _i32
+_lib.lowbit_linear_batched_grouped.argtypes = [_i32, _D, _PP, _PP, _PP, _PP, _i32, _PP, _PP, _P]
+_lib.lowbit_linear_batched_grouped.restype = _i32
 _lib.lowbit_linear_fused.argtypes = [_D, _P, _P, _P, _i32, _P, _P, _P, _P, _P]
 _lib.lowbit_linear_fused.restype = _i32
 _lib.lowbit_linear_grouped_fused.argtypes = [_i32, _D, _PP, _PP, _PP, _PP, _PP, _i32, _PP, _P, _P]
@@ -105,7 +107,8 @@ for _f in ("lowbit_describe", "lowbit_pack", "lowbit_act_quant", "lowbit_linear"
     getattr(_lib, _f).restype = _i32
 
 EXPORTS = ("lowbit_describe", "lowbit_pack", "lowbit_act_quant", "lowbit_linear", "lowbit_linear_batched",
-           "lowbit_linear_grouped", "lowbit_linear_fused", "lowbit_linear_grouped_fused",
+           "lowbit_linear_grouped", "lowbit_linear_batched_grouped", "lowbit_linear_fused",
+           "lowbit_linear_grouped_fused",
            "lowbit_model_work_bytes", "lowbit_model_trace_floats", "lowbit_decode_step",
            "lowbit_rmsnorm", "lowbit_rope_attention", "lowbit_swiglu",
            "lowbit_max_k", "lowbit_status_string", "lowbit_abi_version", "lowbit_last_hip_error")
@@ -199,9 +202,11 @@ def lowbit_linear_batched(d: lowbit_desc, packed, scales, q, sx, y, acc=None, st
 class GroupedCall:
     """Marshalled arguments of one lowbit_linear_grouped call (the pointer
     arrays are built once, so replaying the call costs no Python work beyond
-    the foreign call itself)."""
+    the foreign call itself); batched=True marshals
+    lowbit_linear_batched_grouped (the prefill GEMMs) instead."""
 
-    def __init__(self, descs, packed, scales, q, sx, y, acc=None):
+    def __init__(self, descs, packed, scales, q, sx, y, acc=None, batched=False):
+        self.batched = batched
         n = len(descs)
         if not (n == len(packed) == len(scales) == len(q) == len(sx) == len(y)) or n < 1:
             raise ValueError("lowbit_linear_grouped: argument lists differ in length")
@@ -223,8 +228,14 @@ class GroupedCall:
         self._keep = (packed, scales, q, sx, y, acc)    # the tensors must outlive the call
 
     def __call__(self, stream=None):
-        _check(_lib.lowbit_linear_grouped(self.count, self.descs, self.packed, self.scales, self.q, self.sx,
-                                          self.t, self.y, self.acc, _stream(stream)), "lowbit_linear_grouped")
+        fn = "lowbit_linear_batched_grouped" if self.batched else "lowbit_linear_grouped"
+        _check(getattr(_lib, fn)(self.count, self.descs, self.packed, self.scales, self.q, self.sx,
+                                 self.t, self.y, self.acc, _stream(stream)), fn)
+
+
+def lowbit_linear_batched_grouped(descs, packed, scales, q, sx, y, acc=None, stream=None) -> None:
+    """Device: several independent prefill GEMMs of equal k and t, 24 per launch."""
+    GroupedCall(descs, packed, scales, q, sx, y, acc, batched=True)(stream)
 
 
 def lowbit_linear_grouped(descs, packed, scales, q, sx, y, acc=None, stream=None) -> None:

@@ -104,11 +104,13 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const ActQuantTable tab,
 }
 
 // Register-resident variant for rows of up to TPR * 4 * R floats (16-byte
-// aligned, k % 4 == 0): TPR threads (a wavefront, or a whole 256-thread
-// workgroup) share one row, every element is read from HBM exactly once into
-// registers, the row max is reduced with lane shuffles (and LDS across the
-// workgroup's wavefronts), and the codes are written from the same registers.
-// All loads of a thread are issued before any is consumed.
+// aligned, k % 4 == 0): TPR threads (8, 16 or 32 lanes of a wavefront, a
+// wavefront, or a whole 256-thread workgroup) share one row, every element is
+// read from HBM exactly once into registers, the row max is reduced with lane
+// shuffles (and LDS across the workgroup's wavefronts), and the codes are
+// written from the same registers.  All loads of a thread are issued before
+// any is consumed.  Short rows share a wavefront so that a launch is not
+// thousands of nearly idle workgroups.
 template <int TPR, int R>
 __global__ __launch_bounds__(256) void act_quant_reg_kernel(const ActQuantTable tab, int k,
                                                             int32_t* __restrict__ status) {
@@ -122,9 +124,13 @@ __global__ __launch_bounds__(256) void act_quant_reg_kernel(const ActQuantTable 
     const int row = blockIdx.x * RPW + (int)threadIdx.x / TPR;
     const int sub = threadIdx.x % TPR;
     const int lane = threadIdx.x & 63;
-    if (TPR == 64 && row >= t) return;                       // whole wavefronts exit together
+    if constexpr (TPR <= 64) {                               // whole wavefronts exit together
+        if (blockIdx.x * RPW + (int)(threadIdx.x >> 6) * (64 / TPR) >= t) return;
+    }
+    const bool row_ok = row < t;                             // (a wavefront's rows may run past t)
+    const int rowc = row_ok ? row : t - 1;
     const int k4 = k >> 2;
-    const float4* x4 = reinterpret_cast<const float4*>(x + (size_t)row * k);
+    const float4* x4 = reinterpret_cast<const float4*>(x + (size_t)rowc * k);
     float4 v[R];
     #pragma unroll
     for (int i = 0; i < R; ++i) {
@@ -139,8 +145,17 @@ __global__ __launch_bounds__(256) void act_quant_reg_kernel(const ActQuantTable 
         const float a0 = fabsf(v[i].x), a1 = fabsf(v[i].y), a2 = fabsf(v[i].z), a3 = fabsf(v[i].w);
         m = a0 > m ? a0 : m; m = a1 > m ? a1 : m; m = a2 > m ? a2 : m; m = a3 > m ? a3 : m;
     }
-    m = wave_max(m);
-    bad = wave_or(bad);
+    if constexpr (TPR < 64) {                                // the row's lanes only
+        #pragma unroll
+        for (int off = TPR / 2; off > 0; off >>= 1) {
+            const float o = __shfl_xor(m, off, 64);
+            m = o > m ? o : m;
+            bad |= __shfl_xor(bad, off, 64);
+        }
+    } else {
+        m = wave_max(m);
+        bad = wave_or(bad);
+    }
     if constexpr (TPR == 256) {
         const int w = threadIdx.x >> 6;
         if (lane == 0) { red_m[w] = m; red_bad[w] = bad; }
@@ -156,11 +171,11 @@ __global__ __launch_bounds__(256) void act_quant_reg_kernel(const ActQuantTable 
         r = 127.0f / m;
         if (!isfinite(r)) flag = LOWBIT_ACT_OVERFLOW;
     }
-    uint32_t* q4 = reinterpret_cast<uint32_t*>(q + (size_t)row * k);
+    uint32_t* q4 = reinterpret_cast<uint32_t*>(q + (size_t)rowc * k);
     #pragma unroll
     for (int i = 0; i < R; ++i) {
         const int idx = sub + i * TPR;
-        if (idx < k4) {
+        if (idx < k4 && row_ok) {
             uint32_t p = 0u;   // a rejected row gets zero codes
             if (!flag)
                 p = (uint32_t)(uint8_t)quant1(v[i].x, r) | ((uint32_t)(uint8_t)quant1(v[i].y, r) << 8) |
@@ -168,7 +183,7 @@ __global__ __launch_bounds__(256) void act_quant_reg_kernel(const ActQuantTable 
             q4[idx] = p;
         }
     }
-    if (sub == 0) {
+    if (sub == 0 && row_ok) {
         sx[row] = flag ? __builtin_nanf("") : m / 127.0f;
         if (flag && status) atomicOr(status, flag);
     }
@@ -188,7 +203,13 @@ hipError_t launch_act_quant_group(const float* const* x, int8_t* const* q, float
             vec = vec && (uintptr_t)x[b + i] % 16 == 0 && (uintptr_t)q[b + i] % 4 == 0;
         }
         const int k4 = k / 4;
-        if (vec && k4 <= 64 * 8) {
+        if (vec && k4 <= 8 * 8) {
+            act_quant_reg_kernel<8, 8><<<dim3((unsigned)((t + 31) / 32), n), dim3(256), 0, stream>>>(tab, k, status);
+        } else if (vec && k4 <= 16 * 8) {
+            act_quant_reg_kernel<16, 8><<<dim3((unsigned)((t + 15) / 16), n), dim3(256), 0, stream>>>(tab, k, status);
+        } else if (vec && k4 <= 32 * 8) {
+            act_quant_reg_kernel<32, 8><<<dim3((unsigned)((t + 7) / 8), n), dim3(256), 0, stream>>>(tab, k, status);
+        } else if (vec && k4 <= 64 * 8) {
             act_quant_reg_kernel<64, 8><<<dim3((unsigned)((t + 3) / 4), n), dim3(256), 0, stream>>>(tab, k, status);
         } else if (vec && k4 <= 256 * 4) {
             act_quant_reg_kernel<256, 4><<<dim3((unsigned)t, n), dim3(256), 0, stream>>>(tab, k, status);

@@ -308,4 +308,15 @@ hipError_t launch_gemm(const LinearArgs& a, hipStream_t stream) {
     return gemm_mfma_supported(a) ? launch_gemm_mfma(a, stream) : launch_gemm_generic(a, stream);
 }
 
+hipError_t launch_gemm_group(const LinearArgs* mats, int count, hipStream_t stream) {
+    bool all = true;
+    for (int i = 0; i < count; ++i) all = all && gemm_mfma_supported(mats[i]);
+    if (all) return launch_gemm_mfma_group(mats, count, stream);
+    for (int i = 0; i < count; ++i) {                        // the general path: one launch each
+        hipError_t e = launch_gemm(mats[i], stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 }  // namespace lowbit

@@ -34,6 +34,7 @@
 // Workgroups are numbered so that each XCD (workgroup i runs on XCD i % 8)
 // owns a contiguous run of output tiles, token-block-major: the weight matrix
 // and a few activation blocks stay in that XCD's L2.
+#include <algorithm>
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -43,20 +44,32 @@ namespace lowbit {
 
 typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
 
-struct GemmFastArgs {
+// One launch: up to kGemmMaxMats products of equal k, token count, format and
+// scale mode; workgroups run over the matrices' output tiles in order.
+constexpr int kGemmMaxMats = 24;
+
+struct GemmMat {
     const uint8_t* packed;
     const float* scales;
     const int8_t* q;
     const float* sx;
     float* y;
     int32_t* acc;
-    int T, N, K;
-    int n_steps;        // packed-layout k-steps
+    int N;
     int n_tiles;        // ceil(N / 16)
+    int nb;             // row blocks of the launch's tile
+};
+
+struct GemmFastArgs {
+    int T, K;
+    int n_steps;        // packed-layout k-steps
     int group;          // group mode: columns per group
     int G;              // group mode: groups per row
     int scale_per_row;
-    int mb, nb;         // token blocks, row blocks
+    int mb;             // token blocks
+    int n_mats;
+    int wg_start[kGemmMaxMats + 1];   // first workgroup of each matrix; [n_mats] = all; INT_MAX past it
+    GemmMat m[kGemmMaxMats];
 };
 
 // Workgroup tile configurations (blocks of 32 x 32 per wavefront).
@@ -135,11 +148,25 @@ __global__ __launch_bounds__(TILE == 1 ? 512 : 256) void gemm_mfma_kernel(const 
     const int lane = tid & 63, h = lane >> 5, j = lane & 31;
     const int wm = wave / S::WAVES_N, wn = wave % S::WAVES_N;
 
-    // XCD-aware tile order: XCD x runs a contiguous run of tiles
-    const int total = a.mb * a.nb;
+    // XCD-aware tile order: XCD x runs a contiguous run of the launch's tiles
+    // (matrix after matrix); then this tile's matrix, one batch of scalar
+    // compares
+    const int total = a.wg_start[a.n_mats];
     const int xcd = (int)blockIdx.x % 8, jx = (int)blockIdx.x / 8;
-    const int logical = xcd * (total / 8) + min(xcd, total % 8) + jx;
-    const int tb_m = logical / a.nb, tb_n = logical % a.nb;
+    const int glogical = xcd * (total / 8) + min(xcd, total % 8) + jx;
+    int mi = 0;
+    #pragma unroll
+    for (int i = 1; i < kGemmMaxMats; ++i) mi += glogical >= a.wg_start[i] ? 1 : 0;
+    const GemmMat& mat = a.m[mi];
+    const uint8_t* const m_packed = mat.packed;
+    const float* const m_scales = mat.scales;
+    const int8_t* const m_q = mat.q;
+    const float* const m_sx = mat.sx;
+    float* const m_y = mat.y;
+    int32_t* const m_acc = mat.acc;
+    const int m_N = mat.N, m_ntiles = mat.n_tiles, m_nb = mat.nb;
+    const int logical = glogical - a.wg_start[mi];
+    const int tb_m = logical / m_nb, tb_n = logical % m_nb;
     const int m0 = tb_m * BM, n0 = tb_n * BN;
     const int K = a.K, T = a.T;
     auto swz = [](int r) { return (r / S::SW_DIV) % S::SW_MOD; };
@@ -148,7 +175,7 @@ __global__ __launch_bounds__(TILE == 1 ? 512 : 256) void gemm_mfma_kernel(const 
     // activation piece p: rows p * RPP .. of the tile, lane i reading chunk
     // (i % CPR) ^ swz(row) of row p * RPP + i / CPR, which lands at LDS byte
     // p * 1024 + 16 i = row * SK + 16 * ((i % CPR)): the swizzled position
-    const int8_t* const qt = a.q + (size_t)m0 * K;
+    const int8_t* const qt = m_q + (size_t)m0 * K;
     int aoff[LA], akc[LA];                                   // row offset in the tile, chunk byte offset
     #pragma unroll
     for (int ii = 0; ii < LA; ++ii) {
@@ -168,8 +195,8 @@ __global__ __launch_bounds__(TILE == 1 ? 512 : 256) void gemm_mfma_kernel(const 
         b_dst[i] = A_BYTES + p * 1024;
         const int c = 64 * p + lane;
         const int tt = c / (16 * WPL), cc = c % (16 * WPL);
-        const int tile = min(tb_n * S::NTILE + tt, a.n_tiles - 1);
-        b_src[i] = a.packed + (size_t)tile * a.n_steps * (256 * WPL) + cc * 16;
+        const int tile = min(tb_n * S::NTILE + tt, m_ntiles - 1);
+        b_src[i] = m_packed + (size_t)tile * a.n_steps * (256 * WPL) + cc * 16;
     }
 
     // The direct loads of one step, numbered 0 .. NDMA-1 for this wave:
@@ -215,8 +242,8 @@ __global__ __launch_bounds__(TILE == 1 ? 512 : 256) void gemm_mfma_kernel(const 
         #pragma unroll
         for (int jb = 0; jb < WNB; ++jb) {
             const int n = n0 + wn * (32 * WNB) + jb * 32 + j;
-            const int nc = min(n, a.N - 1);
-            const float sg = a.scales[((size_t)(nc >> 4) * a.G + gi) * 16 + (nc & 15)];
+            const int nc = min(n, m_N - 1);
+            const float sg = m_scales[((size_t)(nc >> 4) * a.G + gi) * 16 + (nc & 15)];
             #pragma unroll
             for (int i = 0; i < WMB; ++i) {
                 #pragma unroll
@@ -225,7 +252,7 @@ __global__ __launch_bounds__(TILE == 1 ? 512 : 256) void gemm_mfma_kernel(const 
                     yp[i][jb][r] = yp[i][jb][r] + sg * (float)v;
                     if constexpr (ACC) {
                         const int t = m0 + wm * (32 * WMB) + i * 32 + 8 * (r / 4) + 4 * h + (r % 4);
-                        if (a.acc && t < T && n < a.N) a.acc[((size_t)t * a.N + n) * a.G + gi] = v;
+                        if (m_acc && t < T && n < m_N) m_acc[((size_t)t * m_N + n) * a.G + gi] = v;
                     }
                 }
                 C[i][jb] = i32x16{};
@@ -385,11 +412,11 @@ __global__ __launch_bounds__(TILE == 1 ? 512 : 256) void gemm_mfma_kernel(const 
     for (int i = 0; i < WMB; ++i)
         #pragma unroll
         for (int r = 0; r < 16; ++r)
-            sxv[i][r] = a.sx[min(m0 + wm * (32 * WMB) + i * 32 + 8 * (r / 4) + 4 * h + (r % 4), T - 1)];
+            sxv[i][r] = m_sx[min(m0 + wm * (32 * WMB) + i * 32 + 8 * (r / 4) + 4 * h + (r % 4), T - 1)];
     #pragma unroll
     for (int jb = 0; jb < WNB; ++jb) {
-        const int nc = min(n0 + wn * (32 * WNB) + jb * 32 + j, a.N - 1);
-        swv[jb] = GROUP ? 0.0f : a.scales[a.scale_per_row ? nc : 0];
+        const int nc = min(n0 + wn * (32 * WNB) + jb * 32 + j, m_N - 1);
+        swv[jb] = GROUP ? 0.0f : m_scales[a.scale_per_row ? nc : 0];
     }
     if constexpr (GROUP) {
         #pragma unroll
@@ -400,7 +427,7 @@ __global__ __launch_bounds__(TILE == 1 ? 512 : 256) void gemm_mfma_kernel(const 
                 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int t = m0 + wm * (32 * WMB) + i * 32 + 8 * (r / 4) + 4 * h + (r % 4);
-                    if (t < T && n < a.N) a.y[(size_t)t * a.N + n] = sxv[i][r] * yp[i][jb][r];
+                    if (t < T && n < m_N) m_y[(size_t)t * m_N + n] = sxv[i][r] * yp[i][jb][r];
                 }
         }
     } else {
@@ -411,9 +438,9 @@ __global__ __launch_bounds__(TILE == 1 ? 512 : 256) void gemm_mfma_kernel(const 
         // Each store writes 32 consecutive columns of two token rows.
         const int rows_here = min(BM, T - m0);
         const __amdgpu_buffer_rsrc_t ry =
-            __builtin_amdgcn_make_buffer_rsrc(a.y + (size_t)m0 * a.N, 0, rows_here * a.N * 4, 0x00020000);
+            __builtin_amdgcn_make_buffer_rsrc(m_y + (size_t)m0 * m_N, 0, rows_here * m_N * 4, 0x00020000);
         const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-            a.acc ? (void*)(a.acc + (size_t)m0 * a.N) : (void*)a.y, 0, (ACC && a.acc) ? rows_here * a.N * 4 : 0,
+            m_acc ? (void*)(m_acc + (size_t)m0 * m_N) : (void*)m_y, 0, (ACC && m_acc) ? rows_here * m_N * 4 : 0,
             0x00020000);
         // column byte offsets; a column past n gets 2^30, beyond any resource
         // size here (rows * n * 4 <= 256 * 2^20 * 4)
@@ -421,9 +448,9 @@ __global__ __launch_bounds__(TILE == 1 ? 512 : 256) void gemm_mfma_kernel(const 
         #pragma unroll
         for (int jb = 0; jb < WNB; ++jb) {
             const int n = n0 + wn * (32 * WNB) + jb * 32 + j;
-            col[jb] = n < a.N ? 4 * n : (1 << 30);
+            col[jb] = n < m_N ? 4 * n : (1 << 30);
         }
-        const int row_bytes = 4 * a.N;
+        const int row_bytes = 4 * m_N;
         #pragma unroll
         for (int i = 0; i < WMB; ++i) {
             #pragma unroll
@@ -444,7 +471,7 @@ __global__ __launch_bounds__(TILE == 1 ? 512 : 256) void gemm_mfma_kernel(const 
 
 template <int FMT, int WPL, int TILE>
 void gemm_mfma_launch_tile(const GemmFastArgs& ga, bool group, bool acc, hipStream_t st) {
-    const dim3 grid((unsigned)(ga.mb * ga.nb)), block(64 * GemmShape<FMT, WPL, TILE>::NW);
+    const dim3 grid((unsigned)ga.wg_start[ga.n_mats]), block(64 * GemmShape<FMT, WPL, TILE>::NW);
     if (group) {                                             // group mode runs the small tile only
         if constexpr (TILE == 0) {
             if (acc) gemm_mfma_kernel<FMT, WPL, TILE, true, true><<<grid, block, 0, st>>>(ga);
@@ -456,34 +483,47 @@ void gemm_mfma_launch_tile(const GemmFastArgs& ga, bool group, bool acc, hipStre
     }
 }
 
-// Tile choice: the least work on the busiest CU, rounds of tiles per CU times
-// the tile's area, weighted by how close each tile shape runs to the matrix
-// cores' rate (the 256 x 256 tile best: two wavefronts per SIMD and the most
-// MFMA work per staged byte).  Group mode runs the 128 x 128 tile only.
+// Tile choice: the least work on the busiest CU over all the launch's tiles,
+// rounds of tiles per CU times the tile's area, weighted by how close each
+// tile shape runs to the matrix cores' rate (the 256 x 256 tile best: two
+// wavefronts per SIMD and the most MFMA work per staged byte).  Group mode
+// runs the 128 x 128 tile only.
 template <int FMT, int WPL>
 void gemm_mfma_launch(GemmFastArgs ga, bool group, bool acc, hipStream_t st) {
     using Big = GemmShape<FMT, WPL, 1>;
     using Mid = GemmShape<FMT, WPL, 2>;
     using Small = GemmShape<FMT, WPL, 0>;
     const long cus = device_cu_count();
+    auto tiles_of = [&](int bm, int bn) {
+        long tiles = 0;
+        for (int i = 0; i < ga.n_mats; ++i) tiles += (long)((ga.T + bm - 1) / bm) * ((ga.m[i].N + bn - 1) / bn);
+        return tiles;
+    };
     auto cost = [&](int bm, int bn, double eff) {
-        const long tiles = (long)((ga.T + bm - 1) / bm) * ((ga.N + bn - 1) / bn);
-        return (double)((tiles + cus - 1) / cus) * bm * bn / eff;
+        return (double)((tiles_of(bm, bn) + cus - 1) / cus) * bm * bn / eff;
+    };
+    auto place = [&](int bm, int bn) {                       // token blocks, row blocks, first workgroups
+        ga.mb = (ga.T + bm - 1) / bm;
+        int wgs = 0;
+        for (int i = 0; i < ga.n_mats; ++i) {
+            ga.m[i].nb = (ga.m[i].N + bn - 1) / bn;
+            ga.wg_start[i] = wgs;
+            wgs += ga.mb * ga.m[i].nb;
+        }
+        ga.wg_start[ga.n_mats] = wgs;
+        for (int i = ga.n_mats + 1; i <= kGemmMaxMats; ++i) ga.wg_start[i] = 0x7fffffff;
     };
     const double c_big = Big::FITS && !group ? cost(Big::BM, Big::BN, 1.0) : 1e300;
     const double c_mid = Mid::FITS && !group ? cost(Mid::BM, Mid::BN, 0.9) : 1e300;
     const double c_small = cost(Small::BM, Small::BN, 0.8);
     if (c_big <= c_mid && c_big <= c_small) {
-        ga.mb = (ga.T + Big::BM - 1) / Big::BM;
-        ga.nb = (ga.N + Big::BN - 1) / Big::BN;
+        place(Big::BM, Big::BN);
         if constexpr (Big::FITS) gemm_mfma_launch_tile<FMT, WPL, 1>(ga, false, acc, st);
     } else if (c_mid <= c_small) {
-        ga.mb = (ga.T + Mid::BM - 1) / Mid::BM;
-        ga.nb = (ga.N + Mid::BN - 1) / Mid::BN;
+        place(Mid::BM, Mid::BN);
         if constexpr (Mid::FITS) gemm_mfma_launch_tile<FMT, WPL, 2>(ga, false, acc, st);
     } else {
-        ga.mb = (ga.T + Small::BM - 1) / Small::BM;
-        ga.nb = (ga.N + Small::BN - 1) / Small::BN;
+        place(Small::BM, Small::BN);
         gemm_mfma_launch_tile<FMT, WPL, 0>(ga, group, acc, st);
     }
 }
@@ -493,34 +533,55 @@ bool gemm_mfma_supported(const LinearArgs& a) {
     return a.k % 16 == 0 && (uintptr_t)a.q % 16 == 0 && (uintptr_t)a.packed % 16 == 0 && a.n <= (1 << 20);
 }
 
-hipError_t launch_gemm_mfma(const LinearArgs& a, hipStream_t stream) {
-    GemmFastArgs ga;
-    ga.packed = a.packed; ga.scales = a.scales; ga.q = a.q; ga.sx = a.sx; ga.y = a.y; ga.acc = a.acc;
-    ga.T = a.t; ga.N = a.n; ga.K = a.k;
-    ga.n_steps = a.n_steps;
-    ga.n_tiles = (a.n + 15) / 16;
-    const bool group = a.scale == LOWBIT_SCALE_GROUP;
-    ga.group = group ? a.group : 0;
-    ga.G = group ? a.n_groups : 1;
-    ga.scale_per_row = a.scale == LOWBIT_SCALE_ROW;
-    const bool acc = a.acc != nullptr;
-    switch (a.fmt) {
-        case FMT_TERNARY:
-            if (a.wpl == 4) gemm_mfma_launch<FMT_TERNARY, 4>(ga, group, acc, stream);
-            else if (a.wpl == 2) gemm_mfma_launch<FMT_TERNARY, 2>(ga, group, acc, stream);
-            else gemm_mfma_launch<FMT_TERNARY, 1>(ga, group, acc, stream);
-            break;
-        case FMT_INT4:
-            if (a.wpl == 4) gemm_mfma_launch<FMT_INT4, 4>(ga, group, acc, stream);
-            else gemm_mfma_launch<FMT_INT4, 2>(ga, group, acc, stream);
-            break;
-        default:
-            if (a.wpl == 4) gemm_mfma_launch<FMT_BINARY, 4>(ga, group, acc, stream);
-            else if (a.wpl == 2) gemm_mfma_launch<FMT_BINARY, 2>(ga, group, acc, stream);
-            else gemm_mfma_launch<FMT_BINARY, 1>(ga, group, acc, stream);
-            break;
+// `count` products of equal fmt, scale mode, group, k and t, every one
+// gemm_mfma_supported: as few launches as kGemmMaxMats allows, of near-equal
+// size (a short last launch would run mostly as a tail).
+hipError_t launch_gemm_mfma_group(const LinearArgs* mats, int count, hipStream_t stream) {
+    const int launches = (count + kGemmMaxMats - 1) / kGemmMaxMats;
+    for (int li = 0, b = 0; li < launches; ++li) {
+        const int e = (int)((int64_t)count * (li + 1) / launches);
+        const int n = e - b;
+        const LinearArgs& a = mats[b];
+        GemmFastArgs ga{};
+        ga.T = a.t; ga.K = a.k;
+        ga.n_steps = a.n_steps;
+        const bool group = a.scale == LOWBIT_SCALE_GROUP;
+        ga.group = group ? a.group : 0;
+        ga.G = group ? a.n_groups : 1;
+        ga.scale_per_row = a.scale == LOWBIT_SCALE_ROW;
+        ga.n_mats = n;
+        bool acc = false;
+        for (int i = 0; i < n; ++i) {
+            const LinearArgs& c = mats[b + i];
+            GemmMat& m = ga.m[i];
+            m.packed = c.packed; m.scales = c.scales; m.q = c.q; m.sx = c.sx; m.y = c.y; m.acc = c.acc;
+            m.N = c.n;
+            m.n_tiles = (c.n + 15) / 16;
+            acc = acc || c.acc != nullptr;
+        }
+        switch (a.fmt) {
+            case FMT_TERNARY:
+                if (a.wpl == 4) gemm_mfma_launch<FMT_TERNARY, 4>(ga, group, acc, stream);
+                else if (a.wpl == 2) gemm_mfma_launch<FMT_TERNARY, 2>(ga, group, acc, stream);
+                else gemm_mfma_launch<FMT_TERNARY, 1>(ga, group, acc, stream);
+                break;
+            case FMT_INT4:
+                if (a.wpl == 4) gemm_mfma_launch<FMT_INT4, 4>(ga, group, acc, stream);
+                else gemm_mfma_launch<FMT_INT4, 2>(ga, group, acc, stream);
+                break;
+            default:
+                if (a.wpl == 4) gemm_mfma_launch<FMT_BINARY, 4>(ga, group, acc, stream);
+                else if (a.wpl == 2) gemm_mfma_launch<FMT_BINARY, 2>(ga, group, acc, stream);
+                else gemm_mfma_launch<FMT_BINARY, 1>(ga, group, acc, stream);
+                break;
+        }
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+        b = e;
     }
-    return hipGetLastError();
+    return hipSuccess;
 }
+
+hipError_t launch_gemm_mfma(const LinearArgs& a, hipStream_t stream) { return launch_gemm_mfma_group(&a, 1, stream); }
 
 }  // namespace lowbit

@@ -41,6 +41,9 @@ hipError_t launch_gemv(const LinearArgs& a, hipStream_t stream);
 // several matrices of equal fmt / scale mode / group / k and t <= 16 in one launch
 hipError_t launch_gemv_group(const LinearArgs* mats, int count, hipStream_t stream);
 hipError_t launch_gemm(const LinearArgs& a, hipStream_t stream);
+// several products of equal fmt / scale mode / group / k / t in as few launches as possible
+hipError_t launch_gemm_group(const LinearArgs* mats, int count, hipStream_t stream);
+hipError_t launch_gemm_mfma_group(const LinearArgs* mats, int count, hipStream_t stream);
 // the streaming GEMM (k % 16 == 0, 16-byte aligned q and packed) and the general one
 bool gemm_mfma_supported(const LinearArgs& a);
 hipError_t launch_gemm_mfma(const LinearArgs& a, hipStream_t stream);

@@ -513,6 +513,26 @@ lowbit_status lowbit_linear_fused(const lowbit_desc* d, const uint8_t* packed, c
     return hip_status(lowbit::launch_gemv(a, (hipStream_t)hip_stream));
 }
 
+lowbit_status lowbit_linear_batched_grouped(int32_t count, const lowbit_desc* descs, const uint8_t* const* packed,
+                                            const float* const* scales, const int8_t* const* q,
+                                            const float* const* sx, int32_t t, float* const* y,
+                                            int32_t* const* acc, void* hip_stream) {
+    if (count < 1 || !descs || !packed || !scales || !q || !sx || !y || t < 1) return LOWBIT_E_ARG;
+    std::vector<lowbit::LinearArgs> args((size_t)count);
+    for (int32_t i = 0; i < count; ++i) {
+        const lowbit_desc& d0 = descs[0];
+        const lowbit_desc& d = descs[i];
+        if (d.format != d0.format || d.scale != d0.scale || d.group != d0.group || d.flags != d0.flags ||
+            d.k != d0.k)
+            return LOWBIT_E_ARG;
+        lowbit_status st = linear_common(&d, packed[i], scales[i], q[i], sx[i], t, y[i], acc ? acc[i] : nullptr,
+                                         &args[(size_t)i]);
+        if (st != LOWBIT_OK) return st;
+    }
+    clear_hip_error();
+    return hip_status(lowbit::launch_gemm_group(args.data(), count, (hipStream_t)hip_stream));
+}
+
 lowbit_status lowbit_linear_grouped(int32_t count, const lowbit_desc* descs, const uint8_t* const* packed,
                                     const float* const* scales, const int8_t* const* q, const float* const* sx,
                                     int32_t t, float* const* y, int32_t* const* acc, void* hip_stream) {

@@ -208,6 +208,23 @@ lowbit_status lowbit_linear_grouped(int32_t count, const lowbit_desc* descs, con
                                     int32_t* const* acc, void* hip_stream);
 
 /*
+ * lowbit_linear_batched_grouped - several independent prefill products
+ * (lowbit_linear_batched each) of equal format, scale mode, group, flags and
+ * k, and one token count t, in as few launches as the argument space allows
+ * (24 per launch): product i reads q[i] [t, k], sx[i] [t] and writes y[i]
+ * [t, n_i] (and acc[i] when acc and acc[i] are not NULL).  One launch fills
+ * the chip with the output tiles of all its products, which small products
+ * (n of a few hundred) cannot do alone.  Results equal those of the single
+ * calls bit for bit.
+ * Errors: as lowbit_linear_batched; LOWBIT_E_ARG when the descriptors differ
+ *         in format, scale mode, group, flags or k.
+ */
+lowbit_status lowbit_linear_batched_grouped(int32_t count, const lowbit_desc* descs, const uint8_t* const* packed,
+                                            const float* const* scales, const int8_t* const* q,
+                                            const float* const* sx, int32_t t, float* const* y,
+                                            int32_t* const* acc, void* hip_stream);
+
+/*
  * lowbit_linear_fused - the decode product with the activation quantiser fused
  * into it (M8.8 "Native Binary and Ternary Transformers" 0x02C / 0x05C
  * quantiser, 0x02D product): what lowbit_act_quant(x, t, k, q, sx, status)

@@ -220,6 +220,49 @@ def test_grouped_matches_single_and_oracle(fmt, scale, group, t):
         check_y(ys[i].cpu().numpy(), y32, y64, f"grouped {i}")
 
 
+@pytest.mark.parametrize("fmt,scale,group,k,t,ns", [
+    ("binary", "row", 0, 192, 300, [96, 192, 768, 20, 130]),
+    ("int4", "row", 0, 1280, 260, [1280, 17, 384]),
+    ("ternary", "group", 128, 256, 129, [64, 300, 16]),
+    ("ternary", "tensor", 0, 1000, 70, [50, 33]),              # k % 16 != 0: the general kernel, one each
+    ("binary", "row", 0, 192, 77, [16 + 8 * (i % 9) for i in range(30)]),   # two launches of at most 24
+])
+def test_batched_grouped_matches_single_and_oracle(fmt, scale, group, k, t, ns):
+    """lowbit_linear_batched_grouped (one launch's tiles over several
+    products of equal k) equals per-matrix lowbit_linear_batched bit-for-bit
+    in acc and y, and the oracle on each (all at sizes the oracle runs in
+    seconds)."""
+    import torch
+    lb = pytest.importorskip("bit_weight_linear_bitlinear_amd")
+    say(f"[case] batched grouped fmt={fmt} scale={scale} group={group} k={k} t={t} count={len(ns)}")
+    descs, packed, scales, qs, sxs, ys, accs, refs = [], [], [], [], [], [], [], []
+    for i, n in enumerate(ns):
+        w, x = workloads.random_case(700 + i, n, k, t)
+        d, p, s, _, _ = pack_upload(w, fmt, scale, group, fmt == "int4")
+        q, sx, _ = act_quant_dev(to_dev(x))
+        descs.append(d); packed.append(p); scales.append(s); qs.append(q); sxs.append(sx)
+        ys.append(torch.full((t, n), float("nan"), device="cuda"))
+        accs.append(torch.full((t, n, d.n_groups), -7, dtype=torch.int32, device="cuda") if i % 3 != 2 else None)
+        refs.append((w, x))
+    lb.lowbit_linear_batched_grouped(descs, packed, scales, qs, sxs, ys, accs)
+    ys2 = [torch.full_like(y, float("nan")) for y in ys]
+    lb.lowbit_linear_batched_grouped(descs, packed, scales, qs, sxs, ys2)          # no integer outputs
+    for i in range(len(ns)):
+        y1, a1 = linear_dev("gemm", descs[i], packed[i], scales[i], qs[i], sxs[i])
+        torch.cuda.synchronize()
+        assert torch.equal(ys[i], y1) and torch.equal(ys2[i], y1), i
+        if accs[i] is not None:
+            assert torch.equal(accs[i], a1), i
+    for i in range(min(len(ns), 6)):
+        w, x = refs[i]
+        p_ref, s_ref, _, _ = oracle.quantize_and_pack(w, fmt, scale, group, fmt == "int4")
+        q_ref, sx_ref, _ = oracle.act_quant(x)
+        y32, y64, acc_ref = oracle.linear(p_ref, s_ref, fmt, scale, group, w.shape[0], k, q_ref, sx_ref)
+        if accs[i] is not None:
+            assert (accs[i].cpu().numpy() == acc_ref).all(), i
+        check_y(ys[i].cpu().numpy(), y32, y64, f"batched grouped {i}")
+
+
 @pytest.mark.parametrize("fmt", ["ternary", "binary", "int4"])
 def test_gemm_tile_shapes(fmt):
     """Prefill shapes that select each workgroup tile of the batched kernel
