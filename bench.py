@@ -651,8 +651,9 @@ def decode_model_view():
     L = cfg["layers"]
     out = {"what": "greedy decode, batch 1, of the 256-d 6-layer ternary decoder (4 heads, 4096 vocabulary, "
                    "128-token context; RMSNorm, rotary attention over an fp32 KV cache, SwiGLU, ternary head), "
-                   f"{steps} tokens per timed run from position 0; 3 + 8 * {L} launches per token",
-           "launches_per_token": 3 + 8 * L, "final_state": s, **res,
+                   f"{steps} tokens per timed run from position 0; 3 + 5 * {L} launches per token (residual adds, "
+                   f"norms and SwiGLU inside the products' quantiser prologues)",
+           "launches_per_token": 3 + 5 * L, "final_state": s, **res,
            "context_not_target": "the engine's README quotes ~170-185 tokens/s for this configuration on one "
                                  "Apple M-series CPU thread without a KV cache"}
     log(f"[bench] decode model: {res}")

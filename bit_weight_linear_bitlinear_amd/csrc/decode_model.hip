@@ -162,28 +162,36 @@ __global__ __launch_bounds__(256) void rope_attn_kernel(const float* __restrict_
     }
     __syncthreads();                                         // this position's key and value, and qs
 
-    // scores: thread 4 j + c takes dimensions 16 c .. 16 c + 15 of position j
+    // scores: thread 4 j + c takes dimensions 16 c .. 16 c + 15 of position j,
+    // two 64-position chunks per pass with all their loads issued together
     const int c = tid & 3;
-    for (int j0 = 0; j0 <= pos; j0 += 64) {
-        const int j = j0 + (tid >> 2);
-        const int jj = j <= pos ? j : pos;                   // (clamped: a valid row, result unused)
-        const float4* kj = reinterpret_cast<const float4*>(kc + (size_t)jj * d + hb + 16 * c);
-        const float4* qv = reinterpret_cast<const float4*>(qs + 16 * c);
-        float4 kv[4];
+    const float4* qv = reinterpret_cast<const float4*>(qs + 16 * c);
+    for (int j0 = 0; j0 <= pos; j0 += 128) {
+        float4 kv[2][4];
         #pragma unroll
-        for (int u = 0; u < 4; ++u) kv[u] = kj[u];
-        float s = 0.0f;
-        #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const float4 q4 = qv[u];
-            s += q4.x * kv[u].x;
-            s += q4.y * kv[u].y;
-            s += q4.z * kv[u].z;
-            s += q4.w * kv[u].w;
+        for (int h2 = 0; h2 < 2; ++h2) {
+            const int j = j0 + 64 * h2 + (tid >> 2);
+            const int jj = j <= pos ? j : pos;               // (clamped: a valid row, result unused)
+            const float4* kj = reinterpret_cast<const float4*>(kc + (size_t)jj * d + hb + 16 * c);
+            #pragma unroll
+            for (int u = 0; u < 4; ++u) kv[h2][u] = kj[u];
         }
-        s += __shfl_xor(s, 1, 64);
-        s += __shfl_xor(s, 2, 64);
-        if (c == 0 && j <= pos) ps[j] = s * 0.125f;          // 1 / sqrt(64), exact
+        #pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+            const int j = j0 + 64 * h2 + (tid >> 2);
+            float s = 0.0f;
+            #pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float4 q4 = qv[u];
+                s += q4.x * kv[h2][u].x;
+                s += q4.y * kv[h2][u].y;
+                s += q4.z * kv[h2][u].z;
+                s += q4.w * kv[h2][u].w;
+            }
+            s += __shfl_xor(s, 1, 64);
+            s += __shfl_xor(s, 2, 64);
+            if (c == 0 && j <= pos) ps[j] = s * 0.125f;      // 1 / sqrt(64), exact
+        }
     }
     __syncthreads();
     if (tid < 64) {                                          // softmax weights (unnormalised) and their sum
@@ -200,11 +208,21 @@ __global__ __launch_bounds__(256) void rope_attn_kernel(const float* __restrict_
         if (tid == 0) denom = sum;
     }
     __syncthreads();
+    // weighted values: thread (grp, dim) sums positions grp, grp + 4, ... in
+    // four independent chains, so that its loads run ahead of the adds
     const int dim = tid & 63, grp = tid >> 6;
-    float acc = 0.0f;
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     const float* vp = vc + hb + dim;
-    for (int j = grp; j <= pos; j += 4) acc += ps[j] * vp[(size_t)j * d];
-    part[grp][dim] = acc;
+    int j = grp;
+    for (; j + 12 <= pos; j += 16) {
+        float v[4];
+        #pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = vp[(size_t)(j + 4 * u) * d];
+        #pragma unroll
+        for (int u = 0; u < 4; ++u) acc[u] += ps[j + 4 * u] * v[u];
+    }
+    for (; j <= pos; j += 4) acc[0] += ps[j] * vp[(size_t)j * d];
+    part[grp][dim] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
     __syncthreads();
     if (tid < 64) attn[hb + tid] = ((part[0][tid] + part[1][tid]) + (part[2][tid] + part[3][tid])) / denom;
 }

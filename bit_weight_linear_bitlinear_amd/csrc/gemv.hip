@@ -76,6 +76,17 @@ hipError_t launch_gemv_group(const LinearArgs* mats, int count, hipStream_t stre
     bool x_vec = a.k % 4 == 0;
     for (int i = 0; fused_in && i < count; ++i) x_vec = x_vec && (uintptr_t)mats[i].x % 16 == 0;
     cfg.fuse = fused_in && small_stage && x_vec && a.t == 1;
+    // an input transform needs the fused prologue with one load round (k <= 3072),
+    // 16-byte aligned operands, and one x shared by every matrix of the launch
+    cfg.pre = a.pre;
+    if (a.pre != 0) {
+        bool ok = cfg.fuse && a.k <= 3 * 256 * 4 && (uintptr_t)a.pre_r % 16 == 0 && (uintptr_t)a.pre_g % 16 == 0 &&
+                  (uintptr_t)a.pre_xo % 16 == 0 && (uintptr_t)a.pre_ho % 16 == 0 &&
+                  (a.pre == 1 ? (a.pre_g != nullptr && a.pre_xo != nullptr) : a.pre_r != nullptr);
+        for (int i = 1; i < count; ++i) ok = ok && mats[i].x == a.x;
+        if (!ok) return hipErrorInvalidValue;
+    }
+    gp.pre_r = a.pre_r; gp.pre_g = a.pre_g; gp.pre_eps = a.pre_eps; gp.pre_xo = a.pre_xo; gp.pre_ho = a.pre_ho;
     if (fused_in && !cfg.fuse) {                             // every matrix's input in one launch
         const float* xs[kGemvMaxMats];
         int8_t* qs[kGemvMaxMats];

@@ -12,6 +12,9 @@ constexpr int kGemvLdsA = 56 * 1024; // activation bytes a 4-wavefront workgroup
 constexpr int kGemvLdsWide = 20 * 1024;   // above this stage, 16-wavefront workgroups share it (t > 1)
 constexpr int kGemvLdsMax = 160 * 1024;   // LDS of a CU
 
+// input transforms of the fused prologue (PRE_* of gemv_kernel)
+enum { PRE_NONE = 0, PRE_NORM = 1, PRE_SWIGLU = 2 };
+
 struct GemvMat {
     const uint8_t* packed;
     const float* scales;
@@ -42,6 +45,13 @@ struct GemvParams {
     int lds_a_bytes;     // T * stride when activations are staged in LDS, else 0
     int q_word;          // fused: k % 4 == 0 and every q 4-byte aligned
     int32_t* status;     // fused: LOWBIT_ACT_* bits of rejected rows (nullable)
+    // PRE_NORM: residual r (nullable), gain g, eps; out: x + r (pre_xo), h (pre_ho, nullable)
+    // PRE_SWIGLU: up (pre_r); out: a (pre_ho, nullable).  Every matrix of the launch shares x.
+    const float* pre_r;
+    const float* pre_g;
+    float pre_eps;
+    float* pre_xo;
+    float* pre_ho;
     int wg_start[kGemvMaxMats + 1];   // first workgroup of each matrix (ascending; INT_MAX past n_mats)
     GemvMat m[kGemvMaxMats];
 };
@@ -55,6 +65,7 @@ struct GemvCfg {
     bool acc;            // some matrix wants the integer products
     bool fuse;           // activations quantised in the kernel's prologue (needs lds_a, 4 waves)
     int waves;           // wavefronts per workgroup: 4, or 16 with a large LDS stage
+    int pre;             // PRE_*: the fused prologue's input transform
     int grid;
     size_t lds_bytes;
 };

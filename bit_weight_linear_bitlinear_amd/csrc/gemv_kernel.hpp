@@ -90,11 +90,16 @@ __device__ __forceinline__ uint32_t quant_word(const float4 v, float r, int vali
 // (kept out of the streaming instantiations: optional stores inside the
 // k-loop make the compiler's wait counting conservative).
 // WV: wavefronts per workgroup (4; 16 only for LDSA without FUSE).
+// PRE (with FUSE, one load round): what the prologue quantises.  PRE_NONE: x.
+// PRE_NORM: h = RMSNorm(x + r; g) (r nullable), the residual sum and h
+// written out by the launch's first workgroup (a decoder block's residual add
+// and the norm before its next projection).  PRE_SWIGLU: a = SiLU(x) * up
+// (the gated FFN between gate/up and down), a written out likewise.
 // FUSE (with LDSA, one token): the stage is filled from fp32 x by the
 // per-token absmax quantiser itself (M8.8 0x02C, 0x05C: m = max|x|,
 // r = 127 / m, codes clip(rint(x r)), s_x = m / 127), every workgroup for its
 // own stage; the matrix's first workgroup also writes the codes and scale out.
-template <int FMT, int WPL, int NR, int SPS, bool UPG1, bool LDSA, bool ACC, bool FUSE, int WV>
+template <int FMT, int WPL, int NR, int SPS, bool UPG1, bool LDSA, bool ACC, bool FUSE, int WV, int PRE>
 __global__ __launch_bounds__(64 * WV) void gemv_kernel(const GemvParams p) {
     using S = GemvShape<FMT, WPL>;
     constexpr int D = kGemvD;
@@ -108,9 +113,11 @@ __global__ __launch_bounds__(64 * WV) void gemv_kernel(const GemvParams p) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     static_assert(!FUSE || LDSA, "the fused quantiser fills the LDS stage");
     static_assert(WV == 4 || (WV == 16 && LDSA && !FUSE), "16-wavefront workgroups share an LDS stage");
+    static_assert(PRE == PRE_NONE || FUSE, "the input transforms run in the fused prologue");
     constexpr int NT = 64 * WV;                              // threads per workgroup
     __shared__ float fz_m[4];                                // fused: per-wave max |x|
     __shared__ int fz_bad[4];                                // fused: per-wave non-finite flag
+    __shared__ float fz_ss[4];                               // PRE_NORM: per-wave sum of squares
 
     // the wavefront index is uniform; saying so keeps every value derived
     // from it (tile, part, k-range) in scalar registers
@@ -235,6 +242,60 @@ __global__ __launch_bounds__(64 * WV) void gemv_kernel(const GemvParams p) {
         const bool writer = (int)blockIdx.x == p.wg_start[mi];
         const int npad = (p.n_steps * SK) >> 2;              // words of the stage row
         const bool one_round = nword <= 256 * FR;
+        if constexpr (PRE != PRE_NONE) {
+            // the transform of the (single) load round, in place in xv;
+            // words past nword are clamped duplicates and never counted
+            const bool first = blockIdx.x == 0;
+            float4 yv[FR], gv[FR];
+            #pragma unroll
+            for (int j = 0; j < FR; ++j) {
+                const int idx = min(tid + 256 * j, nword - 1);
+                if constexpr (PRE == PRE_NORM) {
+                    yv[j] = p.pre_r ? reinterpret_cast<const float4*>(p.pre_r)[idx] : make_float4(0.f, 0.f, 0.f, 0.f);
+                    gv[j] = reinterpret_cast<const float4*>(p.pre_g)[idx];
+                } else {
+                    yv[j] = reinterpret_cast<const float4*>(p.pre_r)[idx];
+                }
+            }
+            if constexpr (PRE == PRE_NORM) {
+                float ss = 0.0f;
+                #pragma unroll
+                for (int j = 0; j < FR; ++j) {
+                    if (p.pre_r) {
+                        xv[j].x = xv[j].x + yv[j].x; xv[j].y = xv[j].y + yv[j].y;
+                        xv[j].z = xv[j].z + yv[j].z; xv[j].w = xv[j].w + yv[j].w;
+                    }
+                    if (tid + 256 * j < nword)
+                        ss += xv[j].x * xv[j].x + xv[j].y * xv[j].y + xv[j].z * xv[j].z + xv[j].w * xv[j].w;
+                }
+                #pragma unroll
+                for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+                if (lane == 0) fz_ss[wave] = ss;
+                __syncthreads();
+                ss = (fz_ss[0] + fz_ss[1]) + (fz_ss[2] + fz_ss[3]);
+                const float rr = 1.0f / sqrtf(ss / (float)K + p.pre_eps);
+                #pragma unroll
+                for (int j = 0; j < FR; ++j) {
+                    const int w = tid + 256 * j;
+                    if (first && w < nword) reinterpret_cast<float4*>(p.pre_xo)[w] = xv[j];
+                    xv[j].x = xv[j].x * rr * gv[j].x; xv[j].y = xv[j].y * rr * gv[j].y;
+                    xv[j].z = xv[j].z * rr * gv[j].z; xv[j].w = xv[j].w * rr * gv[j].w;
+                    if (first && p.pre_ho && w < nword) reinterpret_cast<float4*>(p.pre_ho)[w] = xv[j];
+                }
+            } else {
+                #pragma unroll
+                for (int j = 0; j < FR; ++j) {
+                    const float z[4] = {xv[j].x, xv[j].y, xv[j].z, xv[j].w};
+                    const float u[4] = {yv[j].x, yv[j].y, yv[j].z, yv[j].w};
+                    float a[4];
+                    #pragma unroll
+                    for (int e = 0; e < 4; ++e) a[e] = z[e] / (1.0f + expf(-z[e])) * u[e];
+                    xv[j] = make_float4(a[0], a[1], a[2], a[3]);
+                    const int w = tid + 256 * j;
+                    if (first && p.pre_ho && w < nword) reinterpret_cast<float4*>(p.pre_ho)[w] = xv[j];
+                }
+            }
+        }
         float m = 0.0f;
         int bad = 0;
         auto reduce_round = [&]() {
@@ -482,23 +543,28 @@ void gemv_launch_lds(const GemvParams& p, const GemvCfg& c, hipStream_t st) {
     if (c.lds_a) {
         if constexpr (NR == 1) {   // fused launches have one token
             if (c.fuse) {
-                gemv_kernel<FMT, WPL, 1, SPS, UPG1, true, false, true, 4><<<grid, block, c.lds_bytes, st>>>(p);
+                if (c.pre == PRE_NORM)
+                    gemv_kernel<FMT, WPL, 1, SPS, UPG1, true, false, true, 4, PRE_NORM><<<grid, block, c.lds_bytes, st>>>(p);
+                else if (c.pre == PRE_SWIGLU)
+                    gemv_kernel<FMT, WPL, 1, SPS, UPG1, true, false, true, 4, PRE_SWIGLU><<<grid, block, c.lds_bytes, st>>>(p);
+                else
+                    gemv_kernel<FMT, WPL, 1, SPS, UPG1, true, false, true, 4, PRE_NONE><<<grid, block, c.lds_bytes, st>>>(p);
                 return;
             }
         }
         if constexpr (NR == 4) {   // a large stage shared by 16 wavefronts (several tokens)
             if (c.waves == 16) {
-                if (c.acc) gemv_kernel<FMT, WPL, 4, SPS, UPG1, true, true, false, 16><<<grid, block, c.lds_bytes, st>>>(p);
-                else gemv_kernel<FMT, WPL, 4, SPS, UPG1, true, false, false, 16><<<grid, block, c.lds_bytes, st>>>(p);
+                if (c.acc) gemv_kernel<FMT, WPL, 4, SPS, UPG1, true, true, false, 16, PRE_NONE><<<grid, block, c.lds_bytes, st>>>(p);
+                else gemv_kernel<FMT, WPL, 4, SPS, UPG1, true, false, false, 16, PRE_NONE><<<grid, block, c.lds_bytes, st>>>(p);
                 return;
             }
         }
-        if (c.acc) gemv_kernel<FMT, WPL, NR, SPS, UPG1, true, true, false, 4><<<grid, block, c.lds_bytes, st>>>(p);
-        else gemv_kernel<FMT, WPL, NR, SPS, UPG1, true, false, false, 4><<<grid, block, c.lds_bytes, st>>>(p);
+        if (c.acc) gemv_kernel<FMT, WPL, NR, SPS, UPG1, true, true, false, 4, PRE_NONE><<<grid, block, c.lds_bytes, st>>>(p);
+        else gemv_kernel<FMT, WPL, NR, SPS, UPG1, true, false, false, 4, PRE_NONE><<<grid, block, c.lds_bytes, st>>>(p);
     } else {
         // activations from L2: the fallback for stages too large for LDS, always 4 token registers
-        if (c.acc) gemv_kernel<FMT, WPL, 4, SPS, UPG1, false, true, false, 4><<<grid, block, c.lds_bytes, st>>>(p);
-        else gemv_kernel<FMT, WPL, 4, SPS, UPG1, false, false, false, 4><<<grid, block, c.lds_bytes, st>>>(p);
+        if (c.acc) gemv_kernel<FMT, WPL, 4, SPS, UPG1, false, true, false, 4, PRE_NONE><<<grid, block, c.lds_bytes, st>>>(p);
+        else gemv_kernel<FMT, WPL, 4, SPS, UPG1, false, false, false, 4, PRE_NONE><<<grid, block, c.lds_bytes, st>>>(p);
     }
 }
 

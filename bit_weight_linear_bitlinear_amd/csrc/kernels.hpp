@@ -29,6 +29,16 @@ struct LinearArgs {
     // codes and scales lowbit_act_quant would write); nullptr = q / sx given
     const float* x = nullptr;
     int32_t* status = nullptr;   // nullable: LOWBIT_ACT_* bits of rejected rows
+    // an input transform in the fused prologue (one token; see gemv_kernel's
+    // PRE): pre = 1 norm (x + pre_r, RMSNorm with pre_g / pre_eps; x + pre_r to
+    // pre_xo, the norm to pre_ho), 2 SwiGLU (SiLU(x) * pre_r to pre_ho); taken
+    // from the first matrix of a launch, whose matrices all share x
+    int pre = 0;
+    const float* pre_r = nullptr;
+    const float* pre_g = nullptr;
+    float pre_eps = 0.0f;
+    float* pre_xo = nullptr;
+    float* pre_ho = nullptr;
 };
 
 hipError_t launch_act_quant(const float* x, int t, int k, int8_t* q, float* sx, int32_t* status,

@@ -201,7 +201,7 @@ def test_model_sizes():
     m = _model_struct()
     d, ff, L = 256, 1024, 6
     up16 = lambda b: (b + 15) // 16 * 16
-    want = sum(up16(b) for b in (4 * d, 4 * d, 12 * d, 4 * d, 4 * d, 4 * ff, 4 * ff, 4 * ff, 4 * d, 16,
+    want = sum(up16(b) for b in (4 * d, 4 * d, 4 * d, 12 * d, 4 * d, 4 * d, 4 * ff, 4 * ff, 4 * ff, 4 * d, 16,
                                  max(d, ff), ff))
     assert lib.lowbit_model_work_bytes(ctypes.byref(m)) == want
     assert lib.lowbit_model_trace_floats(ctypes.byref(m)) == d + L * (12 * d + 3 * ff) + d

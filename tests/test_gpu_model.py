@@ -48,13 +48,9 @@ def _shapes(d, ff, vocab):
     return [(3 * d, d), (d, d), (ff, d), (ff, d), (d, ff), (vocab, d)]
 
 
-@pytest.fixture(scope="module")
-def model_pair():
-    """The GPU model (packed by the library) and the oracle model (packed by
-    the oracle) from the same seeded latent weights, embedding and gains."""
+def _build_pair(d, L, H, ff, V, C, latent):
     import torch
     lb = _lb()
-    d, L, H, ff, V, C = (CFG[k] for k in ("d", "layers", "heads", "d_ff", "vocab", "context"))
     shapes = _shapes(d, ff, V)
     descs = [lb.lowbit_describe(lb.TERNARY2, lb.SCALE_TENSOR, n, k) for n, k in shapes]
     embed = workloads.decode_model_embedding(V, d)
@@ -63,7 +59,7 @@ def model_pair():
     for layer in range(L + 1):
         for slot in (range(5) if layer < L else [5]):
             n, k = shapes[slot]
-            w = _latent(layer if slot < 5 else 0, slot, n, k)
+            w = latent(layer if slot < 5 else 0, slot, n, k)
             pk = np.empty(descs[slot].packed_bytes, np.uint8)
             sc = np.empty(descs[slot].n_scales, np.float32)
             lb.lowbit_pack(descs[slot], w, pk, sc)
@@ -76,6 +72,24 @@ def model_pair():
                         g_packed, g_scales)
     om_ = om.Model(d, L, H, ff, V, C, embed, norms, o_packed, o_scales)
     return gm, om_
+
+
+@pytest.fixture(scope="module")
+def model_pair():
+    """The GPU model (packed by the library) and the oracle model (packed by
+    the oracle) from the same seeded latent weights, embedding and gains: the
+    256-d model, whose step runs in the fused form (norms and SwiGLU inside
+    the products' quantiser prologues)."""
+    return _build_pair(*(CFG[k] for k in ("d", "layers", "heads", "d_ff", "vocab", "context")), _latent)
+
+
+@pytest.fixture(scope="module")
+def small_pair():
+    """An irregular small model (one head, an FFN width that is not a multiple
+    of 4) whose step takes the general form, every operation its own launch."""
+    def latent(layer, slot, n, k):
+        return workloads.random_case(1200 + 7 * layer + slot, n, k, 1)[0]
+    return _build_pair(64, 2, 1, 98, 300, 16, latent)
 
 
 def _rel(a, b):
@@ -178,13 +192,15 @@ def _state(tok, pos):
     return torch.tensor([tok, pos, 0, 0], dtype=torch.int32, device="cuda")
 
 
-def test_decode_steps_against_oracle(model_pair):
+@pytest.mark.parametrize("which", ["model_pair", "small_pair"])
+def test_decode_steps_against_oracle(which, request):
     """Twelve teacher-forced steps of the seeded prompt: every intermediate
     and the logits against the independent oracle run (before the first
     quantised input exactly / to fp32 rounding, after it within the code-flip
-    bound), the caches, the greedy token and the state."""
+    bound), the caches, the greedy token and the state; the 256-d model (the
+    fused form) and the small irregular one (the general form)."""
     import torch
-    gm, om_ = model_pair
+    gm, om_ = request.getfixturevalue(which)
     d, L, ff, V, C = om_.d, om_.n_layers, om_.d_ff, om_.vocab, om_.context
     prompt = workloads.decode_model_tokens(12, V)
     gm.k_cache.zero_()
