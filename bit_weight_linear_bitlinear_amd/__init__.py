@@ -62,6 +62,8 @@ _i32 = ctypes.c_int32
 _lib.lowbit_describe.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _D]
 _lib.lowbit_pack.argtypes = [_D, _P, _P, _P]
 _lib.lowbit_act_quant.argtypes = [_P, _i32, _i32, _P, _P, _P, _P]
+_lib.lowbit_act_quant_h4.argtypes = [_P, _i32, _i32, _P, _P, _P, _P]
+_lib.lowbit_act_quant_h4.restype = _i32
 _lib.lowbit_linear.argtypes = [_D, _P, _P, _P, _P, _i32, _P, _P, _P]
 _lib.lowbit_linear_batched.argtypes = [_D, _P, _P, _P, _P, _i32, _P, _P, _P]
 _PP = ctypes.POINTER(ctypes.c_void_p)
@@ -106,7 +108,8 @@ _lib.lowbit_last_hip_error.restype = ctypes.c_char_p
 for _f in ("lowbit_describe", "lowbit_pack", "lowbit_act_quant", "lowbit_linear", "lowbit_linear_batched"):
     getattr(_lib, _f).restype = _i32
 
-EXPORTS = ("lowbit_describe", "lowbit_pack", "lowbit_act_quant", "lowbit_linear", "lowbit_linear_batched",
+EXPORTS = ("lowbit_describe", "lowbit_pack", "lowbit_act_quant", "lowbit_act_quant_h4", "lowbit_linear",
+           "lowbit_linear_batched",
            "lowbit_linear_grouped", "lowbit_linear_batched_grouped", "lowbit_linear_fused",
            "lowbit_linear_grouped_fused",
            "lowbit_model_work_bytes", "lowbit_model_trace_floats", "lowbit_decode_step",
@@ -176,6 +179,14 @@ def lowbit_act_quant(x, q, sx, status=None, stream=None) -> None:
     t, k = x.shape
     _check(_lib.lowbit_act_quant(_dev(x, "x", 4 * t * k), t, k, _dev(q, "q", t * k), _dev(sx, "sx", 4 * t),
                                  _dev(status, "status", 4), _stream(stream)), "lowbit_act_quant")
+
+
+def lowbit_act_quant_h4(x, q, sx, status=None, stream=None) -> None:
+    """Device: x fp32[t, k] -> block-Hadamard-rotated INT4 codes q int8[t, k]
+    (in [-7, 7]) and sx fp32[t]; status int32[1] or None."""
+    t, k = x.shape
+    _check(_lib.lowbit_act_quant_h4(_dev(x, "x", 4 * t * k), t, k, _dev(q, "q", t * k), _dev(sx, "sx", 4 * t),
+                                    _dev(status, "status", 4), _stream(stream)), "lowbit_act_quant_h4")
 
 
 def _linear_ptrs(d, packed, scales, q, sx, y, acc):

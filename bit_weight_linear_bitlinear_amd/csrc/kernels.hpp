@@ -47,6 +47,13 @@ hipError_t launch_act_quant(const float* x, int t, int k, int8_t* q, float* sx, 
 constexpr int kActQuantMaxSrc = 40;
 hipError_t launch_act_quant_group(const float* const* x, int8_t* const* q, float* const* sx, int count, int t,
                                   int k, int32_t* status, hipStream_t stream);
+// H-BitLinear's rotated 4-bit quantiser (hadamard.hip): block size of a row
+// width (0 when k has no power-of-two factor of 64 or more), widest row
+constexpr int kH4MaxBlock = 2048;
+constexpr int kH4MaxK = 65536;
+int h4_block(int k);
+hipError_t launch_act_quant_h4(const float* x, int t, int k, int8_t* q, float* sx, int32_t* status,
+                               hipStream_t stream);
 hipError_t launch_gemv(const LinearArgs& a, hipStream_t stream);
 // several matrices of equal fmt / scale mode / group / k and t <= 16 in one launch
 hipError_t launch_gemv_group(const LinearArgs* mats, int count, hipStream_t stream);

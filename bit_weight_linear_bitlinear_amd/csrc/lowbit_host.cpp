@@ -563,6 +563,15 @@ lowbit_status lowbit_act_quant(const float* x, int32_t t, int32_t k, int8_t* q, 
     return hip_status(lowbit::launch_act_quant(x, t, k, q, sx, status, (hipStream_t)hip_stream));
 }
 
+lowbit_status lowbit_act_quant_h4(const float* x, int32_t t, int32_t k, int8_t* q, float* sx, int32_t* status,
+                                  void* hip_stream) {
+    if (!x || !q || !sx || t < 1 || k < 64 || k % 64) return LOWBIT_E_ARG;
+    if ((uintptr_t)x % 16 || (uintptr_t)q % 4 || (uintptr_t)sx % 4 || (uintptr_t)status % 4) return LOWBIT_E_ARG;
+    if (k > lowbit::kH4MaxK) return LOWBIT_E_RANGE;
+    clear_hip_error();
+    return hip_status(lowbit::launch_act_quant_h4(x, t, k, q, sx, status, (hipStream_t)hip_stream));
+}
+
 lowbit_status lowbit_linear(const lowbit_desc* d, const uint8_t* packed, const float* scales, const int8_t* q,
                             const float* sx, int32_t t, float* y, int32_t* acc, void* hip_stream) {
     lowbit::LinearArgs a;

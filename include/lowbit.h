@@ -156,6 +156,31 @@ lowbit_status lowbit_act_quant(const float* x, int32_t t, int32_t k, int8_t* q, 
                                int32_t* status, void* hip_stream);
 
 /*
+ * lowbit_act_quant_h4 - H-BitLinear's activation quantiser (M8.8 "Native
+ * Binary and Ternary Transformers", 0x07C, BitNet v2): each token row is
+ * rotated by the orthonormal Walsh-Hadamard transform (Sylvester order) over
+ * consecutive blocks of B channels, B the largest power of two dividing k
+ * (at most 2048), and the rotated row x' gets per-token absmax INT4 codes.
+ *   x      device float [t, k], 16-byte aligned
+ *   q      device int8  [t, k], 4-byte aligned   out: clip(rint(x' * (7 / m)),
+ *                              -7, 7), fp32, ties to even, m = max_k |x'[row]|
+ *   sx     device float [t]    out: m / 7 (fp32); 0 for an all-zero row
+ *   status device int32 [1] or NULL: LOWBIT_ACT_* bits ORed in, as
+ *          lowbit_act_quant; a row whose x' holds NaN/Inf, or whose 7 / m
+ *          overflows, gets zero codes and sx = NaN.
+ *   t >= 1; k a multiple of 64, at most 65536.
+ * x' is computed as fp32 butterflies in increasing half-width (each pair
+ * (a, c) -> (a + c, a - c)), then one multiply by fp32(1 / sqrt(B)), so the
+ * codes are a deterministic function of x.  q and sx are the operands of
+ * lowbit_linear / lowbit_linear_batched: y = s_w * sx * (Q(W) . q) is the
+ * layer's output when W was trained (or rotated) in the transformed basis.
+ * Errors: LOWBIT_E_ARG (null or misaligned pointer, t < 1, k not a multiple
+ *         of 64), LOWBIT_E_RANGE (k > 65536), LOWBIT_E_HIP.
+ */
+lowbit_status lowbit_act_quant_h4(const float* x, int32_t t, int32_t k, int8_t* q, float* sx,
+                                  int32_t* status, void* hip_stream);
+
+/*
  * lowbit_linear - decode-shaped product (GEMV), tuned for t <= 16 and correct
  * for any t (tokens are processed 16 at a time).
  *   d       descriptor of the packed matrix (from lowbit_describe)

@@ -47,15 +47,16 @@ def fwht_blocks(x: np.ndarray, b: int) -> np.ndarray:
     assert k % b == 0 and b & (b - 1) == 0
     v = x.reshape(t, k // b, b).copy()
     h = 1
-    while h < b:
-        w = v.reshape(t, k // b, b // (2 * h), 2, h)
-        a = w[:, :, :, 0, :].copy()
-        c = w[:, :, :, 1, :].copy()
-        w[:, :, :, 0, :] = a + c
-        w[:, :, :, 1, :] = a - c
-        h *= 2
-    scale = np.float32(1.0 / np.sqrt(np.float64(b)))
-    return (v * scale).reshape(t, k).astype(np.float32)
+    with np.errstate(over="ignore", invalid="ignore"):   # Inf / NaN rows are rejected later
+        while h < b:
+            w = v.reshape(t, k // b, b // (2 * h), 2, h)
+            a = w[:, :, :, 0, :].copy()
+            c = w[:, :, :, 1, :].copy()
+            w[:, :, :, 0, :] = a + c
+            w[:, :, :, 1, :] = a - c
+            h *= 2
+        scale = np.float32(1.0 / np.sqrt(np.float64(b)))
+        return (v * scale).reshape(t, k).astype(np.float32)
 
 
 def act_quant4(xr: np.ndarray):

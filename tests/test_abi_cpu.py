@@ -230,3 +230,18 @@ def test_decode_step_rejects_bad_arguments_on_the_host():
     m.work = 1 << 20
     arr[7] = None                                            # a missing weight pointer
     assert lib.lowbit_decode_step(ctypes.byref(m), fake, fake, None, None, None) == 1
+
+
+def test_act_quant_h4_rejects_bad_arguments_on_the_host():
+    """Row widths without a power-of-two block of 64, widths above 65536 and
+    misaligned buffers are refused before any launch."""
+    lib = lb.raw_library()
+    x = ctypes.c_void_p(1 << 20)                             # never dereferenced: the checks fail first
+    q, sx = ctypes.c_void_p(2 << 20), ctypes.c_void_p(3 << 20)
+    assert lib.lowbit_act_quant_h4(x, 1, 100, q, sx, None, None) == 1      # k % 64
+    assert lib.lowbit_act_quant_h4(x, 1, 32, q, sx, None, None) == 1
+    assert lib.lowbit_act_quant_h4(x, 0, 256, q, sx, None, None) == 1      # t < 1
+    assert lib.lowbit_act_quant_h4(ctypes.c_void_p((1 << 20) + 4), 1, 256, q, sx, None, None) == 1
+    assert lib.lowbit_act_quant_h4(x, 1, 256, ctypes.c_void_p((2 << 20) + 2), sx, None, None) == 1
+    assert lib.lowbit_act_quant_h4(None, 1, 256, q, sx, None, None) == 1
+    assert lib.lowbit_act_quant_h4(x, 1, 65536 + 64, q, sx, None, None) == 2   # LOWBIT_E_RANGE
