@@ -7,7 +7,8 @@ slack of a G-term fp32 sum taken in another order than the oracle's, since a
 bound relative to |y| cannot hold where the group terms cancel).
 
 Row widths cover every launch shape of the kernel: a wavefront per row
-(k <= 1024), a 256-thread workgroup per row, and a 1024-thread workgroup for
+(up to 32 floats per lane), two wavefronts per row (two rows per workgroup,
+odd token counts leaving the last one half empty), four, and sixteen for
 rows above 16384; blocks of 64, 128, 256, 512, 1024 and 2048; ragged token
 counts; the 4B-class widths (2560 attention, 9728 FFN) and the 4-bit QAT
 model's (1280, 3584)."""
@@ -55,10 +56,10 @@ def _check_codes(x, q, sx, st, what):
 
 @pytest.mark.parametrize("t,k", [
     (1, 64), (5, 192), (3, 128), (17, 320), (2, 256), (9, 512), (4, 768), (6, 1024),     # a wavefront per row
-    (1, 1280), (3, 2560), (16, 2560), (4, 3584), (2, 4096), (1, 6912), (5, 9728),        # a workgroup per row
-    (2, 16384), (3, 16320),
+    (3, 1280), (1, 2048), (257, 1280), (100, 576),
+    (3, 2560), (16, 2560), (4, 3584), (1, 4096), (3, 6144), (1, 6912), (5, 8192),        # two per row
+    (5, 9728), (2, 16384), (3, 16320),                                                   # four per row
     (1, 20480), (2, 65536), (1, 65344),                                                  # 1024 threads
-    (257, 1280), (100, 576),
 ])
 def test_codes_match_oracle(t, k):
     say(f"[case] act_quant_h4 t={t} k={k} block={oh.block_size(k)}")
