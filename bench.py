@@ -660,6 +660,93 @@ def decode_model_view():
     return out
 
 
+def h4_launches(lb, shapes, reps, graph=True):
+    """Average duration of one lowbit_act_quant_h4 launch per [t, k] (and of
+    the int8 quantiser on the same input beside it): `reps` launches back to
+    back, captured in a HIP graph (so that host-side call overhead does not
+    stand in for short kernels) and replayed three times between events on
+    the replaying stream: {(t, k): (h4_s, int8_s)}."""
+    import torch
+    out = {}
+    g = torch.Generator(device="cuda").manual_seed(7)
+    for t, k in shapes:
+        x = torch.randn((t, k), device="cuda", generator=g)
+        q = torch.empty((t, k), dtype=torch.int8, device="cuda")
+        sx = torch.empty(t, device="cuda")
+        res = []
+        for fn in (lb.lowbit_act_quant_h4, lb.lowbit_act_quant):
+            body = (lambda fn=fn: [fn(x, q, sx) for _ in range(reps)])
+            run = (capture(body) if graph else None) or body
+            el, _ = time_steps(run, 3, 1)
+            res.append(el / (3 * reps))
+        out[(t, k)] = tuple(res)
+        del x, q, sx
+    return out
+
+
+def h_bitlinear_view():
+    """H-BitLinear ("Native Binary and Ternary Transformers", 0x07C): the
+    rotated 4-bit quantiser on its own (per launch, against the HBM roofline:
+    4 bytes read and 1 written per element, 4 per row), and the int4 4-bit
+    QAT model's attention-output and FFN-down products at 4096 tokens with
+    that quantiser in place of the int8 one (the rotation's overhead on a
+    layer)."""
+    import torch
+    import workloads
+    lb = __import__("bit_weight_linear_bitlinear_amd")
+    shapes = [(4096, 1280), (4096, 3584), (1, 2560), (1, 9728), (16, 9728)]
+    times = h4_launches(lb, shapes, reps=50)
+    per = {}
+    for (t, k), (th, t8) in times.items():
+        nb = 5 * t * k + 4 * t
+        per[f"t{t}_k{k}"] = {"us": round(th * 1e6, 2), "GBps": round(nb / th / 1e9, 1),
+                             "frac_hbm_peak": round(nb / th / 1e9 / HBM_PEAK_GBS, 4),
+                             "int8_quantiser_us": round(t8 * 1e6, 2), "block": int(k & -k if (k & -k) <= 2048 else 2048)}
+    # the o and down products of layer 0 of the int4 prefill workload
+    wl = workloads.BY_NAME["int4_t4nt"]
+    T = wl.tokens[0]
+    layer = {}
+    for mi in (1, 4):
+        m = wl.matrices[mi]
+        d = lb.lowbit_describe(lb.FORMATS[wl.fmt], lb.SCALES[wl.scale], m.n, m.k, wl.group,
+                               lb.FLAG_TANH3 if wl.tanh_premap else 0)
+        pk = np.empty(d.packed_bytes, np.uint8)
+        sc = np.empty(d.n_scales, np.float32)
+        lb.lowbit_pack(d, workloads.latent_weights(wl.index, 0, mi, m.n, m.k), pk, sc)
+        pk, sc = torch.from_numpy(pk).cuda(), torch.from_numpy(sc).cuda()
+        x = torch.from_numpy(workloads.workload_activations(wl, 0, mi, T, m.k)).cuda()
+        q = torch.empty((T, m.k), dtype=torch.int8, device="cuda")
+        sx = torch.empty(T, device="cuda")
+        y = torch.empty((T, m.n), device="cuda")
+        res = {}
+        for name, quant in (("bitlinear_int8", lb.lowbit_act_quant), ("h_bitlinear_int4", lb.lowbit_act_quant_h4)):
+            def fn(quant=quant):
+                quant(x, q, sx)
+                lb.lowbit_linear_batched(d, pk, sc, q, sx, y)
+            run = capture(fn) or fn
+            el, _ = time_steps(run, 20, 3)
+            res[name] = round(el / 20 * 1e6, 2)
+        res["overhead_pct"] = round(100 * (res["h_bitlinear_int4"] / res["bitlinear_int8"] - 1), 2)
+        layer[f"{m.name}_[{m.n},{m.k}]"] = res
+    out = {"what": "H-BitLinear's rotated INT4 activation quantiser (block Walsh-Hadamard over B = largest "
+                   "power of two dividing k, at most 2048; per-token absmax codes in [-7, 7]); per launch vs "
+                   "the HBM roofline (5 B per element + 4 B per row), and the int4 model's o / down layers "
+                   "at 4096 tokens (quantiser + GEMM, us per layer) with it in place of the int8 quantiser",
+           "kernel": "act_quant_h4_kernel", "per_launch": per, "layers_t4096": layer}
+    log(f"[bench] h-bitlinear: {per}; layers {layer}")
+    return out
+
+
+def h4_profile():
+    """The rotated quantiser's prefill launches only (for profiler runs)."""
+    lb = __import__("bit_weight_linear_bitlinear_amd")
+    times = h4_launches(lb, [(4096, 3584), (4096, 1280)], reps=20, graph=False)
+    for (t, k), (th, _) in times.items():
+        nb = 5 * t * k + 4 * t
+        print(json.dumps({"h4_t": t, "k": k, "us": round(th * 1e6, 2), "GBps": round(nb / th / 1e9, 1),
+                          "bytes_per_launch": nb}), flush=True)
+
+
 def extra_views(args):
     """The other timing views: (iii) the streaming ceiling on one large cold
     matrix, the cache-resident 256-d decode stack at t = 1, and the binary
@@ -741,6 +828,7 @@ def extra_views(args):
     del p1
 
     views["decode_model_t1"] = decode_model_view()
+    views["h_bitlinear"] = h_bitlinear_view()
 
     # the binary 8192-token GEMM pass
     wl2 = workloads.BY_NAME["binary_gqa"]
@@ -777,6 +865,8 @@ def main():
     ap.add_argument("--quick", action="store_true", help="grouped schedule only")
     ap.add_argument("--profile-gemm", action="store_true",
                     help="batched GEMM pass only, with per-shape launch timings (for profiler runs)")
+    ap.add_argument("--profile-h4", action="store_true",
+                    help="the rotated 4-bit quantiser's prefill launches only (for profiler runs)")
     ap.add_argument("--profile-pass", action="store_true",
                     help="copy calibration + grouped GEMV pass only (for profiler runs)")
     args = ap.parse_args()
@@ -797,6 +887,9 @@ def main():
 
     if args.profile_gemm:
         gemm_profile(args)
+        return
+    if args.profile_h4:
+        h4_profile()
         return
 
     # ---- GEMV line: ternary_4b decode pass
