@@ -356,6 +356,46 @@ def per_launch(p: Pass, reps: int):
     return total / (n * reps), sum(p.linear_bytes) / n, sum(p.linear_ops) / n
 
 
+def gemm_shapes_vs_library(p: Pass, reps: int = 10):
+    """Each distinct product shape of a prefill pass as its own launch (one
+    matrix, inputs quantised beforehand, 'reps' launches captured in a HIP
+    graph), next to the ROCm library's plain int8 GEMM (torch._int_mm, int8 x
+    int8 -> int32: unpacked int8 weights, no scales, no fp32 output; launched
+    eagerly, back to back) on the same t, n, k.  Context for the matrix-core
+    fraction, not a parity check."""
+    import torch
+    p.act_quant()
+    torch.cuda.synchronize()
+    seen, rows = set(), []
+    g = torch.Generator(device="cuda").manual_seed(11)
+    for i, (_, _, m) in enumerate(p.mats):
+        if (m.n, m.k) in seen:
+            continue
+        seen.add((m.n, m.k))
+        d, (q, sx) = p.desc[i], p.views[i]
+        ops = 2 * p.t * m.n * m.k
+        body = (lambda i=i, d=d, q=q, sx=sx: [p.fn(d, p.packed[i], p.scales[i], q, sx, p.y[i]) for _ in range(reps)])
+        el, _ = time_steps(capture(body) or body, 3, 1)
+        ours = el / (3 * reps)
+        a = torch.randint(-127, 128, (p.t, m.k), dtype=torch.int8, device="cuda", generator=g)
+        b = torch.randint(-7, 8, (m.n, m.k), dtype=torch.int8, device="cuda", generator=g)
+        lib_us = None
+        try:
+            lbody = (lambda: [torch._int_mm(a, b.t()) for _ in range(reps)])
+            el, _ = time_steps(lbody, 3, 1)      # eager: the library call is not captured
+            lib_us = el / (3 * reps)
+        except Exception as e:   # the library path may be missing on some builds
+            log(f"[bench] torch._int_mm unavailable: {e}")
+        rows.append({"n": m.n, "k": m.k, "t": p.t, "us": round(ours * 1e6, 2),
+                     "TOPS": round(ops / ours / 1e12, 1), "pct_mfma_peak": round(100 * ops / ours / 1e12 / I8_PEAK_TOPS, 2),
+                     "library_int8_us": None if lib_us is None else round(lib_us * 1e6, 2),
+                     "library_int8_pct_mfma_peak": None if lib_us is None else
+                     round(100 * ops / lib_us / 1e12 / I8_PEAK_TOPS, 2)})
+        del a, b
+    log(f"[bench] gemm shapes vs library int8: {rows}")
+    return rows
+
+
 def gemm_profile(args):
     """The int4 prefill pass alone as the bench runs it (one act-quant launch
     per k, equal-k products as grouped launches), then each distinct GEMM
@@ -963,6 +1003,7 @@ def main():
         d4, ops_per_launch = dg, opg                           # the launches the pass runs (grouped)
         tops_launch = ops_per_launch / d4 / 1e12
         chk4 = None if args.skip_check else sampled_check(p4, [0, 1, 4], rows_per=32)
+        shapes4 = gemm_shapes_vs_library(p4)
         # the second roofline of a prefill product: its HBM bytes (fp32 y
         # dominates) at peak bandwidth; the larger of the two floors bounds it
         bytes4 = sum(p4.linear_bytes)
@@ -984,6 +1025,11 @@ def main():
                                     "mfma_floor_us_per_launch": round(floor_mfma / n4 * 1e6, 2),
                                     "hbm_floor_us_per_launch": round(floor_hbm / n4 * 1e6, 2),
                                     "frac_of_larger_floor": round(max(floor_mfma, floor_hbm) / n4 / d4, 4)},
+                       "shapes_vs_library_int8": {
+                           "what": "each distinct shape as its own launch (graph-captured runs), beside the ROCm "
+                                   "library's plain int8 GEMM (torch._int_mm: unpacked int8 weights, int32 output, "
+                                   "no scales) on the same t, n, k",
+                           "shapes": shapes4},
                        "check": chk4}
         log(f"[bench] gemm pass: {ops4 / st4 / 1e12:.1f} TOPS/step; per launch {tops_launch:.1f} TOPS")
         del p4
