@@ -21,6 +21,8 @@ READINGS (the pages leave these open):
 * the activation arithmetic is fp32 in the forward's own order: d =
   fp32(gamma + fp32(eps)), then each code from fp32(fp32(x * 128) / d),
   rounded half to even; s_x = gamma / 128.
+* a row whose gamma is 0 gets zero codes and s_x = 0 also when eps = 0
+  (the forward states that a zero row produces zero codes and output);
 * rows holding NaN or Inf are rejected (zero codes, s_x = NaN, status 1), as
   the int8 quantiser rejects them; so are rows whose max |x| * 128 overflows
   fp32 (status 2).  In per-tensor mode one rejected element rejects the
@@ -91,6 +93,9 @@ def act_quant_v1(x: np.ndarray, per_tensor: bool = False, eps: float = EPS):
     e32 = np.float32(eps)
     for i in range(t):
         if rs[i]:
+            continue
+        if gam[i] == 0:                           # a zero row: zero codes and output (0x02E)
+            sx[i] = np.float32(0)
             continue
         d = np.float32(gam[i] + e32)
         v = (x[i] * np.float32(QB)) / d           # fp32: exact * 128, then one rounded division
