@@ -25,8 +25,10 @@ READINGS (the pages leave these open):
   (the forward states that a zero row produces zero codes and output);
 * rows holding NaN or Inf are rejected (zero codes, s_x = NaN, status 1), as
   the int8 quantiser rejects them; so are rows whose max |x| * 128 overflows
-  fp32 (status 2).  In per-tensor mode one rejected element rejects the
-  tensor: every row gets zero codes and s_x = NaN.
+  fp32 (status 2).  In per-tensor mode the tensor has one scale and one
+  verdict: a non-finite value anywhere rejects every row (status 1), else a
+  128 gamma that overflows does (status 2); rejected rows get zero codes and
+  s_x = NaN.
 * SubLN is LayerNorm without an affine map unless a gain / bias is given:
   (x - mean) / sqrt(var + eps_ln), population variance, eps_ln = 1e-5; here
   in binary64 (it feeds the quantiser through a rounding to fp32).
@@ -84,9 +86,11 @@ def act_quant_v1(x: np.ndarray, per_tensor: bool = False, eps: float = EPS):
         over = finite & ~np.isfinite(amax * np.float32(QB))
     rs[~finite] = 1
     rs[over] = 2
-    if per_tensor:
-        if (rs != 0).any():                       # one bad element rejects the tensor
-            return q, sx, np.where(rs != 0, rs, 1 if (rs == 1).any() else 2).astype(np.int32)
+    if per_tensor:                                # one scale, so one verdict for every row:
+        if (rs == 1).any():                       # non-finite anywhere,
+            return q, sx, np.ones(t, np.int32)
+        if (rs == 2).any():                       # else 128 * gamma overflowing
+            return q, sx, np.full(t, 2, np.int32)
         gam = np.full(t, amax.max() if t else 0, np.float32)
     else:
         gam = amax
