@@ -23,6 +23,7 @@ LIB_PATH = os.path.join(_HERE, "liblowbit.so")
 TERNARY2, BINARY1, INT4 = 0, 1, 2
 SCALE_TENSOR, SCALE_ROW, SCALE_GROUP = 0, 1, 2
 FLAG_TANH3 = 1
+FLAG_CENTERED = 2
 ACT_NONFINITE, ACT_OVERFLOW = 1, 2
 FORMATS = {"ternary": TERNARY2, "binary": BINARY1, "int4": INT4}
 SCALES = {"tensor": SCALE_TENSOR, "row": SCALE_ROW, "group": SCALE_GROUP}
@@ -64,6 +65,10 @@ _lib.lowbit_pack.argtypes = [_D, _P, _P, _P]
 _lib.lowbit_act_quant.argtypes = [_P, _i32, _i32, _P, _P, _P, _P]
 _lib.lowbit_act_quant_h4.argtypes = [_P, _i32, _i32, _P, _P, _P, _P]
 _lib.lowbit_act_quant_h4.restype = _i32
+_lib.lowbit_act_quant_v1.argtypes = [_P, _i32, _i32, ctypes.c_float, _i32, _P, _P, _P, _P, _P]
+_lib.lowbit_act_quant_v1.restype = _i32
+_lib.lowbit_layernorm.argtypes = [_P, _i32, _i32, ctypes.c_float, _P, _P, _P, _P]
+_lib.lowbit_layernorm.restype = _i32
 _lib.lowbit_linear.argtypes = [_D, _P, _P, _P, _P, _i32, _P, _P, _P]
 _lib.lowbit_linear_batched.argtypes = [_D, _P, _P, _P, _P, _i32, _P, _P, _P]
 _PP = ctypes.POINTER(ctypes.c_void_p)
@@ -108,7 +113,8 @@ _lib.lowbit_last_hip_error.restype = ctypes.c_char_p
 for _f in ("lowbit_describe", "lowbit_pack", "lowbit_act_quant", "lowbit_linear", "lowbit_linear_batched"):
     getattr(_lib, _f).restype = _i32
 
-EXPORTS = ("lowbit_describe", "lowbit_pack", "lowbit_act_quant", "lowbit_act_quant_h4", "lowbit_linear",
+EXPORTS = ("lowbit_describe", "lowbit_pack", "lowbit_act_quant", "lowbit_act_quant_h4", "lowbit_act_quant_v1",
+           "lowbit_layernorm", "lowbit_linear",
            "lowbit_linear_batched",
            "lowbit_linear_grouped", "lowbit_linear_batched_grouped", "lowbit_linear_fused",
            "lowbit_linear_grouped_fused",
@@ -187,6 +193,24 @@ def lowbit_act_quant_h4(x, q, sx, status=None, stream=None) -> None:
     t, k = x.shape
     _check(_lib.lowbit_act_quant_h4(_dev(x, "x", 4 * t * k), t, k, _dev(q, "q", t * k), _dev(sx, "sx", 4 * t),
                                     _dev(status, "status", 4), _stream(stream)), "lowbit_act_quant_h4")
+
+
+def lowbit_act_quant_v1(x, q, sx, eps=1e-5, per_tensor=False, status=None, work=None, stream=None) -> None:
+    """Device: the original BitNet's Q_b = 128 codes of x fp32[t, k] -> q
+    int8[t, k] in [-128, 127], sx fp32[t] = gamma / 128; per_tensor needs
+    work, a device uint32[2] (or int32[2]) workspace."""
+    t, k = x.shape
+    _check(_lib.lowbit_act_quant_v1(_dev(x, "x", 4 * t * k), t, k, float(eps), int(bool(per_tensor)),
+                                    _dev(q, "q", t * k), _dev(sx, "sx", 4 * t), _dev(status, "status", 4),
+                                    _dev(work, "work", 8), _stream(stream)), "lowbit_act_quant_v1")
+
+
+def lowbit_layernorm(x, out, eps=1e-5, gain=None, bias=None, stream=None) -> None:
+    """Device: out = LayerNorm(x) per row (fp32), optional gain / bias [d]."""
+    t, d = x.shape
+    _check(_lib.lowbit_layernorm(_dev(x, "x", 4 * t * d), t, d, float(eps), _dev(gain, "gain", 4 * d),
+                                 _dev(bias, "bias", 4 * d), _dev(out, "out", 4 * t * d), _stream(stream)),
+           "lowbit_layernorm")
 
 
 def _linear_ptrs(d, packed, scales, q, sx, y, acc):

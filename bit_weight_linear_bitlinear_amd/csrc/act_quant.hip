@@ -32,9 +32,54 @@ struct ActQuantTable {
     const float* x[kActQuantMaxSrc];
     int8_t* q[kActQuantMaxSrc];
     float* sx[kActQuantMaxSrc];
+    float eps;                    // MODE 1, 2: the encoder epsilon
+    const uint32_t* tensor;       // MODE 2: [0] fp32 bits of the tensor's max |x|, [1] non-finite flag
 };
 
-template <bool VEC>
+// The code rule of a launch (M8.8 "Native Binary and Ternary Transformers"):
+//   MODE 0  the per-token absmax int8 rule of 0x02C / 0x05C: r = 127 / m,
+//           code = clip(rint(x r), -127, 127), s_x = m / 127;
+//   MODE 1  the original BitNet forward of 0x02E, Q_b = 128: d = m + eps,
+//           code = clip(rint((128 x) / d), -128, 127) (one exact multiply and
+//           one IEEE division, in that order), s_x = m / 128; a zero row
+//           codes to 0; a row whose 128 m overflows is rejected;
+//   MODE 2  MODE 1 with the tensor-wide m of a prior reduction.
+// rowdiv() returns the row's flag and sets rr (MODE 0: r; MODE 1, 2: d).
+template <int MODE>
+__device__ __forceinline__ int rowdiv(float m, int bad, float eps, float& rr) {
+    rr = 0.0f;
+    if (bad) return LOWBIT_ACT_NONFINITE;
+    if constexpr (MODE == 0) {
+        if (m > 0.0f) {
+            rr = 127.0f / m;
+            if (!isfinite(rr)) return LOWBIT_ACT_OVERFLOW;
+        }
+    } else {
+        if (!isfinite(m * 128.0f)) return LOWBIT_ACT_OVERFLOW;
+        rr = m + eps;
+    }
+    return 0;
+}
+
+template <int MODE>
+__device__ __forceinline__ int8_t code_of(float v, float rr, float m) {
+    if constexpr (MODE == 0) {
+        return quant1(v, rr);
+    } else {
+        if (m == 0.0f) return 0;
+        float c = rintf((v * 128.0f) / rr);
+        c = c < -128.0f ? -128.0f : (c > 127.0f ? 127.0f : c);
+        return (int8_t)(int)c;
+    }
+}
+
+template <int MODE>
+__device__ __forceinline__ float scale_of(float m) {
+    if constexpr (MODE == 0) return m / 127.0f;
+    else return m / 128.0f;
+}
+
+template <bool VEC, int MODE>
 __global__ __launch_bounds__(256) void act_quant_kernel(const ActQuantTable tab, int k,
                                                         int32_t* __restrict__ status) {
     const float* __restrict__ x = tab.x[blockIdx.y];
@@ -68,15 +113,13 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const ActQuantTable tab,
     }
     m = wave_max(m);
     bad = wave_or(bad);
-
-    float r = 0.0f;
-    int flag = 0;
-    if (bad) {
-        flag = LOWBIT_ACT_NONFINITE;
-    } else if (m > 0.0f) {
-        r = 127.0f / m;
-        if (!isfinite(r)) flag = LOWBIT_ACT_OVERFLOW;
+    if constexpr (MODE == 2) {
+        m = __uint_as_float(tab.tensor[0]);
+        bad = tab.tensor[1] != 0u;
     }
+
+    float r;
+    const int flag = rowdiv<MODE>(m, bad, tab.eps, r);
     if (flag) {   // a rejected row gets zero codes
         if (VEC) {
             uint32_t* q4 = reinterpret_cast<uint32_t*>(qr);
@@ -90,15 +133,17 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const ActQuantTable tab,
         const int k4 = k >> 2;
         for (int i = lane; i < k4; i += 64) {
             float4 v = x4[i];
-            uint32_t p = (uint32_t)(uint8_t)quant1(v.x, r) | ((uint32_t)(uint8_t)quant1(v.y, r) << 8) |
-                         ((uint32_t)(uint8_t)quant1(v.z, r) << 16) | ((uint32_t)(uint8_t)quant1(v.w, r) << 24);
+            uint32_t p = (uint32_t)(uint8_t)code_of<MODE>(v.x, r, m) |
+                         ((uint32_t)(uint8_t)code_of<MODE>(v.y, r, m) << 8) |
+                         ((uint32_t)(uint8_t)code_of<MODE>(v.z, r, m) << 16) |
+                         ((uint32_t)(uint8_t)code_of<MODE>(v.w, r, m) << 24);
             q4[i] = p;
         }
     } else {
-        for (int i = lane; i < k; i += 64) qr[i] = quant1(xr[i], r);
+        for (int i = lane; i < k; i += 64) qr[i] = code_of<MODE>(xr[i], r, m);
     }
     if (lane == 0) {
-        sx[row] = flag ? __builtin_nanf("") : m / 127.0f;
+        sx[row] = flag ? __builtin_nanf("") : scale_of<MODE>(m);
         if (flag && status) atomicOr(status, flag);
     }
 }
@@ -111,7 +156,7 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const ActQuantTable tab,
 // written from the same registers.  All loads of a thread are issued before
 // any is consumed.  Short rows share a wavefront so that a launch is not
 // thousands of nearly idle workgroups.
-template <int TPR, int R>
+template <int TPR, int R, int MODE>
 __global__ __launch_bounds__(256) void act_quant_reg_kernel(const ActQuantTable tab, int k,
                                                             int32_t* __restrict__ status) {
     const float* __restrict__ x = tab.x[blockIdx.y];
@@ -163,14 +208,12 @@ __global__ __launch_bounds__(256) void act_quant_reg_kernel(const ActQuantTable 
         #pragma unroll
         for (int i = 0; i < 4; ++i) { m = red_m[i] > m ? red_m[i] : m; bad |= red_bad[i]; }
     }
-    float r = 0.0f;
-    int flag = 0;
-    if (bad) {
-        flag = LOWBIT_ACT_NONFINITE;
-    } else if (m > 0.0f) {
-        r = 127.0f / m;
-        if (!isfinite(r)) flag = LOWBIT_ACT_OVERFLOW;
+    if constexpr (MODE == 2) {
+        m = __uint_as_float(tab.tensor[0]);
+        bad = tab.tensor[1] != 0u;
     }
+    float r;
+    const int flag = rowdiv<MODE>(m, bad, tab.eps, r);
     uint32_t* q4 = reinterpret_cast<uint32_t*>(q + (size_t)rowc * k);
     #pragma unroll
     for (int i = 0; i < R; ++i) {
@@ -178,15 +221,44 @@ __global__ __launch_bounds__(256) void act_quant_reg_kernel(const ActQuantTable 
         if (idx < k4 && row_ok) {
             uint32_t p = 0u;   // a rejected row gets zero codes
             if (!flag)
-                p = (uint32_t)(uint8_t)quant1(v[i].x, r) | ((uint32_t)(uint8_t)quant1(v[i].y, r) << 8) |
-                    ((uint32_t)(uint8_t)quant1(v[i].z, r) << 16) | ((uint32_t)(uint8_t)quant1(v[i].w, r) << 24);
+                p = (uint32_t)(uint8_t)code_of<MODE>(v[i].x, r, m) |
+                    ((uint32_t)(uint8_t)code_of<MODE>(v[i].y, r, m) << 8) |
+                    ((uint32_t)(uint8_t)code_of<MODE>(v[i].z, r, m) << 16) |
+                    ((uint32_t)(uint8_t)code_of<MODE>(v[i].w, r, m) << 24);
             q4[idx] = p;
         }
     }
     if (sub == 0 && row_ok) {
-        sx[row] = flag ? __builtin_nanf("") : m / 127.0f;
+        sx[row] = flag ? __builtin_nanf("") : scale_of<MODE>(m);
         if (flag && status) atomicOr(status, flag);
     }
+}
+
+// One launch of the rule MODE over the table's n inputs.
+template <int MODE>
+hipError_t launch_table(const ActQuantTable& tab, int n, int t, int k, bool vec, int32_t* status,
+                        hipStream_t stream) {
+    const int k4 = k / 4;
+    if (vec && k4 <= 8 * 8) {
+        act_quant_reg_kernel<8, 8, MODE><<<dim3((unsigned)((t + 31) / 32), n), dim3(256), 0, stream>>>(tab, k, status);
+    } else if (vec && k4 <= 16 * 8) {
+        act_quant_reg_kernel<16, 8, MODE><<<dim3((unsigned)((t + 15) / 16), n), dim3(256), 0, stream>>>(tab, k, status);
+    } else if (vec && k4 <= 32 * 8) {
+        act_quant_reg_kernel<32, 8, MODE><<<dim3((unsigned)((t + 7) / 8), n), dim3(256), 0, stream>>>(tab, k, status);
+    } else if (vec && k4 <= 64 * 8) {
+        act_quant_reg_kernel<64, 8, MODE><<<dim3((unsigned)((t + 3) / 4), n), dim3(256), 0, stream>>>(tab, k, status);
+    } else if (vec && k4 <= 256 * 4) {
+        act_quant_reg_kernel<256, 4, MODE><<<dim3((unsigned)t, n), dim3(256), 0, stream>>>(tab, k, status);
+    } else if (vec && k4 <= 256 * 16) {
+        act_quant_reg_kernel<256, 16, MODE><<<dim3((unsigned)t, n), dim3(256), 0, stream>>>(tab, k, status);
+    } else {
+        dim3 grid((unsigned)((t + kActWaves - 1) / kActWaves), n), block(256);
+        if (vec)
+            act_quant_kernel<true, MODE><<<grid, block, 0, stream>>>(tab, k, status);
+        else
+            act_quant_kernel<false, MODE><<<grid, block, 0, stream>>>(tab, k, status);
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_act_quant_group(const float* const* x, int8_t* const* q, float* const* sx, int count, int t,
@@ -202,30 +274,24 @@ hipError_t launch_act_quant_group(const float* const* x, int8_t* const* q, float
             tab.sx[i] = sx[b + i];
             vec = vec && (uintptr_t)x[b + i] % 16 == 0 && (uintptr_t)q[b + i] % 4 == 0;
         }
-        const int k4 = k / 4;
-        if (vec && k4 <= 8 * 8) {
-            act_quant_reg_kernel<8, 8><<<dim3((unsigned)((t + 31) / 32), n), dim3(256), 0, stream>>>(tab, k, status);
-        } else if (vec && k4 <= 16 * 8) {
-            act_quant_reg_kernel<16, 8><<<dim3((unsigned)((t + 15) / 16), n), dim3(256), 0, stream>>>(tab, k, status);
-        } else if (vec && k4 <= 32 * 8) {
-            act_quant_reg_kernel<32, 8><<<dim3((unsigned)((t + 7) / 8), n), dim3(256), 0, stream>>>(tab, k, status);
-        } else if (vec && k4 <= 64 * 8) {
-            act_quant_reg_kernel<64, 8><<<dim3((unsigned)((t + 3) / 4), n), dim3(256), 0, stream>>>(tab, k, status);
-        } else if (vec && k4 <= 256 * 4) {
-            act_quant_reg_kernel<256, 4><<<dim3((unsigned)t, n), dim3(256), 0, stream>>>(tab, k, status);
-        } else if (vec && k4 <= 256 * 16) {
-            act_quant_reg_kernel<256, 16><<<dim3((unsigned)t, n), dim3(256), 0, stream>>>(tab, k, status);
-        } else {
-            dim3 grid((unsigned)((t + kActWaves - 1) / kActWaves), n), block(256);
-            if (vec)
-                act_quant_kernel<true><<<grid, block, 0, stream>>>(tab, k, status);
-            else
-                act_quant_kernel<false><<<grid, block, 0, stream>>>(tab, k, status);
-        }
-        hipError_t e = hipGetLastError();
+        hipError_t e = launch_table<0>(tab, n, t, k, vec, status, stream);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+hipError_t launch_act_quant_v1(const float* x, int t, int k, float eps, const uint32_t* tensor, int8_t* q,
+                               float* sx, int32_t* status, hipStream_t stream) {
+    ActQuantTable tab{};
+    tab.t = t;
+    tab.x[0] = x;
+    tab.q[0] = q;
+    tab.sx[0] = sx;
+    tab.eps = eps;
+    tab.tensor = tensor;
+    const bool vec = k % 4 == 0 && (uintptr_t)x % 16 == 0 && (uintptr_t)q % 4 == 0;
+    return tensor ? launch_table<2>(tab, 1, t, k, vec, status, stream)
+                  : launch_table<1>(tab, 1, t, k, vec, status, stream);
 }
 
 hipError_t launch_act_quant(const float* x, int t, int k, int8_t* q, float* sx, int32_t* status,

@@ -54,6 +54,14 @@ constexpr int kH4MaxK = 65536;
 int h4_block(int k);
 hipError_t launch_act_quant_h4(const float* x, int t, int k, int8_t* q, float* sx, int32_t* status,
                                hipStream_t stream);
+// the original BitNet forward's pieces: Q_b = 128 codes with the encoder
+// epsilon, per token (tensor == nullptr) or with the tensor-wide max a prior
+// launch_tensor_absmax left in tensor[0..1]; the sub-layer LayerNorm
+hipError_t launch_act_quant_v1(const float* x, int t, int k, float eps, const uint32_t* tensor, int8_t* q,
+                               float* sx, int32_t* status, hipStream_t stream);
+hipError_t launch_tensor_absmax(const float* x, int64_t n, uint32_t* work, hipStream_t stream);
+hipError_t launch_layernorm(const float* x, int t, int d, float eps, const float* g, const float* b, float* out,
+                            hipStream_t stream);
 hipError_t launch_gemv(const LinearArgs& a, hipStream_t stream);
 // several matrices of equal fmt / scale mode / group / k and t <= 16 in one launch
 hipError_t launch_gemv_group(const LinearArgs* mats, int count, hipStream_t stream);

@@ -9,6 +9,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstring>
+#include <limits>
 #include <thread>
 #include <vector>
 
@@ -40,7 +41,8 @@ lowbit_status fill_desc(int32_t format, int32_t scale, int32_t n, int32_t k, int
     if (format < LOWBIT_TERNARY2 || format > LOWBIT_INT4) return LOWBIT_E_ARG;
     if (scale < LOWBIT_SCALE_TENSOR || scale > LOWBIT_SCALE_GROUP) return LOWBIT_E_ARG;
     if (n < 1 || k < 1) return LOWBIT_E_ARG;
-    if ((flags & ~LOWBIT_FLAG_TANH3) != 0) return LOWBIT_E_ARG;
+    if ((flags & ~(LOWBIT_FLAG_TANH3 | LOWBIT_FLAG_CENTERED)) != 0) return LOWBIT_E_ARG;
+    if ((flags & LOWBIT_FLAG_CENTERED) && format != LOWBIT_BINARY1) return LOWBIT_E_ARG;
     if (scale == LOWBIT_SCALE_GROUP) {
         const int32_t step = block_k(format);
         if (group < step || group % step != 0) return LOWBIT_E_ARG;
@@ -99,9 +101,19 @@ float domain_scale(int32_t fmt, int64_t count, Get get) {
     return (float)(total / (double)count);
 }
 
-// One code from a (premapped) weight and its domain scale.
-inline int code_of(int32_t fmt, float v, float s) {
-    if (fmt == LOWBIT_BINARY1) return v >= 0.0f ? 1 : -1;
+// Mean of one domain (the centered binary rule's threshold, M8.8 0x02B):
+// binary64 sum in ascending order / count, rounded once.
+template <class Get>
+float domain_mean(int64_t count, Get get) {
+    double total = 0.0;
+    for (int64_t i = 0; i < count; ++i) total += (double)get(i);
+    return (float)(total / (double)count);
+}
+
+// One code from a (premapped) weight, its domain scale and, for centered
+// binary codes, the domain mean (a NaN threshold otherwise).
+inline int code_of(int32_t fmt, float v, float s, float centre) {
+    if (fmt == LOWBIT_BINARY1) return centre == centre ? (v > centre ? 1 : -1) : (v >= 0.0f ? 1 : -1);
     if (s == 0.0f) return 0;
     const float lim = fmt == LOWBIT_INT4 ? 7.0f : 1.0f;
     float r = std::rint(v / s);
@@ -114,6 +126,7 @@ struct RowPacker {
     uint8_t* packed;
     float* scales;
     float tensor_scale;
+    float tensor_mean;   // centered binary, tensor domain; NaN when unused
     std::atomic<int>* bad;
 
     void operator()(int64_t r0, int64_t r1) const {
@@ -129,15 +142,19 @@ struct RowPacker {
             }
             // scale domains of this row
             const int64_t span = d.scale == LOWBIT_SCALE_GROUP ? d.group : K;
+            const bool centered = (d.flags & LOWBIT_FLAG_CENTERED) != 0;
             for (int64_t c0 = 0, gi = 0; c0 < K; c0 += span, ++gi) {
                 const int64_t c1 = std::min(K, c0 + span);
-                float s = tensor_scale;
+                float s = tensor_scale, centre = tensor_mean;
                 if (d.scale != LOWBIT_SCALE_TENSOR) {
-                    s = domain_scale(d.format, c1 - c0, [&](int64_t i) { return row[(size_t)(c0 + i)]; });
+                    auto get = [&](int64_t i) { return row[(size_t)(c0 + i)]; };
+                    s = domain_scale(d.format, c1 - c0, get);
+                    if (centered) centre = domain_mean(c1 - c0, get);
                     if (d.scale == LOWBIT_SCALE_ROW) scales[r] = s;
                     else scales[((r / 16) * d.n_groups + gi) * 16 + r % 16] = s;   // [tile][group][16]
                 }
-                for (int64_t c = c0; c < c1; ++c) codes[(size_t)c] = (int8_t)code_of(d.format, row[(size_t)c], s);
+                for (int64_t c = c0; c < c1; ++c)
+                    codes[(size_t)c] = (int8_t)code_of(d.format, row[(size_t)c], s, centre);
             }
             emit_row(r, codes.data());
         }
@@ -527,11 +544,13 @@ lowbit_status lowbit_pack(const lowbit_desc* d, const float* w, uint8_t* packed,
     const int64_t N = d->n, K = d->k;
     const bool tanh3 = (d->flags & LOWBIT_FLAG_TANH3) != 0;
 
-    float tensor_scale = 0.0f;
+    float tensor_scale = 0.0f, tensor_mean = std::numeric_limits<float>::quiet_NaN();
     if (d->scale == LOWBIT_SCALE_TENSOR) {   // one sequential pass over all of W
         for (int64_t i = 0; i < N * K; ++i)
             if (!std::isfinite(w[i])) return LOWBIT_E_NONFINITE;
-        tensor_scale = domain_scale(d->format, N * K, [&](int64_t i) { return premapped(w[i], tanh3); });
+        auto get = [&](int64_t i) { return premapped(w[i], tanh3); };
+        tensor_scale = domain_scale(d->format, N * K, get);
+        if (d->flags & LOWBIT_FLAG_CENTERED) tensor_mean = domain_mean(N * K, get);
         scales[0] = tensor_scale;
     }
 
@@ -539,7 +558,7 @@ lowbit_status lowbit_pack(const lowbit_desc* d, const float* w, uint8_t* packed,
     if (d->scale == LOWBIT_SCALE_GROUP) std::memset(scales, 0, (size_t)d->n_scales * sizeof(float));
 
     std::atomic<int> bad{0};
-    RowPacker job{*d, w, packed, scales, tensor_scale, &bad};
+    RowPacker job{*d, w, packed, scales, tensor_scale, tensor_mean, &bad};
     const int64_t work = N * K;
     unsigned hw = std::max(1u, std::thread::hardware_concurrency());
     unsigned nthreads = (unsigned)std::min<int64_t>({(int64_t)hw, N, std::max<int64_t>(1, work / (1 << 16))});
@@ -561,6 +580,30 @@ lowbit_status lowbit_act_quant(const float* x, int32_t t, int32_t k, int8_t* q, 
     if (!x || !q || !sx || t < 1 || k < 1) return LOWBIT_E_ARG;
     clear_hip_error();
     return hip_status(lowbit::launch_act_quant(x, t, k, q, sx, status, (hipStream_t)hip_stream));
+}
+
+lowbit_status lowbit_act_quant_v1(const float* x, int32_t t, int32_t k, float eps, int32_t per_tensor, int8_t* q,
+                                  float* sx, int32_t* status, uint32_t* work, void* hip_stream) {
+    if (!x || !q || !sx || t < 1 || k < 1 || !(eps >= 0.0f) || !std::isfinite(eps)) return LOWBIT_E_ARG;
+    if (per_tensor != 0 && per_tensor != 1) return LOWBIT_E_ARG;
+    if (per_tensor && (!work || (uintptr_t)work % 4)) return LOWBIT_E_ARG;
+    if ((uintptr_t)x % 4 || (uintptr_t)sx % 4 || (uintptr_t)status % 4) return LOWBIT_E_ARG;
+    if (k > 262143) return LOWBIT_E_RANGE;
+    clear_hip_error();
+    hipStream_t st = (hipStream_t)hip_stream;
+    if (per_tensor) {
+        hipError_t e = lowbit::launch_tensor_absmax(x, (int64_t)t * k, work, st);
+        if (e != hipSuccess) return hip_status(e);
+    }
+    return hip_status(lowbit::launch_act_quant_v1(x, t, k, eps, per_tensor ? work : nullptr, q, sx, status, st));
+}
+
+lowbit_status lowbit_layernorm(const float* x, int32_t t, int32_t d, float eps, const float* g, const float* b,
+                               float* out, void* hip_stream) {
+    if (!x || !out || t < 1 || d < 1 || !(eps >= 0.0f) || !std::isfinite(eps)) return LOWBIT_E_ARG;
+    if ((uintptr_t)x % 4 || (uintptr_t)out % 4 || (uintptr_t)g % 4 || (uintptr_t)b % 4) return LOWBIT_E_ARG;
+    clear_hip_error();
+    return hip_status(lowbit::launch_layernorm(x, t, d, eps, g, b, out, (hipStream_t)hip_stream));
 }
 
 lowbit_status lowbit_act_quant_h4(const float* x, int32_t t, int32_t k, int8_t* q, float* sx, int32_t* status,

@@ -86,7 +86,9 @@ typedef enum lowbit_scale {
 } lowbit_scale;
 
 /* lowbit_desc.flags */
-#define LOWBIT_FLAG_TANH3 1  /* lowbit_pack maps w -> 3 tanh(w / 3) first (T4NT soft clipping) */
+#define LOWBIT_FLAG_TANH3 1     /* lowbit_pack maps w -> 3 tanh(w / 3) first (T4NT soft clipping) */
+#define LOWBIT_FLAG_CENTERED 2  /* binary only: code = +1 where w > mean of the scale domain, else -1
+                                   (the original BitNet's centered sign, M8.8 0x02B) */
 
 /* lowbit_act_quant *status bits */
 #define LOWBIT_ACT_NONFINITE 1   /* some row held NaN or Inf */
@@ -114,7 +116,7 @@ typedef struct lowbit_desc {
  *   group: group mode needs a positive multiple of 64 (ternary, int4) or of
  *          128 (binary) - the k-extent of one matrix-core step of the kernels;
  *          it must be 0 otherwise.
- *   flags: LOWBIT_FLAG_TANH3 or 0.
+ *   flags: LOWBIT_FLAG_TANH3, LOWBIT_FLAG_CENTERED (binary only), both or 0.
  * Errors: LOWBIT_E_ARG for any invalid field or a null `out`;
  *         LOWBIT_E_RANGE when k exceeds lowbit_max_k(format).
  */
@@ -130,7 +132,10 @@ lowbit_status lowbit_describe(int32_t format, int32_t scale, int32_t n, int32_t 
  *   ternary: s = mean |w| (binary64 sum in ascending index order / count,
  *            rounded once to fp32); code = clip(rint(w / s), -1, 1) in fp32
  *            with ties to even; a zero domain gets s = 0 and codes 0.
- *   binary : s = mean |w| as above; code = +1 if w >= 0 (either zero) else -1.
+ *   binary : s = mean |w| as above; code = +1 if w >= 0 (either zero) else -1;
+ *            with LOWBIT_FLAG_CENTERED, code = +1 if w > a else -1 (a tie
+ *            goes to -1), a = the domain's mean (binary64 sum in ascending
+ *            index order / count, rounded once to fp32), compared in fp32.
  *   int4   : s = max |w| / 7 in fp32; code = clip(rint(w / s), -7, 7).
  *   LOWBIT_FLAG_TANH3 first maps w -> fp32(3 tanh(w / 3)) (binary64 tanh).
  * Runs on host threads; reads and writes host memory only.
@@ -179,6 +184,46 @@ lowbit_status lowbit_act_quant(const float* x, int32_t t, int32_t k, int8_t* q, 
  */
 lowbit_status lowbit_act_quant_h4(const float* x, int32_t t, int32_t k, int8_t* q, float* sx,
                                   int32_t* status, void* hip_stream);
+
+/*
+ * lowbit_act_quant_v1 - the original BitNet forward's activation codes (M8.8
+ * "Native Binary and Ternary Transformers", 0x02C and the forward of 0x02E),
+ * Q_b = 128, for the normalised input x (lowbit_layernorm):
+ *   gamma  = max |x| over the token row (per_tensor = 0, the inference rule)
+ *            or over all of x (per_tensor = 1, the training rule)
+ *   q      = clip(rint((128 x) / (gamma + eps)), -128, 127): an exact
+ *            multiply, then one IEEE fp32 division by fp32(gamma + eps),
+ *            ties to even; a row with gamma = 0 gets zero codes
+ *   sx     = gamma / 128 (fp32), so that lowbit_linear / lowbit_linear_batched
+ *            on (q, sx) yield y = acc * s_w * gamma / 128, the forward's rescale
+ *   x      device float [t, k]
+ *   q      device int8  [t, k]  out        sx device float [t]  out
+ *   eps    >= 0, finite (the forward's default is 1e-5)
+ *   status device int32 [1] or NULL: LOWBIT_ACT_* bits ORed in.  A row holding
+ *          NaN / Inf, or whose 128 gamma overflows fp32, gets zero codes and
+ *          sx = NaN; with per_tensor = 1 such a value anywhere rejects every row.
+ *   work   device uint32 [2], 4-byte aligned, required when per_tensor = 1
+ *          (the tensor-wide max is reduced into it; its contents on entry do
+ *          not matter), ignored otherwise.  Concurrent calls need their own.
+ *   t >= 1; 1 <= k <= 262143: the codes reach -128, and the products' int32
+ *   sums stay exact for k * 128 * 64 < 2^31 with binary or ternary weights
+ *   (k <= 149796 with int4 weights).
+ * Errors: LOWBIT_E_ARG (null or misaligned pointer, bad t / eps / per_tensor,
+ *         per_tensor without work), LOWBIT_E_RANGE (k > 262143), LOWBIT_E_HIP.
+ */
+lowbit_status lowbit_act_quant_v1(const float* x, int32_t t, int32_t k, float eps, int32_t per_tensor, int8_t* q,
+                                  float* sx, int32_t* status, uint32_t* work, void* hip_stream);
+
+/*
+ * lowbit_layernorm - the sub-layer LayerNorm ahead of the original BitNet's
+ * quantiser (M8.8 0x02E, 0x03A): per row of t, out = (x - mean) /
+ * sqrt(var + eps) [* g] [+ b], population variance, fp32 sums.
+ *   x, out device float [t, d] (may be the same buffer); g, b device float [d]
+ *   or NULL; 1 <= d, eps >= 0 finite.
+ * Errors: LOWBIT_E_ARG, LOWBIT_E_HIP.
+ */
+lowbit_status lowbit_layernorm(const float* x, int32_t t, int32_t d, float eps, const float* g, const float* b,
+                               float* out, void* hip_stream);
 
 /*
  * lowbit_linear - decode-shaped product (GEMV), tuned for t <= 16 and correct

@@ -245,3 +245,57 @@ def test_act_quant_h4_rejects_bad_arguments_on_the_host():
     assert lib.lowbit_act_quant_h4(x, 1, 256, ctypes.c_void_p((2 << 20) + 2), sx, None, None) == 1
     assert lib.lowbit_act_quant_h4(None, 1, 256, q, sx, None, None) == 1
     assert lib.lowbit_act_quant_h4(x, 1, 65536 + 64, q, sx, None, None) == 2   # LOWBIT_E_RANGE
+
+
+def _pack_centered_oracle(w, scale, group=0):
+    """Centered binary codes of the BitNet v1 oracle, packed by the main
+    oracle; the scales are the binary rule's mean |w|, unchanged by centering."""
+    from oracle import bitnet_v1
+    n, k = w.shape
+    codes = bitnet_v1.centered_binary_codes(w, scale, group)
+    _, natural = oracle.weight_codes(w, "binary", scale, group)
+    return oracle.pack(codes, "binary"), oracle.pack_scales(natural, scale, n, k, group)
+
+
+@pytest.mark.parametrize("scale", ["tensor", "row", "group"])
+def test_host_pack_centered_matches_oracle(scale):
+    """LOWBIT_FLAG_CENTERED: the packed bytes of the original BitNet's
+    centered signs (ties to -1) and the mean |w| scales, against the oracle,
+    on shifted weights (mean 0.05) where the plain rule would differ."""
+    group = 128 if scale == "group" else 0
+    for seed, (n, k) in enumerate([(1, 1), (3, 5), (17, 300), (33, 257), (64, 768)]):
+        w, _ = workloads.random_case(seed, n, k, 1)
+        w = (w + np.float32(0.05)).astype(np.float32)
+        w[0, 0] = np.float32(0.05)
+        d = lb.lowbit_describe(lb.BINARY1, lb.SCALES[scale], n, k, group, lb.FLAG_CENTERED)
+        p1 = np.empty(d.packed_bytes, np.uint8)
+        s1 = np.empty(d.n_scales, np.float32)
+        lb.lowbit_pack(d, w, p1, s1)
+        p2, s2 = _pack_centered_oracle(w, scale, group)
+        assert (p1 == p2).all() and (s1.view(np.uint32) == s2.view(np.uint32)).all(), (scale, n, k)
+    plain = _pack_lib(w, "binary", scale, group)[0]
+    assert (plain != p1).any()                              # centering changed some codes
+
+
+def test_centered_flag_is_binary_only():
+    for fmt in (lb.TERNARY2, lb.INT4):
+        with pytest.raises(lb.LowbitError):
+            lb.lowbit_describe(fmt, lb.SCALE_ROW, 16, 64, 0, lb.FLAG_CENTERED)
+    with pytest.raises(lb.LowbitError):
+        lb.lowbit_describe(lb.BINARY1, lb.SCALE_ROW, 16, 64, 0, 4)
+
+
+def test_v1_quantiser_and_layernorm_reject_bad_arguments_on_the_host():
+    lib = lb.raw_library()
+    x, q, sx, w = (ctypes.c_void_p(a << 20) for a in (1, 2, 3, 4))   # never dereferenced
+    assert lib.lowbit_act_quant_v1(x, 1, 64, ctypes.c_float(1e-5), 1, q, sx, None, None, None) == 1   # no work
+    assert lib.lowbit_act_quant_v1(x, 1, 64, ctypes.c_float(-1.0), 0, q, sx, None, None, None) == 1
+    assert lib.lowbit_act_quant_v1(x, 1, 64, ctypes.c_float(float("nan")), 0, q, sx, None, None, None) == 1
+    assert lib.lowbit_act_quant_v1(x, 1, 64, ctypes.c_float(1e-5), 2, q, sx, None, w, None) == 1
+    assert lib.lowbit_act_quant_v1(x, 0, 64, ctypes.c_float(1e-5), 0, q, sx, None, None, None) == 1
+    assert lib.lowbit_act_quant_v1(x, 1, 262144, ctypes.c_float(1e-5), 0, q, sx, None, None, None) == 2
+    assert lib.lowbit_act_quant_v1(x, 1, 64, ctypes.c_float(1e-5), 1, q, sx, None,
+                                   ctypes.c_void_p((4 << 20) + 2), None) == 1                   # misaligned work
+    assert lib.lowbit_layernorm(x, 1, 0, ctypes.c_float(1e-5), None, None, q, None) == 1
+    assert lib.lowbit_layernorm(x, 1, 64, ctypes.c_float(-1e-5), None, None, q, None) == 1
+    assert lib.lowbit_layernorm(None, 1, 64, ctypes.c_float(1e-5), None, None, q, None) == 1
