@@ -777,6 +777,71 @@ def h_bitlinear_view():
     return out
 
 
+def bitnet_v1_view():
+    """The original BitNet forward ("Native Binary and Ternary Transformers",
+    0x02B-0x02E) on the binary d = 192 model's shapes at 8192 tokens: the
+    sub-layer LayerNorm (8 bytes per element), the Q_b = 128 quantiser per
+    token and per tensor beside the int8 one (5 bytes per element), each
+    launch run 20 times in a captured HIP graph; and the FFN up projection
+    [768, 192] with centered binary weights as LayerNorm + quantiser + GEMM
+    against the int8 quantiser + GEMM."""
+    import torch
+    import workloads
+    lb = __import__("bit_weight_linear_bitlinear_amd")
+    wl = workloads.BY_NAME["binary_gqa"]
+    T = wl.tokens[0]
+    reps = 20
+    out = {"what": " ".join(bitnet_v1_view.__doc__.split()), "tokens": T}
+    g = torch.Generator(device="cuda").manual_seed(5)
+    work = torch.zeros(2, dtype=torch.int32, device="cuda")
+
+    def timed(fn):
+        body = (lambda: [fn() for _ in range(reps)])
+        el, _ = time_steps(capture(body) or body, 3, 1)
+        return el / (3 * reps)
+    for k in (192, 768):
+        x = torch.randn((T, k), device="cuda", generator=g)
+        xn = torch.empty_like(x)
+        q = torch.empty((T, k), dtype=torch.int8, device="cuda")
+        sx = torch.empty(T, device="cuda")
+        res = {"layernorm": timed(lambda: lb.lowbit_layernorm(x, xn)),
+               "v1_per_token": timed(lambda: lb.lowbit_act_quant_v1(x, q, sx)),
+               "v1_per_tensor": timed(lambda: lb.lowbit_act_quant_v1(x, q, sx, per_tensor=True, work=work)),
+               "int8_absmax": timed(lambda: lb.lowbit_act_quant(x, q, sx))}
+        byt = {"layernorm": 8 * T * k}
+        out[f"k{k}"] = {n: {"us": round(v * 1e6, 2),
+                            "GBps": round(byt.get(n, 5 * T * k + 4 * T) / v / 1e9, 1)} for n, v in res.items()}
+        del x, xn, q, sx
+    m = wl.matrices[4]                                       # up [768, 192]
+    w = workloads.latent_weights(wl.index, 0, 4, m.n, m.k)
+    x = torch.from_numpy(workloads.workload_activations(wl, 0, 4, T, m.k)).cuda()
+    xn = torch.empty_like(x)
+    q = torch.empty((T, m.k), dtype=torch.int8, device="cuda")
+    sx = torch.empty(T, device="cuda")
+    y = torch.empty((T, m.n), device="cuda")
+    layer = {}
+    for name, flags in (("v1_centered", lb.FLAG_CENTERED), ("b1_sign", 0)):
+        d = lb.lowbit_describe(lb.BINARY1, lb.SCALE_ROW, m.n, m.k, 0, flags)
+        pk = np.empty(d.packed_bytes, np.uint8)
+        sc = np.empty(d.n_scales, np.float32)
+        lb.lowbit_pack(d, w, pk, sc)
+        pk, sc = torch.from_numpy(pk).cuda(), torch.from_numpy(sc).cuda()
+        if flags:
+            def fwd(d=d, pk=pk, sc=sc):
+                lb.lowbit_layernorm(x, xn)
+                lb.lowbit_act_quant_v1(xn, q, sx)
+                lb.lowbit_linear_batched(d, pk, sc, q, sx, y)
+        else:
+            def fwd(d=d, pk=pk, sc=sc):
+                lb.lowbit_act_quant(x, q, sx)
+                lb.lowbit_linear_batched(d, pk, sc, q, sx, y)
+        layer[name] = round(timed(fwd) * 1e6, 2)
+    out["up_projection_t8192_us"] = {"layernorm_v1_quant_gemm": layer["v1_centered"],
+                                     "int8_quant_gemm": layer["b1_sign"]}
+    log(f"[bench] bitnet v1: {out}")
+    return out
+
+
 def h4_profile():
     """The rotated quantiser's prefill launches only (for profiler runs)."""
     lb = __import__("bit_weight_linear_bitlinear_amd")
@@ -869,6 +934,7 @@ def extra_views(args):
 
     views["decode_model_t1"] = decode_model_view()
     views["h_bitlinear"] = h_bitlinear_view()
+    views["bitnet_v1"] = bitnet_v1_view()
 
     # the binary 8192-token GEMM pass
     wl2 = workloads.BY_NAME["binary_gqa"]

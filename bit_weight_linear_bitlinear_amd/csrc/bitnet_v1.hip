@@ -9,9 +9,9 @@
 // the existing GEMV / GEMM; here are
 //  - the tensor-wide max |x| for the per-tensor rule: a workspace is cleared
 //    by a one-wavefront kernel (not a memset, so a captured graph replays it),
-//    then every workgroup reduces a grid-strided share and merges it with one
-//    atomicMax on the fp32 bits (|x| >= 0 orders like its bits) and one
-//    atomicOr of a non-finite flag;
+//    then each of at most 512 workgroups reduces a grid-strided share and
+//    merges it with one atomicMax on the fp32 bits (|x| >= 0 orders like its
+//    bits) and one atomicOr of a non-finite flag;
 //  - LayerNorm without (or with) an affine map: a wavefront per row, fp32
 //    sums reduced across lanes, mean first, then the centred second moment.
 #include <math.h>
@@ -49,9 +49,17 @@ __global__ __launch_bounds__(256) void tensor_absmax_kernel(const float* __restr
             m = fmaxf(m, fabsf(v));
         }
     }
+    // one atomic per workgroup: the wavefronts' results meet in LDS first
+    // (thousands of atomics on one address serialise at the L2)
+    __shared__ float red_m[4];
+    __shared__ int red_bad[4];
     m = wave_max(m);
     bad = wave_or(bad);
-    if ((threadIdx.x & 63) == 0) {
+    if ((threadIdx.x & 63) == 0) { red_m[threadIdx.x >> 6] = m; red_bad[threadIdx.x >> 6] = bad; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        m = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
+        bad = red_bad[0] | red_bad[1] | red_bad[2] | red_bad[3];
         if (bad) atomicOr(&w[1], 1u);
         atomicMax(&w[0], __float_as_uint(m));
     }
@@ -95,7 +103,7 @@ hipError_t launch_tensor_absmax(const float* x, int64_t n, uint32_t* work, hipSt
     if (e != hipSuccess) return e;
     const bool vec = n % 4 == 0 && (uintptr_t)x % 16 == 0;
     const int64_t items = vec ? n / 4 : n;
-    const unsigned grid = (unsigned)std::min<int64_t>(std::max<int64_t>((items + 255) / 256, 1), 2048);
+    const unsigned grid = (unsigned)std::min<int64_t>(std::max<int64_t>((items + 1023) / 1024, 1), 512);
     if (vec)
         tensor_absmax_kernel<true><<<grid, 256, 0, stream>>>(x, n, work);
     else
