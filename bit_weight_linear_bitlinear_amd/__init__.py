@@ -69,6 +69,8 @@ _lib.lowbit_act_quant_v1.argtypes = [_P, _i32, _i32, ctypes.c_float, _i32, _P, _
 _lib.lowbit_act_quant_v1.restype = _i32
 _lib.lowbit_layernorm.argtypes = [_P, _i32, _i32, ctypes.c_float, _P, _P, _P, _P]
 _lib.lowbit_layernorm.restype = _i32
+_lib.lowbit_onebit_linear.argtypes = [_D, _P, _P, _P, _P, _i32, _P, _P]
+_lib.lowbit_onebit_linear.restype = _i32
 _lib.lowbit_linear.argtypes = [_D, _P, _P, _P, _P, _i32, _P, _P, _P]
 _lib.lowbit_linear_batched.argtypes = [_D, _P, _P, _P, _P, _i32, _P, _P, _P]
 _PP = ctypes.POINTER(ctypes.c_void_p)
@@ -114,7 +116,7 @@ for _f in ("lowbit_describe", "lowbit_pack", "lowbit_act_quant", "lowbit_linear"
     getattr(_lib, _f).restype = _i32
 
 EXPORTS = ("lowbit_describe", "lowbit_pack", "lowbit_act_quant", "lowbit_act_quant_h4", "lowbit_act_quant_v1",
-           "lowbit_layernorm", "lowbit_linear",
+           "lowbit_layernorm", "lowbit_onebit_linear", "lowbit_linear",
            "lowbit_linear_batched",
            "lowbit_linear_grouped", "lowbit_linear_batched_grouped", "lowbit_linear_fused",
            "lowbit_linear_grouped_fused",
@@ -211,6 +213,17 @@ def lowbit_layernorm(x, out, eps=1e-5, gain=None, bias=None, stream=None) -> Non
     _check(_lib.lowbit_layernorm(_dev(x, "x", 4 * t * d), t, d, float(eps), _dev(gain, "gain", 4 * d),
                                  _dev(bias, "bias", 4 * d), _dev(out, "out", 4 * t * d), _stream(stream)),
            "lowbit_layernorm")
+
+
+def lowbit_onebit_linear(d: lowbit_desc, packed, g, h, x, y, stream=None) -> None:
+    """Device: OneBit's projection y fp32[t, n] = h * (fp16(x * g) . S^T) from
+    x fp16[t, k], g fp16[k], h fp16[n] and binary packed signs."""
+    t = x.shape[0]
+    if x.dim() != 2 or x.shape[1] != d.k or x.element_size() != 2 or g.element_size() != 2 or h.element_size() != 2:
+        raise ValueError("onebit: x [t, k], g [k], h [n] must be fp16")
+    _check(_lib.lowbit_onebit_linear(ctypes.byref(d), _dev(packed, "packed", d.packed_bytes), _dev(g, "g", 2 * d.k),
+                                     _dev(h, "h", 2 * d.n), _dev(x, "x", 2 * t * d.k), t, _dev(y, "y", 4 * t * d.n),
+                                     _stream(stream)), "lowbit_onebit_linear")
 
 
 def _linear_ptrs(d, packed, scales, q, sx, y, acc):

@@ -62,6 +62,9 @@ hipError_t launch_act_quant_v1(const float* x, int t, int k, float eps, const ui
 hipError_t launch_tensor_absmax(const float* x, int64_t n, uint32_t* work, hipStream_t stream);
 hipError_t launch_layernorm(const float* x, int t, int d, float eps, const float* g, const float* b, float* out,
                             hipStream_t stream);
+// OneBit's W1A16 projection: y = h * (fp16(x * g) . S^T), signs in the binary layout
+hipError_t launch_onebit(const uint8_t* packed, const uint16_t* g, const uint16_t* h, const uint16_t* x, float* y,
+                         int n, int k, int t, int wpl, int step_k, int n_steps, hipStream_t stream);
 hipError_t launch_gemv(const LinearArgs& a, hipStream_t stream);
 // several matrices of equal fmt / scale mode / group / k and t <= 16 in one launch
 hipError_t launch_gemv_group(const LinearArgs* mats, int count, hipStream_t stream);

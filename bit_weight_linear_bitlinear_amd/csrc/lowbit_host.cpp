@@ -598,6 +598,18 @@ lowbit_status lowbit_act_quant_v1(const float* x, int32_t t, int32_t k, float ep
     return hip_status(lowbit::launch_act_quant_v1(x, t, k, eps, per_tensor ? work : nullptr, q, sx, status, st));
 }
 
+lowbit_status lowbit_onebit_linear(const lowbit_desc* d, const uint8_t* packed, const uint16_t* g, const uint16_t* h,
+                                   const uint16_t* x, int32_t t, float* y, void* hip_stream) {
+    lowbit_status st = check_desc(d);
+    if (st != LOWBIT_OK) return st;
+    if (d->format != LOWBIT_BINARY1 || !packed || !g || !h || !x || !y || t < 1) return LOWBIT_E_ARG;
+    if ((uintptr_t)packed % 16 || (uintptr_t)g % 2 || (uintptr_t)h % 2 || (uintptr_t)x % 2 || (uintptr_t)y % 4)
+        return LOWBIT_E_ARG;
+    clear_hip_error();
+    return hip_status(lowbit::launch_onebit(packed, g, h, x, y, d->n, d->k, t, d->wpl, d->step_k, (int)d->n_steps,
+                                            (hipStream_t)hip_stream));
+}
+
 lowbit_status lowbit_layernorm(const float* x, int32_t t, int32_t d, float eps, const float* g, const float* b,
                                float* out, void* hip_stream) {
     if (!x || !out || t < 1 || d < 1 || !(eps >= 0.0f) || !std::isfinite(eps)) return LOWBIT_E_ARG;

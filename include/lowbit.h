@@ -215,6 +215,28 @@ lowbit_status lowbit_act_quant_v1(const float* x, int32_t t, int32_t k, float ep
                                   float* sx, int32_t* status, uint32_t* work, void* hip_stream);
 
 /*
+ * lowbit_onebit_linear - OneBit's W1A16 projection (M8.8 "Native Binary and
+ * Ternary Transformers", 0x06A): a sign matrix S, an FP16 input vector g and
+ * an FP16 output vector h,
+ *     y[t, n] = h[n] * sum_k S[n, k] * fp16(x[t, k] * g[k])
+ * with fp16 products and fp32 sums on the matrix cores (the sum's order is
+ * the kernel's: y differs from an exact evaluation by fp32 rounding only).
+ * The layer's LayerNorm over n is lowbit_layernorm(y, t, n, ...) after it.
+ *   d       a binary descriptor (LOWBIT_BINARY1, any scale mode; its scales
+ *           are not used); packed from lowbit_pack: S = +1 where w >= 0
+ *           (either zero), else -1
+ *   packed  device uint8 [d->packed_bytes], 16-byte aligned
+ *   g       device fp16 bits [k]      h  device fp16 bits [n]
+ *   x       device fp16 bits [t, k]   (2-byte aligned)
+ *   y       device float [t, n]       out
+ *   t >= 1
+ * Errors: LOWBIT_E_ARG (null or misaligned pointer, t < 1, a descriptor that
+ *         is not binary or does not check out), LOWBIT_E_HIP.
+ */
+lowbit_status lowbit_onebit_linear(const lowbit_desc* d, const uint8_t* packed, const uint16_t* g, const uint16_t* h,
+                                   const uint16_t* x, int32_t t, float* y, void* hip_stream);
+
+/*
  * lowbit_layernorm - the sub-layer LayerNorm ahead of the original BitNet's
  * quantiser (M8.8 0x02E, 0x03A): per row of t, out = (x - mean) /
  * sqrt(var + eps) [* g] [+ b], population variance, fp32 sums.
