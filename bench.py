@@ -38,6 +38,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 I8_PEAK_TOPS = 5000.0          # MI355X dense int8 MFMA, TOPS
+F16_PEAK_TFLOPS = 2500.0       # MI355X dense fp16 / bf16 MFMA, TFLOP/s
 METRIC = "ternary GEMV HBM GB/s (% peak) at batch 1; batched GEMM int8 TOPS (% MFMA peak)"
 
 
@@ -842,6 +843,41 @@ def bitnet_v1_view():
     return out
 
 
+def onebit_view():
+    """OneBit's W1A16 projection ("Native Binary and Ternary Transformers",
+    0x06A): h * (fp16(x * g) . S^T) with 1-bit signs, at the section's
+    N = K = 4096 and the 4B-class shapes; t = 1 against the HBM roofline
+    (n k / 8 bytes of signs + fp16 x, g, h + fp32 y per call), t = 4096
+    against the dense fp16 matrix-core peak.  Launch runs captured in a HIP
+    graph; the LayerNorm after it is the bitnet_v1 view's kernel."""
+    import torch
+    lb = __import__("bit_weight_linear_bitlinear_amd")
+    g = torch.Generator(device="cuda").manual_seed(9)
+    rows = []
+    for n, k, t in ((4096, 4096, 1), (9728, 2560, 1), (2560, 9728, 1), (4096, 4096, 16), (4096, 4096, 4096)):
+        d = lb.lowbit_describe(lb.BINARY1, lb.SCALE_ROW, n, k, 0, 0)
+        packed = torch.randint(0, 256, (d.packed_bytes,), dtype=torch.uint8, device="cuda", generator=g)
+        x = torch.randn((t, k), device="cuda", generator=g).half()
+        gv = (1 + 0.1 * torch.randn(k, device="cuda", generator=g)).half()
+        hv = (0.02 * torch.rand(n, device="cuda", generator=g)).half()
+        y = torch.empty((t, n), device="cuda")
+        reps = 20 if t < 4096 else 5
+        body = (lambda d=d, packed=packed, x=x, gv=gv, hv=hv, y=y:
+                [lb.lowbit_onebit_linear(d, packed, gv, hv, x, y) for _ in range(reps)])
+        el, _ = time_steps(capture(body) or body, 3, 1)
+        dt = el / (3 * reps)
+        nbytes = d.packed_bytes + 2 * t * k + 2 * k + 2 * n + 4 * t * n
+        flops = 2 * t * n * k
+        rows.append({"n": n, "k": k, "t": t, "us": round(dt * 1e6, 2), "GBps": round(nbytes / dt / 1e9, 1),
+                     "frac_hbm_peak": round(nbytes / dt / 1e9 / HBM_PEAK_GBS, 4),
+                     "TFLOPS": round(flops / dt / 1e12, 1),
+                     "frac_fp16_mfma_peak": round(flops / dt / 1e12 / F16_PEAK_TFLOPS, 4)})
+        del packed, x, y
+    out = {"what": " ".join(onebit_view.__doc__.split()), "kernel": "onebit_kernel", "shapes": rows}
+    log(f"[bench] onebit: {rows}")
+    return out
+
+
 def h4_profile():
     """The rotated quantiser's prefill launches only (for profiler runs)."""
     lb = __import__("bit_weight_linear_bitlinear_amd")
@@ -935,6 +971,7 @@ def extra_views(args):
     views["decode_model_t1"] = decode_model_view()
     views["h_bitlinear"] = h_bitlinear_view()
     views["bitnet_v1"] = bitnet_v1_view()
+    views["onebit"] = onebit_view()
 
     # the binary 8192-token GEMM pass
     wl2 = workloads.BY_NAME["binary_gqa"]

@@ -25,10 +25,12 @@
 // halves of the same codes.  Codes past k stage as 0, so the padding signs
 // (+1) add nothing.
 //
-// Work split.  A 256-thread workgroup owns one 16-row tile and 16 tokens;
-// its four wavefronts take every fourth packed k-step, and their fp32
-// partials meet in LDS.  The workgroup stages 1024 codes of x * g at a time
-// (32 KB of LDS, so that several workgroups share a CU).
+// Work split.  A 256-thread workgroup owns 16 tokens and 64 R rows: each
+// wavefront streams R 16-row tiles over all of k (R = 1 at decode, so that
+// small matrices spread over the chip; R = 4 at prefill, so that one staged
+// operand serves 256 rows), reusing each activation operand for its R tiles.
+// x * g of the tile's real tokens is staged up to 32 KB at a time (a decode
+// row of up to 16384 codes in one pass).
 #include <algorithm>
 
 #include "device_common.hpp"
@@ -41,7 +43,7 @@ namespace {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kObChunk = 1024;                    // codes of x * g staged at a time (32 KB)
+constexpr int kObLds = 32768;                     // bytes of staged x * g per workgroup
 
 struct OneBitArgs {
     const uint8_t* packed;
@@ -50,87 +52,129 @@ struct OneBitArgs {
     const uint16_t* x;
     float* y;
     int n, k, t;
-    int wpl, step_k, n_steps;
+    int wpl, step_k, n_steps, n_tiles;
+    int chunk;                                     // codes staged at a time: a multiple of 512
+    int vec;                                       // x and g 16-byte aligned and k % 8 == 0
 };
 
 __device__ __forceinline__ int perm32(int c) {    // staged position of code c of a 32-code chunk
     return c < 16 ? 8 * (c >> 2) + 2 * (c & 3) : 8 * ((c - 16) >> 2) + 2 * (c & 3) + 1;
 }
 
-template <int WPL>
+// R 16-row tiles per wavefront, four wavefronts: 64 R rows x 16 tokens
+template <int WPL, int R>
 __global__ __launch_bounds__(256) void onebit_kernel(const OneBitArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    _Float16* xs = reinterpret_cast<_Float16*>(smem);      // [16 tokens][kObChunk]
+    _Float16* xs = reinterpret_cast<_Float16*>(smem);      // [tokens of this tile][chunk]
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int q = lane >> 4, r = lane & 15;
-    const int tile = blockIdx.x, t0 = blockIdx.y * 16;
-    const int K = a.k, SK = a.step_k;
-    const uint8_t* pk = a.packed + (size_t)tile * a.n_steps * (256 * WPL) + (size_t)(q * 16 + r) * WPL * 4;
+    const int t0 = blockIdx.y * 16, tv = min(16, a.t - t0);   // tokens of this tile
+    const int K = a.k, SK = a.step_k, CH = a.chunk;
+    const int tile0 = (blockIdx.x * 4 + wave) * R;            // this wavefront's first row tile
+    const uint8_t* pk[R];
+    #pragma unroll
+    for (int i = 0; i < R; ++i)
+        pk[i] = a.packed + (size_t)min(tile0 + i, a.n_tiles - 1) * a.n_steps * (256 * WPL) +
+                (size_t)(q * 16 + r) * WPL * 4;
+    const bool x_vec = a.vec != 0;                            // rows of x and g 16-byte aligned
 
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4 acc[R];
+    #pragma unroll
+    for (int i = 0; i < R; ++i) acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     const int kpad = a.n_steps * SK;
-    for (int c0 = 0; c0 < kpad; c0 += kObChunk) {
-        const int cl = min(kObChunk, kpad - c0);           // a multiple of SK (kObChunk is)
-        // stage fp16(x * g) for the 16 tokens, permuted within 32-code chunks
-        for (int e = tid; e < 16 * cl; e += 256) {
-            const int ti = e / cl, kk = e - ti * cl, kg = c0 + kk, tt = t0 + ti;
-            _Float16 v = (_Float16)0.0f;
-            if (tt < a.t && kg < K) {
-                const float xf = (float)__builtin_bit_cast(_Float16, a.x[(size_t)tt * K + kg]);
-                const float gf = (float)__builtin_bit_cast(_Float16, a.g[kg]);
-                v = (_Float16)(xf * gf);                   // exact in fp32, one rounding to fp16
+    for (int c0 = 0; c0 < kpad; c0 += CH) {
+        const int cl = min(CH, kpad - c0);                    // a multiple of SK
+        // stage fp16(x * g) of the real tokens, eight codes per thread and
+        // pass; token rows past t are never staged (their outputs, which
+        // depend only on their own row of the operand, are not stored)
+        const int per_row = cl / 8;
+        for (int e = tid; e < tv * per_row; e += 256) {
+            const int ti = e / per_row, kk = (e - ti * per_row) * 8, kg = c0 + kk;
+            _Float16 v[8];
+            if (x_vec && kg + 8 <= K) {
+                const u32x4 xv = *reinterpret_cast<const u32x4*>(a.x + (size_t)(t0 + ti) * K + kg);
+                const u32x4 gv = *reinterpret_cast<const u32x4*>(a.g + kg);
+                #pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const uint16_t xb = (uint16_t)(xv[j / 2] >> (16 * (j & 1)));
+                    const uint16_t gb = (uint16_t)(gv[j / 2] >> (16 * (j & 1)));
+                    v[j] = (_Float16)((float)__builtin_bit_cast(_Float16, xb) * (float)__builtin_bit_cast(_Float16, gb));
+                }
+            } else {
+                #pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    v[j] = (_Float16)0.0f;                    // codes past k: their +1 signs add nothing
+                    if (kg + j < K)
+                        v[j] = (_Float16)((float)__builtin_bit_cast(_Float16, a.x[(size_t)(t0 + ti) * K + kg + j]) *
+                                          (float)__builtin_bit_cast(_Float16, a.g[kg + j]));
+                }
             }
-            xs[ti * kObChunk + (kk & ~31) + perm32(kk & 31)] = v;
+            _Float16* dst = xs + ti * CH + (kk & ~31);
+            #pragma unroll
+            for (int j = 0; j < 8; ++j) dst[perm32((kk & 31) + j)] = v[j];   // x * g exact in fp32, one rounding
         }
         __syncthreads();
-        const int s_end = c0 / SK + cl / SK;
-        for (int s = c0 / SK + wave; s < s_end; s += 4) {
-            uint32_t w[WPL];
-            if constexpr (WPL == 4) {
-                const u32x4 v = *reinterpret_cast<const u32x4*>(pk + (size_t)s * (256 * WPL));
-                w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
-            } else if constexpr (WPL == 2) {
-                const u32x2 v = *reinterpret_cast<const u32x2*>(pk + (size_t)s * (256 * WPL));
-                w[0] = v[0]; w[1] = v[1];
-            } else {
-                w[0] = *reinterpret_cast<const uint32_t*>(pk + (size_t)s * (256 * WPL));
+        const int s0 = c0 / SK, s1 = s0 + cl / SK;
+        for (int s = s0; s < s1; ++s) {
+            uint32_t w[R][WPL];
+            #pragma unroll
+            for (int i = 0; i < R; ++i) {
+                const uint8_t* p = pk[i] + (size_t)s * (256 * WPL);
+                if constexpr (WPL == 4) {
+                    const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+                    w[i][0] = v[0]; w[i][1] = v[1]; w[i][2] = v[2]; w[i][3] = v[3];
+                } else if constexpr (WPL == 2) {
+                    const u32x2 v = *reinterpret_cast<const u32x2*>(p);
+                    w[i][0] = v[0]; w[i][1] = v[1];
+                } else {
+                    w[i][0] = *reinterpret_cast<const uint32_t*>(p);
+                }
             }
             #pragma unroll
             for (int ww = 0; ww < WPL; ++ww) {
                 // this lane quarter's 32 codes of block ww: k = s SK + 128 ww + 32 q
-                const _Float16* arow = xs + r * kObChunk + (s * SK - c0) + 128 * ww + 32 * q;
+                // (token rows past t read the last staged row: their outputs are dropped)
+                const _Float16* arow = xs + min(r, tv - 1) * CH + (s * SK - c0) + 128 * ww + 32 * q;
                 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
-                    u32x4 b;
-                    #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int c = 4 * m + i;
-                        b[i] = ((w[ww] << (15 - c)) & 0x80008000u) | 0x3C003C00u;
-                    }
                     const half8 av = *reinterpret_cast<const half8*>(arow + 8 * m);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(half8, b), acc, 0, 0, 0);
+                    #pragma unroll
+                    for (int i = 0; i < R; ++i) {
+                        u32x4 b;
+                        #pragma unroll
+                        for (int jj = 0; jj < 4; ++jj) {
+                            const int c = 4 * m + jj;
+                            b[jj] = ((w[i][ww] << (15 - c)) & 0x80008000u) | 0x3C003C00u;
+                        }
+                        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(half8, b), acc[i], 0, 0, 0);
+                    }
                 }
             }
         }
         __syncthreads();                                   // before the next chunk overwrites xs
     }
-    // the four wavefronts' partials: acc element e of lane (q, r) is token
-    // 4q + e of the tile's 16, row r of its 16
-    f32x4* red = reinterpret_cast<f32x4*>(smem);
-    red[wave * 64 + lane] = acc;
-    __syncthreads();
-    if (wave == 0) {
-        const f32x4 s1 = red[64 + lane], s2 = red[128 + lane], s3 = red[192 + lane];
-        const int n = tile * 16 + r;
+    // acc[i] element e of lane (q, r): token 4q + e of the 16, row r of tile tile0 + i
+    #pragma unroll
+    for (int i = 0; i < R; ++i) {
+        const int n = (tile0 + i) * 16 + r;
         if (n < a.n) {
             const float hv = (float)__builtin_bit_cast(_Float16, a.h[n]);
             #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int tt = t0 + 4 * q + e;
-                if (tt < a.t) a.y[(size_t)tt * a.n + n] = (((acc[e] + s1[e]) + s2[e]) + s3[e]) * hv;
+                if (tt < a.t) a.y[(size_t)tt * a.n + n] = acc[i][e] * hv;
             }
         }
+    }
+}
+
+template <int R>
+void launch_r(const OneBitArgs& a, dim3 grid, size_t lds, hipStream_t stream) {
+    switch (a.wpl) {
+        case 4: onebit_kernel<4, R><<<grid, 256, lds, stream>>>(a); break;
+        case 2: onebit_kernel<2, R><<<grid, 256, lds, stream>>>(a); break;
+        default: onebit_kernel<1, R><<<grid, 256, lds, stream>>>(a); break;
     }
 }
 
@@ -138,14 +182,19 @@ __global__ __launch_bounds__(256) void onebit_kernel(const OneBitArgs a) {
 
 hipError_t launch_onebit(const uint8_t* packed, const uint16_t* g, const uint16_t* h, const uint16_t* x, float* y,
                          int n, int k, int t, int wpl, int step_k, int n_steps, hipStream_t stream) {
-    OneBitArgs a{packed, g, h, x, y, n, k, t, wpl, step_k, n_steps};
-    const dim3 grid((unsigned)((n + 15) / 16), (unsigned)((t + 15) / 16));
-    const size_t lds = (size_t)16 * kObChunk * 2;
-    switch (wpl) {
-        case 4: onebit_kernel<4><<<grid, 256, lds, stream>>>(a); break;
-        case 2: onebit_kernel<2><<<grid, 256, lds, stream>>>(a); break;
-        default: onebit_kernel<1><<<grid, 256, lds, stream>>>(a); break;
-    }
+    const int tiles = (n + 15) / 16;
+    const int tv = std::min(t, 16);
+    // staged codes per pass: what 32 KB holds for the tile's tokens, a
+    // multiple of 512 (every k-step size divides it)
+    const int chunk = std::max(512, (kObLds / (2 * tv)) / 512 * 512);
+    const int vec = k % 8 == 0 && (uintptr_t)x % 16 == 0 && (uintptr_t)g % 16 == 0;
+    OneBitArgs a{packed, g, h, x, y, n, k, t, wpl, step_k, n_steps, tiles, chunk, vec};
+    const size_t lds = (size_t)2 * tv * chunk;
+    const unsigned ty = (unsigned)((t + 15) / 16);
+    // prefill: 256 rows per workgroup share the staged operand; decode: 64,
+    // so that small matrices still spread over the chip
+    if (t > 16) launch_r<4>(a, dim3((unsigned)((tiles + 15) / 16), ty), lds, stream);
+    else launch_r<1>(a, dim3((unsigned)((tiles + 3) / 4), ty), lds, stream);
     return hipGetLastError();
 }
 
