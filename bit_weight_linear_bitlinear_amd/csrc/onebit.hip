@@ -26,9 +26,10 @@
 // (+1) add nothing.
 //
 // Work split.  A 256-thread workgroup owns 16 tokens and 64 R rows: each
-// wavefront streams R 16-row tiles over all of k (R = 1 at decode, so that
-// small matrices spread over the chip; R = 4 at prefill, so that one staged
-// operand serves 256 rows), reusing each activation operand for its R tiles.
+// wavefront streams R 16-row tiles over all of k (R = 1 at decode; R = 4 at
+// prefill, so that one staged operand serves 256 rows), reusing each
+// activation operand for its R tiles.  At decode with fewer than 1024 tiles
+// a workgroup instead owns one tile and its wavefronts split k four ways.
 // x * g of the tile's real tokens is staged up to 32 KB at a time (a decode
 // row of up to 16384 codes in one pass).
 #include <algorithm>
@@ -61,8 +62,10 @@ __device__ __forceinline__ int perm32(int c) {    // staged position of code c o
     return c < 16 ? 8 * (c >> 2) + 2 * (c & 3) : 8 * ((c - 16) >> 2) + 2 * (c & 3) + 1;
 }
 
-// R 16-row tiles per wavefront, four wavefronts: 64 R rows x 16 tokens
-template <int WPL, int R>
+// R 16-row tiles per wavefront, four wavefronts: 64 R rows x 16 tokens; or
+// (KS) one 16-row tile per workgroup whose four wavefronts take every fourth
+// k-step, their fp32 partials summed in LDS
+template <int WPL, int R, bool KS>
 __global__ __launch_bounds__(256) void onebit_kernel(const OneBitArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     _Float16* xs = reinterpret_cast<_Float16*>(smem);      // [tokens of this tile][chunk]
@@ -71,7 +74,7 @@ __global__ __launch_bounds__(256) void onebit_kernel(const OneBitArgs a) {
     const int q = lane >> 4, r = lane & 15;
     const int t0 = blockIdx.y * 16, tv = min(16, a.t - t0);   // tokens of this tile
     const int K = a.k, SK = a.step_k, CH = a.chunk;
-    const int tile0 = (blockIdx.x * 4 + wave) * R;            // this wavefront's first row tile
+    const int tile0 = KS ? (int)blockIdx.x : (blockIdx.x * 4 + wave) * R;   // this wavefront's first row tile
     const uint8_t* pk[R];
     #pragma unroll
     for (int i = 0; i < R; ++i)
@@ -116,7 +119,7 @@ __global__ __launch_bounds__(256) void onebit_kernel(const OneBitArgs a) {
         }
         __syncthreads();
         const int s0 = c0 / SK, s1 = s0 + cl / SK;
-        for (int s = s0; s < s1; ++s) {
+        for (int s = s0 + (KS ? wave : 0); s < s1; s += KS ? 4 : 1) {
             uint32_t w[R][WPL];
             #pragma unroll
             for (int i = 0; i < R; ++i) {
@@ -154,6 +157,13 @@ __global__ __launch_bounds__(256) void onebit_kernel(const OneBitArgs a) {
         }
         __syncthreads();                                   // before the next chunk overwrites xs
     }
+    if constexpr (KS) {                                       // the four partials, in wave order
+        f32x4* red = reinterpret_cast<f32x4*>(smem);
+        red[wave * 64 + lane] = acc[0];
+        __syncthreads();
+        if (wave != 0) return;
+        acc[0] = ((acc[0] + red[64 + lane]) + red[128 + lane]) + red[192 + lane];
+    }
     // acc[i] element e of lane (q, r): token 4q + e of the 16, row r of tile tile0 + i
     #pragma unroll
     for (int i = 0; i < R; ++i) {
@@ -169,12 +179,12 @@ __global__ __launch_bounds__(256) void onebit_kernel(const OneBitArgs a) {
     }
 }
 
-template <int R>
+template <int R, bool KS>
 void launch_r(const OneBitArgs& a, dim3 grid, size_t lds, hipStream_t stream) {
     switch (a.wpl) {
-        case 4: onebit_kernel<4, R><<<grid, 256, lds, stream>>>(a); break;
-        case 2: onebit_kernel<2, R><<<grid, 256, lds, stream>>>(a); break;
-        default: onebit_kernel<1, R><<<grid, 256, lds, stream>>>(a); break;
+        case 4: onebit_kernel<4, R, KS><<<grid, 256, lds, stream>>>(a); break;
+        case 2: onebit_kernel<2, R, KS><<<grid, 256, lds, stream>>>(a); break;
+        default: onebit_kernel<1, R, KS><<<grid, 256, lds, stream>>>(a); break;
     }
 }
 
@@ -192,9 +202,11 @@ hipError_t launch_onebit(const uint8_t* packed, const uint16_t* g, const uint16_
     const size_t lds = (size_t)2 * tv * chunk;
     const unsigned ty = (unsigned)((t + 15) / 16);
     // prefill: 256 rows per workgroup share the staged operand; decode: 64,
-    // so that small matrices still spread over the chip
-    if (t > 16) launch_r<4>(a, dim3((unsigned)((tiles + 15) / 16), ty), lds, stream);
-    else launch_r<1>(a, dim3((unsigned)((tiles + 3) / 4), ty), lds, stream);
+    // or one tile with k split four ways when that leaves under 256
+    // workgroups, so that small and short-wide matrices spread over the chip
+    if (t > 16) launch_r<4, false>(a, dim3((unsigned)((tiles + 15) / 16), ty), lds, stream);
+    else if (tiles < 1024) launch_r<1, true>(a, dim3((unsigned)tiles, ty), lds, stream);
+    else launch_r<1, false>(a, dim3((unsigned)((tiles + 3) / 4), ty), lds, stream);
     return hipGetLastError();
 }
 

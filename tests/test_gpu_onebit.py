@@ -41,7 +41,7 @@ def _bound(x, gv, hv, y64, k):
 
 
 @pytest.mark.parametrize("n,k,t", [(2560, 2560, 1), (768, 192, 4), (1000, 1000, 17), (96, 8192, 3), (64, 20000, 2),
-                                   (1000, 1001, 5), (4096, 1024, 300),
+                                   (1000, 1001, 5), (4096, 1024, 300), (16400, 256, 2),
                                    (4096, 4096, 16), (300, 2048, 33), (17, 128, 1)])
 def test_projection_matches_oracle(n, k, t):
     say(f"[case] onebit projection n={n} k={k} t={t}")
