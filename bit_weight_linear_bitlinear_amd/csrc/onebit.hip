@@ -65,14 +65,14 @@ __device__ __forceinline__ int perm32(int c) {    // staged position of code c o
 // R 16-row tiles per wavefront, four wavefronts: 64 R rows x 16 tokens; or
 // (KS) one 16-row tile per workgroup whose four wavefronts take every fourth
 // k-step, their fp32 partials summed in LDS
-template <int WPL, int R, bool KS>
+template <int WPL, int R, bool KS, int TT>
 __global__ __launch_bounds__(256) void onebit_kernel(const OneBitArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     _Float16* xs = reinterpret_cast<_Float16*>(smem);      // [tokens of this tile][chunk]
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int q = lane >> 4, r = lane & 15;
-    const int t0 = blockIdx.y * 16, tv = min(16, a.t - t0);   // tokens of this tile
+    const int t0 = blockIdx.y * 16 * TT, tv = min(16 * TT, a.t - t0);   // tokens of this tile
     const int K = a.k, SK = a.step_k, CH = a.chunk;
     const int tile0 = KS ? (int)blockIdx.x : (blockIdx.x * 4 + wave) * R;   // this wavefront's first row tile
     const uint8_t* pk[R];
@@ -82,9 +82,11 @@ __global__ __launch_bounds__(256) void onebit_kernel(const OneBitArgs a) {
                 (size_t)(q * 16 + r) * WPL * 4;
     const bool x_vec = a.vec != 0;                            // rows of x and g 16-byte aligned
 
-    f32x4 acc[R];
+    f32x4 acc[R][TT];
     #pragma unroll
-    for (int i = 0; i < R; ++i) acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int i = 0; i < R; ++i)
+        #pragma unroll
+        for (int u = 0; u < TT; ++u) acc[i][u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     const int kpad = a.n_steps * SK;
     for (int c0 = 0; c0 < kpad; c0 += CH) {
         const int cl = min(CH, kpad - c0);                    // a multiple of SK
@@ -138,19 +140,25 @@ __global__ __launch_bounds__(256) void onebit_kernel(const OneBitArgs a) {
             for (int ww = 0; ww < WPL; ++ww) {
                 // this lane quarter's 32 codes of block ww: k = s SK + 128 ww + 32 q
                 // (token rows past t read the last staged row: their outputs are dropped)
-                const _Float16* arow = xs + min(r, tv - 1) * CH + (s * SK - c0) + 128 * ww + 32 * q;
+                const int kof = (s * SK - c0) + 128 * ww + 32 * q;
                 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
-                    const half8 av = *reinterpret_cast<const half8*>(arow + 8 * m);
+                    half8 av[TT];
+                    #pragma unroll
+                    for (int u = 0; u < TT; ++u)
+                        av[u] = *reinterpret_cast<const half8*>(xs + min(16 * u + r, tv - 1) * CH + kof + 8 * m);
                     #pragma unroll
                     for (int i = 0; i < R; ++i) {
-                        u32x4 b;
+                        u32x4 b;                                  // decoded once, used by the TT token tiles
                         #pragma unroll
                         for (int jj = 0; jj < 4; ++jj) {
                             const int c = 4 * m + jj;
                             b[jj] = ((w[i][ww] << (15 - c)) & 0x80008000u) | 0x3C003C00u;
                         }
-                        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, __builtin_bit_cast(half8, b), acc[i], 0, 0, 0);
+                        #pragma unroll
+                        for (int u = 0; u < TT; ++u)
+                            acc[i][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[u], __builtin_bit_cast(half8, b),
+                                                                              acc[i][u], 0, 0, 0);
                     }
                 }
             }
@@ -159,32 +167,34 @@ __global__ __launch_bounds__(256) void onebit_kernel(const OneBitArgs a) {
     }
     if constexpr (KS) {                                       // the four partials, in wave order
         f32x4* red = reinterpret_cast<f32x4*>(smem);
-        red[wave * 64 + lane] = acc[0];
+        red[wave * 64 + lane] = acc[0][0];
         __syncthreads();
         if (wave != 0) return;
-        acc[0] = ((acc[0] + red[64 + lane]) + red[128 + lane]) + red[192 + lane];
+        acc[0][0] = ((acc[0][0] + red[64 + lane]) + red[128 + lane]) + red[192 + lane];
     }
-    // acc[i] element e of lane (q, r): token 4q + e of the 16, row r of tile tile0 + i
+    // acc[i][u] element e of lane (q, r): token 16 u + 4q + e, row r of tile tile0 + i
     #pragma unroll
     for (int i = 0; i < R; ++i) {
         const int n = (tile0 + i) * 16 + r;
         if (n < a.n) {
             const float hv = (float)__builtin_bit_cast(_Float16, a.h[n]);
             #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int tt = t0 + 4 * q + e;
-                if (tt < a.t) a.y[(size_t)tt * a.n + n] = acc[i][e] * hv;
-            }
+            for (int u = 0; u < TT; ++u)
+                #pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int tt = t0 + 16 * u + 4 * q + e;
+                    if (tt < a.t) a.y[(size_t)tt * a.n + n] = acc[i][u][e] * hv;
+                }
         }
     }
 }
 
-template <int R, bool KS>
+template <int R, bool KS, int TT>
 void launch_r(const OneBitArgs& a, dim3 grid, size_t lds, hipStream_t stream) {
     switch (a.wpl) {
-        case 4: onebit_kernel<4, R, KS><<<grid, 256, lds, stream>>>(a); break;
-        case 2: onebit_kernel<2, R, KS><<<grid, 256, lds, stream>>>(a); break;
-        default: onebit_kernel<1, R, KS><<<grid, 256, lds, stream>>>(a); break;
+        case 4: onebit_kernel<4, R, KS, TT><<<grid, 256, lds, stream>>>(a); break;
+        case 2: onebit_kernel<2, R, KS, TT><<<grid, 256, lds, stream>>>(a); break;
+        default: onebit_kernel<1, R, KS, TT><<<grid, 256, lds, stream>>>(a); break;
     }
 }
 
@@ -193,20 +203,23 @@ void launch_r(const OneBitArgs& a, dim3 grid, size_t lds, hipStream_t stream) {
 hipError_t launch_onebit(const uint8_t* packed, const uint16_t* g, const uint16_t* h, const uint16_t* x, float* y,
                          int n, int k, int t, int wpl, int step_k, int n_steps, hipStream_t stream) {
     const int tiles = (n + 15) / 16;
-    const int tv = std::min(t, 16);
-    // staged codes per pass: what 32 KB holds for the tile's tokens, a
-    // multiple of 512 (every k-step size divides it)
-    const int chunk = std::max(512, (kObLds / (2 * tv)) / 512 * 512);
+    const bool prefill = t > 16;                   // two 16-token tiles per workgroup
+    const int tv = std::min(t, prefill ? 32 : 16);
+    // staged codes per pass: what the stage (32 KB, 64 KB at prefill) holds
+    // for the tile's tokens, a multiple of 512 (every k-step size divides it)
+    const int budget = prefill ? 2 * kObLds : kObLds;
+    const int chunk = std::max(512, (budget / (2 * tv)) / 512 * 512);
     const int vec = k % 8 == 0 && (uintptr_t)x % 16 == 0 && (uintptr_t)g % 16 == 0;
     OneBitArgs a{packed, g, h, x, y, n, k, t, wpl, step_k, n_steps, tiles, chunk, vec};
     const size_t lds = (size_t)2 * tv * chunk;
-    const unsigned ty = (unsigned)((t + 15) / 16);
-    // prefill: 256 rows per workgroup share the staged operand; decode: 64,
-    // or one tile with k split four ways when that leaves under 256
-    // workgroups, so that small and short-wide matrices spread over the chip
-    if (t > 16) launch_r<4, false>(a, dim3((unsigned)((tiles + 15) / 16), ty), lds, stream);
-    else if (tiles < 1024) launch_r<1, true>(a, dim3((unsigned)tiles, ty), lds, stream);
-    else launch_r<1, false>(a, dim3((unsigned)((tiles + 3) / 4), ty), lds, stream);
+    // prefill: 256 rows and 32 tokens per workgroup, so that one staged
+    // operand serves 256 rows and one decoded sign operand two token tiles;
+    // decode: 64 rows, or one tile with k split four ways when that leaves
+    // under 256 workgroups, so that small and short-wide matrices spread over
+    // the chip
+    if (prefill) launch_r<4, false, 2>(a, dim3((unsigned)((tiles + 15) / 16), (unsigned)((t + 31) / 32)), lds, stream);
+    else if (tiles < 1024) launch_r<1, true, 1>(a, dim3((unsigned)tiles, (unsigned)((t + 15) / 16)), lds, stream);
+    else launch_r<1, false, 1>(a, dim3((unsigned)((tiles + 3) / 4), (unsigned)((t + 15) / 16)), lds, stream);
     return hipGetLastError();
 }
 
