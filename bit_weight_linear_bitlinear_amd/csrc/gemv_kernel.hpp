@@ -371,25 +371,44 @@ __global__ __launch_bounds__(64 * WV) void gemv_kernel(const GemvParams p) {
         #pragma unroll
         for (int r = 0; r < NR; ++r) sxv[r] = st;
     } else if constexpr (LDSA) {
+        // the (token, chunk) space of the stage in batches of SB chunks per
+        // thread, every load of a batch issued before its stores, so that a
+        // thread waits for one L2 round trip per batch, not one per token row
+        constexpr int SB = 4;
+        constexpr int CB = FMT == FMT_BINARY ? 32 : 16;      // codes per chunk
         const int kpad = p.n_steps * SK;
         const int8_t* q = M.q;
-        for (int t = 0; t < T; ++t) {
-            uint8_t* dst = smem + (size_t)t * p.stride;
-            if constexpr (FMT == FMT_BINARY) {
-                // 32-code chunks permuted to the order decode_binary yields
-                for (int c = threadIdx.x; c < kpad / 32; c += NT) {
-                    const i32x4 lo = load_q16(q + (size_t)t * K, 32 * c, K, p.q_vec);
-                    const i32x4 hi = load_q16(q + (size_t)t * K, 32 * c + 16, K, p.q_vec);
-                    const uint32_t X[8] = {(uint32_t)lo[0], (uint32_t)lo[1], (uint32_t)lo[2], (uint32_t)lo[3],
-                                           (uint32_t)hi[0], (uint32_t)hi[1], (uint32_t)hi[2], (uint32_t)hi[3]};
-                    i32x4 a0, a1;
-                    perm_binary_a(X, a0, a1);
-                    *reinterpret_cast<i32x4*>(dst + 32 * c) = a0;
-                    *reinterpret_cast<i32x4*>(dst + 32 * c + 16) = a1;
+        const int per_row = kpad / CB, total = T * per_row;
+        for (int base = threadIdx.x; base < total; base += NT * SB) {
+            i32x4 lo[SB], hi[SB];
+            #pragma unroll
+            for (int b = 0; b < SB; ++b) {
+                const int c = base + b * NT;
+                if (c < total) {
+                    const int t = c / per_row, cc = c - t * per_row;
+                    lo[b] = load_q16(q + (size_t)t * K, CB * cc, K, p.q_vec);
+                    if constexpr (FMT == FMT_BINARY) hi[b] = load_q16(q + (size_t)t * K, CB * cc + 16, K, p.q_vec);
                 }
-            } else {
-                for (int c = threadIdx.x; c < kpad / 16; c += NT)
-                    *reinterpret_cast<i32x4*>(dst + 16 * c) = load_q16(q + (size_t)t * K, 16 * c, K, p.q_vec);
+            }
+            #pragma unroll
+            for (int b = 0; b < SB; ++b) {
+                const int c = base + b * NT;
+                if (c < total) {
+                    const int t = c / per_row, cc = c - t * per_row;
+                    uint8_t* dst = smem + (size_t)t * p.stride + CB * cc;
+                    if constexpr (FMT == FMT_BINARY) {
+                        // 32-code chunks permuted to the order decode_binary yields
+                        const uint32_t X[8] = {(uint32_t)lo[b][0], (uint32_t)lo[b][1], (uint32_t)lo[b][2],
+                                               (uint32_t)lo[b][3], (uint32_t)hi[b][0], (uint32_t)hi[b][1],
+                                               (uint32_t)hi[b][2], (uint32_t)hi[b][3]};
+                        i32x4 a0, a1;
+                        perm_binary_a(X, a0, a1);
+                        *reinterpret_cast<i32x4*>(dst) = a0;
+                        *reinterpret_cast<i32x4*>(dst + 16) = a1;
+                    } else {
+                        *reinterpret_cast<i32x4*>(dst) = lo[b];
+                    }
+                }
             }
         }
         __syncthreads();
