@@ -188,7 +188,7 @@ class Pass:
     def launches(self, calls):
         if self.entry == "gemm":
             return sum((c.count + 23) // 24 for c in calls)
-        return sum((c.count + 39) // 40 * ((c.t + 15) // 16) for c in calls)
+        return sum((c.count + 255) // 256 * ((c.t + 15) // 16) for c in calls)
 
     def step(self, schedule="per_matrix"):
         if schedule in ("grouped_fused", "layer_fused", "layer_dep"):

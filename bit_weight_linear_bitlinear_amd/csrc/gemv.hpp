@@ -7,7 +7,7 @@
 
 namespace lowbit {
 
-constexpr int kGemvMaxMats = 40;     // matrices per launch (kernel-argument space)
+constexpr int kGemvMaxMats = 256;    // matrices per launch (a 17 KB kernel-argument table)
 constexpr int kGemvLdsA = 56 * 1024; // activation bytes a 4-wavefront workgroup may stage in LDS
 constexpr int kGemvLdsWide = 20 * 1024;   // above this stage, 16-wavefront workgroups share it (t > 1)
 constexpr int kGemvLdsMax = 160 * 1024;   // LDS of a CU

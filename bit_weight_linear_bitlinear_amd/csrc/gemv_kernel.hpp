@@ -126,11 +126,15 @@ __global__ __launch_bounds__(64 * WV) void gemv_kernel(const GemvParams p) {
     const int g = lane >> 4;                                 // lane group
     const int rl = lane & 15;                                // weight row in the tile / token of A
 
-    // matrix of this workgroup: one batch of independent scalar loads and
-    // compares (no chain of dependent loads before the first weight load)
-    int mi = 0;
-    #pragma unroll
-    for (int i = 1; i < kGemvMaxMats; ++i) mi += (int)blockIdx.x >= p.wg_start[i] ? 1 : 0;
+    // matrix of this workgroup: a binary search of the ascending workgroup
+    // starts (log2 n_mats dependent scalar loads; a scan of the whole table
+    // cost more than it saved once a launch holds a hundred matrices)
+    int mi = 0, hi = p.n_mats - 1;
+    while (mi < hi) {
+        const int mid = (mi + hi + 1) >> 1;
+        if ((int)blockIdx.x >= p.wg_start[mid]) mi = mid;
+        else hi = mid - 1;
+    }
     const GemvMat& M = p.m[mi];
     const int part = wave & (p.ksplit - 1);
     const int tile_raw = ((int)blockIdx.x - p.wg_start[mi]) * p.tiles_per_wg + (wave >> p.ksplit_log);

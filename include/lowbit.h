@@ -280,7 +280,7 @@ lowbit_status lowbit_linear_batched(const lowbit_desc* d, const uint8_t* packed,
 
 /*
  * lowbit_linear_grouped - `count` independent decode products in as few
- * launches as possible (up to 40 matrices per launch), e.g. the projections
+ * launches as possible (up to 256 matrices per launch), e.g. the projections
  * that read one input (q/k/v, gate/up) or any set of same-width layers whose
  * inputs are ready.  Each matrix i computes exactly what lowbit_linear
  * computes for (descs[i], packed[i], scales[i], q[i], sx[i], t, y[i], acc[i]).
