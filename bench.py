@@ -163,7 +163,7 @@ class Pass:
         layer_dep quantises each call's inputs right before it (what a model
         whose next input is the previous output must do), layer_fused does that
         inside the product kernel.  A prefill pass has the grouped schedule
-        only (lowbit_linear_batched_grouped, 24 products per launch)."""
+        only (lowbit_linear_batched_grouped, 64 products per launch)."""
         self.grouped_calls = [self._grouped(idx) for idx in self.kgroups.values()]
         if self.entry == "gemm":
             return
@@ -187,7 +187,7 @@ class Pass:
 
     def launches(self, calls):
         if self.entry == "gemm":
-            return sum((c.count + 23) // 24 for c in calls)
+            return sum((c.count + 63) // 64 for c in calls)
         return sum((c.count + 255) // 256 * ((c.t + 15) // 16) for c in calls)
 
     def step(self, schedule="per_matrix"):
@@ -1114,7 +1114,7 @@ def main():
         floor_hbm = bytes4 / (HBM_PEAK_GBS * 1e9)
         n4 = p4.launches(p4.grouped_calls)
         out["gemm"] = {"workload": "int4_t4nt prefill pass: 100 int4 row-scale GEMMs, T=4096, act-quant included; "
-                                   "equal-k products as grouped launches (24 per launch)",
+                                   "equal-k products as grouped launches (64 per launch)",
                        "tops_step": round(ops4 / st4 / 1e12, 2), "ms_per_step": round(st4 * 1e3, 4),
                        "schedules_ms_per_step": {k: round(v * 1e3, 4) for k, v in sched4.items()},
                        "single_product_launch": {"avg_us": round(d1 * 1e6, 2),

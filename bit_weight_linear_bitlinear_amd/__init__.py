@@ -282,7 +282,7 @@ class GroupedCall:
 
 
 def lowbit_linear_batched_grouped(descs, packed, scales, q, sx, y, acc=None, stream=None) -> None:
-    """Device: several independent prefill GEMMs of equal k and t, 24 per launch."""
+    """Device: several independent prefill GEMMs of equal k and t, 64 per launch."""
     GroupedCall(descs, packed, scales, q, sx, y, acc, batched=True)(stream)
 
 

@@ -46,7 +46,7 @@ typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
 
 // One launch: up to kGemmMaxMats products of equal k, token count, format and
 // scale mode; workgroups run over the matrices' output tiles in order.
-constexpr int kGemmMaxMats = 24;
+constexpr int kGemmMaxMats = 64;
 
 struct GemmMat {
     const uint8_t* packed;
@@ -152,14 +152,16 @@ __global__ __launch_bounds__(TILE == 1 ? 512 : 256) void gemm_mfma_kernel(const 
     const int wm = wave / S::WAVES_N, wn = wave % S::WAVES_N;
 
     // XCD-aware tile order: XCD x runs a contiguous run of the launch's tiles
-    // (matrix after matrix); then this tile's matrix, one batch of scalar
-    // compares
+    // (matrix after matrix); then this tile's matrix
     const int total = a.wg_start[a.n_mats];
     const int xcd = (int)blockIdx.x % 8, jx = (int)blockIdx.x / 8;
     const int glogical = xcd * (total / 8) + min(xcd, total % 8) + jx;
-    int mi = 0;
-    #pragma unroll
-    for (int i = 1; i < kGemmMaxMats; ++i) mi += glogical >= a.wg_start[i] ? 1 : 0;
+    int mi = 0, hi = a.n_mats - 1;                          // binary search of the ascending starts
+    while (mi < hi) {
+        const int mid = (mi + hi + 1) >> 1;
+        if (glogical >= a.wg_start[mid]) mi = mid;
+        else hi = mid - 1;
+    }
     const GemmMat& mat = a.m[mi];
     const uint8_t* const m_packed = mat.packed;
     const float* const m_scales = mat.scales;

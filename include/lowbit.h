@@ -303,7 +303,7 @@ lowbit_status lowbit_linear_grouped(int32_t count, const lowbit_desc* descs, con
  * lowbit_linear_batched_grouped - several independent prefill products
  * (lowbit_linear_batched each) of equal format, scale mode, group, flags and
  * k, and one token count t, in as few launches as the argument space allows
- * (24 per launch): product i reads q[i] [t, k], sx[i] [t] and writes y[i]
+ * (64 per launch): product i reads q[i] [t, k], sx[i] [t] and writes y[i]
  * [t, n_i] (and acc[i] when acc and acc[i] are not NULL).  One launch fills
  * the chip with the output tiles of all its products, which small products
  * (n of a few hundred) cannot do alone.  Results equal those of the single
