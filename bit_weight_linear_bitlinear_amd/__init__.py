@@ -65,6 +65,10 @@ _lib.lowbit_pack.argtypes = [_D, _P, _P, _P]
 _lib.lowbit_act_quant.argtypes = [_P, _i32, _i32, _P, _P, _P, _P]
 _lib.lowbit_act_quant_h4.argtypes = [_P, _i32, _i32, _P, _P, _P, _P]
 _lib.lowbit_act_quant_h4.restype = _i32
+_lib.lowbit_act_quant_a4.argtypes = [_P, _i32, _i32, _P, _P, _P, _P]
+_lib.lowbit_act_quant_a4.restype = _i32
+_lib.lowbit_act_quant_sparse8.argtypes = [_P, _i32, _i32, _i32, _P, _P, _P, _P]
+_lib.lowbit_act_quant_sparse8.restype = _i32
 _lib.lowbit_act_quant_v1.argtypes = [_P, _i32, _i32, ctypes.c_float, _i32, _P, _P, _P, _P, _P]
 _lib.lowbit_act_quant_v1.restype = _i32
 _lib.lowbit_layernorm.argtypes = [_P, _i32, _i32, ctypes.c_float, _P, _P, _P, _P]
@@ -115,7 +119,8 @@ _lib.lowbit_last_hip_error.restype = ctypes.c_char_p
 for _f in ("lowbit_describe", "lowbit_pack", "lowbit_act_quant", "lowbit_linear", "lowbit_linear_batched"):
     getattr(_lib, _f).restype = _i32
 
-EXPORTS = ("lowbit_describe", "lowbit_pack", "lowbit_act_quant", "lowbit_act_quant_h4", "lowbit_act_quant_v1",
+EXPORTS = ("lowbit_describe", "lowbit_pack", "lowbit_act_quant", "lowbit_act_quant_h4", "lowbit_act_quant_a4",
+           "lowbit_act_quant_sparse8", "lowbit_act_quant_v1",
            "lowbit_layernorm", "lowbit_onebit_linear", "lowbit_linear",
            "lowbit_linear_batched",
            "lowbit_linear_grouped", "lowbit_linear_batched_grouped", "lowbit_linear_fused",
@@ -195,6 +200,24 @@ def lowbit_act_quant_h4(x, q, sx, status=None, stream=None) -> None:
     t, k = x.shape
     _check(_lib.lowbit_act_quant_h4(_dev(x, "x", 4 * t * k), t, k, _dev(q, "q", t * k), _dev(sx, "sx", 4 * t),
                                     _dev(status, "status", 4), _stream(stream)), "lowbit_act_quant_h4")
+
+
+def lowbit_act_quant_a4(x, q, sx, status=None, stream=None) -> None:
+    """Device: x fp32[t, k] -> per-token INT4 codes q int8[t, k] (in [-7, 7])
+    and sx fp32[t] = max|x| / 7; status int32[1] or None."""
+    t, k = x.shape
+    _check(_lib.lowbit_act_quant_a4(_dev(x, "x", 4 * t * k), t, k, _dev(q, "q", t * k), _dev(sx, "sx", 4 * t),
+                                    _dev(status, "status", 4), _stream(stream)), "lowbit_act_quant_a4")
+
+
+def lowbit_act_quant_sparse8(x, q, sx, keep, status=None, stream=None) -> None:
+    """Device: each row of x fp32[t, k] keeps its `keep` largest |x| (ties to
+    the lower channel) with per-token INT8 codes, the rest code 0 -> q
+    int8[t, k], sx fp32[t] = max|x| / 127; status int32[1] or None."""
+    t, k = x.shape
+    _check(_lib.lowbit_act_quant_sparse8(_dev(x, "x", 4 * t * k), t, k, int(keep), _dev(q, "q", t * k),
+                                         _dev(sx, "sx", 4 * t), _dev(status, "status", 4), _stream(stream)),
+           "lowbit_act_quant_sparse8")
 
 
 def lowbit_act_quant_v1(x, q, sx, eps=1e-5, per_tensor=False, status=None, work=None, stream=None) -> None:

@@ -19,7 +19,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "liblowbit.so")
 ARCH = os.environ.get("LOWBIT_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["act_quant.hip", "hadamard.hip", "bitnet_v1.hip", "onebit.hip", "gemv.hip", "gemv_ternary.hip", "gemv_int4.hip", "gemv_binary.hip", "gemm.hip",
+SOURCES = ["act_quant.hip", "hadamard.hip", "bitnet_v1.hip", "onebit.hip", "sparse8.hip", "gemv.hip", "gemv_ternary.hip", "gemv_int4.hip", "gemv_binary.hip", "gemm.hip",
            "decode_model.hip",
            "gemm_mfma.hip", "lowbit_host.cpp"]
 

@@ -43,15 +43,17 @@ struct ActQuantTable {
 //           code = clip(rint((128 x) / d), -128, 127) (one exact multiply and
 //           one IEEE division, in that order), s_x = m / 128; a zero row
 //           codes to 0; a row whose 128 m overflows is rejected;
-//   MODE 2  MODE 1 with the tensor-wide m of a prior reduction.
+//   MODE 2  MODE 1 with the tensor-wide m of a prior reduction;
+//   MODE 3  BitNet a4.8's 4-bit input codes (0x07B): the INT4 counterpart of
+//           MODE 0, r = 7 / m, code = clip(rint(x r), -7, 7), s_x = m / 7.
 // rowdiv() returns the row's flag and sets rr (MODE 0: r; MODE 1, 2: d).
 template <int MODE>
 __device__ __forceinline__ int rowdiv(float m, int bad, float eps, float& rr) {
     rr = 0.0f;
     if (bad) return LOWBIT_ACT_NONFINITE;
-    if constexpr (MODE == 0) {
+    if constexpr (MODE == 0 || MODE == 3) {
         if (m > 0.0f) {
-            rr = 127.0f / m;
+            rr = (MODE == 0 ? 127.0f : 7.0f) / m;
             if (!isfinite(rr)) return LOWBIT_ACT_OVERFLOW;
         }
     } else {
@@ -65,6 +67,10 @@ template <int MODE>
 __device__ __forceinline__ int8_t code_of(float v, float rr, float m) {
     if constexpr (MODE == 0) {
         return quant1(v, rr);
+    } else if constexpr (MODE == 3) {
+        float c = rintf(v * rr);
+        c = c < -7.0f ? -7.0f : (c > 7.0f ? 7.0f : c);
+        return (int8_t)(int)c;
     } else {
         if (m == 0.0f) return 0;
         float c = rintf((v * 128.0f) / rr);
@@ -76,6 +82,7 @@ __device__ __forceinline__ int8_t code_of(float v, float rr, float m) {
 template <int MODE>
 __device__ __forceinline__ float scale_of(float m) {
     if constexpr (MODE == 0) return m / 127.0f;
+    else if constexpr (MODE == 3) return m / 7.0f;
     else return m / 128.0f;
 }
 
@@ -292,6 +299,17 @@ hipError_t launch_act_quant_v1(const float* x, int t, int k, float eps, const ui
     const bool vec = k % 4 == 0 && (uintptr_t)x % 16 == 0 && (uintptr_t)q % 4 == 0;
     return tensor ? launch_table<2>(tab, 1, t, k, vec, status, stream)
                   : launch_table<1>(tab, 1, t, k, vec, status, stream);
+}
+
+hipError_t launch_act_quant_a4(const float* x, int t, int k, int8_t* q, float* sx, int32_t* status,
+                               hipStream_t stream) {
+    ActQuantTable tab{};
+    tab.t = t;
+    tab.x[0] = x;
+    tab.q[0] = q;
+    tab.sx[0] = sx;
+    const bool vec = k % 4 == 0 && (uintptr_t)x % 16 == 0 && (uintptr_t)q % 4 == 0;
+    return launch_table<3>(tab, 1, t, k, vec, status, stream);
 }
 
 hipError_t launch_act_quant(const float* x, int t, int k, int8_t* q, float* sx, int32_t* status,

@@ -54,6 +54,14 @@ constexpr int kH4MaxK = 65536;
 int h4_block(int k);
 hipError_t launch_act_quant_h4(const float* x, int t, int k, int8_t* q, float* sx, int32_t* status,
                                hipStream_t stream);
+// BitNet a4.8's codes: 4-bit per-token codes of projection inputs
+// (act_quant.hip), and the sparse 8-bit codes of intermediate states, each
+// row keeping its `keep` largest |x| (sparse8.hip), rows up to kSparse8MaxK
+constexpr int kSparse8MaxK = 32768;
+hipError_t launch_act_quant_a4(const float* x, int t, int k, int8_t* q, float* sx, int32_t* status,
+                               hipStream_t stream);
+hipError_t launch_act_quant_sparse8(const float* x, int t, int k, int keep, int8_t* q, float* sx, int32_t* status,
+                                    hipStream_t stream);
 // the original BitNet forward's pieces: Q_b = 128 codes with the encoder
 // epsilon, per token (tensor == nullptr) or with the tensor-wide max a prior
 // launch_tensor_absmax left in tensor[0..1]; the sub-layer LayerNorm

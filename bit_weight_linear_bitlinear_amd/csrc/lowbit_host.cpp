@@ -627,6 +627,23 @@ lowbit_status lowbit_act_quant_h4(const float* x, int32_t t, int32_t k, int8_t* 
     return hip_status(lowbit::launch_act_quant_h4(x, t, k, q, sx, status, (hipStream_t)hip_stream));
 }
 
+lowbit_status lowbit_act_quant_a4(const float* x, int32_t t, int32_t k, int8_t* q, float* sx, int32_t* status,
+                                  void* hip_stream) {
+    if (!x || !q || !sx || t < 1 || k < 1) return LOWBIT_E_ARG;
+    if ((uintptr_t)x % 4 || (uintptr_t)sx % 4 || (uintptr_t)status % 4) return LOWBIT_E_ARG;
+    clear_hip_error();
+    return hip_status(lowbit::launch_act_quant_a4(x, t, k, q, sx, status, (hipStream_t)hip_stream));
+}
+
+lowbit_status lowbit_act_quant_sparse8(const float* x, int32_t t, int32_t k, int32_t keep, int8_t* q, float* sx,
+                                       int32_t* status, void* hip_stream) {
+    if (!x || !q || !sx || t < 1 || k < 4 || k % 4 || keep < 1 || keep > k) return LOWBIT_E_ARG;
+    if ((uintptr_t)x % 16 || (uintptr_t)q % 4 || (uintptr_t)sx % 4 || (uintptr_t)status % 4) return LOWBIT_E_ARG;
+    if (k > lowbit::kSparse8MaxK) return LOWBIT_E_RANGE;
+    clear_hip_error();
+    return hip_status(lowbit::launch_act_quant_sparse8(x, t, k, keep, q, sx, status, (hipStream_t)hip_stream));
+}
+
 lowbit_status lowbit_linear(const lowbit_desc* d, const uint8_t* packed, const float* scales, const int8_t* q,
                             const float* sx, int32_t t, float* y, int32_t* acc, void* hip_stream) {
     lowbit::LinearArgs a;

@@ -1,0 +1,228 @@
+// sparse8.hip - BitNet a4.8's sparse 8-bit codes for intermediate states
+// (gfx950).
+//
+// M8.8 "Native Binary and Ternary Transformers", 0x07B: the states in front of
+// the attention output and FFN down projections are sparsified, then given
+// 8-bit codes.  For each token row of x [t, k]:
+//     keep the `keep` entries of largest |x| (at the threshold magnitude, the
+//     lower channels first), set the others to zero,
+//     m   = max |x| (always kept),  r = 127 / m,
+//     q   = clip(rint(x r), -127, 127) where kept, else 0;  s_x = m / 127
+// so the kept codes are exactly the dense per-token INT8 codes.
+//
+// One workgroup per row; the row stays in registers from load to store (up
+// to 8 float4 per thread).  The threshold is a radix select over the 31-bit
+// magnitude keys (the fp32 bits without the sign order like the magnitudes):
+// four passes of eight bits from the top, each a 256-bin LDS histogram of the
+// keys that still match the chosen prefix, then one wavefront scans the bins
+// from the top for the digit where the count of larger keys reaches the
+// number still to keep.  Keys above the threshold are kept; keys equal to it
+// are kept in channel order up to the remaining count, which needs a
+// workgroup scan per register slot only when more keys tie at the threshold
+// than may be kept (rare for real-valued rows).
+//
+// HBM-bound: 4 bytes read and 1 byte written per element, as the dense
+// quantiser; the select runs on registers and LDS.
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace lowbit {
+
+namespace {
+
+__device__ __forceinline__ float comp(const float4& v, int c) {
+    return c == 0 ? v.x : (c == 1 ? v.y : (c == 2 ? v.z : v.w));
+}
+
+__device__ __forceinline__ uint32_t mag_key(float v) { return __float_as_uint(v) & 0x7fffffffu; }
+
+template <int NT, int R>
+__global__ __launch_bounds__(NT) void sparse8_kernel(const float* __restrict__ x, int k, int keep,
+                                                     int8_t* __restrict__ q, float* __restrict__ sx,
+                                                     int32_t* __restrict__ status) {
+    constexpr int NW = NT / 64;
+    __shared__ uint32_t hist[256];
+    __shared__ float red_m[NW];
+    __shared__ int red_bad[NW];
+    __shared__ uint32_t wtot[NW];
+    __shared__ uint32_t sel[3];                 // chosen digit, keys above it, keys equal to it
+    const int row = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int k4 = k >> 2;
+    const float4* x4 = reinterpret_cast<const float4*>(x + (size_t)row * k);
+    float4 v[R];
+    #pragma unroll
+    for (int i = 0; i < R; ++i) {
+        const int idx = tid + i * NT;
+        v[i] = idx < k4 ? x4[idx] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
+    float m = 0.0f;
+    int bad = 0;
+    #pragma unroll
+    for (int i = 0; i < R; ++i) {
+        bad |= !(isfinite(v[i].x) && isfinite(v[i].y) && isfinite(v[i].z) && isfinite(v[i].w));
+        const float a0 = fabsf(v[i].x), a1 = fabsf(v[i].y), a2 = fabsf(v[i].z), a3 = fabsf(v[i].w);
+        m = a0 > m ? a0 : m; m = a1 > m ? a1 : m; m = a2 > m ? a2 : m; m = a3 > m ? a3 : m;
+    }
+    m = wave_max(m);
+    bad = wave_or(bad);
+    if (lane == 0) { red_m[w] = m; red_bad[w] = bad; }
+    __syncthreads();
+    #pragma unroll
+    for (int i = 0; i < NW; ++i) { m = red_m[i] > m ? red_m[i] : m; bad |= red_bad[i]; }
+    int flag = 0;
+    float r = 0.0f;
+    if (bad) {
+        flag = LOWBIT_ACT_NONFINITE;
+    } else if (m > 0.0f) {
+        r = 127.0f / m;
+        if (!isfinite(r)) flag = LOWBIT_ACT_OVERFLOW;
+    }
+
+    // the threshold key T and how many keys equal to it are kept
+    uint32_t T = 0u;
+    uint32_t need = 0u;
+    bool ranked = false;                          // ties at T beyond `need`: rank them by channel
+    const bool select = !flag && m > 0.0f && keep < k;   // the same for every thread
+    if (select) {
+        // pfx: the digits chosen so far, in place; hi: the bits they cover
+        uint32_t pfx = 0u, rem = (uint32_t)keep, eq = 0u;
+        #pragma unroll 1
+        for (int pass = 0; pass < 4; ++pass) {
+            const int shift = 24 - 8 * pass;
+            const uint32_t hi = (uint32_t)(0xffffffffull << (shift + 8));
+            for (int i = tid; i < 256; i += NT) hist[i] = 0u;
+            __syncthreads();
+            #pragma unroll
+            for (int i = 0; i < R; ++i) {
+                if (tid + i * NT < k4) {
+                    #pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const uint32_t key = mag_key(comp(v[i], c));
+                        if ((key & hi) == pfx) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+                    }
+                }
+            }
+            __syncthreads();
+            if (w == 0) {
+                // lane l scans bins 255 - 4l down to 252 - 4l
+                const int top = 255 - 4 * lane;
+                const uint32_t h0 = hist[top], h1 = hist[top - 1], h2 = hist[top - 2], h3 = hist[top - 3];
+                const uint32_t s = h0 + h1 + h2 + h3;
+                uint32_t inc = s;
+                #pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const uint32_t o = __shfl_up(inc, off, 64);
+                    if (lane >= off) inc += o;
+                }
+                const uint32_t exc = inc - s;
+                if (exc < rem && rem <= inc) {          // exactly one lane: rem <= the total
+                    uint32_t above = exc, d = top, he = h0;
+                    if (above + h0 < rem) {
+                        above += h0; d = top - 1; he = h1;
+                        if (above + h1 < rem) {
+                            above += h1; d = top - 2; he = h2;
+                            if (above + h2 < rem) { above += h2; d = top - 3; he = h3; }
+                        }
+                    }
+                    sel[0] = d; sel[1] = above; sel[2] = he;
+                }
+            }
+            __syncthreads();
+            pfx |= sel[0] << shift;
+            rem -= sel[1];
+            eq = sel[2];
+        }
+        T = pfx;
+        need = rem;
+        ranked = eq > need && T != 0u;          // (zero magnitudes code to 0 kept or not)
+    }
+
+    // kept-entry bits, 4 per register slot, in channel order within the float4
+    uint32_t kb[R];
+    #pragma unroll
+    for (int i = 0; i < R; ++i) {
+        uint32_t b = 0u;
+        #pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const uint32_t key = mag_key(comp(v[i], c));
+            const bool kept = !select || key > T || (key == T && !ranked);
+            b |= (uint32_t)kept << c;
+        }
+        kb[i] = b;
+    }
+    if (ranked) {
+        // channel order is slot-major: channel 4 (tid + i NT) + c.  The ties
+        // in slot i ahead of this thread's come from the slots before it
+        // (base) and from lower threads in slot i (a workgroup scan).
+        uint32_t base = 0u;
+        #pragma unroll
+        for (int i = 0; i < R; ++i) {
+            uint32_t tie = 0u;
+            if (tid + i * NT < k4) {
+                #pragma unroll
+                for (int c = 0; c < 4; ++c) tie |= (uint32_t)(mag_key(comp(v[i], c)) == T) << c;
+            }
+            const uint32_t cnt = __builtin_popcount(tie);
+            uint32_t inc = cnt;
+            #pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const uint32_t o = __shfl_up(inc, off, 64);
+                if (lane >= off) inc += o;
+            }
+            if (lane == 63) wtot[w] = inc;
+            __syncthreads();
+            uint32_t before = base + inc - cnt, total = 0u;
+            #pragma unroll
+            for (int j = 0; j < NW; ++j) {
+                const uint32_t tw = wtot[j];
+                before += j < w ? tw : 0u;
+                total += tw;
+            }
+            __syncthreads();                        // wtot is rewritten by the next slot
+            #pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                if ((tie >> c) & 1u) {
+                    if (before < need) kb[i] |= 1u << c;
+                    ++before;
+                }
+            }
+            base += total;
+        }
+    }
+
+    uint32_t* q4 = reinterpret_cast<uint32_t*>(q + (size_t)row * k);
+    #pragma unroll
+    for (int i = 0; i < R; ++i) {
+        const int idx = tid + i * NT;
+        if (idx < k4) {
+            uint32_t p = 0u;   // a rejected row gets zero codes
+            if (!flag) {
+                #pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    if ((kb[i] >> c) & 1u) p |= (uint32_t)(uint8_t)quant1(comp(v[i], c), r) << (8 * c);
+            }
+            q4[idx] = p;
+        }
+    }
+    if (tid == 0) {
+        sx[row] = flag ? __builtin_nanf("") : m / 127.0f;
+        if (flag && status) atomicOr(status, flag);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_act_quant_sparse8(const float* x, int t, int k, int keep, int8_t* q, float* sx, int32_t* status,
+                                    hipStream_t stream) {
+    const int k4 = k / 4;
+    if (k4 <= 256 * 4)
+        sparse8_kernel<256, 4><<<dim3((unsigned)t), dim3(256), 0, stream>>>(x, k, keep, q, sx, status);
+    else if (k4 <= 512 * 8)
+        sparse8_kernel<512, 8><<<dim3((unsigned)t), dim3(512), 0, stream>>>(x, k, keep, q, sx, status);
+    else
+        sparse8_kernel<1024, 8><<<dim3((unsigned)t), dim3(1024), 0, stream>>>(x, k, keep, q, sx, status);
+    return hipGetLastError();
+}
+
+}  // namespace lowbit

@@ -186,6 +186,48 @@ lowbit_status lowbit_act_quant_h4(const float* x, int32_t t, int32_t k, int8_t* 
                                   int32_t* status, void* hip_stream);
 
 /*
+ * lowbit_act_quant_a4 - BitNet a4.8's 4-bit codes for the inputs of the
+ * attention and FFN projections (M8.8 "Native Binary and Ternary
+ * Transformers", 0x07B), the per-token absmax INT4 rule without a rotation:
+ *   x      device float [t, k]
+ *   q      device int8  [t, k]   out: clip(rint(x * (7 / m)), -7, 7), fp32,
+ *                                ties to even, m = max_k |x[row]|
+ *   sx     device float [t]      out: m / 7 (fp32); 0 for an all-zero row
+ *   status device int32 [1] or NULL: LOWBIT_ACT_* bits ORed in; a row holding
+ *          NaN / Inf, or whose 7 / m overflows, gets zero codes and sx = NaN.
+ *   t >= 1, k >= 1.  q and sx are the operands of lowbit_linear /
+ *   lowbit_linear_batched.
+ * Errors: LOWBIT_E_ARG (null pointer, t < 1, k < 1), LOWBIT_E_HIP.
+ */
+lowbit_status lowbit_act_quant_a4(const float* x, int32_t t, int32_t k, int8_t* q, float* sx,
+                                  int32_t* status, void* hip_stream);
+
+/*
+ * lowbit_act_quant_sparse8 - BitNet a4.8's sparse 8-bit codes for the
+ * intermediate states in front of the attention output and FFN down
+ * projections (M8.8 "Native Binary and Ternary Transformers", 0x07B): each
+ * token row keeps its `keep` entries of largest |x| - at the threshold
+ * magnitude the lower channels first - and the kept entries get the
+ * per-token INT8 codes of lowbit_act_quant; the others get code 0.
+ *   x      device float [t, k], 16-byte aligned
+ *   keep   1 <= keep <= k: entries kept per row (keep = k is lowbit_act_quant)
+ *   q      device int8  [t, k], 4-byte aligned   out: clip(rint(x * (127 / m)),
+ *          -127, 127) where kept, else 0; m = max_k |x[row]|, always kept
+ *   sx     device float [t]    out: m / 127 (fp32); 0 for an all-zero row
+ *   status device int32 [1] or NULL: LOWBIT_ACT_* bits ORed in; a row holding
+ *          NaN / Inf anywhere, or whose 127 / m overflows, gets zero codes and
+ *          sx = NaN.
+ *   t >= 1; k a multiple of 4, at most 32768.
+ * The product of (q, sx) with packed weights is then the dense product over
+ * the kept entries (lowbit_linear / lowbit_linear_batched).
+ * Errors: LOWBIT_E_ARG (null or misaligned pointer, t < 1, k not a positive
+ *         multiple of 4, keep outside [1, k]), LOWBIT_E_RANGE (k > 32768),
+ *         LOWBIT_E_HIP.
+ */
+lowbit_status lowbit_act_quant_sparse8(const float* x, int32_t t, int32_t k, int32_t keep, int8_t* q, float* sx,
+                                       int32_t* status, void* hip_stream);
+
+/*
  * lowbit_act_quant_v1 - the original BitNet forward's activation codes (M8.8
  * "Native Binary and Ternary Transformers", 0x02C and the forward of 0x02E),
  * Q_b = 128, for the normalised input x (lowbit_layernorm):

@@ -247,6 +247,27 @@ def test_act_quant_h4_rejects_bad_arguments_on_the_host():
     assert lib.lowbit_act_quant_h4(x, 1, 65536 + 64, q, sx, None, None) == 2   # LOWBIT_E_RANGE
 
 
+def test_act_quant_a48_rejects_bad_arguments_on_the_host():
+    """The a4.8 quantisers refuse bad shapes, keep counts and alignments
+    before any launch."""
+    lib = lb.raw_library()
+    x = ctypes.c_void_p(1 << 20)                             # never dereferenced: the checks fail first
+    q, sx = ctypes.c_void_p(2 << 20), ctypes.c_void_p(3 << 20)
+    assert lib.lowbit_act_quant_a4(x, 0, 64, q, sx, None, None) == 1       # t < 1
+    assert lib.lowbit_act_quant_a4(x, 1, 0, q, sx, None, None) == 1        # k < 1
+    assert lib.lowbit_act_quant_a4(None, 1, 64, q, sx, None, None) == 1
+    assert lib.lowbit_act_quant_a4(ctypes.c_void_p((1 << 20) + 2), 1, 64, q, sx, None, None) == 1
+    sp = lib.lowbit_act_quant_sparse8
+    assert sp(x, 1, 64, 0, q, sx, None, None) == 1                          # keep < 1
+    assert sp(x, 1, 64, 65, q, sx, None, None) == 1                         # keep > k
+    assert sp(x, 1, 66, 8, q, sx, None, None) == 1                          # k % 4
+    assert sp(x, 0, 64, 8, q, sx, None, None) == 1                          # t < 1
+    assert sp(ctypes.c_void_p((1 << 20) + 4), 1, 64, 8, q, sx, None, None) == 1
+    assert sp(x, 1, 64, 8, ctypes.c_void_p((2 << 20) + 2), sx, None, None) == 1
+    assert sp(x, 1, 64, 8, None, sx, None, None) == 1
+    assert sp(x, 1, 32768 + 4, 8, q, sx, None, None) == 2                   # LOWBIT_E_RANGE
+
+
 def _pack_centered_oracle(w, scale, group=0):
     """Centered binary codes of the BitNet v1 oracle, packed by the main
     oracle; the scales are the binary rule's mean |w|, unchanged by centering."""
