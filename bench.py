@@ -888,6 +888,61 @@ def h4_profile():
                           "bytes_per_launch": nb}), flush=True)
 
 
+def a48_launches(lb, shapes, reps, graph=True):
+    """Average launch duration of BitNet a4.8's two quantisers per [t, k]:
+    the sparse 8-bit one keeping half of each row, the dense int8 one on the
+    same input beside it, and the 4-bit one; `reps` launches captured in a
+    HIP graph and replayed three times between events on the replaying
+    stream: {(t, k): {"sparse8": s, "int8": s, "a4": s}}."""
+    import torch
+    out = {}
+    g = torch.Generator(device="cuda").manual_seed(11)
+    for t, k in shapes:
+        x = torch.randn((t, k), device="cuda", generator=g)
+        q = torch.empty((t, k), dtype=torch.int8, device="cuda")
+        sx = torch.empty(t, device="cuda")
+        fns = {"sparse8": lambda: lb.lowbit_act_quant_sparse8(x, q, sx, k // 2),
+               "int8": lambda: lb.lowbit_act_quant(x, q, sx),
+               "a4": lambda: lb.lowbit_act_quant_a4(x, q, sx)}
+        res = {}
+        for name, fn in fns.items():
+            body = (lambda fn=fn: [fn() for _ in range(reps)])
+            run = (capture(body) if graph else None) or body
+            el, _ = time_steps(run, 3, 1)
+            res[name] = el / (3 * reps)
+        out[(t, k)] = res
+        del x, q, sx
+    return out
+
+
+def a48_view():
+    """BitNet a4.8 ("Native Binary and Ternary Transformers", 0x07B) on the
+    4B-class ternary model's widths: the sparse 8-bit codes of the states in
+    front of the attention output (k = 2560) and FFN down (k = 9728)
+    projections, half of each row kept, and the 4-bit input codes, at 4096
+    tokens and at one; per launch against the HBM roofline (4 bytes read and
+    1 written per element, 4 per row), the dense int8 quantiser beside them."""
+    lb = __import__("bit_weight_linear_bitlinear_amd")
+    out = {"what": " ".join(a48_view.__doc__.split())}
+    for (t, k), res in a48_launches(lb, [(4096, 2560), (4096, 9728), (1, 2560), (1, 9728)], reps=50).items():
+        nb = 5 * t * k + 4 * t
+        out[f"t{t}_k{k}"] = {name: {"us": round(v * 1e6, 2), "GBps": round(nb / v / 1e9, 1),
+                                    "frac_hbm_peak": round(nb / v / 1e9 / HBM_PEAK_GBS, 4)}
+                             for name, v in res.items()}
+    log(f"[bench] a4.8: {out}")
+    return out
+
+
+def a48_profile():
+    """The a4.8 quantisers' prefill launches only (for profiler runs)."""
+    lb = __import__("bit_weight_linear_bitlinear_amd")
+    for (t, k), res in a48_launches(lb, [(4096, 9728), (4096, 2560)], reps=20, graph=False).items():
+        nb = 5 * t * k + 4 * t
+        print(json.dumps({"a48_t": t, "k": k, "bytes_per_launch": nb,
+                          **{name: {"us": round(v * 1e6, 2), "GBps": round(nb / v / 1e9, 1)}
+                             for name, v in res.items()}}), flush=True)
+
+
 def extra_views(args):
     """The other timing views: (iii) the streaming ceiling on one large cold
     matrix, the cache-resident 256-d decode stack at t = 1, and the binary
@@ -972,6 +1027,7 @@ def extra_views(args):
     views["h_bitlinear"] = h_bitlinear_view()
     views["bitnet_v1"] = bitnet_v1_view()
     views["onebit"] = onebit_view()
+    views["a48"] = a48_view()
 
     # the binary 8192-token GEMM pass
     wl2 = workloads.BY_NAME["binary_gqa"]
@@ -1010,6 +1066,8 @@ def main():
                     help="batched GEMM pass only, with per-shape launch timings (for profiler runs)")
     ap.add_argument("--profile-h4", action="store_true",
                     help="the rotated 4-bit quantiser's prefill launches only (for profiler runs)")
+    ap.add_argument("--profile-a48", action="store_true",
+                    help="the a4.8 quantisers' prefill launches only (for profiler runs)")
     ap.add_argument("--profile-pass", action="store_true",
                     help="copy calibration + grouped GEMV pass only (for profiler runs)")
     args = ap.parse_args()
@@ -1033,6 +1091,9 @@ def main():
         return
     if args.profile_h4:
         h4_profile()
+        return
+    if args.profile_a48:
+        a48_profile()
         return
 
     # ---- GEMV line: ternary_4b decode pass

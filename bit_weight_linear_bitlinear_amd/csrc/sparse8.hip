@@ -13,10 +13,10 @@
 // One workgroup per row; the row stays in registers from load to store (up
 // to 8 float4 per thread).  The threshold is a radix select over the 31-bit
 // magnitude keys (the fp32 bits without the sign order like the magnitudes):
-// four passes of eight bits from the top, each a 256-bin LDS histogram of the
-// keys that still match the chosen prefix, then one wavefront scans the bins
-// from the top for the digit where the count of larger keys reaches the
-// number still to keep.  Keys above the threshold are kept; keys equal to it
+// three passes of 11, 10 and 10 bits from the top, each an LDS histogram of
+// the keys that still match the chosen prefix, then a workgroup scan of the
+// bins from the top finds the digit where the count of larger keys reaches
+// the number still to keep.  Keys above the threshold are kept; keys equal to it
 // are kept in channel order up to the remaining count, which needs a
 // workgroup scan per register slot only when more keys tie at the threshold
 // than may be kept (rare for real-valued rows).
@@ -36,12 +36,58 @@ __device__ __forceinline__ float comp(const float4& v, int c) {
 
 __device__ __forceinline__ uint32_t mag_key(float v) { return __float_as_uint(v) & 0x7fffffffu; }
 
-template <int NT, int R>
-__global__ __launch_bounds__(NT) void sparse8_kernel(const float* __restrict__ x, int k, int keep,
-                                                     int8_t* __restrict__ q, float* __restrict__ sx,
-                                                     int32_t* __restrict__ status) {
+constexpr int kBins = 2048;                     // the first digit's; the others use 1024
+
+// The workgroup finds the bin, counted from the top, where the running count
+// reaches rem (1 <= rem <= the histogram's total of NT BPT bins): thread i
+// sums its BPT bins (the highest BPT for thread 0), a workgroup scan places
+// the thread whose range holds the crossing, and that thread walks its bins.
+// sel receives the bin, the count of keys above it and the count in it.
+// Ends with the workgroup synchronised and sel visible to all.
+template <int NT, int BPT>
+__device__ __forceinline__ void pick_bin(const uint32_t* hist, uint32_t rem, uint32_t* wtot, uint32_t* sel) {
     constexpr int NW = NT / 64;
-    __shared__ uint32_t hist[256];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int lo = (NT - 1 - tid) * BPT;             // this thread's lowest bin
+    uint32_t h[BPT];
+    uint32_t s = 0u;
+    #pragma unroll
+    for (int j = 0; j < BPT; ++j) { h[j] = hist[lo + j]; s += h[j]; }
+    uint32_t inc = s;
+    #pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t o = __shfl_up(inc, off, 64);
+        if (lane >= off) inc += o;
+    }
+    if (lane == 63) wtot[w] = inc;
+    __syncthreads();
+    #pragma unroll
+    for (int j = 0; j < NW; ++j) inc += j < w ? wtot[j] : 0u;
+    const uint32_t exc = inc - s;
+    if (exc < rem && rem <= inc) {                  // exactly one thread
+        uint32_t above = exc, d = 0u, he = 0u;
+        bool found = false;
+        #pragma unroll
+        for (int j = BPT - 1; j >= 0; --j) {
+            if (!found) {
+                if (above + h[j] >= rem) { found = true; d = (uint32_t)(lo + j); he = h[j]; }
+                else above += h[j];
+            }
+        }
+        sel[0] = d; sel[1] = above; sel[2] = he;
+    }
+    __syncthreads();
+}
+
+template <int NT, int R>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sparse8_kernel(
+        const float* __restrict__ x, int k, int keep, int8_t* __restrict__ q, float* __restrict__ sx,
+        int32_t* __restrict__ status) {
+    constexpr int NW = NT / 64;
+    // two histograms: the first digit's 2048 bins (its lower half serves the
+    // third digit), the second digit's 1024; each is cleared a pass ahead
+    __shared__ __align__(16) uint32_t hist_a[kBins];
+    __shared__ __align__(16) uint32_t hist_b[kBins / 2];
     __shared__ float red_m[NW];
     __shared__ int red_bad[NW];
     __shared__ uint32_t wtot[NW];
@@ -56,6 +102,12 @@ __global__ __launch_bounds__(NT) void sparse8_kernel(const float* __restrict__ x
         const int idx = tid + i * NT;
         v[i] = idx < k4 ? x4[idx] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     }
+    for (int i = tid; i < kBins / 4; i += NT) reinterpret_cast<uint4*>(hist_a)[i] = make_uint4(0u, 0u, 0u, 0u);
+    for (int i = tid; i < kBins / 8; i += NT) reinterpret_cast<uint4*>(hist_b)[i] = make_uint4(0u, 0u, 0u, 0u);
+    __syncthreads();
+    // the row max, finiteness, and the first digit's histogram (key bits
+    // 30-20: the exponent and three mantissa bits, so that magnitudes of one
+    // binade spread over eight bins and a wavefront's atomics rarely meet)
     float m = 0.0f;
     int bad = 0;
     #pragma unroll
@@ -63,6 +115,10 @@ __global__ __launch_bounds__(NT) void sparse8_kernel(const float* __restrict__ x
         bad |= !(isfinite(v[i].x) && isfinite(v[i].y) && isfinite(v[i].z) && isfinite(v[i].w));
         const float a0 = fabsf(v[i].x), a1 = fabsf(v[i].y), a2 = fabsf(v[i].z), a3 = fabsf(v[i].w);
         m = a0 > m ? a0 : m; m = a1 > m ? a1 : m; m = a2 > m ? a2 : m; m = a3 > m ? a3 : m;
+        if (tid + i * NT < k4) {
+            #pragma unroll
+            for (int c = 0; c < 4; ++c) atomicAdd(&hist_a[mag_key(comp(v[i], c)) >> 20], 1u);
+        }
     }
     m = wave_max(m);
     bad = wave_or(bad);
@@ -79,63 +135,55 @@ __global__ __launch_bounds__(NT) void sparse8_kernel(const float* __restrict__ x
         if (!isfinite(r)) flag = LOWBIT_ACT_OVERFLOW;
     }
 
-    // the threshold key T and how many keys equal to it are kept
+    // The threshold key T: keys above it are kept, and of the keys equal to
+    // it the first `need` in channel order (all of them unless ranked).  A
+    // pass whose chosen bin is kept whole ends the search, T then being the
+    // digits so far with the lower bits zero.
     uint32_t T = 0u;
     uint32_t need = 0u;
-    bool ranked = false;                          // ties at T beyond `need`: rank them by channel
+    bool ranked = false;
     const bool select = !flag && m > 0.0f && keep < k;   // the same for every thread
     if (select) {
-        // pfx: the digits chosen so far, in place; hi: the bits they cover
-        uint32_t pfx = 0u, rem = (uint32_t)keep, eq = 0u;
-        #pragma unroll 1
-        for (int pass = 0; pass < 4; ++pass) {
-            const int shift = 24 - 8 * pass;
-            const uint32_t hi = (uint32_t)(0xffffffffull << (shift + 8));
-            for (int i = tid; i < 256; i += NT) hist[i] = 0u;
-            __syncthreads();
+        uint32_t rem = (uint32_t)keep;
+        pick_bin<NT, kBins / NT>(hist_a, rem, wtot, sel);
+        T = sel[0] << 20;
+        rem -= sel[1];
+        if (rem != sel[2]) {                         // the second digit, key bits 19-10
+            for (int i = tid; i < kBins / 8; i += NT)  // (the third digit's bins)
+                reinterpret_cast<uint4*>(hist_a)[i] = make_uint4(0u, 0u, 0u, 0u);
             #pragma unroll
             for (int i = 0; i < R; ++i) {
                 if (tid + i * NT < k4) {
                     #pragma unroll
                     for (int c = 0; c < 4; ++c) {
                         const uint32_t key = mag_key(comp(v[i], c));
-                        if ((key & hi) == pfx) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+                        if ((key & 0xfff00000u) == T) atomicAdd(&hist_b[(key >> 10) & 1023u], 1u);
                     }
                 }
             }
             __syncthreads();
-            if (w == 0) {
-                // lane l scans bins 255 - 4l down to 252 - 4l
-                const int top = 255 - 4 * lane;
-                const uint32_t h0 = hist[top], h1 = hist[top - 1], h2 = hist[top - 2], h3 = hist[top - 3];
-                const uint32_t s = h0 + h1 + h2 + h3;
-                uint32_t inc = s;
+            pick_bin<NT, kBins / 2 / NT>(hist_b, rem, wtot, sel);
+            T |= sel[0] << 10;
+            rem -= sel[1];
+            if (rem != sel[2]) {                     // the third digit, key bits 9-0
                 #pragma unroll
-                for (int off = 1; off < 64; off <<= 1) {
-                    const uint32_t o = __shfl_up(inc, off, 64);
-                    if (lane >= off) inc += o;
-                }
-                const uint32_t exc = inc - s;
-                if (exc < rem && rem <= inc) {          // exactly one lane: rem <= the total
-                    uint32_t above = exc, d = top, he = h0;
-                    if (above + h0 < rem) {
-                        above += h0; d = top - 1; he = h1;
-                        if (above + h1 < rem) {
-                            above += h1; d = top - 2; he = h2;
-                            if (above + h2 < rem) { above += h2; d = top - 3; he = h3; }
+                for (int i = 0; i < R; ++i) {
+                    if (tid + i * NT < k4) {
+                        #pragma unroll
+                        for (int c = 0; c < 4; ++c) {
+                            const uint32_t key = mag_key(comp(v[i], c));
+                            if ((key & 0xfffffc00u) == T) atomicAdd(&hist_a[key & 1023u], 1u);
                         }
                     }
-                    sel[0] = d; sel[1] = above; sel[2] = he;
                 }
+                __syncthreads();
+                pick_bin<NT, kBins / 2 / NT>(hist_a, rem, wtot, sel);
+                T |= sel[0];
+                rem -= sel[1];
+                need = rem;
+                ranked = sel[2] > rem && T != 0u;    // (zero magnitudes code to 0 kept or not)
             }
-            __syncthreads();
-            pfx |= sel[0] << shift;
-            rem -= sel[1];
-            eq = sel[2];
         }
-        T = pfx;
-        need = rem;
-        ranked = eq > need && T != 0u;          // (zero magnitudes code to 0 kept or not)
     }
 
     // kept-entry bits, 4 per register slot, in channel order within the float4
@@ -216,8 +264,10 @@ __global__ __launch_bounds__(NT) void sparse8_kernel(const float* __restrict__ x
 hipError_t launch_act_quant_sparse8(const float* x, int t, int k, int keep, int8_t* q, float* sx, int32_t* status,
                                     hipStream_t stream) {
     const int k4 = k / 4;
-    if (k4 <= 256 * 4)
-        sparse8_kernel<256, 4><<<dim3((unsigned)t), dim3(256), 0, stream>>>(x, k, keep, q, sx, status);
+    if (k4 <= 256 * 3)
+        sparse8_kernel<256, 3><<<dim3((unsigned)t), dim3(256), 0, stream>>>(x, k, keep, q, sx, status);
+    else if (k4 <= 256 * 10)
+        sparse8_kernel<256, 10><<<dim3((unsigned)t), dim3(256), 0, stream>>>(x, k, keep, q, sx, status);
     else if (k4 <= 512 * 8)
         sparse8_kernel<512, 8><<<dim3((unsigned)t), dim3(512), 0, stream>>>(x, k, keep, q, sx, status);
     else
