@@ -186,19 +186,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sp
         }
     }
 
-    // kept-entry bits, 4 per register slot, in channel order within the float4
-    uint32_t kb[R];
-    #pragma unroll
-    for (int i = 0; i < R; ++i) {
-        uint32_t b = 0u;
-        #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const uint32_t key = mag_key(comp(v[i], c));
-            const bool kept = !select || key > T || (key == T && !ranked);
-            b |= (uint32_t)kept << c;
-        }
-        kb[i] = b;
-    }
+    // Kept: keys above T, and keys equal to T unless ranked; ranked ties are
+    // kept by their channel order, their bits (4 per register slot) in rk.
+    static_assert(R <= 16, "rk holds 4 bits per register slot");
+    uint64_t rk = 0u;
     if (ranked) {
         // channel order is slot-major: channel 4 (tid + i NT) + c.  The ties
         // in slot i ahead of this thread's come from the slots before it
@@ -231,7 +222,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sp
             #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 if ((tie >> c) & 1u) {
-                    if (before < need) kb[i] |= 1u << c;
+                    if (before < need) rk |= (uint64_t)1u << (4 * i + c);
                     ++before;
                 }
             }
@@ -247,8 +238,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sp
             uint32_t p = 0u;   // a rejected row gets zero codes
             if (!flag) {
                 #pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    if ((kb[i] >> c) & 1u) p |= (uint32_t)(uint8_t)quant1(comp(v[i], c), r) << (8 * c);
+                for (int c = 0; c < 4; ++c) {
+                    const float xv = comp(v[i], c);
+                    const uint32_t key = mag_key(xv);
+                    const bool kept = !select || key > T ||
+                                      (key == T && (!ranked || ((rk >> (4 * i + c)) & 1u)));
+                    if (kept) p |= (uint32_t)(uint8_t)quant1(xv, r) << (8 * c);
+                }
             }
             q4[idx] = p;
         }
