@@ -267,6 +267,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(6))) void sp
 hipError_t launch_act_quant_sparse8(const float* x, int t, int k, int keep, int8_t* q, float* sx, int32_t* status,
                                     hipStream_t stream) {
     const int k4 = k / 4;
+    if (t <= 64 && k4 <= 1024 * 3) {
+        // few rows (decode): a row's latency is the launch's, so spread each
+        // row over 16 wavefronts (fewer serial atomics per thread)
+        if (k4 <= 1024)
+            sparse8_kernel<1024, 1><<<dim3((unsigned)t), dim3(1024), 0, stream>>>(x, k, keep, q, sx, status);
+        else
+            sparse8_kernel<1024, 3><<<dim3((unsigned)t), dim3(1024), 0, stream>>>(x, k, keep, q, sx, status);
+        return hipGetLastError();
+    }
     if (k4 <= 256 * 3)
         sparse8_kernel<256, 3><<<dim3((unsigned)t), dim3(256), 0, stream>>>(x, k, keep, q, sx, status);
     else if (k4 <= 256 * 10)

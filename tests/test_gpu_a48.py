@@ -74,10 +74,12 @@ def _keeps(k):
 
 
 @pytest.mark.parametrize("t,k", [(5, 4), (7, 64), (33, 192), (9, 1000), (4, 2560), (3, 4096), (3, 4100),
-                                 (2, 9728), (2, 16384), (2, 16388), (1, 32768)])
+                                 (2, 9728), (2, 16384), (2, 16388), (1, 32768),
+                                 (65, 192), (70, 2560), (66, 3076), (65, 9728), (65, 12288)])
 def test_sparse8_codes_match_oracle(t, k):
-    """Every launch shape (256, 512 and 1024 threads per row, slots past k
-    empty) at keep counts from 1 to k."""
+    """Every launch shape at keep counts from 1 to k: up to 64 rows, 1024
+    threads per row for k <= 12288; above, 256 threads (3 or 10 float4
+    each), 512 and 1024 threads (8 each); slots past k empty."""
     x = _rows(t, k, t * 7 + k)
     xd = to_dev(x)
     for keep in _keeps(k):
@@ -99,11 +101,12 @@ def test_sparse8_ties_at_the_threshold(k):
     x[3, : k // 2] = 0.0
     x[4] = (g.integers(-2, 3, k) * 1e-3).astype(np.float32)
     x[5, g.integers(0, k, 7)] = 9.0                # a few outliers above a tied mass
-    xd = to_dev(x)
-    for keep in (1, 3, 7, 8, k // 5, k // 2, k - 3):
-        say(f"[case] sparse8 ties k={k} keep={keep}")
-        got = _run(lib().lowbit_act_quant_sparse8, xd, keep)
-        _check(got, a48.sparse_codes(x, keep), f"sparse8 ties k={k} keep={keep}")
+    for rows in (x, np.tile(x, (11, 1))):             # 6 rows, and 66 (the many-row launch shapes)
+        xd = to_dev(rows)
+        for keep in (1, 3, 7, 8, k // 5, k // 2, k - 3):
+            say(f"[case] sparse8 ties t={rows.shape[0]} k={k} keep={keep}")
+            got = _run(lib().lowbit_act_quant_sparse8, xd, keep)
+            _check(got, a48.sparse_codes(rows, keep), f"sparse8 ties t={rows.shape[0]} k={k} keep={keep}")
 
 
 def test_sparse8_rejected_and_degenerate_rows():
@@ -121,10 +124,11 @@ def test_sparse8_rejected_and_degenerate_rows():
     x[3] = np.float32(2.0 ** -140)                 # 127 / m overflows
     x[4] = (np.arange(k) % 17 * 2.0 ** -135).astype(np.float32)   # denormals, finite 127 / m
     x[5] = -0.0
-    for keep in (1, 64, 511, 512):
-        got = _run(lib().lowbit_act_quant_sparse8, to_dev(x), keep)
-        _check(got, a48.sparse_codes(x, keep), f"sparse8 rejected rows keep={keep}")
-        assert got[2] == 3 and got[1][2] == 0 and not got[0][2].any()
+    for rows in (x, np.tile(x, (10, 1))):            # 7 rows, and 70 (the many-row launch shapes)
+        for keep in (1, 64, 511, 512):
+            got = _run(lib().lowbit_act_quant_sparse8, to_dev(rows), keep)
+            _check(got, a48.sparse_codes(rows, keep), f"sparse8 rejected rows t={rows.shape[0]} keep={keep}")
+            assert got[2] == 3 and got[1][2] == 0 and not got[0][2].any()
 
 
 @pytest.mark.parametrize("k", [2560, 9728])
