@@ -75,7 +75,7 @@ def _keeps(k):
 
 @pytest.mark.parametrize("t,k", [(5, 4), (7, 64), (33, 192), (9, 1000), (4, 2560), (3, 4096), (3, 4100),
                                  (2, 9728), (2, 16384), (2, 16388), (1, 32768),
-                                 (65, 192), (70, 2560), (66, 3076), (65, 9728), (65, 12288)])
+                                 (65, 192), (70, 2560), (66, 3072), (66, 3076), (65, 9728), (65, 12288)])
 def test_sparse8_codes_match_oracle(t, k):
     """Every launch shape at keep counts from 1 to k: up to 64 rows, 1024
     threads per row for k <= 12288; above, 256 threads (3 or 10 float4
