@@ -11,7 +11,8 @@
 // so the kept codes are exactly the dense per-token INT8 codes.
 //
 // One workgroup per row; the row stays in registers from load to store (up
-// to 8 float4 per thread).  The threshold is a radix select over the 31-bit
+// to 10 float4 per thread; 1024 threads per row when there are at most 64
+// rows, for latency).  The threshold is a radix select over the 31-bit
 // magnitude keys (the fp32 bits without the sign order like the magnitudes):
 // three passes of 11, 10 and 10 bits from the top, each an LDS histogram of
 // the keys that still match the chosen prefix, then a workgroup scan of the
