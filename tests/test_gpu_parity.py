@@ -227,6 +227,8 @@ def test_grouped_matches_single_and_oracle(fmt, scale, group, t, count):
     ("ternary", "group", 128, 256, 129, [64, 300, 16]),
     ("ternary", "tensor", 0, 1000, 70, [50, 33]),              # k % 16 != 0: the general kernel, one each
     ("binary", "row", 0, 192, 77, [16 + 8 * (i % 9) for i in range(140)]),  # three launches of at most 64
+    ("ternary", "group", 64, 256, 40, [16 + 16 * (i % 5) + (i % 3) for i in range(70)]),   # two launches
+    ("int4", "row", 0, 128, 33, [32 + 8 * (i % 7) for i in range(65)]),
 ])
 def test_batched_grouped_matches_single_and_oracle(fmt, scale, group, k, t, ns):
     """lowbit_linear_batched_grouped (one launch's tiles over several
