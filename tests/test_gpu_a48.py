@@ -198,3 +198,60 @@ def test_sparse8_layer(entry, fmt, scale, n, k, t):
         _, natural = oracle.weight_codes(w, fmt, scale, group, fmt == "int4")
         slack = group_sum_slack(acc_ref, natural.reshape(n, -1), sx_ref)
     check_y(y.cpu().numpy(), y32, y64, f"sparse8 layer {entry}", slack)
+
+
+def test_a48_graph_replays_match_eager():
+    """The a4.8 quantisers feeding the products, captured in a HIP graph on a
+    side stream: every replay (with eager work and synchronisations between
+    replays, and a changed input before the last two) equals the eager calls
+    bit for bit."""
+    import torch
+    say("[case] a4.8 graph replays")
+    L = lib()
+    t, k, n = 300, 2560, 640
+    g = np.random.default_rng(21)
+    w = (0.02 * g.standard_normal((n, k))).astype(np.float32)
+    d, pd, sd, _, _ = pack_upload(w, "ternary", "row", 0)
+    x = to_dev(_rows(t, k, 5))
+    q8 = torch.empty((t, k), dtype=torch.int8, device="cuda")
+    s8 = torch.empty((t,), device="cuda")
+    q4 = torch.empty((1, k), dtype=torch.int8, device="cuda")
+    s4 = torch.empty((1,), device="cuda")
+    y8 = torch.empty((t, n), device="cuda")
+    y4 = torch.empty((1, n), device="cuda")
+
+    def body():
+        L.lowbit_act_quant_sparse8(x, q8, s8, k // 2)
+        L.lowbit_linear_batched(d, pd, sd, q8, s8, y8)
+        L.lowbit_act_quant_a4(x[:1], q4, s4)
+        L.lowbit_linear(d, pd, sd, q4, s4, y4)
+
+    def eager():
+        body()
+        torch.cuda.synchronize()
+        return [a.cpu().clone() for a in (q8, s8, y8, q4, s4, y4)]
+
+    ref = eager()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        body()                                            # warm-up on the capturing stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        body()
+    torch.cuda.synchronize()
+    for rep in range(5):
+        if rep == 3:                                      # a new input: the replay must follow it
+            x.copy_(to_dev(_rows(t, k, 6)))
+            torch.cuda.synchronize()
+            ref = eager()
+        for a in (q8, s8, y8, q4, s4, y4):
+            a.zero_()                                     # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [a.cpu() for a in (q8, s8, y8, q4, s4, y4)]
+        for name, a, b in zip(("q8", "s8", "y8", "q4", "s4", "y4"), got, ref):
+            assert torch.equal(a, b), f"replay {rep}: {name} differs from the eager calls"
