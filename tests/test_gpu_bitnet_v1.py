@@ -170,3 +170,60 @@ def test_bitlinear_v1_forward(entry, scale, n, k, t):
         bound += group_sum_slack(expect, natural.reshape(n, -1), sxg)
     err = np.abs(yg.astype(np.float64) - y32)
     assert (err <= bound).all(), f"y: worst {err.max():.3e}"
+
+
+def test_graph_replays_match_eager():
+    """LayerNorm, the per-tensor Q_b = 128 codes (whose workspace a kernel
+    clears, so that a replay starts from zero) and the rotated 4-bit codes,
+    captured in a HIP graph: replays on a smaller-max input after a larger
+    one, with eager work and synchronisations between them, equal the eager
+    calls bit for bit (a stale tensor max would not)."""
+    import torch
+    say("[case] v1 / h4 graph replays")
+    L = lib()
+    t, k = 257, 768
+    x = torch.empty((t, k), device="cuda")
+    xn = torch.empty_like(x)
+    qv = torch.empty((t, k), dtype=torch.int8, device="cuda")
+    sv = torch.empty((t,), device="cuda")
+    qh = torch.empty((t, k), dtype=torch.int8, device="cuda")
+    sh = torch.empty((t,), device="cuda")
+    work = torch.zeros(2, dtype=torch.int32, device="cuda")
+
+    def body():
+        L.lowbit_layernorm(x, xn, eps=1e-5)
+        L.lowbit_act_quant_v1(x, qv, sv, per_tensor=True, work=work)
+        L.lowbit_act_quant_h4(x, qh, sh)
+
+    def inputs(seed, scale):
+        g = np.random.default_rng(seed)
+        x.copy_(to_dev((g.standard_normal((t, k)) * scale).astype(np.float32)))
+        torch.cuda.synchronize()
+
+    def eager():
+        body()
+        torch.cuda.synchronize()
+        return [a.cpu().clone() for a in (xn, qv, sv, qh, sh)]
+
+    inputs(1, 8.0)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        body()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        body()
+    torch.cuda.synchronize()
+    for rep, (seed, scale) in enumerate([(1, 8.0), (1, 8.0), (2, 0.5), (2, 0.5), (3, 2.0)]):
+        inputs(seed, scale)
+        ref = eager()
+        for a in (xn, qv, sv, qh, sh):
+            a.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, a, b in zip(("layernorm", "v1 codes", "v1 s_x", "h4 codes", "h4 s_x"),
+                              [a.cpu() for a in (xn, qv, sv, qh, sh)], ref):
+            assert torch.equal(a, b), f"replay {rep}: {name} differs from the eager calls"
