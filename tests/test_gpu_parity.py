@@ -365,3 +365,76 @@ def test_fused_quantiser_edges(fmt):
         assert int(st.cpu()[0]) == 0
         for i in range(len(descs)):
             assert torch.equal(qfs[i], qs[i]) and torch.equal(sxfs[i], sxs[i]) and torch.equal(yfs[i], ys[i]), i
+
+
+def test_grouped_schedules_replay_equal_to_eager():
+    """The schedules the bench times as graph replays - the int8 quantiser
+    then grouped GEMVs, the grouped fused GEMVs, and grouped prefill GEMMs -
+    captured once: every replay, with eager work and synchronisations
+    between replays and new inputs before the last two, equals the eager
+    calls bit for bit."""
+    import torch
+    lb = pytest.importorskip("bit_weight_linear_bitlinear_amd")
+    say("[case] grouped schedules as graph replays")
+    k, tp = 2560, 260
+    ns = [2560, 640, 640, 2560, 1000, 48]
+    descs, packed, scales = [], [], []
+    for i, n in enumerate(ns):
+        w, _ = workloads.random_case(900 + i, n, k, 1)
+        d, p, s, _, _ = pack_upload(w, "ternary", "group", 128)
+        descs.append(d); packed.append(p); scales.append(s)
+    xs = [torch.empty((1, k), device="cuda") for _ in ns]
+    xp = [torch.empty((tp, k), device="cuda") for _ in ns]
+    q1 = [torch.empty((1, k), dtype=torch.int8, device="cuda") for _ in ns]
+    s1 = [torch.empty((1,), device="cuda") for _ in ns]
+    qf = [torch.empty((1, k), dtype=torch.int8, device="cuda") for _ in ns]
+    sf = [torch.empty((1,), device="cuda") for _ in ns]
+    qp = [torch.empty((tp, k), dtype=torch.int8, device="cuda") for _ in ns]
+    sp = [torch.empty((tp,), device="cuda") for _ in ns]
+    y1 = [torch.empty((1, n), device="cuda") for n in ns]
+    yf = [torch.empty((1, n), device="cuda") for n in ns]
+    yp = [torch.empty((tp, n), device="cuda") for n in ns]
+    outs = q1 + s1 + y1 + qf + sf + yf + qp + sp + yp
+
+    def body():
+        for x, q, s in zip(xs, q1, s1):
+            lb.lowbit_act_quant(x, q, s)
+        lb.lowbit_linear_grouped(descs, packed, scales, q1, s1, y1)
+        lb.lowbit_linear_grouped_fused(descs, packed, scales, xs, qf, sf, yf)
+        for x, q, s in zip(xp, qp, sp):
+            lb.lowbit_act_quant(x, q, s)
+        lb.lowbit_linear_batched_grouped(descs, packed, scales, qp, sp, yp)
+
+    def inputs(seed):
+        g = np.random.default_rng(seed)
+        for x in xs + xp:
+            x.copy_(to_dev(g.standard_normal(tuple(x.shape)).astype(np.float32)))
+        torch.cuda.synchronize()
+
+    def eager():
+        body()
+        torch.cuda.synchronize()
+        return [a.cpu().clone() for a in outs]
+
+    inputs(1)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        body()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        body()
+    torch.cuda.synchronize()
+    for rep, seed in enumerate([1, 1, 1, 2, 3]):
+        inputs(seed)
+        ref = eager()
+        for a in outs:
+            a.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for j, (a, b) in enumerate(zip([a.cpu() for a in outs], ref)):
+            assert torch.equal(a, b), f"replay {rep}: output {j} differs from the eager calls"
+    assert torch.equal(yf[0].cpu(), y1[0].cpu())        # the fused schedule equals the two-call one
