@@ -70,3 +70,53 @@ def test_layer_with_layernorm(n, k, t):
     b = _bound(x, gv, hv, p64, k).max(axis=1, keepdims=True)
     err = np.abs(y.cpu().numpy().astype(np.float64) - ref)
     assert (err <= 3 * b / std * (1 + np.abs(ref)) + 1e-5 * (1 + np.abs(ref))).all(), f"worst {err.max():.3e}"
+
+
+@pytest.mark.parametrize("t", [1, 300])
+def test_graph_replays_match_eager(t):
+    """The projection captured in a HIP graph (decode and prefill work
+    splits): every replay, with eager work, synchronisations and a new input
+    between replays, equals the eager call bit for bit."""
+    import torch
+    say(f"[case] onebit graph replays t={t}")
+    L = lib()
+    n, k = 1024, 2560
+    g = np.random.default_rng(t)
+    w = g.standard_normal((n, k)).astype(np.float32)
+    d = L.lowbit_describe(L.BINARY1, L.SCALE_ROW, n, k)
+    packed = np.empty(d.packed_bytes, np.uint8)
+    L.lowbit_pack(d, w, packed, np.empty(d.n_scales, np.float32))
+    pd = to_dev(packed)
+    gv = to_dev((1 + 0.1 * g.standard_normal(k)).astype(np.float16))
+    hv = to_dev((0.01 + 0.01 * np.abs(g.standard_normal(n))).astype(np.float16))
+    x = to_dev(g.standard_normal((t, k)).astype(np.float16))
+    y = torch.empty((t, n), device="cuda")
+
+    def body():
+        L.lowbit_onebit_linear(d, pd, gv, hv, x, y)
+
+    body()
+    torch.cuda.synchronize()
+    ref = y.cpu().clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        body()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        body()
+    torch.cuda.synchronize()
+    for rep in range(5):
+        if rep == 3:
+            x.copy_(to_dev(g.standard_normal((t, k)).astype(np.float16)))
+            torch.cuda.synchronize()
+            body()
+            torch.cuda.synchronize()
+            ref = y.cpu().clone()
+        y.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.cpu(), ref), f"replay {rep} differs from the eager call"
