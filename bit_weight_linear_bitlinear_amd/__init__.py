@@ -148,6 +148,20 @@ def _check(status: int, call: str) -> None:
         raise LowbitError(status, call)
 
 
+# element types the C ABI reads or writes behind each argument name
+_F32, _I8, _U8, _I32, _F16 = "float32", "int8", "uint8", "int32", "float16"
+
+
+def _types(**args):
+    """Element types, checked for every argument before any other check:
+    name=(tensor or list of tensors or None, dtype name or tuple of names)."""
+    for name, (t, dtype) in args.items():
+        allowed = (dtype,) if isinstance(dtype, str) else dtype
+        for v in (t if isinstance(t, (list, tuple)) else (t,)):
+            if v is not None and str(v.dtype).replace("torch.", "") not in allowed:
+                raise ValueError(f"{name}: expected dtype {' or '.join(allowed)}, got {v.dtype}")
+
+
 def _dev(t, name, nbytes=None):
     """Data pointer of a contiguous device tensor holding >= nbytes (None -> NULL)."""
     if t is None:
@@ -189,34 +203,42 @@ def lowbit_pack(d: lowbit_desc, w: np.ndarray, packed: np.ndarray, scales: np.nd
 
 def lowbit_act_quant(x, q, sx, status=None, stream=None) -> None:
     """Device: x fp32[t, k] -> q int8[t, k], sx fp32[t]; status int32[1] or None."""
+    _types(x=(x, _F32), q=(q, _I8), sx=(sx, _F32), status=(status, _I32))
     t, k = x.shape
-    _check(_lib.lowbit_act_quant(_dev(x, "x", 4 * t * k), t, k, _dev(q, "q", t * k), _dev(sx, "sx", 4 * t),
-                                 _dev(status, "status", 4), _stream(stream)), "lowbit_act_quant")
+    _check(_lib.lowbit_act_quant(_dev(x, "x", 4 * t * k), t, k, _dev(q, "q", t * k),
+                                 _dev(sx, "sx", 4 * t), _dev(status, "status", 4), _stream(stream)),
+           "lowbit_act_quant")
 
 
 def lowbit_act_quant_h4(x, q, sx, status=None, stream=None) -> None:
     """Device: x fp32[t, k] -> block-Hadamard-rotated INT4 codes q int8[t, k]
     (in [-7, 7]) and sx fp32[t]; status int32[1] or None."""
+    _types(x=(x, _F32), q=(q, _I8), sx=(sx, _F32), status=(status, _I32))
     t, k = x.shape
-    _check(_lib.lowbit_act_quant_h4(_dev(x, "x", 4 * t * k), t, k, _dev(q, "q", t * k), _dev(sx, "sx", 4 * t),
-                                    _dev(status, "status", 4), _stream(stream)), "lowbit_act_quant_h4")
+    _check(_lib.lowbit_act_quant_h4(_dev(x, "x", 4 * t * k), t, k, _dev(q, "q", t * k),
+                                    _dev(sx, "sx", 4 * t), _dev(status, "status", 4), _stream(stream)),
+           "lowbit_act_quant_h4")
 
 
 def lowbit_act_quant_a4(x, q, sx, status=None, stream=None) -> None:
     """Device: x fp32[t, k] -> per-token INT4 codes q int8[t, k] (in [-7, 7])
     and sx fp32[t] = max|x| / 7; status int32[1] or None."""
+    _types(x=(x, _F32), q=(q, _I8), sx=(sx, _F32), status=(status, _I32))
     t, k = x.shape
-    _check(_lib.lowbit_act_quant_a4(_dev(x, "x", 4 * t * k), t, k, _dev(q, "q", t * k), _dev(sx, "sx", 4 * t),
-                                    _dev(status, "status", 4), _stream(stream)), "lowbit_act_quant_a4")
+    _check(_lib.lowbit_act_quant_a4(_dev(x, "x", 4 * t * k), t, k, _dev(q, "q", t * k),
+                                    _dev(sx, "sx", 4 * t), _dev(status, "status", 4), _stream(stream)),
+           "lowbit_act_quant_a4")
 
 
 def lowbit_act_quant_sparse8(x, q, sx, keep, status=None, stream=None) -> None:
     """Device: each row of x fp32[t, k] keeps its `keep` largest |x| (ties to
     the lower channel) with per-token INT8 codes, the rest code 0 -> q
     int8[t, k], sx fp32[t] = max|x| / 127; status int32[1] or None."""
+    _types(x=(x, _F32), q=(q, _I8), sx=(sx, _F32), status=(status, _I32))
     t, k = x.shape
     _check(_lib.lowbit_act_quant_sparse8(_dev(x, "x", 4 * t * k), t, k, int(keep), _dev(q, "q", t * k),
-                                         _dev(sx, "sx", 4 * t), _dev(status, "status", 4), _stream(stream)),
+                                         _dev(sx, "sx", 4 * t), _dev(status, "status", 4),
+                                         _stream(stream)),
            "lowbit_act_quant_sparse8")
 
 
@@ -224,14 +246,17 @@ def lowbit_act_quant_v1(x, q, sx, eps=1e-5, per_tensor=False, status=None, work=
     """Device: the original BitNet's Q_b = 128 codes of x fp32[t, k] -> q
     int8[t, k] in [-128, 127], sx fp32[t] = gamma / 128; per_tensor needs
     work, a device uint32[2] (or int32[2]) workspace."""
+    _types(x=(x, _F32), q=(q, _I8), sx=(sx, _F32), status=(status, _I32), work=(work, (_I32, "uint32")))
     t, k = x.shape
     _check(_lib.lowbit_act_quant_v1(_dev(x, "x", 4 * t * k), t, k, float(eps), int(bool(per_tensor)),
-                                    _dev(q, "q", t * k), _dev(sx, "sx", 4 * t), _dev(status, "status", 4),
-                                    _dev(work, "work", 8), _stream(stream)), "lowbit_act_quant_v1")
+                                    _dev(q, "q", t * k), _dev(sx, "sx", 4 * t),
+                                    _dev(status, "status", 4), _dev(work, "work", 8),
+                                    _stream(stream)), "lowbit_act_quant_v1")
 
 
 def lowbit_layernorm(x, out, eps=1e-5, gain=None, bias=None, stream=None) -> None:
     """Device: out = LayerNorm(x) per row (fp32), optional gain / bias [d]."""
+    _types(x=(x, _F32), out=(out, _F32), gain=(gain, _F32), bias=(bias, _F32))
     t, d = x.shape
     _check(_lib.lowbit_layernorm(_dev(x, "x", 4 * t * d), t, d, float(eps), _dev(gain, "gain", 4 * d),
                                  _dev(bias, "bias", 4 * d), _dev(out, "out", 4 * t * d), _stream(stream)),
@@ -241,15 +266,18 @@ def lowbit_layernorm(x, out, eps=1e-5, gain=None, bias=None, stream=None) -> Non
 def lowbit_onebit_linear(d: lowbit_desc, packed, g, h, x, y, stream=None) -> None:
     """Device: OneBit's projection y fp32[t, n] = h * (fp16(x * g) . S^T) from
     x fp16[t, k], g fp16[k], h fp16[n] and binary packed signs."""
+    _types(packed=(packed, _U8), g=(g, _F16), h=(h, _F16), x=(x, _F16), y=(y, _F32))
     t = x.shape[0]
-    if x.dim() != 2 or x.shape[1] != d.k or x.element_size() != 2 or g.element_size() != 2 or h.element_size() != 2:
-        raise ValueError("onebit: x [t, k], g [k], h [n] must be fp16")
-    _check(_lib.lowbit_onebit_linear(ctypes.byref(d), _dev(packed, "packed", d.packed_bytes), _dev(g, "g", 2 * d.k),
-                                     _dev(h, "h", 2 * d.n), _dev(x, "x", 2 * t * d.k), t, _dev(y, "y", 4 * t * d.n),
+    if x.dim() != 2 or x.shape[1] != d.k:
+        raise ValueError(f"onebit: x: expected [t, {d.k}], got {tuple(x.shape)}")
+    _check(_lib.lowbit_onebit_linear(ctypes.byref(d), _dev(packed, "packed", d.packed_bytes),
+                                     _dev(g, "g", 2 * d.k), _dev(h, "h", 2 * d.n),
+                                     _dev(x, "x", 2 * t * d.k), t, _dev(y, "y", 4 * t * d.n),
                                      _stream(stream)), "lowbit_onebit_linear")
 
 
 def _linear_ptrs(d, packed, scales, q, sx, y, acc):
+    _types(packed=(packed, _U8), scales=(scales, _F32), q=(q, _I8), sx=(sx, _F32), y=(y, _F32), acc=(acc, _I32))
     t = q.shape[0]
     if q.dim() != 2 or q.shape[1] != d.k:
         raise ValueError(f"q: expected [t, {d.k}], got {tuple(q.shape)}")
@@ -315,6 +343,7 @@ def lowbit_linear_grouped(descs, packed, scales, q, sx, y, acc=None, stream=None
 
 
 def _fused_ptrs(d, packed, scales, x, q, sx, y):
+    _types(packed=(packed, _U8), scales=(scales, _F32), x=(x, _F32), q=(q, _I8), sx=(sx, _F32), y=(y, _F32))
     t = x.shape[0]
     if x.dim() != 2 or x.shape[1] != d.k or tuple(q.shape) != (t, d.k):
         raise ValueError(f"x, q: expected [t, {d.k}], got {tuple(x.shape)}, {tuple(q.shape)}")
@@ -326,6 +355,7 @@ def _fused_ptrs(d, packed, scales, x, q, sx, y):
 def lowbit_linear_fused(d: lowbit_desc, packed, scales, x, q, sx, y, status=None, stream=None) -> None:
     """Device GEMV from fp32 x: the activation quantiser runs inside the product;
     q int8[t, k] and sx fp32[t] receive the codes and scales as by-products."""
+    _types(status=(status, _I32))
     _check(_lib.lowbit_linear_fused(ctypes.byref(d), *_fused_ptrs(d, packed, scales, x, q, sx, y),
                                     _dev(status, "status", 4), _stream(stream)), "lowbit_linear_fused")
 
@@ -334,6 +364,7 @@ class GroupedFusedCall:
     """Marshalled arguments of one lowbit_linear_grouped_fused call."""
 
     def __init__(self, descs, packed, scales, x, q, sx, y, status=None):
+        _types(status=(status, _I32))
         n = len(descs)
         if not (n == len(packed) == len(scales) == len(x) == len(q) == len(sx) == len(y)) or n < 1:
             raise ValueError("lowbit_linear_grouped_fused: argument lists differ in length")
@@ -413,6 +444,7 @@ class DecodeModel:
         import torch
         if len(descs) != 6 or len(packed) != 5 * n_layers + 1 or len(scales) != len(packed):
             raise ValueError("DecodeModel: 6 descriptors and 5 * n_layers + 1 weight / scale tensors expected")
+        _types(embed=(embed, _F32), norms=(norms, _F32), packed=(list(packed), _U8), scales=(list(scales), _F32))
         m = lowbit_model()
         m.d_model, m.n_layers, m.n_heads, m.d_ff, m.vocab, m.context = d_model, n_layers, n_heads, d_ff, vocab, context
         m.norm_eps, m.rope_base = norm_eps, rope_base
@@ -440,8 +472,10 @@ class DecodeModel:
         self._keep = (embed, norms, list(packed), list(scales))
 
     def step(self, state, logits, tokens=None, trace=None, stream=None) -> None:
+        _types(state=(state, _I32), logits=(logits, _F32), tokens=(tokens, _I32), trace=(trace, _F32))
         m = self.model
-        _check(_lib.lowbit_decode_step(ctypes.byref(m), _dev(state, "state", 16), _dev(logits, "logits", 4 * m.vocab),
+        _check(_lib.lowbit_decode_step(ctypes.byref(m), _dev(state, "state", 16),
+                                       _dev(logits, "logits", 4 * m.vocab),
                                        _dev(tokens, "tokens", 4 * m.context),
                                        _dev(trace, "trace", 4 * self.trace_floats), _stream(stream)),
                "lowbit_decode_step")

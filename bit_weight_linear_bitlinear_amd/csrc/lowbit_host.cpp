@@ -19,18 +19,20 @@
 
 namespace {
 
-constexpr int32_t kAbiVersion = 4;
+constexpr int32_t kAbiVersion = 5;
 
 // Field geometry of the packed formats (the layout comment of lowbit.h).
 int codes_per_word(int32_t fmt) { return fmt == LOWBIT_TERNARY2 ? 16 : (fmt == LOWBIT_INT4 ? 8 : 32); }
 int block_k(int32_t fmt) { return fmt == LOWBIT_BINARY1 ? 128 : 64; }   // k of one matrix-core step
 
 int32_t max_k_of(int32_t fmt) {
-    // int32 sums of (scaled code) x (activation code): |sum| <= k * 127 * qmax * scale
+    // int32 sums of (scaled code) x (activation code): |sum| <= k * 128 * qmax
+    // * scale.  128, not 127: the Q_b = 128 quantiser's codes reach -128 and
+    // feed the same products.
     switch (fmt) {
         case LOWBIT_TERNARY2:
-        case LOWBIT_BINARY1: return (int32_t)(2147483647LL / (127LL * 1 * 64));
-        case LOWBIT_INT4:    return (int32_t)(2147483647LL / (127LL * 7 * 16));
+        case LOWBIT_BINARY1: return (int32_t)(2147483647LL / (128LL * 1 * 64));
+        case LOWBIT_INT4:    return (int32_t)(2147483647LL / (128LL * 7 * 16));
         default:             return 0;
     }
 }
@@ -309,9 +311,28 @@ WorkLayout work_layout(const lowbit_model* m) {
     return w;
 }
 
-int64_t trace_floats(const lowbit_model* m) {
+// The trace: the float intermediates, padded to a whole 16 bytes, then one
+// code record per product (per layer qkv, o, gate, up, down; then the head):
+// 16 bytes holding s_x (first float), then the product's k int8 codes padded
+// to a multiple of 16 bytes.
+int64_t trace_float_part(const lowbit_model* m) {
     const int64_t d = m->d_model, ff = m->d_ff;
-    return d + (int64_t)m->n_layers * (12 * d + 3 * ff) + d;
+    return (d + (int64_t)m->n_layers * (12 * d + 3 * ff) + d + 3) / 4 * 4;
+}
+
+int64_t code_record_bytes(int64_t k) { return 16 + up16(k); }
+
+// byte offset of the code record of (layer, slot) from the start of the code part
+int64_t code_record_offset(const lowbit_model* m, int layer, int slot) {
+    const int64_t d = m->d_model, ff = m->d_ff;
+    const int64_t per_layer = 4 * code_record_bytes(d) + code_record_bytes(ff);
+    if (layer >= m->n_layers) return (int64_t)m->n_layers * per_layer;
+    return layer * per_layer + (int64_t)slot * code_record_bytes(d);   // down (slot 4) follows the four k = d records
+}
+
+int64_t trace_floats(const lowbit_model* m) {
+    return trace_float_part(m) + code_record_offset(m, m->n_layers, LOWBIT_PROJ_HEAD) / 4 +
+           code_record_bytes(m->d_model) / 4;
 }
 
 }  // namespace
@@ -374,10 +395,17 @@ lowbit_status lowbit_decode_step(const lowbit_model* m, int32_t* state, float* l
     int8_t* q1 = reinterpret_cast<int8_t*>(wb + wl.q1);
     int32_t* act_status = state + 2;
 
-    // one fused BitLinear on one token
+    // one fused BitLinear on one token; with a trace its codes and s_x go to
+    // the product's own code record
     auto product = [&](int slot, int layer, const float* x, int8_t* q, float* sxp, float* y,
                        lowbit::LinearArgs* out) -> lowbit_status {
         const int i = layer < L ? 5 * layer + slot : 5 * L;
+        if (trace) {
+            uint8_t* rec = reinterpret_cast<uint8_t*>(trace + trace_float_part(m)) +
+                           code_record_offset(m, layer, layer < L ? slot : LOWBIT_PROJ_HEAD);
+            sxp = reinterpret_cast<float*>(rec);
+            q = reinterpret_cast<int8_t*>(rec + 16);
+        }
         lowbit_status s = linear_common(&m->proj[slot], m->packed[i], m->scales[i], q, sxp, 1, y, nullptr, out);
         out->x = x;
         out->status = act_status;

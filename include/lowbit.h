@@ -468,11 +468,20 @@ lowbit_status lowbit_swiglu(const float* gate, const float* up, int64_t n, float
  * or -1 when the model's sizes are invalid. */
 int64_t lowbit_model_work_bytes(const lowbit_model* m);
 
-/* Floats of the optional trace buffer of lowbit_decode_step: x0 [d] (the
- * embedding row), then per layer h [d], qkv [3d], q rotated [d], k rotated
- * [d], attention output [d], o [d], x after attention [d], h2 [d], gate [ff],
- * up [ff], SwiGLU output [ff], down [d], x after the FFN [d], and last the
- * final norm's output [d]; -1 when the model's sizes are invalid. */
+/* 4-byte words of the optional trace buffer of lowbit_decode_step; -1 when
+ * the model's sizes are invalid.  Two parts:
+ *  - floats: x0 [d] (the embedding row), then per layer h [d], qkv [3d],
+ *    q rotated [d], k rotated [d], attention output [d], o [d], x after
+ *    attention [d], h2 [d], gate [ff], up [ff], SwiGLU output [ff], down [d],
+ *    x after the FFN [d], and last the final norm's output [d]; padded with
+ *    up to 3 unused floats to a multiple of 4;
+ *  - code records, one per product in the order per layer qkv, o, gate, up,
+ *    down, then the head: 16 bytes whose first float is the product's s_x,
+ *    then its input's k int8 codes (k = d, or ff for down), padded with
+ *    unused bytes to a multiple of 16.  These are the per-token codes
+ *    (M8.8 0x02C) the product consumed, so a test can hold each BitLinear of
+ *    the step against the oracle's codes and integer product of its own
+ *    traced input. */
 int64_t lowbit_model_trace_floats(const lowbit_model* m);
 
 /*
@@ -499,8 +508,9 @@ lowbit_status lowbit_decode_step(const lowbit_model* m, int32_t* state, float* l
 
 /* Largest k the kernels accept for a format.  The operator's own bound
  * (M8.8 0x09C) is k * 127 * qmax < 2^31; the kernels hold each code scaled
- * by 64 (ternary, binary) or 16 (int4) in int8 lanes, so their int32 sums need
- * k * 127 * qmax * scale < 2^31: k <= 264208 (ternary, binary), 150976 (int4). */
+ * by 64 (ternary, binary) or 16 (int4) in int8 lanes, and activation codes
+ * reach -128 (lowbit_act_quant_v1), so their int32 sums need
+ * k * 128 * qmax * scale < 2^31: k <= 262143 (ternary, binary), 149796 (int4). */
 int32_t lowbit_max_k(int32_t format);
 
 const char* lowbit_status_string(lowbit_status s);

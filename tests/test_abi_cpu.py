@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol():
     lib = ctypes.CDLL(lb.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
-    assert lb.lowbit_abi_version() == 4
+    assert lb.lowbit_abi_version() == 5
 
 
 def test_describe_sizes():
@@ -80,8 +80,11 @@ def test_describe_range_bound():
         with pytest.raises(lb.LowbitError) as e:
             lb.lowbit_describe(fmt, 0, 1, kmax + 1)
         assert e.value.status == 2
-    assert lb.lowbit_max_k(lb.TERNARY2) * 127 * 64 < 2**31 <= (lb.lowbit_max_k(lb.TERNARY2) + 1) * 127 * 64
-    assert lb.lowbit_max_k(lb.INT4) * 127 * 7 * 16 < 2**31 <= (lb.lowbit_max_k(lb.INT4) + 1) * 127 * 7 * 16
+    # |activation code| <= 128 (the Q_b = 128 codes reach -128)
+    assert lb.lowbit_max_k(lb.TERNARY2) * 128 * 64 < 2**31 <= (lb.lowbit_max_k(lb.TERNARY2) + 1) * 128 * 64
+    assert lb.lowbit_max_k(lb.BINARY1) == lb.lowbit_max_k(lb.TERNARY2) == 262143
+    assert lb.lowbit_max_k(lb.INT4) * 128 * 7 * 16 < 2**31 <= (lb.lowbit_max_k(lb.INT4) + 1) * 128 * 7 * 16
+    assert lb.lowbit_max_k(lb.INT4) == 149796
 
 
 def test_device_calls_reject_bad_arguments_before_launch():
@@ -204,7 +207,19 @@ def test_model_sizes():
     want = sum(up16(b) for b in (4 * d, 4 * d, 4 * d, 12 * d, 4 * d, 4 * d, 4 * ff, 4 * ff, 4 * ff, 4 * d, 16,
                                  max(d, ff), ff))
     assert lib.lowbit_model_work_bytes(ctypes.byref(m)) == want
-    assert lib.lowbit_model_trace_floats(ctypes.byref(m)) == d + L * (12 * d + 3 * ff) + d
+    # floats (padded to 4), then per layer code records of qkv, o, gate, up
+    # (k = d) and down (k = ff), then the head's: 16 bytes of s_x + codes
+    floats = (d + L * (12 * d + 3 * ff) + d + 3) // 4 * 4
+    codes = L * (4 * (16 + up16(d)) + 16 + up16(ff)) + 16 + up16(d)
+    assert lib.lowbit_model_trace_floats(ctypes.byref(m)) == floats + codes // 4
+    m.d_ff = ff = 98                                          # ragged widths pad both parts
+    m.proj[lb.PROJ_GATE] = lb.lowbit_describe(lb.TERNARY2, lb.SCALE_TENSOR, ff, d)
+    m.proj[lb.PROJ_UP] = lb.lowbit_describe(lb.TERNARY2, lb.SCALE_TENSOR, ff, d)
+    m.proj[lb.PROJ_DOWN] = lb.lowbit_describe(lb.TERNARY2, lb.SCALE_TENSOR, d, ff)
+    floats = (d + L * (12 * d + 3 * ff) + d + 3) // 4 * 4
+    codes = L * (4 * (16 + up16(d)) + 16 + up16(ff)) + 16 + up16(d)
+    assert floats % 4 == 0 and codes % 16 == 0
+    assert lib.lowbit_model_trace_floats(ctypes.byref(m)) == floats + codes // 4
     for field, bad in (("n_heads", 3), ("d_model", 250), ("context", 0), ("context", 8193), ("vocab", 0),
                        ("n_layers", 0), ("rope_base", 0.0), ("norm_eps", -1.0)):
         mb = _model_struct()
@@ -320,3 +335,62 @@ def test_v1_quantiser_and_layernorm_reject_bad_arguments_on_the_host():
     assert lib.lowbit_layernorm(x, 1, 0, ctypes.c_float(1e-5), None, None, q, None) == 1
     assert lib.lowbit_layernorm(x, 1, 64, ctypes.c_float(-1e-5), None, None, q, None) == 1
     assert lib.lowbit_layernorm(None, 1, 64, ctypes.c_float(1e-5), None, None, q, None) == 1
+
+
+def _bad_dtype(fn, name):
+    with pytest.raises(ValueError) as e:
+        fn()
+    assert f"{name}: expected dtype" in str(e.value), str(e.value)
+
+
+def test_binding_rejects_wrong_dtypes():
+    """Every device wrapper checks element types before any pointer reaches
+    the library (a float64 x, an int32 q or a float y would otherwise be
+    read or written as another type).  CPU tensors suffice: the dtype check
+    comes first, so nothing touches a GPU."""
+    import torch
+    t, k, n = 2, 64, 16
+    d = lb.lowbit_describe(lb.TERNARY2, lb.SCALE_TENSOR, n, k)
+    f32 = lambda *s: torch.zeros(*s, dtype=torch.float32)
+    i8 = lambda *s: torch.zeros(*s, dtype=torch.int8)
+    x, q, sx, y = f32(t, k), i8(t, k), f32(t), f32(t, n)
+    packed, scales = torch.zeros(d.packed_bytes, dtype=torch.uint8), f32(d.n_scales)
+    acc = torch.zeros(t, n, 1, dtype=torch.int32)
+    x64, q32, y64 = x.double(), q.int(), y.double()
+    for quant in (lb.lowbit_act_quant, lb.lowbit_act_quant_h4, lb.lowbit_act_quant_a4):
+        _bad_dtype(lambda: quant(x64, q, sx), "x")
+        _bad_dtype(lambda: quant(x, q32, sx), "q")
+        _bad_dtype(lambda: quant(x, q, sx.double()), "sx")
+        _bad_dtype(lambda: quant(x, q, sx, status=f32(1)), "status")
+    _bad_dtype(lambda: lb.lowbit_act_quant_sparse8(x64, q, sx, 3), "x")
+    _bad_dtype(lambda: lb.lowbit_act_quant_sparse8(x, q32, sx, 3), "q")
+    _bad_dtype(lambda: lb.lowbit_act_quant_v1(x, q32, sx), "q")
+    _bad_dtype(lambda: lb.lowbit_act_quant_v1(x, q, sx, per_tensor=True, work=f32(2)), "work")
+    _bad_dtype(lambda: lb.lowbit_layernorm(x64, x), "x")
+    _bad_dtype(lambda: lb.lowbit_layernorm(x, x64), "out")
+    for fn in (lb.lowbit_linear, lb.lowbit_linear_batched):
+        _bad_dtype(lambda: fn(d, packed.to(torch.int8), scales, q, sx, y), "packed")
+        _bad_dtype(lambda: fn(d, packed, scales.double(), q, sx, y), "scales")
+        _bad_dtype(lambda: fn(d, packed, scales, q32, sx, y), "q")
+        _bad_dtype(lambda: fn(d, packed, scales, q, sx.half(), y), "sx")
+        _bad_dtype(lambda: fn(d, packed, scales, q, sx, y64), "y")
+        _bad_dtype(lambda: fn(d, packed, scales, q, sx, y, acc.long()), "acc")
+    _bad_dtype(lambda: lb.lowbit_linear_grouped([d], [packed], [scales], [q32], [sx], [y]), "q")
+    _bad_dtype(lambda: lb.lowbit_linear_batched_grouped([d], [packed], [scales], [q], [sx], [y64]), "y")
+    _bad_dtype(lambda: lb.lowbit_linear_fused(d, packed, scales, x64, q, sx, y), "x")
+    _bad_dtype(lambda: lb.lowbit_linear_fused(d, packed, scales, x, q32, sx, y), "q")
+    _bad_dtype(lambda: lb.lowbit_linear_grouped_fused([d], [packed], [scales], [x], [q], [sx], [y64]), "y")
+    db = lb.lowbit_describe(lb.BINARY1, lb.SCALE_ROW, n, k)
+    h16, g16, x16 = torch.zeros(n, dtype=torch.float16), torch.zeros(k, dtype=torch.float16), x.half()
+    _bad_dtype(lambda: lb.lowbit_onebit_linear(db, packed, g16, h16, x16.bfloat16(), y), "x")
+    _bad_dtype(lambda: lb.lowbit_onebit_linear(db, packed, g16.float(), h16, x16, y), "g")
+    _bad_dtype(lambda: lb.lowbit_onebit_linear(db, packed, g16, h16, x16, y.half()), "y")
+    _bad_dtype(lambda: lb.lowbit_linear_fused(d, packed, scales, x, q, sx, y, status=f32(1)), "status")
+    descs6 = [lb.lowbit_describe(lb.TERNARY2, lb.SCALE_TENSOR, nn, kk)
+              for nn, kk in ((192, 64), (64, 64), (128, 64), (128, 64), (64, 128), (100, 64))]
+    pk = [torch.zeros(dd.packed_bytes, dtype=torch.uint8) for dd in descs6[:5]] + \
+         [torch.zeros(descs6[5].packed_bytes, dtype=torch.int8)]
+    sc = [f32(dd.n_scales) for dd in descs6[:5]] + [f32(1)]
+    _bad_dtype(lambda: lb.DecodeModel(64, 1, 1, 128, 100, 8, descs6, f32(100, 64), f32(3, 64), pk, sc), "packed")
+    _bad_dtype(lambda: lb.DecodeModel(64, 1, 1, 128, 100, 8, descs6, f32(100, 64).double(), f32(3, 64), pk, sc),
+               "embed")

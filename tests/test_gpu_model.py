@@ -5,8 +5,20 @@ CPU oracle (oracle/model.py), through the C ABI.
 * The step's operations on their own (lowbit_rmsnorm, lowbit_rope_attention,
   lowbit_swiglu) on seeded inputs, element by element, with tolerances derived
   from their fp32 arithmetic.
+* Whole steps, stage by stage (the check that decides parity): every stage
+  of the step is held against the oracle applied to the GPU's own traced
+  input of that stage.  Each BitLinear's int8 codes and s_x are bit-exact
+  against the oracle's quantiser of its traced fp32 input, its int32
+  accumulators (the library's product rerun on those codes with the integer
+  output) bit-exact against the oracle's integer product, and its fp32
+  output within 1e-5 relative + 1e-6 absolute of the oracle's epilogue; the
+  residual adds are bit-exact fp32 sums; the fused RMSNorm and SwiGLU
+  prologues, the rotary embedding and the attention are element-wise within
+  bounds derived from their fp32 arithmetic; the next token is the argmax of
+  the GPU's logits.
 * Whole steps, teacher-forced over a seeded prompt, against the oracle run
-  independently from the same seeded weights and tokens.  Up to the first
+  independently from the same seeded weights and tokens (a trajectory smoke
+  check on top of the stage-by-stage one).  Up to the first
   quantised activation the two agree to fp32 rounding; after it, a value that
   the GPU (fp32) and the oracle (binary64, rounded to fp32) place on opposite
   sides of a rounding boundary moves one int8 code by one step, which moves the
@@ -192,13 +204,159 @@ def _state(tok, pos):
     return torch.tensor([tok, pos, 0, 0], dtype=torch.int32, device="cuda")
 
 
+def _split_trace(tr, d, L, ff):
+    """The trace's float part and an accessor of its code records (layout in
+    include/lowbit.h, lowbit_model_trace_floats): code(layer, slot) -> (int8
+    codes [k], s_x as a float32 scalar); layer L is the head."""
+    nf = d + L * (12 * d + 3 * ff) + d
+    raw = tr[(nf + 3) // 4 * 4:].view(np.uint8)
+    rec = lambda k: 16 + (k + 15) // 16 * 16
+    per_layer = 4 * rec(d) + rec(ff)
+
+    def code(layer, slot):
+        off = L * per_layer if layer >= L else layer * per_layer + slot * rec(d)
+        k = ff if (layer < L and slot == 4) else d
+        return raw[off + 16:off + 16 + k].view(np.int8).copy(), raw[off:off + 4].view(np.float32)[0]
+    return tr[:nf], code
+
+
+def _bits(a):
+    return np.asarray(a, np.float32).view(np.uint32)
+
+
+@pytest.mark.parametrize("which", ["model_pair", "small_pair"])
+def test_decode_step_stages_exact(which, request):
+    """Twelve teacher-forced steps; at each, every stage against the oracle
+    applied to the GPU's own traced input of that stage:
+      - each of the 5 L + 1 BitLinears: codes and s_x bit-exact against
+        oracle.act_quant of its traced input; int32 accumulators bit-exact
+        against the oracle's integer product (the library's GEMV rerun on the
+        traced codes with its integer output); y within 1e-5 relative + 1e-6
+        absolute of the oracle's fp32 epilogue, and of its binary64 twin;
+      - residual adds x_mid = x + o and x_out = x_mid + down bit-exact (one
+        fp32 add each);
+      - the fused RMSNorm prologues (h, h2, the final norm) within 1e-5
+        relative per element of the binary64 norm of the GPU's traced
+        residual stream (fp32 sums of <= 4096 squares, one square root, two
+        products), the SwiGLU prologue within 1e-6 relative (fp32 exp, add,
+        divide, multiply);
+      - rotated q and k within 1e-6 of each pair's length; the cache rows at
+        the position equal the traced key and value; the attention output
+        within 1e-5 of max |v| of the binary64 attention over the GPU's
+        cache rows 0 .. pos;
+      - the state's next token is the argmax of the GPU's logits."""
+    import torch
+    lb = _lb()
+    gm, om_ = request.getfixturevalue(which)
+    d, L, H, ff, V = om_.d, om_.n_layers, om_.n_heads, om_.d_ff, om_.vocab
+    g_packed, g_scales = gm._keep[2], gm._keep[3]
+    prompt = workloads.decode_model_tokens(12, V)
+    gm.k_cache.zero_()
+    gm.v_cache.zero_()
+    ls = 12 * d + 3 * ff
+    shapes = _shapes(d, ff, V)
+    names = ["h", "qkv", "q", "k", "attn", "o", "x_mid", "h2", "gate", "up", "a", "down", "x_out"]
+    widths = [d, 3 * d, d, d, d, d, d, d, ff, ff, ff, d, d]
+    worst = {"y_rel": 0.0, "norm_rel": 0.0, "swiglu_rel": 0.0}
+    n_products = 0
+
+    def bitlinear_stage(tag, layer, slot, x_in, y_gpu, code):
+        nonlocal n_products
+        q_g, sx_g = code(layer, slot if layer < L else 5)
+        n, k = shapes[slot if layer < L else 5]
+        q_ref, sx_ref, rs = oracle.act_quant(np.asarray(x_in, np.float32).reshape(1, k))
+        assert rs[0] == 0, tag
+        assert np.array_equal(q_g, q_ref[0]), f"{tag}: codes differ"
+        assert _bits(sx_g) == _bits(sx_ref[0]), f"{tag}: s_x differs"
+        pk, sc = om_.proj(layer, slot if layer < L else 0)
+        y32, y64, acc_ref = oracle.linear(pk, sc, "ternary", "tensor", 0, n, k, q_ref, sx_ref)
+        for ref in (y32[0], y64[0]):
+            err = np.abs(np.asarray(y_gpu, np.float64) - ref)
+            assert np.all(err <= 1e-6 + 1e-5 * np.abs(ref)), f"{tag}: y out of tolerance"
+        worst["y_rel"] = max(worst["y_rel"], float((np.abs(y_gpu - y32[0]) / (1e-6 + 1e-5 * np.abs(y32[0]))).max()))
+        # the integer product of the step's own codes, through the library's GEMV
+        i = 5 * layer + slot if layer < L else 5 * L
+        qd = torch.from_numpy(q_g.reshape(1, k)).cuda()
+        sxd = torch.from_numpy(np.array([sx_g], np.float32)).cuda()
+        yd = torch.empty((1, n), device="cuda")
+        accd = torch.empty((1, n, 1), dtype=torch.int32, device="cuda")
+        lb.lowbit_linear(gm.model.proj[slot if layer < L else 5], g_packed[i], g_scales[i], qd, sxd, yd, accd)
+        torch.cuda.synchronize()
+        assert np.array_equal(accd.cpu().numpy(), acc_ref), f"{tag}: accumulators differ"
+        n_products += 1
+
+    def norm_stage(tag, got, x, g):
+        ref = om.rmsnorm(x, g)
+        rel = np.abs(np.asarray(got, np.float64) - ref) / (np.abs(ref) + 1e-30)
+        worst["norm_rel"] = max(worst["norm_rel"], float(rel.max()))
+        assert np.all(rel <= 1e-5), f"{tag}: RMSNorm out of its fp32 bound"
+
+    for pos, tok in enumerate(prompt):
+        say(f"[case] {which} decode step pos={pos} token={tok} (stage by stage)")
+        st = _state(int(tok), pos)
+        logits = torch.empty(V, device="cuda")
+        trace = torch.full((gm.trace_floats,), float("nan"), device="cuda")
+        gm.step(st, logits, trace=trace)
+        torch.cuda.synchronize()
+        tr, code = _split_trace(trace.cpu().numpy(), d, L, ff)
+        lg = logits.cpu().numpy()
+        kc, vc = gm.k_cache.cpu().numpy(), gm.v_cache.cpu().numpy()
+        s = st.cpu().numpy()
+        assert s.tolist() == [int(np.flatnonzero(lg == lg.max())[0]), pos + 1, 0, 0]
+        x = tr[:d]
+        assert np.array_equal(x, om_.embed[tok])
+        for l in range(L):
+            off = d + l * ls
+            t = {}
+            for nm, w in zip(names, widths):
+                t[nm] = tr[off:off + w]
+                off += w
+            tag = f"pos {pos} layer {l}"
+            norm_stage(f"{tag} h", t["h"], x, om_.norms[2 * l])
+            bitlinear_stage(f"{tag} qkv", l, 0, t["h"], t["qkv"], code)
+            qkv = t["qkv"]
+            kk = qkv[d:2 * d].astype(np.float64).reshape(H, 2, 32)
+            hyp = np.hypot(kk[:, 0], kk[:, 1])
+            qq = qkv[:d].astype(np.float64).reshape(H, 2, 32)
+            hq = np.hypot(qq[:, 0], qq[:, 1])
+            pair_k = np.stack([hyp, hyp], axis=1).reshape(-1)
+            pair_q = np.stack([hq, hq], axis=1).reshape(-1)
+            assert np.all(np.abs(t["q"] - om.rope(qkv[:d], pos, H)) <= 1e-6 * pair_q + 1e-30), f"{tag} q rot"
+            assert np.all(np.abs(t["k"] - om.rope(qkv[d:2 * d], pos, H)) <= 1e-6 * pair_k + 1e-30), f"{tag} k rot"
+            assert np.array_equal(kc[l, pos], t["k"]) and np.array_equal(vc[l, pos], qkv[2 * d:]), f"{tag} cache"
+            ref_attn = om.attend(t["q"], kc[l, :pos + 1], vc[l, :pos + 1], H)
+            assert np.all(np.abs(t["attn"] - ref_attn) <= 1e-5 * np.abs(vc[l, :pos + 1]).max()), f"{tag} attn"
+            bitlinear_stage(f"{tag} o", l, 1, t["attn"], t["o"], code)
+            assert np.array_equal(t["x_mid"], x + t["o"]), f"{tag} x_mid"
+            norm_stage(f"{tag} h2", t["h2"], t["x_mid"], om_.norms[2 * l + 1])
+            bitlinear_stage(f"{tag} gate", l, 2, t["h2"], t["gate"], code)
+            bitlinear_stage(f"{tag} up", l, 3, t["h2"], t["up"], code)
+            ref_a = om.swiglu(t["gate"], t["up"])
+            rel = np.abs(t["a"] - ref_a) / (np.abs(ref_a) + 1e-37)
+            worst["swiglu_rel"] = max(worst["swiglu_rel"], float(rel.max()))
+            assert np.all(np.abs(t["a"] - ref_a) <= 1e-6 * np.abs(ref_a) + 1e-37), f"{tag} SwiGLU"
+            bitlinear_stage(f"{tag} down", l, 4, t["a"], t["down"], code)
+            assert np.array_equal(t["x_out"], t["x_mid"] + t["down"]), f"{tag} x_out"
+            x = t["x_out"]
+        hf = tr[d + L * ls:d + L * ls + d]
+        norm_stage(f"pos {pos} final norm", hf, x, om_.norms[2 * L])
+        bitlinear_stage(f"pos {pos} head", L, 0, hf, lg, code)
+    assert n_products == len(prompt) * (5 * L + 1)
+    say(f"[info] {which}: {n_products} products exact; worst y error / tolerance {worst['y_rel']:.3f}, "
+        f"worst norm rel {worst['norm_rel']:.2e}, worst SwiGLU rel {worst['swiglu_rel']:.2e}")
+
+
 @pytest.mark.parametrize("which", ["model_pair", "small_pair"])
 def test_decode_steps_against_oracle(which, request):
-    """Twelve teacher-forced steps of the seeded prompt: every intermediate
-    and the logits against the independent oracle run (before the first
-    quantised input exactly / to fp32 rounding, after it within the code-flip
-    bound), the caches, the greedy token and the state; the 256-d model (the
-    fused form) and the small irregular one (the general form)."""
+    """Trajectory smoke check on top of the stage-by-stage test: twelve
+    teacher-forced steps of the seeded prompt against an oracle run that never
+    sees the GPU's values.  Before the first quantised input the two agree to
+    fp32 rounding; after it a value that fp32 and binary64 place on opposite
+    sides of a rounding boundary may move one int8 code, so the intermediates,
+    logits and caches are compared by relative norm (5e-2), and the greedy
+    token must match unless the oracle's top two logits are within the
+    observed logit error; the 256-d model (the fused form) and the small
+    irregular one (the general form)."""
     import torch
     gm, om_ = request.getfixturevalue(which)
     d, L, ff, V, C = om_.d, om_.n_layers, om_.d_ff, om_.vocab, om_.context

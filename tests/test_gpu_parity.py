@@ -137,9 +137,10 @@ def test_act_quant_edge_rows():
 
 
 def test_accumulator_bound_worst_case():
-    """At the largest accepted k every activation code 127 times every weight
-    code at its extreme must still be exact (the scaled int32 sums sit one
-    step below 2^31)."""
+    """At the largest accepted k every activation code at its extreme (127,
+    and -128 from the Q_b = 128 quantiser) times every weight code at its
+    extreme must still be exact (the scaled int32 sums sit one step below
+    2^31)."""
     import torch
     lb = pytest.importorskip("bit_weight_linear_bitlinear_amd")
     for fmt, code_w, qmax in (("ternary", 0.5, 1), ("int4", 1.0, 7), ("binary", -0.5, 1)):
@@ -159,6 +160,20 @@ def test_accumulator_bound_worst_case():
             sign_w = np.where(np.arange(n) % 2 == 0, 1, -1) * (1 if code_w > 0 else -1)
             expect = np.outer(np.array([127, -127]), sign_w * qmax) * k
             assert (a == expect).all(), (fmt, entry)
+        # rows of -1 under the Q_b = 128 rule: gamma = 1, codes -128
+        xv = torch.from_numpy(-np.ones((t, k), np.float32)).cuda()
+        qv = torch.empty((t, k), dtype=torch.int8, device="cuda")
+        sxv = torch.empty((t,), dtype=torch.float32, device="cuda")
+        lb.lowbit_act_quant_v1(xv, qv, sxv)
+        torch.cuda.synchronize()
+        assert (qv.cpu().numpy() == -128).all()
+        for entry in ("gemv", "gemm"):
+            y, acc = linear_dev(entry, d, packed, scales, qv, sxv)
+            torch.cuda.synchronize()
+            a = acc.cpu().numpy()[:, :, 0].astype(np.int64)
+            sign_w = np.where(np.arange(n) % 2 == 0, 1, -1) * (1 if code_w > 0 else -1)
+            expect = np.outer(np.array([-128, -128]), sign_w * qmax) * k
+            assert (a == expect).all(), (fmt, entry, "codes -128")
 
 
 def test_entry_points_agree_on_random_large():
