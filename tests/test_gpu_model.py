@@ -397,7 +397,7 @@ def test_decode_steps_against_oracle(which, request):
                 e = _rel(v, ot[nm])
                 worst[nm] = max(worst.get(nm, 0.0), e)
                 assert e <= 5e-2, (pos, l, nm, e)
-        hf = tr[d + L * ls:]
+        hf = tr[d + L * ls:d + L * ls + d]
         o_hf = om.rmsnorm(o_tr[-1]["x_out"], om_.norms[2 * L])
         assert _rel(hf, o_hf) <= 5e-2
         el = _rel(lg, o_logits)
