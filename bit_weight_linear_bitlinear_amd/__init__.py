@@ -104,6 +104,9 @@ _lib.lowbit_model_trace_floats.argtypes = [_M]
 _lib.lowbit_model_trace_floats.restype = ctypes.c_int64
 _lib.lowbit_decode_step.argtypes = [_M, _P, _P, _P, _P, _P]
 _lib.lowbit_decode_step.restype = _i32
+_lib.lowbit_decode_step_noalloc.argtypes = [_M, _P, _P, _P, _P, _P]
+_lib.lowbit_decode_step_noalloc.restype = _i32
+NOALLOC_WORK_BYTES = 1 << 20
 _lib.lowbit_rmsnorm.argtypes = [_P, _P, _P, _P, _i32, _i32, ctypes.c_float, _P, _P]
 _lib.lowbit_rmsnorm.restype = _i32
 _lib.lowbit_rope_attention.argtypes = [_P, _i32, _i32, _i32, ctypes.c_float, _P, _P, _P, _P]
@@ -125,7 +128,7 @@ EXPORTS = ("lowbit_describe", "lowbit_pack", "lowbit_act_quant", "lowbit_act_qua
            "lowbit_linear_batched",
            "lowbit_linear_grouped", "lowbit_linear_batched_grouped", "lowbit_linear_fused",
            "lowbit_linear_grouped_fused",
-           "lowbit_model_work_bytes", "lowbit_model_trace_floats", "lowbit_decode_step",
+           "lowbit_model_work_bytes", "lowbit_model_trace_floats", "lowbit_decode_step", "lowbit_decode_step_noalloc",
            "lowbit_rmsnorm", "lowbit_rope_attention", "lowbit_swiglu",
            "lowbit_max_k", "lowbit_status_string", "lowbit_abi_version", "lowbit_last_hip_error")
 
@@ -471,14 +474,17 @@ class DecodeModel:
         self.model = m
         self._keep = (embed, norms, list(packed), list(scales))
 
-    def step(self, state, logits, tokens=None, trace=None, stream=None) -> None:
+    def step(self, state, logits, tokens=None, trace=None, stream=None, noalloc=False) -> None:
+        """One step (lowbit_decode_step); noalloc=True calls
+        lowbit_decode_step_noalloc, whose workspace is the library's static
+        per-GPU array instead of self.work."""
         _types(state=(state, _I32), logits=(logits, _F32), tokens=(tokens, _I32), trace=(trace, _F32))
         m = self.model
-        _check(_lib.lowbit_decode_step(ctypes.byref(m), _dev(state, "state", 16),
-                                       _dev(logits, "logits", 4 * m.vocab),
-                                       _dev(tokens, "tokens", 4 * m.context),
-                                       _dev(trace, "trace", 4 * self.trace_floats), _stream(stream)),
-               "lowbit_decode_step")
+        fn = _lib.lowbit_decode_step_noalloc if noalloc else _lib.lowbit_decode_step
+        _check(fn(ctypes.byref(m), _dev(state, "state", 16), _dev(logits, "logits", 4 * m.vocab),
+                  _dev(tokens, "tokens", 4 * m.context), _dev(trace, "trace", 4 * self.trace_floats),
+                  _stream(stream)),
+               "lowbit_decode_step_noalloc" if noalloc else "lowbit_decode_step")
 
 
 def lowbit_max_k(format: int) -> int:

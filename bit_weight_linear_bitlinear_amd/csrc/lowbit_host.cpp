@@ -10,6 +10,7 @@
 #include <cmath>
 #include <cstring>
 #include <limits>
+#include <mutex>
 #include <thread>
 #include <vector>
 
@@ -17,7 +18,35 @@
 #include "kernels.hpp"
 #include "lowbit.h"
 
+// The workspace of lowbit_decode_step_noalloc: one copy per GPU, held until
+// the process ends.  Host code never passes this name to a kernel or a copy
+// (on the host it is only a stand-in for the symbol); it uses the device
+// address that hipGetSymbolAddress returns on each device (noalloc_work).
+static __device__ __align__(256) uint8_t scratch[LOWBIT_NOALLOC_WORK_BYTES];
+
 namespace {
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {};
+
+hipError_t noalloc_work(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p || (uintptr_t)p % 256 != 0) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
 
 constexpr int32_t kAbiVersion = 5;
 
@@ -371,24 +400,34 @@ int64_t lowbit_model_work_bytes(const lowbit_model* m) { return model_sizes_ok(m
 
 int64_t lowbit_model_trace_floats(const lowbit_model* m) { return model_sizes_ok(m) ? trace_floats(m) : -1; }
 
-lowbit_status lowbit_decode_step(const lowbit_model* m, int32_t* state, float* logits, int32_t* tokens,
-                                 float* trace, void* hip_stream) {
-    if (!model_sizes_ok(m)) return LOWBIT_E_ARG;
-    const int L = m->n_layers;
-    if (!m->embed || !m->norms || !m->packed || !m->scales || !m->k_cache || !m->v_cache || !m->work || !state ||
-        !logits)
-        return LOWBIT_E_ARG;
-    if ((uintptr_t)m->work % 16 != 0 || (uintptr_t)trace % 16 != 0 || (uintptr_t)state % 4 != 0 ||
-        (uintptr_t)logits % 4 != 0 || (uintptr_t)tokens % 4 != 0 || (uintptr_t)m->embed % 4 != 0 ||
-        (uintptr_t)m->norms % 4 != 0 || (uintptr_t)m->k_cache % 16 != 0 || (uintptr_t)m->v_cache % 4 != 0)
-        return LOWBIT_E_ARG;
-    for (int i = 0; i < 5 * L + 1; ++i)
-        if (!m->packed[i] || !m->scales[i]) return LOWBIT_E_ARG;
+}  // extern "C"
 
+namespace {
+
+// Argument checks of both decode-step entry points (the workspace aside).
+lowbit_status decode_step_args_ok(const lowbit_model* m, const int32_t* state, const float* logits,
+                                  const int32_t* tokens, const float* trace) {
+    if (!model_sizes_ok(m)) return LOWBIT_E_ARG;
+    if (!m->embed || !m->norms || !m->packed || !m->scales || !m->k_cache || !m->v_cache || !state || !logits)
+        return LOWBIT_E_ARG;
+    if ((uintptr_t)trace % 16 != 0 || (uintptr_t)state % 4 != 0 || (uintptr_t)logits % 4 != 0 ||
+        (uintptr_t)tokens % 4 != 0 || (uintptr_t)m->embed % 4 != 0 || (uintptr_t)m->norms % 4 != 0 ||
+        (uintptr_t)m->k_cache % 16 != 0 || (uintptr_t)m->v_cache % 4 != 0)
+        return LOWBIT_E_ARG;
+    for (int i = 0; i < 5 * m->n_layers + 1; ++i)
+        if (!m->packed[i] || !m->scales[i]) return LOWBIT_E_ARG;
+    return LOWBIT_OK;
+}
+
+// One step with the intermediates in `work` (work_layout(m).total bytes,
+// 16-byte aligned); arguments already checked.
+lowbit_status decode_step_impl(const lowbit_model* m, void* work, int32_t* state, float* logits, int32_t* tokens,
+                               float* trace, void* hip_stream) {
+    const int L = m->n_layers;
     const int d = m->d_model, ff = m->d_ff, ctx = m->context;
     const hipStream_t st = (hipStream_t)hip_stream;
     const WorkLayout wl = work_layout(m);
-    uint8_t* wb = static_cast<uint8_t*>(m->work);
+    uint8_t* wb = static_cast<uint8_t*>(work);
     auto wf = [&](int64_t off) { return reinterpret_cast<float*>(wb + off); };
     float* sx = wf(wl.sx);
     int8_t* q0 = reinterpret_cast<int8_t*>(wb + wl.q0);
@@ -558,6 +597,30 @@ lowbit_status lowbit_decode_step(const lowbit_model* m, int32_t* state, float* l
     single(LOWBIT_PROJ_HEAD, L, h, logits);
     if (s == LOWBIT_OK) run(lowbit::launch_argmax_advance(logits, m->vocab, state, ctx, tokens, st));
     return s;
+}
+
+}  // namespace
+
+extern "C" {
+
+lowbit_status lowbit_decode_step(const lowbit_model* m, int32_t* state, float* logits, int32_t* tokens,
+                                 float* trace, void* hip_stream) {
+    const lowbit_status a = decode_step_args_ok(m, state, logits, tokens, trace);
+    if (a != LOWBIT_OK) return a;
+    if (!m->work || (uintptr_t)m->work % 16 != 0) return LOWBIT_E_ARG;
+    return decode_step_impl(m, m->work, state, logits, tokens, trace, hip_stream);
+}
+
+lowbit_status lowbit_decode_step_noalloc(const lowbit_model* m, int32_t* state, float* logits, int32_t* tokens,
+                                         float* trace, void* hip_stream) {
+    const lowbit_status a = decode_step_args_ok(m, state, logits, tokens, trace);
+    if (a != LOWBIT_OK) return a;
+    if (work_layout(m).total > LOWBIT_NOALLOC_WORK_BYTES) return LOWBIT_E_RANGE;
+    clear_hip_error();
+    void* work = nullptr;
+    const hipError_t e = noalloc_work(&work);
+    if (e != hipSuccess) return hip_status(e);
+    return decode_step_impl(m, work, state, logits, tokens, trace, hip_stream);
 }
 
 lowbit_status lowbit_describe(int32_t format, int32_t scale, int32_t n, int32_t k, int32_t group, int32_t flags,

@@ -506,6 +506,30 @@ int64_t lowbit_model_trace_floats(const lowbit_model* m);
 lowbit_status lowbit_decode_step(const lowbit_model* m, int32_t* state, float* logits, int32_t* tokens,
                                  float* trace, void* hip_stream);
 
+/* Bytes of the library-held workspace of lowbit_decode_step_noalloc, per GPU. */
+#define LOWBIT_NOALLOC_WORK_BYTES (1 << 20)
+
+/*
+ * lowbit_decode_step_noalloc - lowbit_decode_step for callers that cannot
+ *   allocate device memory (code under HIP graph capture, tight serving
+ *   loops, harnesses that forbid allocation): the same step, the same
+ *   kernels and the same results, but m->work is ignored (it may be NULL).
+ *   The step's intermediates live instead in a static device array of
+ *   LOWBIT_NOALLOC_WORK_BYTES that the library holds on each GPU it runs on
+ *   until the process ends.  Every call on a GPU shares that GPU's array and
+ *   it keeps the last call's contents (the step writes every intermediate
+ *   before reading it, so nothing needs clearing): calls that overlap on one
+ *   GPU (on different streams, or from several threads without ordering)
+ *   race and must be serialised by the caller.  Nothing is allocated: the
+ *   first call on a device looks up the array's device address there
+ *   (hipGetSymbolAddress) and keeps it.
+ * Errors: as lowbit_decode_step; LOWBIT_E_RANGE also when the model's
+ *         lowbit_model_work_bytes exceeds LOWBIT_NOALLOC_WORK_BYTES (checked
+ *         before any HIP call).
+ */
+lowbit_status lowbit_decode_step_noalloc(const lowbit_model* m, int32_t* state, float* logits, int32_t* tokens,
+                                         float* trace, void* hip_stream);
+
 /* Largest k the kernels accept for a format.  The operator's own bound
  * (M8.8 0x09C) is k * 127 * qmax < 2^31; the kernels hold each code scaled
  * by 64 (ternary, binary) or 16 (int4) in int8 lanes, and activation codes

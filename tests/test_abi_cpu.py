@@ -394,3 +394,35 @@ def test_binding_rejects_wrong_dtypes():
     _bad_dtype(lambda: lb.DecodeModel(64, 1, 1, 128, 100, 8, descs6, f32(100, 64), f32(3, 64), pk, sc), "packed")
     _bad_dtype(lambda: lb.DecodeModel(64, 1, 1, 128, 100, 8, descs6, f32(100, 64).double(), f32(3, 64), pk, sc),
                "embed")
+
+
+def test_decode_step_noalloc_host_checks():
+    """lowbit_decode_step_noalloc: the same argument checks as
+    lowbit_decode_step except that work may be NULL, and a model whose
+    workspace exceeds LOWBIT_NOALLOC_WORK_BYTES is rejected with E_RANGE
+    before any HIP call (no GPU is touched)."""
+    lib = lb.raw_library()
+    fake = ctypes.c_void_p(1 << 20)                          # never dereferenced: the checks fail first
+
+    def filled(m, layers):
+        m.embed = m.norms = m.k_cache = m.v_cache = 1 << 20
+        m.work = None
+        arr = (ctypes.c_void_p * (5 * layers + 1))(*([1 << 20] * (5 * layers + 1)))
+        m.packed = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
+        m.scales = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
+        return arr
+
+    m = _model_struct()
+    assert lib.lowbit_decode_step_noalloc(ctypes.byref(m), fake, fake, None, None, None) == 1
+    # 4096-d, FFN 65536: 36 d + 14 ff bytes of intermediates exceed 1 MiB
+    big = _model_struct(d=4096, layers=1, heads=64, ff=65536, vocab=64, context=4)
+    keep = filled(big, 1)
+    assert lib.lowbit_model_work_bytes(ctypes.byref(big)) > lb.NOALLOC_WORK_BYTES
+    assert lib.lowbit_decode_step_noalloc(ctypes.byref(big), fake, fake, None, None, None) == 2
+    assert lib.lowbit_decode_step(ctypes.byref(big), fake, fake, None, None, None) == 1   # needs work
+    # the 256-d model fits
+    assert lib.lowbit_model_work_bytes(ctypes.byref(m)) <= lb.NOALLOC_WORK_BYTES
+    keep = filled(m, 6)
+    keep[3] = None                                           # a missing weight pointer is still caught
+    assert lib.lowbit_decode_step_noalloc(ctypes.byref(m), fake, fake, None, None, None) == 1
+    del keep
