@@ -53,7 +53,7 @@ class Pass:
     per-call activations stacked by k so one act-quant launch serves all
     inputs of equal width."""
 
-    def __init__(self, wl, tokens, entry, layers=None, threads=16):
+    def __init__(self, wl, tokens, entry, layers=None, threads=16, weights_from=None):
         import torch
         import bit_weight_linear_bitlinear_amd as lb
         import workloads
@@ -65,6 +65,12 @@ class Pass:
                      if layer < m.count]
         fmt, scale = lb.FORMATS[wl.fmt], lb.SCALES[wl.scale]
         flags = lb.FLAG_TANH3 if wl.tanh_premap else 0
+        if weights_from is not None:                     # same packed weights, other token count
+            assert weights_from.mats == self.mats
+            self.desc, self.packed, self.scales = weights_from.desc, weights_from.packed, weights_from.scales
+            xs = [workloads.workload_activations(wl, layer, mi, tokens, m.k) for layer, mi, m in self.mats]
+            self._activations(xs, tokens, entry)
+            return
 
         def prep(item):
             layer, mi, m = item
@@ -86,7 +92,11 @@ class Pass:
                 self.scales.append(torch.from_numpy(scales).cuda())
                 xs.append(x)
         log(f"[bench] {wl.name}: {len(self.mats)} matrices generated and packed in {time.time() - t0:.1f}s")
+        self._activations(xs, tokens, entry)
 
+    def _activations(self, xs, tokens, entry):
+        import torch
+        lb = self.lb
         # activations stacked per k; q / sx / y views per matrix
         self.kgroups = {}
         for i, (_, _, m) in enumerate(self.mats):
@@ -232,20 +242,70 @@ def capture(fn):
         return None
 
 
-def time_steps(run, steps, warmup):
+def time_steps(run, steps, warmup, per_step=None):
+    """Seconds for `steps` runs between two HIP events on the current stream
+    (and the wall time); per_step, a list, receives each run's own duration
+    (an event recorded between consecutive runs)."""
     import torch
     for _ in range(warmup):
         run()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1 if per_step is not None else 2)]
     wall0 = time.perf_counter()
-    e0.record()
-    for _ in range(steps):
+    ev[0].record()
+    for i in range(steps):
         run()
-    e1.record()
+        if per_step is not None:
+            ev[i + 1].record()
+    if per_step is None:
+        ev[1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    return e0.elapsed_time(e1) / 1e3, wall
+    if per_step is not None:
+        per_step.extend(ev[i].elapsed_time(ev[i + 1]) / 1e3 for i in range(steps))
+    return ev[0].elapsed_time(ev[-1]) / 1e3, wall
+
+
+def step_stats(per_step):
+    v = np.asarray(per_step) * 1e3
+    return {"median_ms": round(float(np.median(v)), 4), "min_ms": round(float(v.min()), 4),
+            "max_ms": round(float(v.max()), 4), "steps": len(v)}
+
+
+def calibration(nbytes=2 << 30, reps=5, mfma_iters=40000):
+    """The device's own ceilings (the library's calibration kernels): a 16-byte
+    non-temporal read stream over nbytes (8x the 256 MB last-level cache), and
+    the int8 matrix-core loop (two wavefronts per SIMD, back-to-back
+    v_mfma_i32_32x32x32_i8).  Medians of `reps` event-timed launches."""
+    import torch
+    lb = __import__("bit_weight_linear_bitlinear_amd")
+    buf = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda").fill_(7)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = {}
+    for name, fn in (("read", lambda: lb.lowbit_calib_read(buf, sink)),
+                     ("mfma", lambda: lb.lowbit_calib_mfma_i8(mfma_iters, sink))):
+        fn()
+        torch.cuda.synchronize()
+        t = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            t.append(e0.elapsed_time(e1) / 1e3)
+        out[name] = float(np.median(t))
+    ops = lb.lowbit_calib_mfma_i8(mfma_iters, sink)
+    torch.cuda.synchronize()
+    del buf
+    read_gbs = nbytes / out["read"] / 1e9
+    tops = ops / out["mfma"] / 1e12
+    return {"read_stream_GBps": round(read_gbs, 1), "read_bytes": nbytes,
+            "read_frac_of_spec": round(read_gbs / HBM_PEAK_GBS, 4),
+            "mfma_i8_TOPS": round(tops, 1), "mfma_i8_frac_of_spec": round(tops / I8_PEAK_TOPS, 4),
+            "what": "lowbit_calib_read (16-byte non-temporal read stream, 8x the last-level cache) and "
+                    "lowbit_calib_mfma_i8 (back-to-back 32x32x32 int8 MFMAs, two wavefronts per SIMD), "
+                    f"medians of {reps} launches"}
 
 
 def per_launch_grouped(p: Pass, calls, reps: int, fused: bool):
@@ -305,10 +365,11 @@ def gemm_pass(p: Pass, steps: int, no_graph: bool = False):
     import torch
     p.build_schedules()
     res = {}
+    p.grouped_step_times = []
     for sched in ("per_matrix", "grouped"):
         fn = (lambda sc=sched: p.step(sc))
         run = None if no_graph else capture(fn)
-        el, _ = time_steps(run or fn, steps, 1)
+        el, _ = time_steps(run or fn, steps, 1, per_step=p.grouped_step_times if sched == "grouped" else None)
         res[sched] = el / steps
     p.act_quant()
     torch.cuda.synchronize()
@@ -498,50 +559,95 @@ def sampled_check(p: Pass, picks, rows_per=48, seed=0):
             assert torch.equal(sxf, sx) and torch.equal(yf, y), f"matrix {i}: fused path differs"
         worst = max(worst, float((err / (1e-6 + 1e-5 * np.abs(y32))).max()))
     return {"matrices": len(picks), "rows_each": rows_per, "acc_bit_exact": True,
-            "fused_equals_separate": p.entry == "gemv",
+            "fused_equals_separate": True if p.entry == "gemv" else None,
             "y_worst_frac_of_tol": round(worst, 4)}
 
 
 # --------------------------------------------------------------- CPU oracle
 
-def cpu_baseline(wl, tokens, budget_s=12.0, sample_layers=4):
-    """The oracle as it stands, on the host's cores: act-quant + unpack +
-    integer product + epilogue over the first `sample_layers` layer-equivalents
-    of the same workload, repeated until ~budget_s of timed CPU work (weights
-    are packed by the oracle beforehand, untimed)."""
+def _oracle_items(wl, layers, tokens, token_rows=None):
+    """The oracle's inputs for the first `layers` layer-equivalents of a
+    workload: (matrix, packed, scales, x) with x the workload's activations at
+    `tokens` rows per call, cut to the first `token_rows` (None: all); weights
+    packed by the oracle, untimed."""
     import oracle
     import workloads
-    items = [(layer, mi, m) for layer in range(min(sample_layers, wl.layers))
-             for mi, m in enumerate(wl.matrices) if layer < m.count]
+    items = [(layer, mi, m) for layer in range(min(layers, wl.layers)) for mi, m in enumerate(wl.matrices)
+             if layer < m.count]
 
     def prep(item):
         layer, mi, m = item
         w = workloads.latent_weights(wl.index, layer, mi, m.n, m.k)
         pk, sc, _, _ = oracle.quantize_and_pack(w, wl.fmt, wl.scale, wl.group, wl.tanh_premap)
         x = workloads.workload_activations(wl, layer, mi, tokens, m.k)
+        if token_rows is not None:
+            x = np.ascontiguousarray(x[:token_rows])
         return m, pk, sc, x
 
     with ThreadPoolExecutor(8) as ex:
-        prepped = list(ex.map(prep, items))
+        return list(ex.map(prep, items))
+
+
+def _oracle_rate(wl, items, budget_s):
+    """act-quant + unpack + integer product + fp32 epilogue over every item,
+    repeated until budget_s of timed work (at least once): bytes and ops
+    counted as the GPU step counts them (fp32 x read, codes and s_x written,
+    packed codes and scales read, fp32 y written; 2 t n k operations)."""
+    import oracle
     spent, nbytes, nops, passes = 0.0, 0, 0, 0
-    while spent < budget_s:
-        for m, pk, sc, x in prepped:
+    while passes == 0 or spent < budget_s:
+        for m, pk, sc, x in items:
+            t = x.shape[0]
             t0 = time.perf_counter()
             q, sx, _ = oracle.act_quant(x)
             oracle.linear(pk, sc, wl.fmt, wl.scale, wl.group, m.n, m.k, q, sx)
             spent += time.perf_counter() - t0
-            nbytes += (pk.size + 4 * sc.size + tokens * m.k + 4 * tokens + 4 * tokens * m.n
-                       + tokens * (5 * m.k + 4))
-            nops += 2 * tokens * m.n * m.k
+            nbytes += pk.size + 4 * sc.size + 5 * t * m.k + 4 * t + 4 * t * m.n
+            nops += 2 * t * m.n * m.k
         passes += 1
-    out = {"value": round(nbytes / spent / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
-           "kind": "oracle",
+    return {"GBps": round(nbytes / spent / 1e9, 4), "GOPS": round(nops / spent / 1e9, 3),
+            "wall_s": round(spent, 2), "threads": oracle.num_threads(), "passes": passes}
+
+
+def cpu_baseline(wl, tokens, budget_s=3.0, sample_layers=2):
+    """The oracle as it stands, on the host's cores, beside the GPU figures:
+    the headline (the 4B-class decode pass at `tokens` tokens) over a bounded
+    sample of its layer-equivalents, then every workload (the 4B-class pass at
+    1, 4 and 16 tokens), each over a stated sample, and the single-thread
+    comparables.  A reported baseline, not a target."""
+    items = _oracle_items(wl, sample_layers, tokens)
+    r = _oracle_rate(wl, items, budget_s)
+    out = {"value": r["GBps"], "unit": "GB/s", "cores": r["threads"], "kind": "oracle",
            "sample": f"{len(items)} matrices ({min(sample_layers, wl.layers)} of {wl.layers} layer-equivalents) "
-                     f"x {passes} passes, T={tokens}: act-quant + unpack + int64 product + fp32 epilogue, "
-                     f"{spent:.1f}s timed",
-           "gops": round(nops / spent / 1e9, 3)}
+                     f"x {r['passes']} passes, T={tokens}: act-quant + unpack + int64 product + fp32 epilogue, "
+                     f"{r['wall_s']:.1f}s timed",
+           "gops": r["GOPS"]}
+    out["per_config"] = per_config_baselines()
     out["single_thread"] = single_thread_baselines()
     return out
+
+
+def per_config_baselines(budget_s=1.0):
+    """The oracle on each workload, all host threads: GB/s and GOPS counted
+    as the GPU step counts them, the timed wall time and the sample."""
+    import workloads
+    res = {}
+    plan = [("single_ternary", 1, None, None, "the whole [768, 192] projection, 256 tokens"),
+            ("decode_stack", 6, None, None, "all 31 matrices, 1 token each"),
+            ("binary_gqa", 1, None, 1024, "layer 0 (7 products), 1024 of the 8192 tokens"),
+            ("ternary_4b", 1, 1, None, "layer-equivalent 0 (7 matrices) of 36, 1 token"),
+            ("ternary_4b", 1, 4, None, "layer-equivalent 0 (7 matrices) of 36, 4 tokens"),
+            ("ternary_4b", 1, 16, None, "layer-equivalent 0 (7 matrices) of 36, 16 tokens"),
+            ("int4_t4nt", 1, None, 256, "layer 0 (5 products) of 20, 256 of the 4096 tokens")]
+    for name, layers, tokens, rows, what in plan:
+        wl = workloads.BY_NAME[name]
+        t = tokens if tokens is not None else wl.tokens[0]
+        items = _oracle_items(wl, layers, t, rows)
+        r = _oracle_rate(wl, items, budget_s)
+        r["sample"] = what
+        res[name if tokens is None else f"{name}_t{tokens}"] = r
+    log(f"[bench] cpu oracle per config: {res}")
+    return res
 
 
 def single_thread_baselines(min_s=1.0):
@@ -1085,6 +1191,9 @@ def main():
         args.quick = args.skip_gemm = args.skip_cpu = args.skip_check = args.skip_views = True
     calib = copy_calibration()
     log(f"[bench] copy calibration: {calib}")
+    ceilings = None if args.profile_pass or args.profile_gemm or args.profile_h4 or args.profile_a48 else calibration()
+    if ceilings:
+        log(f"[bench] device ceilings: {ceilings}")
 
     if args.profile_gemm:
         gemm_profile(args)
@@ -1112,10 +1221,12 @@ def main():
         torch.cuda.synchronize()
     order = (["grouped"] if args.quick else
              ["grouped", "grouped_fused", "layer", "layer_dep", "layer_fused", "per_matrix"])
+    head_steps = []
     for sched in order:
         fn = (lambda sc=sched: p.step(sc))
         run = None if args.no_graph else capture(fn)
-        elapsed, wall = time_steps(run or fn, args.steps, args.warmup)
+        elapsed, wall = time_steps(run or fn, args.steps, args.warmup,
+                                   per_step=head_steps if sched == "grouped" else None)
         st = elapsed / args.steps
         n_l = {"grouped": p.launches(p.grouped_calls), "grouped_fused": p.launches(p.fused_calls),
                "layer": p.launches(p.layer_calls), "layer_dep": p.launches(p.layer_calls),
@@ -1135,6 +1246,31 @@ def main():
         schedules["grouped_fused"]["per_launch"] = {"avg_launch_us": round(dur_f * 1e6, 3),
                                                     "GBps": round(bytes_f / dur_f / 1e9, 2)}
     check = None if args.skip_check else sampled_check(p, [0, 4, 6, len(p.mats) - 1])
+    # the same pass at 4 and 16 tokens per call (the same packed weights)
+    tok_lines = {}
+    if not args.quick:
+        for tt in (4, 16):
+            if tt == args.tokens:
+                continue
+            pt = Pass(wl, tt, "gemv", layers=args.layers, weights_from=p)
+            pt.build_schedules()
+            fn = lambda: pt.step("grouped")
+            run = (None if args.no_graph else capture(fn)) or fn
+            per = []
+            el, _ = time_steps(run, args.steps, args.warmup, per_step=per)
+            st_t = el / args.steps
+            d_t, b_t = per_launch_grouped(pt, pt.grouped_calls, reps=10, fused=False)
+            ach_t = b_t / d_t / 1e9
+            tok_lines[f"t{tt}"] = {
+                "tokens": tt, "ms_per_step": round(st_t * 1e3, 4), "GBps_step": round(pt.step_bytes / st_t / 1e9, 2),
+                "pct_hbm_peak_step": round(100 * pt.step_bytes / st_t / 1e9 / HBM_PEAK_GBS, 2),
+                "step": step_stats(per), "launches": pt.launches(pt.grouped_calls),
+                "per_launch": {"avg_us": round(d_t * 1e6, 3), "bytes": round(b_t), "GBps": round(ach_t, 2),
+                               "frac_hbm_peak": round(ach_t / HBM_PEAK_GBS, 4),
+                               "frac_of_measured_read": (round(ach_t / ceilings["read_stream_GBps"], 4)
+                                                         if ceilings else None)}}
+            log(f"[bench] gemv t={tt}: {tok_lines[f't{tt}']}")
+            del pt
 
     out.update({
         "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -1149,8 +1285,13 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": committed_traffic(),
                      "kernel": "gemv_kernel (grouped schedule)", "avg_launch_us": round(dur * 1e6, 3),
-                     "bytes_per_launch": round(bytes_per_launch)},
+                     "bytes_per_launch": round(bytes_per_launch),
+                     "measured_peak": ceilings["read_stream_GBps"] if ceilings else None,
+                     "frac_of_measured": round(achieved / ceilings["read_stream_GBps"], 4) if ceilings else None},
+        "step": step_stats(head_steps) if head_steps else None,
+        "gemv_tokens": tok_lines,
     })
+    out["device_ceilings"] = ceilings
     out["copy_calibration"] = calib
     if check:
         out["check"] = check
@@ -1177,6 +1318,7 @@ def main():
         out["gemm"] = {"workload": "int4_t4nt prefill pass: 100 int4 row-scale GEMMs, T=4096, act-quant included; "
                                    "equal-k products as grouped launches (64 per launch)",
                        "tops_step": round(ops4 / st4 / 1e12, 2), "ms_per_step": round(st4 * 1e3, 4),
+                       "step": step_stats(p4.grouped_step_times),
                        "schedules_ms_per_step": {k: round(v * 1e3, 4) for k, v in sched4.items()},
                        "single_product_launch": {"avg_us": round(d1 * 1e6, 2),
                                                  "TOPS": round(ops_single / d1 / 1e12, 2)},
@@ -1186,6 +1328,9 @@ def main():
                        "kernel": "gemm_mfma_kernel (grouped launches)",
                        "roofline": {"bound": "mfma", "achieved": round(tops_launch, 2), "peak": I8_PEAK_TOPS,
                                     "unit": "TOPS", "frac": round(tops_launch / I8_PEAK_TOPS, 4),
+                                    "measured_peak": ceilings["mfma_i8_TOPS"] if ceilings else None,
+                                    "frac_of_measured": (round(tops_launch / ceilings["mfma_i8_TOPS"], 4)
+                                                         if ceilings else None),
                                     "mfma_floor_us_per_launch": round(floor_mfma / n4 * 1e6, 2),
                                     "hbm_floor_us_per_launch": round(floor_hbm / n4 * 1e6, 2),
                                     "frac_of_larger_floor": round(max(floor_mfma, floor_hbm) / n4 / d4, 4)},

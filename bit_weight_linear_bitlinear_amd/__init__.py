@@ -113,6 +113,12 @@ _lib.lowbit_rope_attention.argtypes = [_P, _i32, _i32, _i32, ctypes.c_float, _P,
 _lib.lowbit_rope_attention.restype = _i32
 _lib.lowbit_swiglu.argtypes = [_P, _P, ctypes.c_int64, _P, _P]
 _lib.lowbit_swiglu.restype = _i32
+_lib.lowbit_calib_read.argtypes = [_P, ctypes.c_int64, _P, _P]
+_lib.lowbit_calib_read.restype = _i32
+_lib.lowbit_calib_mfma_i8.argtypes = [_i32, _P, _P]
+_lib.lowbit_calib_mfma_i8.restype = _i32
+_lib.lowbit_calib_mfma_i8_ops.argtypes = [_i32]
+_lib.lowbit_calib_mfma_i8_ops.restype = ctypes.c_int64
 _lib.lowbit_max_k.argtypes = [_i32]
 _lib.lowbit_max_k.restype = _i32
 _lib.lowbit_status_string.argtypes = [_i32]
@@ -130,6 +136,7 @@ EXPORTS = ("lowbit_describe", "lowbit_pack", "lowbit_act_quant", "lowbit_act_qua
            "lowbit_linear_grouped_fused",
            "lowbit_model_work_bytes", "lowbit_model_trace_floats", "lowbit_decode_step", "lowbit_decode_step_noalloc",
            "lowbit_rmsnorm", "lowbit_rope_attention", "lowbit_swiglu",
+           "lowbit_calib_read", "lowbit_calib_mfma_i8", "lowbit_calib_mfma_i8_ops",
            "lowbit_max_k", "lowbit_status_string", "lowbit_abi_version", "lowbit_last_hip_error")
 
 # projection slots (lowbit_model.proj and the per-layer weight lists)
@@ -485,6 +492,24 @@ class DecodeModel:
                   _dev(tokens, "tokens", 4 * m.context), _dev(trace, "trace", 4 * self.trace_floats),
                   _stream(stream)),
                "lowbit_decode_step_noalloc" if noalloc else "lowbit_decode_step")
+
+
+def lowbit_calib_read(src, sink, stream=None) -> None:
+    """Device: stream every 16-byte word of src (any contiguous GPU tensor,
+    a multiple of 16 bytes) once; sink: a device int32/uint32 [1] (its value
+    means nothing).  Time it with events for the read ceiling."""
+    _types(sink=(sink, (_I32, "uint32")))
+    nbytes = src.numel() * src.element_size()
+    _check(_lib.lowbit_calib_read(_dev(src, "src"), nbytes, _dev(sink, "sink", 4), _stream(stream)),
+           "lowbit_calib_read")
+
+
+def lowbit_calib_mfma_i8(iters, sink, stream=None) -> int:
+    """Device: the int8 matrix-core loop (iters iterations per wavefront);
+    returns the number of int8 operations the launch does."""
+    _types(sink=(sink, (_I32, "uint32")))
+    _check(_lib.lowbit_calib_mfma_i8(int(iters), _dev(sink, "sink", 4), _stream(stream)), "lowbit_calib_mfma_i8")
+    return int(_lib.lowbit_calib_mfma_i8_ops(int(iters)))
 
 
 def lowbit_max_k(format: int) -> int:

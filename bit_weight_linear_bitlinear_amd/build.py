@@ -21,7 +21,7 @@ ARCH = os.environ.get("LOWBIT_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["act_quant.hip", "hadamard.hip", "bitnet_v1.hip", "onebit.hip", "sparse8.hip", "gemv.hip", "gemv_ternary.hip", "gemv_int4.hip", "gemv_binary.hip", "gemm.hip",
            "decode_model.hip",
-           "gemm_mfma.hip", "lowbit_host.cpp"]
+           "gemm_mfma.hip", "calib.hip", "lowbit_host.cpp"]
 
 COMMON = ["-std=c++17", "-O3", "-fPIC", "-ffp-contract=off", "-fno-fast-math",
           "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-function"]

@@ -101,4 +101,11 @@ hipError_t launch_swiglu(const float* gate, const float* up, float* a, int64_t n
 hipError_t launch_argmax_advance(const float* logits, int vocab, int32_t* state, int context, int32_t* tokens,
                                  hipStream_t st);
 
+// device ceilings (calib.hip): a 16-byte read stream over `bytes` (a multiple
+// of 16, 16-byte aligned), and an int8 matrix-core loop of `iters` iterations
+// whose operations per iteration calib_mfma_i8_ops_per_iter() gives
+hipError_t launch_calib_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream);
+int64_t calib_mfma_i8_ops_per_iter();
+hipError_t launch_calib_mfma_i8(int32_t iters, uint32_t* sink, hipStream_t stream);
+
 }  // namespace lowbit

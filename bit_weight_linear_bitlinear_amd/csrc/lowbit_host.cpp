@@ -623,6 +623,22 @@ lowbit_status lowbit_decode_step_noalloc(const lowbit_model* m, int32_t* state, 
     return decode_step_impl(m, work, state, logits, tokens, trace, hip_stream);
 }
 
+lowbit_status lowbit_calib_read(const void* src, int64_t bytes, uint32_t* sink, void* hip_stream) {
+    if (!src || !sink || bytes < 16 || bytes % 16 || (uintptr_t)src % 16 || (uintptr_t)sink % 4) return LOWBIT_E_ARG;
+    clear_hip_error();
+    return hip_status(lowbit::launch_calib_read(src, bytes, sink, (hipStream_t)hip_stream));
+}
+
+int64_t lowbit_calib_mfma_i8_ops(int32_t iters) {
+    return iters < 1 ? -1 : (int64_t)iters * lowbit::calib_mfma_i8_ops_per_iter();
+}
+
+lowbit_status lowbit_calib_mfma_i8(int32_t iters, uint32_t* sink, void* hip_stream) {
+    if (iters < 1 || !sink || (uintptr_t)sink % 4) return LOWBIT_E_ARG;
+    clear_hip_error();
+    return hip_status(lowbit::launch_calib_mfma_i8(iters, sink, (hipStream_t)hip_stream));
+}
+
 lowbit_status lowbit_describe(int32_t format, int32_t scale, int32_t n, int32_t k, int32_t group, int32_t flags,
                               lowbit_desc* out) {
     return fill_desc(format, scale, n, k, group, flags, out);

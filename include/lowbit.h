@@ -530,6 +530,26 @@ lowbit_status lowbit_decode_step(const lowbit_model* m, int32_t* state, float* l
 lowbit_status lowbit_decode_step_noalloc(const lowbit_model* m, int32_t* state, float* logits, int32_t* tokens,
                                          float* trace, void* hip_stream);
 
+/* Device ceilings for the roofline fractions (measurement utilities, not part
+ * of the operator).  The published MI355X figures are 8 TB/s of HBM and 5.0
+ * POPS of dense int8 matrix-core work; these calls measure what the device
+ * reaches, so a product's rate can be read against both.
+ *
+ * lowbit_calib_read - every lane streams 16-byte words of src (device, 16-byte
+ *   aligned, `bytes` a positive multiple of 16) once, non-temporally, and
+ *   folds them into *sink (device uint32, a value of no meaning).  Time it with
+ *   events: bytes / time is the read rate (HBM-sourced when the buffer is
+ *   several times the 256 MB last-level cache).
+ * lowbit_calib_mfma_i8 - two wavefronts per SIMD on every CU issue
+ *   v_mfma_i32_32x32x32_i8 back to back (eight independent accumulators, no
+ *   memory traffic) `iters` >= 1 times each; lowbit_calib_mfma_i8_ops(iters)
+ *   is the number of int8 operations (2 per multiply-add) that launch does
+ *   (-1 for iters < 1).  *sink as above.
+ * Errors: LOWBIT_E_ARG (null / misaligned pointer, size), LOWBIT_E_HIP. */
+lowbit_status lowbit_calib_read(const void* src, int64_t bytes, uint32_t* sink, void* hip_stream);
+lowbit_status lowbit_calib_mfma_i8(int32_t iters, uint32_t* sink, void* hip_stream);
+int64_t lowbit_calib_mfma_i8_ops(int32_t iters);
+
 /* Largest k the kernels accept for a format.  The operator's own bound
  * (M8.8 0x09C) is k * 127 * qmax < 2^31; the kernels hold each code scaled
  * by 64 (ternary, binary) or 16 (int4) in int8 lanes, and activation codes

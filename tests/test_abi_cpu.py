@@ -426,3 +426,16 @@ def test_decode_step_noalloc_host_checks():
     keep[3] = None                                           # a missing weight pointer is still caught
     assert lib.lowbit_decode_step_noalloc(ctypes.byref(m), fake, fake, None, None, None) == 1
     del keep
+
+
+def test_calibration_calls_reject_bad_arguments_on_the_host():
+    """The ceiling kernels check sizes and pointers before any launch."""
+    lib = lb.raw_library()
+    one = ctypes.c_void_p(1 << 20)                           # never dereferenced
+    assert lib.lowbit_calib_read(None, 1024, one, None) == 1
+    assert lib.lowbit_calib_read(one, 1000, one, None) == 1   # not a multiple of 16
+    assert lib.lowbit_calib_read(one, 0, one, None) == 1
+    assert lib.lowbit_calib_read(ctypes.c_void_p((1 << 20) + 4), 1024, one, None) == 1
+    assert lib.lowbit_calib_mfma_i8(0, one, None) == 1
+    assert lib.lowbit_calib_mfma_i8(10, None, None) == 1
+    assert lib.lowbit_calib_mfma_i8_ops(0) == -1

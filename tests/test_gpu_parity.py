@@ -281,6 +281,47 @@ def test_batched_grouped_matches_single_and_oracle(fmt, scale, group, k, t, ns):
         check_y(ys[i].cpu().numpy(), y32, y64, f"batched grouped {i}")
 
 
+@pytest.mark.parametrize("scale", ["row", "tensor"])
+def test_int4_grouped_gemm_many_tiles(scale):
+    """A grouped int4 prefill launch of 40 products (k = 256 = two packed
+    steps) with several times more workgroup tiles than the chip has CUs,
+    tokens ragged (t % 256 != 0) and rows ragged (n % 256 != 0, some n below
+    one tile): with the integer outputs (all products) and without, against
+    single-product launches (another tile-to-workgroup map) bit for bit, and
+    sampled tokens of six products against the oracle."""
+    import torch
+    lb = pytest.importorskip("bit_weight_linear_bitlinear_amd")
+    t, k = 2085, 256
+    ns = [1020 - 4 * (i % 7) if i % 4 else 100 + 64 * (i % 3) for i in range(40)]
+    say(f"[case] grouped int4 gemm, many tiles, scale={scale} t={t} k={k} count={len(ns)}")
+    rng = np.random.default_rng(5)
+    sample = np.sort(rng.choice(t, size=64, replace=False))
+    sample[0], sample[-1] = 0, t - 1
+    descs, packed, scales, qs, sxs, ys, accs, xs, ws = [], [], [], [], [], [], [], [], []
+    for i, n in enumerate(ns):
+        w, x = workloads.random_case(900 + i, n, k, t)
+        d, p, sc, _, _ = pack_upload(w, "int4", scale, 0, True)
+        q, sx, _ = act_quant_dev(to_dev(x))
+        descs.append(d); packed.append(p); scales.append(sc); qs.append(q); sxs.append(sx)
+        ys.append(torch.full((t, n), float("nan"), device="cuda"))
+        accs.append(torch.full((t, n, 1), -7, dtype=torch.int32, device="cuda"))
+        xs.append(x); ws.append(w)
+    lb.lowbit_linear_batched_grouped(descs, packed, scales, qs, sxs, ys, accs)
+    ys2 = [torch.full_like(y, float("nan")) for y in ys]
+    lb.lowbit_linear_batched_grouped(descs, packed, scales, qs, sxs, ys2)
+    for i in range(len(ns)):
+        y1, a1 = linear_dev("gemm", descs[i], packed[i], scales[i], qs[i], sxs[i])
+        torch.cuda.synchronize()
+        assert torch.equal(ys[i], y1) and torch.equal(ys2[i], y1), i
+        assert torch.equal(accs[i], a1), i
+    for i in (0, 1, 3, 4, 17, 39):
+        p_ref, s_ref, _, _ = oracle.quantize_and_pack(ws[i], "int4", scale, 0, True)
+        q_ref, sx_ref, _ = oracle.act_quant(xs[i][sample])
+        y32, y64, acc_ref = oracle.linear(p_ref, s_ref, "int4", scale, 0, ns[i], k, q_ref, sx_ref)
+        assert (accs[i].cpu().numpy()[sample] == acc_ref).all(), i
+        check_y(ys[i].cpu().numpy()[sample], y32, y64, f"grouped many tiles {i}")
+
+
 @pytest.mark.parametrize("fmt", ["ternary", "binary", "int4"])
 def test_gemm_tile_shapes(fmt):
     """Prefill shapes that select each workgroup tile of the batched kernel
@@ -453,3 +494,25 @@ def test_grouped_schedules_replay_equal_to_eager():
         for j, (a, b) in enumerate(zip([a.cpu() for a in outs], ref)):
             assert torch.equal(a, b), f"replay {rep}: output {j} differs from the eager calls"
     assert torch.equal(yf[0].cpu(), y1[0].cpu())        # the fused schedule equals the two-call one
+
+
+def test_calibration_kernels():
+    """The device-ceiling kernels the bench reads its roofline fractions
+    against: the read stream folds every 32-bit word of the buffer into the
+    sink with XOR (checked against numpy over a 24 MiB buffer, not a multiple
+    of the launch's stride), and the int8 matrix-core loop runs and reports
+    its operation count (2 * 32 * 32 * 32 per MFMA, 8 per iteration per
+    wavefront, 8 wavefronts per CU)."""
+    import torch
+    lb = pytest.importorskip("bit_weight_linear_bitlinear_amd")
+    rng = np.random.default_rng(3)
+    words = rng.integers(0, 2 ** 32, size=(24 << 20) // 4 + 12, dtype=np.uint32)
+    buf = torch.from_numpy(words.view(np.int32)).cuda()
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    lb.lowbit_calib_read(buf, sink)
+    torch.cuda.synchronize()
+    assert int(sink.cpu().numpy().view(np.uint32)[0]) == int(np.bitwise_xor.reduce(words))
+    ops = lb.lowbit_calib_mfma_i8(16, sink)
+    torch.cuda.synchronize()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert ops == 16 * cus * 2 * 4 * 8 * 65536
