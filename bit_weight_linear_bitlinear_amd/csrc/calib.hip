@@ -1,18 +1,21 @@
 // calib.hip - the two ceilings the products' roofline fractions are read
 // against, measured on the device itself (the published figures are 8 TB/s
 // of HBM and 5.0 POPS of dense int8 matrix-core work):
-//  - a read stream: 16 workgroups per CU, each streaming its own contiguous
+//  - a read stream: two workgroups per CU, each streaming its own contiguous
 //    slab in 16-byte words with eight loads in flight per lane,
 //    non-temporal (the data is used once), XOR-reduced so the loads cannot be
 //    dropped; bytes / time is the achievable HBM read rate when the buffer is
-//    several times the 256 MB last-level cache (a grid-stride walk over the
-//    same buffer measured 5.7-6.3 TB/s, slabs 6.9-7.1);
+//    several times the 256 MB last-level cache.  Over 2 GiB a grid-stride
+//    walk measured 5.7-6.3 TB/s and slabs 6.9-7.1; the closing atomics cost
+//    little only while they are few (one per workgroup of 512 workgroups:
+//    7.0 TB/s; one per wavefront of 16384: 5.5);
 //  - an int8 matrix-core loop: two wavefronts per SIMD on every CU, each
 //    issuing v_mfma_i32_32x32x32_i8 back to back on eight independent
 //    accumulators held in registers (no memory traffic); 65536 operations per
 //    MFMA.
-// Each kernel folds its result into one word with an atomic XOR per
-// wavefront, which the caller ignores.
+// Each kernel folds its result into one word with atomic XORs (one per
+// workgroup for the read stream, per wavefront for the matrix-core loop),
+// which the caller ignores.
 #include "device_common.hpp"
 #include "kernels.hpp"
 
@@ -49,8 +52,11 @@ __global__ __launch_bounds__(256) void calib_read_kernel(const u32x4* __restrict
         const u32x4 a = __builtin_nontemporal_load(p + i);
         acc ^= a[0] ^ a[1] ^ a[2] ^ a[3];
     }
+    __shared__ uint32_t part[4];
     acc = wave_xor(acc);
-    if ((threadIdx.x & 63) == 0) atomicXor(sink, acc);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) atomicXor(sink, part[0] ^ part[1] ^ part[2] ^ part[3]);
 }
 
 __global__ __launch_bounds__(256) void calib_mfma_i8_kernel(int iters, uint32_t* __restrict__ sink) {
@@ -76,7 +82,7 @@ __global__ __launch_bounds__(256) void calib_mfma_i8_kernel(int iters, uint32_t*
 }
 
 hipError_t launch_calib_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream) {
-    const int grid = device_cu_count() * 16;
+    const int grid = device_cu_count() * 2;
     calib_read_kernel<<<grid, 256, 0, stream>>>(static_cast<const u32x4*>(src), bytes / 16, sink);
     return hipGetLastError();
 }

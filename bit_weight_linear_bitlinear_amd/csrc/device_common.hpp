@@ -156,6 +156,22 @@ __device__ __forceinline__ void load_words_stream(const uint8_t* p, uint32_t* ou
     }
 }
 
+// The same stream through a buffer resource: NWORDS words at byte offset
+// voff (per lane) + soff (uniform) of the resource, non-temporal.
+template <int NWORDS>
+__device__ __forceinline__ void load_words_stream_buf(__amdgpu_buffer_rsrc_t r, int voff, int soff, uint32_t* out) {
+    constexpr int kNT = 2;                                   // the non-temporal cache policy
+    if constexpr (NWORDS == 4) {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kNT);
+        out[0] = v[0]; out[1] = v[1]; out[2] = v[2]; out[3] = v[3];
+    } else if constexpr (NWORDS == 2) {
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kNT);
+        out[0] = v[0]; out[1] = v[1];
+    } else {
+        out[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kNT);
+    }
+}
+
 // One activation code (M8.8 0x02C, 0x05C): clip(rint(v * r), -127, 127) with
 // r = 127 / max|x| of the token row; one fp32 multiply (files are built without
 // contraction), rintf rounds half to even.

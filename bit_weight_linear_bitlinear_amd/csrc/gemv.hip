@@ -62,10 +62,16 @@ hipError_t launch_gemv_group(const LinearArgs* mats, int count, hipStream_t stre
         gp.upg = a.group / (SK / sps);
         gp.upg_shift = log2_exact(gp.upg);
     }
-    gp.stride = n_steps * SK + 16;
-    const int64_t stage = (int64_t)a.t * gp.stride;          // LDS bytes of the staged activations
+    // LDS row stride: whole k-steps plus 32 bytes, which puts the 16 token
+    // rows' 16-byte operand reads (one row per lane, lane groups 16 bytes
+    // apart) on distinct banks; a 16-byte pad measured 2-way conflicts on
+    // every read
+    constexpr int kPad = 32;
+    gp.stride = n_steps * SK + kPad;
+    gp.ph_steps = n_steps;
+    int64_t stage = (int64_t)a.t * gp.stride;                // LDS bytes of the staged activations
     const bool small_stage = stage <= kGemvLdsA;
-    cfg.nr = (small_stage && a.t == 1) ? 1 : 4;
+    cfg.nr = a.t <= 4 ? 1 : 4;                                // live token registers per lane
 
     // The quantiser runs in the product kernel's prologue for one token (every
     // workgroup redoes the row; for a single token that is cheaper than a
@@ -145,16 +151,33 @@ hipError_t launch_gemv_group(const LinearArgs* mats, int count, hipStream_t stre
     // Where the activations live.  Several tokens make the LDS stage large
     // (t * k bytes): above kGemvLdsWide four-wavefront workgroups would leave
     // the CU short of wavefronts streaming weights, so 16-wavefront workgroups
-    // share one stage, which may then take the whole LDS.  Otherwise the
-    // activations ride in the register ring from L2.
+    // share one stage.  Two of them fit a CU while the stage takes at most
+    // half the LDS; a larger one is staged in phases of k-steps that do
+    // (without a k-split; with one, the whole stage may take the whole LDS).
+    // Otherwise the activations ride in the register ring from L2.
     const int64_t red16 = ksplit > 1 ? (int64_t)16 * cfg.nr * 64 * 4 : 0;
     cfg.waves = 4;
-    if (!cfg.fuse && a.t > 1 && stage > kGemvLdsWide && stage + red16 <= kGemvLdsMax) {
-        cfg.lds_a = true;
-        cfg.waves = 16;
-    } else {
-        cfg.lds_a = small_stage;
+    cfg.lds_a = small_stage;
+    if (!cfg.fuse && a.t > 1 && stage > kGemvLdsWide) {
+        if (stage + red16 <= kGemvLdsHalf) {
+            cfg.lds_a = true;
+            cfg.waves = 16;
+        } else if (ksplit == 1 && q_vec) {
+            // phases of whole ring rounds (kGemvD steps), as few as fit
+            int ph = n_steps;
+            for (int parts = 2; (int64_t)a.t * (ph * SK + kPad) > kGemvLdsHalf; ++parts)
+                ph = ((n_steps + parts - 1) / parts + kGemvD - 1) / kGemvD * kGemvD;
+            gp.ph_steps = ph;
+            gp.stride = ph * SK + kPad;
+            stage = (int64_t)a.t * gp.stride;
+            cfg.lds_a = true;
+            cfg.waves = 16;
+        } else if (stage + red16 <= kGemvLdsMax) {
+            cfg.lds_a = true;
+            cfg.waves = 16;
+        }
     }
+    if (!cfg.lds_a) cfg.nr = 4;                              // the L2 fallback keeps four token registers
     gp.lds_a_bytes = cfg.lds_a ? (int)stage : 0;
     gp.tiles_per_wg = cfg.waves / ksplit;
 

@@ -11,6 +11,8 @@ constexpr int kGemvMaxMats = 256;    // matrices per launch (a 17 KB kernel-argu
 constexpr int kGemvLdsA = 56 * 1024; // activation bytes a 4-wavefront workgroup may stage in LDS
 constexpr int kGemvLdsWide = 20 * 1024;   // above this stage, 16-wavefront workgroups share it (t > 1)
 constexpr int kGemvLdsMax = 160 * 1024;   // LDS of a CU
+constexpr int kGemvLdsHalf = 80 * 1024;   // a 16-wavefront stage that leaves room for a second workgroup
+constexpr int kGemvD = 4;                 // k-steps of weight loads in flight per wavefront
 
 // input transforms of the fused prologue (PRE_* of gemv_kernel)
 enum { PRE_NONE = 0, PRE_NORM = 1, PRE_SWIGLU = 2 };
@@ -40,7 +42,8 @@ struct GemvParams {
     int ksplit_log;
     int part_len;        // k-steps per part (the last part may run short)
     int tiles_per_wg;    // waves per workgroup / ksplit
-    int stride;          // LDS bytes per staged token row (k padded + 16)
+    int stride;          // LDS bytes per staged token row (the phase's k padded, + 16)
+    int ph_steps;        // k-steps per LDS phase (n_steps: the whole row is staged at once)
     int q_vec;           // k % 16 == 0 and every q 16-byte aligned
     int lds_a_bytes;     // T * stride when activations are staged in LDS, else 0
     int q_word;          // fused: k % 4 == 0 and every q 4-byte aligned
@@ -59,7 +62,7 @@ struct GemvParams {
 // Launch configuration chosen on the host.
 struct GemvCfg {
     int wpl;             // packed words per lane per k-step
-    int nr;              // C registers per lane holding live tokens: 1 (t = 1) or 4
+    int nr;              // C registers per lane holding live tokens: 1 (t <= 4) or 4
     int sps;             // group mode: scale units per k-step (1, 2, 4); 0 = tensor/row scales
     bool lds_a;          // activations staged in LDS (else read from global memory)
     bool acc;            // some matrix wants the integer products

@@ -36,13 +36,14 @@
 // converted and accumulated in fp32 with the group's scale.
 #pragma once
 
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "gemv.hpp"
 #include "lowbit.h"
 
 namespace lowbit {
 
-constexpr int kGemvD = 4;   // k-steps of weight loads in flight per wavefront
 
 template <int FMT, int WPL> struct GemvShape {
     static constexpr int kKB = FMT == FMT_BINARY ? 128 : 64;    // k per block (one MFMA k-extent per quarter)
@@ -53,11 +54,12 @@ template <int FMT, int WPL> struct GemvShape {
     static constexpr int kStepBytes = 256 * WPL;                 // bytes of one (tile, k-step)
 };
 
-// 16 activation bytes q[k0 .. k0 + 16) of one token row, zero past K.
-__device__ __forceinline__ i32x4 load_q16(const int8_t* qrow, int k0, int K, bool vec) {
+// 16 activation bytes q[k0 .. k0 + 16) of one token row, zero past K
+// (vec_only: the caller knows vec holds, and the partial-load code is left out).
+__device__ __forceinline__ i32x4 load_q16(const int8_t* qrow, int k0, int K, bool vec, bool vec_only = false) {
     i32x4 v = {0, 0, 0, 0};
     if (k0 < K) {
-        if (vec) {
+        if (vec_only || vec) {
             v = *reinterpret_cast<const i32x4*>(qrow + k0);
         } else {
             const uint8_t* p = reinterpret_cast<const uint8_t*>(qrow + k0);
@@ -83,7 +85,24 @@ __device__ __forceinline__ uint32_t quant_word(const float4 v, float r, int vali
     return w;
 }
 
-// NR: C registers per lane holding live tokens (token = 4 * lane group + r).
+// Sixteen-wavefront workgroups are asked for 8 waves per SIMD (64 VGPRs), so
+// that two of them share a CU: at the compiler's own choice the ternary and
+// int4 kernels take 65-70 registers and one workgroup per CU, which leaves a
+// 360-workgroup launch two rounds deep.  The binary kernels (two MFMAs per
+// block), ternary with four scale units per k-step, several units per group
+// with four token registers, and the kernels that also write the integer
+// products would spill at 64.
+constexpr int gemv_min_waves(int fmt, int nr, int sps, bool upg1, int wv, bool acc) {
+    const bool spills = fmt == FMT_BINARY || acc || (fmt == FMT_TERNARY && sps == 4) || (sps > 0 && !upg1 && nr == 4);
+    return wv == 16 && !spills ? 8 : 1;
+}
+
+// NR: C registers per lane holding live tokens.  MFMA output row i = 4 g + r
+// (lane group g, register r).  With NR = 1 (t <= 4) row i carries token
+// g + 4 r, so the four tokens sit in register 0 of the four lane groups and a
+// group epilogue converts one register per lane, not four; with NR = 4 row i
+// carries token i (the 16 A rows of one LDS read then start on distinct
+// banks).
 // SPS: group mode: scale units per k-step; 0 = tensor/row scales.
 // UPG1: group mode: every scale unit is a whole group.
 // LDSA: activations staged in LDS.  ACC: also write the integer products
@@ -100,7 +119,7 @@ __device__ __forceinline__ uint32_t quant_word(const float4 v, float r, int vali
 // r = 127 / m, codes clip(rint(x r)), s_x = m / 127), every workgroup for its
 // own stage; the matrix's first workgroup also writes the codes and scale out.
 template <int FMT, int WPL, int NR, int SPS, bool UPG1, bool LDSA, bool ACC, bool FUSE, int WV, int PRE>
-__global__ __launch_bounds__(64 * WV) void gemv_kernel(const GemvParams p) {
+__global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(gemv_min_waves(FMT, NR, SPS, UPG1, WV, ACC)))) void gemv_kernel(const GemvParams p) {
     using S = GemvShape<FMT, WPL>;
     constexpr int D = kGemvD;
     constexpr int NB = S::kNB, KB = S::kKB, SK = S::kSK, MPB = S::kMPB;
@@ -144,15 +163,28 @@ __global__ __launch_bounds__(64 * WV) void gemv_kernel(const GemvParams p) {
     const int s_cnt = live ? min(p.n_steps - s0, p.part_len) : 0;
     const int s_loop = (s_cnt + D - 1) / D * D;
     const int K = p.K, T = p.T;
-    const int tok = min(rl, T - 1);                          // A row; rows >= t are never stored
+    // token of A row rl (rows of t >= T are never stored), and of output
+    // register r of lane group g
+    const int tok = min(NR == 1 ? (rl >> 2) + 4 * (rl & 3) : rl, T - 1);
+    auto out_token = [](int g, int r) { return NR == 1 ? g + 4 * r : 4 * g + r; };
 
     const int row = tile * 16 + rl;
 
     // (a fused launch issues its ring unconditionally; a wave without steps
     // then reads its tile's first step, never consumed)
-    const uint8_t* wp = M.packed + ((size_t)tile * p.n_steps + (FUSE && s_cnt <= 0 ? 0 : s0)) * STEP +
-                        lane * (4 * WPL);
-    const float* scp = M.scales + (size_t)tile * p.G * 16 + rl;            // group mode
+    // Buffer resources over the tile's packed steps and its group scales: the
+    // ring's loads then take a per-lane constant offset plus a uniform one
+    // (scalar arithmetic), where flat addresses cost 64-bit vector adds per
+    // load.
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(M.packed) + (size_t)tile * p.n_steps * STEP, 0, p.n_steps * STEP, 0x00020000);
+    const int w_voff = lane * (4 * WPL);
+    const int w_s0 = FUSE && s_cnt <= 0 ? 0 : s0;           // first step of the part
+    __amdgpu_buffer_rsrc_t rs = rw;                          // group mode: [G][16 rows] scales of the tile
+    if constexpr (GROUP)
+        rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(M.scales) + (size_t)tile * p.G * 16, 0,
+                                               p.G * 64, 0x00020000);
+    const int s_voff = rl * 4;
     const int8_t* qrow = M.q + (size_t)tok * K;                            // global activations
 
     uint32_t wv[D][WPL];
@@ -170,11 +202,11 @@ __global__ __launch_bounds__(64 * WV) void gemv_kernel(const GemvParams p) {
         // step, never consumed): the compiler's wait counting then keeps all
         // D steps in flight.
         const int jj = j < s_cnt ? j : max(s_cnt - 1, 0);
-        load_words_stream<WPL>(wp + (size_t)jj * STEP, wv[u]);      // each weight byte is read once
+        load_words_stream_buf<WPL>(rw, w_voff, (w_s0 + jj) * STEP, wv[u]);   // each weight byte is read once
         if constexpr (GROUP) {
             #pragma unroll
             for (int v = 0; v < NU; ++v) {
-                sg[u][v] = scp[min(lg, p.G - 1) * 16];
+                sg[u][v] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, s_voff, min(lg, p.G - 1) * 64, 0));
                 if constexpr (UPG1) {
                     ++lg;
                 } else {
@@ -226,12 +258,59 @@ __global__ __launch_bounds__(64 * WV) void gemv_kernel(const GemvParams p) {
     }
     float sw = 0.0f;
     if constexpr (!GROUP) sw = M.scales[p.scale_per_row ? min(row, M.n - 1) : 0];
-    float sxv[NR];
-    if constexpr (!FUSE) {
-        #pragma unroll
-        for (int r = 0; r < NR; ++r) sxv[r] = M.sx[min(4 * g + r, T - 1)];
-    }
+    float sxv[NR];                                           // token scales (loaded after the k-loop)
     const int8_t* lds_a = reinterpret_cast<const int8_t*>(smem) + (size_t)tok * p.stride + g * (KB / 4);
+
+    // Stage steps [step0, step0 + nsteps) of every token row into LDS (row t
+    // at t * stride): the (token, chunk) space in batches of SB chunks per
+    // thread, every load of a batch issued before its stores, so that a
+    // thread waits for one L2 round trip per batch, not one per token row.
+    // A thread's chunks are NT apart; their (token, chunk) pairs advance
+    // incrementally (one division per phase, not one per chunk).
+    auto stage_phase = [&](auto vec_only, int step0, int nsteps) __attribute__((always_inline)) {
+        constexpr bool VEC_ONLY = decltype(vec_only)::value;   // every q row 16-byte aligned, k % 16 == 0
+        constexpr int SB = 4;
+        constexpr int CB = FMT == FMT_BINARY ? 32 : 16;      // codes per chunk
+        const int8_t* q = M.q;
+        const int per_row = nsteps * SK / CB, total = T * per_row;
+        const int k0 = step0 * SK;
+        const int dt = NT / per_row, dcc = NT - dt * per_row;
+        int t = (int)threadIdx.x / per_row, cc = (int)threadIdx.x - t * per_row;
+        for (int base = threadIdx.x; base < total; base += NT * SB) {
+            i32x4 lo[SB], hi[SB];
+            int tb[SB], cb[SB];
+            #pragma unroll
+            for (int b = 0; b < SB; ++b) {
+                tb[b] = t; cb[b] = cc;
+                cc += dcc; t += dt;
+                if (cc >= per_row) { cc -= per_row; ++t; }
+                if (base + b * NT < total) {
+                    const int8_t* qr = q + (size_t)tb[b] * K;
+                    lo[b] = load_q16(qr, k0 + CB * cb[b], K, VEC_ONLY || p.q_vec, VEC_ONLY);
+                    if constexpr (FMT == FMT_BINARY)
+                        hi[b] = load_q16(qr, k0 + CB * cb[b] + 16, K, VEC_ONLY || p.q_vec, VEC_ONLY);
+                }
+            }
+            #pragma unroll
+            for (int b = 0; b < SB; ++b) {
+                if (base + b * NT < total) {
+                    uint8_t* dst = smem + (size_t)tb[b] * p.stride + CB * cb[b];
+                    if constexpr (FMT == FMT_BINARY) {
+                        // 32-code chunks permuted to the order decode_binary yields
+                        const uint32_t X[8] = {(uint32_t)lo[b][0], (uint32_t)lo[b][1], (uint32_t)lo[b][2],
+                                               (uint32_t)lo[b][3], (uint32_t)hi[b][0], (uint32_t)hi[b][1],
+                                               (uint32_t)hi[b][2], (uint32_t)hi[b][3]};
+                        i32x4 a0, a1;
+                        perm_binary_a(X, a0, a1);
+                        *reinterpret_cast<i32x4*>(dst) = a0;
+                        *reinterpret_cast<i32x4*>(dst + 16) = a1;
+                    } else {
+                        *reinterpret_cast<i32x4*>(dst) = lo[b];
+                    }
+                }
+            }
+        }
+    };
     if constexpr (FUSE) {
         // fp32 x -> int8 codes in the stage (one token).  Thread tid owns the
         // words (4 consecutive k) tid + 256 j and issues their loads in rounds
@@ -375,46 +454,7 @@ __global__ __launch_bounds__(64 * WV) void gemv_kernel(const GemvParams p) {
         #pragma unroll
         for (int r = 0; r < NR; ++r) sxv[r] = st;
     } else if constexpr (LDSA) {
-        // the (token, chunk) space of the stage in batches of SB chunks per
-        // thread, every load of a batch issued before its stores, so that a
-        // thread waits for one L2 round trip per batch, not one per token row
-        constexpr int SB = 4;
-        constexpr int CB = FMT == FMT_BINARY ? 32 : 16;      // codes per chunk
-        const int kpad = p.n_steps * SK;
-        const int8_t* q = M.q;
-        const int per_row = kpad / CB, total = T * per_row;
-        for (int base = threadIdx.x; base < total; base += NT * SB) {
-            i32x4 lo[SB], hi[SB];
-            #pragma unroll
-            for (int b = 0; b < SB; ++b) {
-                const int c = base + b * NT;
-                if (c < total) {
-                    const int t = c / per_row, cc = c - t * per_row;
-                    lo[b] = load_q16(q + (size_t)t * K, CB * cc, K, p.q_vec);
-                    if constexpr (FMT == FMT_BINARY) hi[b] = load_q16(q + (size_t)t * K, CB * cc + 16, K, p.q_vec);
-                }
-            }
-            #pragma unroll
-            for (int b = 0; b < SB; ++b) {
-                const int c = base + b * NT;
-                if (c < total) {
-                    const int t = c / per_row, cc = c - t * per_row;
-                    uint8_t* dst = smem + (size_t)t * p.stride + CB * cc;
-                    if constexpr (FMT == FMT_BINARY) {
-                        // 32-code chunks permuted to the order decode_binary yields
-                        const uint32_t X[8] = {(uint32_t)lo[b][0], (uint32_t)lo[b][1], (uint32_t)lo[b][2],
-                                               (uint32_t)lo[b][3], (uint32_t)hi[b][0], (uint32_t)hi[b][1],
-                                               (uint32_t)hi[b][2], (uint32_t)hi[b][3]};
-                        i32x4 a0, a1;
-                        perm_binary_a(X, a0, a1);
-                        *reinterpret_cast<i32x4*>(dst) = a0;
-                        *reinterpret_cast<i32x4*>(dst + 16) = a1;
-                    } else {
-                        *reinterpret_cast<i32x4*>(dst) = lo[b];
-                    }
-                }
-            }
-        }
+        stage_phase(std::false_type{}, 0, min(p.ph_steps, p.n_steps));
         __syncthreads();
     }
 
@@ -427,13 +467,30 @@ __global__ __launch_bounds__(64 * WV) void gemv_kernel(const GemvParams p) {
     int cu = 0, cg = g0, cunit = unit0;                      // compute side: unit in group, group, unit
     i32x4 Cg = {0, 0, 0, 0};                                 // group partial (groups of several units)
 
+    // LDS phases (16-wavefront workgroups whose whole activation row set
+    // would not leave room for two workgroups per CU): the stage holds
+    // ph_steps k-steps at a time.  At a phase's first step every wavefront of
+    // the workgroup meets at a barrier, the next steps are staged over the
+    // old ones, and a second barrier publishes them; the weight ring runs on
+    // across the change.  Wavefronts run every step in the same order (one
+    // part per tile), so each meets the same barriers.
+    int a_off = 0;                                           // A of step s at lds_a + s * SK - a_off
+    int ph_next = p.ph_steps;                                // first step of the next phase
+    auto next_phase = [&]() __attribute__((always_inline)) {
+        __syncthreads();
+        stage_phase(std::true_type{}, ph_next, min(p.ph_steps, p.n_steps - ph_next));   // phases need q_vec
+        __syncthreads();
+        a_off = ph_next * SK;
+        ph_next += p.ph_steps;
+    };
+
     // MFMAs of block b of slot u into C
     auto block_mfma = [&](int u, int s, int b, i32x4 C, bool fresh) -> i32x4 {
         const i32x4 zero = {0, 0, 0, 0};
         i32x4 A[MPB];
         if constexpr (LDSA) {
             #pragma unroll
-            for (int m = 0; m < MPB; ++m) A[m] = *reinterpret_cast<const i32x4*>(lds_a + s * SK + b * KB + 16 * m);
+            for (int m = 0; m < MPB; ++m) A[m] = *reinterpret_cast<const i32x4*>(lds_a + (s * SK - a_off) + b * KB + 16 * m);
         } else if constexpr (FMT == FMT_BINARY) {
             // binary padding codes decode as +1: activations past K must be zero
             const int k0 = s * SK + b * KB + g * (KB / 4);
@@ -458,15 +515,19 @@ __global__ __launch_bounds__(64 * WV) void gemv_kernel(const GemvParams p) {
         }
         return C;
     };
-    // a group's integer partial is complete: rescale into yp (and record it)
+    // a group's integer partial is complete: rescale into yp (and record it).
+    // Cx holds 2^SHIFT times the partial, and yp is kept 2^SHIFT times too:
+    // converting Cx itself gives exactly 2^SHIFT (float)partial, and scaling
+    // by a power of two commutes with fp32 rounding, so the products and sums
+    // are the unshifted ones times 2^SHIFT, bit for bit (one shift fewer per
+    // register per group; the epilogue scales by 2^-SHIFT).
     auto close_group = [&](const i32x4& Cx, float sc, int gi) {
         #pragma unroll
         for (int r = 0; r < NR; ++r) {
-            const int32_t a = Cx[r] >> SHIFT;
-            yp[r] = yp[r] + sc * (float)a;
+            yp[r] = yp[r] + sc * (float)Cx[r];
             if constexpr (ACC) {
-                const int t = 4 * g + r;
-                if (M.acc && live && t < T && row < M.n) M.acc[((size_t)t * M.n + row) * p.G + gi] = a;
+                const int t = out_token(g, r);
+                if (M.acc && live && t < T && row < M.n) M.acc[((size_t)t * M.n + row) * p.G + gi] = Cx[r] >> SHIFT;
             }
         }
     };
@@ -510,6 +571,9 @@ __global__ __launch_bounds__(64 * WV) void gemv_kernel(const GemvParams p) {
     // last D steps without refills
     int j = 0;
     for (; j + D < s_loop; j += D) {
+        if constexpr (LDSA && !FUSE) {
+            if (j == ph_next) next_phase();                  // (uniform; phases are whole rounds of D steps)
+        }
         #pragma unroll
         for (int u = 0; u < D; ++u) {
             compute_slot(u, j + u);
@@ -517,11 +581,23 @@ __global__ __launch_bounds__(64 * WV) void gemv_kernel(const GemvParams p) {
         }
     }
     if (s_loop > 0) {
+        if constexpr (LDSA && !FUSE) {
+            if (j == ph_next) next_phase();
+        }
         #pragma unroll
         for (int u = 0; u < D; ++u) compute_slot(u, j + u);
     }
+    if constexpr (LDSA && !FUSE) {
+        // a wave without a tile still takes its part in every phase change
+        if (s_cnt <= 0)
+            while (ph_next < p.n_steps) next_phase();
+    }
 
     // ---- combine k-split partials (fixed order), rescale, store
+    if constexpr (!FUSE) {
+        #pragma unroll
+        for (int r = 0; r < NR; ++r) sxv[r] = M.sx[min(out_token(g, r), T - 1)];
+    }
     int32_t ai[NR];
     #pragma unroll
     for (int r = 0; r < NR; ++r) ai[r] = C[r] >> SHIFT;
@@ -545,10 +621,10 @@ __global__ __launch_bounds__(64 * WV) void gemv_kernel(const GemvParams p) {
     if (part == 0 && live && row < M.n) {
         #pragma unroll
         for (int r = 0; r < NR; ++r) {
-            const int t = 4 * g + r;
+            const int t = out_token(g, r);
             if (t < T) {
                 if constexpr (GROUP) {
-                    M.y[(size_t)t * M.n + row] = sxv[r] * yp[r];
+                    M.y[(size_t)t * M.n + row] = sxv[r] * (yp[r] * (1.0f / (float)(1 << SHIFT)));
                 } else {
                     M.y[(size_t)t * M.n + row] = (float)ai[r] * (sxv[r] * sw);
                     if constexpr (ACC) {
@@ -575,12 +651,10 @@ void gemv_launch_lds(const GemvParams& p, const GemvCfg& c, hipStream_t st) {
                 return;
             }
         }
-        if constexpr (NR == 4) {   // a large stage shared by 16 wavefronts (several tokens)
-            if (c.waves == 16) {
-                if (c.acc) gemv_kernel<FMT, WPL, 4, SPS, UPG1, true, true, false, 16, PRE_NONE><<<grid, block, c.lds_bytes, st>>>(p);
-                else gemv_kernel<FMT, WPL, 4, SPS, UPG1, true, false, false, 16, PRE_NONE><<<grid, block, c.lds_bytes, st>>>(p);
-                return;
-            }
+        if (c.waves == 16) {       // a large stage shared by 16 wavefronts (several tokens)
+            if (c.acc) gemv_kernel<FMT, WPL, NR, SPS, UPG1, true, true, false, 16, PRE_NONE><<<grid, block, c.lds_bytes, st>>>(p);
+            else gemv_kernel<FMT, WPL, NR, SPS, UPG1, true, false, false, 16, PRE_NONE><<<grid, block, c.lds_bytes, st>>>(p);
+            return;
         }
         if (c.acc) gemv_kernel<FMT, WPL, NR, SPS, UPG1, true, true, false, 4, PRE_NONE><<<grid, block, c.lds_bytes, st>>>(p);
         else gemv_kernel<FMT, WPL, NR, SPS, UPG1, true, false, false, 4, PRE_NONE><<<grid, block, c.lds_bytes, st>>>(p);

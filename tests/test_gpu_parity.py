@@ -236,6 +236,50 @@ def test_grouped_matches_single_and_oracle(fmt, scale, group, t, count):
         check_y(ys[i].cpu().numpy(), y32, y64, f"grouped {i}")
 
 
+@pytest.mark.parametrize("t,k", [(16, 9728), (7, 12208), (16, 9720)])
+def test_grouped_gemv_large_stages(t, k):
+    """Grouped decode GEMVs whose activation stage (t rows of k codes) exceeds
+    half a CU's LDS, with enough tiles for one part per tile: 48 products
+    (three distinct matrices of 405 rows, 26 tiles each: workgroups of 16
+    tiles, the second with 6 idle wavefronts).  With k % 16 == 0 the stage is
+    filled in phases of whole ring rounds (t = 16, k = 9728: 3 phases;
+    t = 7, k = 12208: 2, the last step ragged); k = 9720 stages the whole row
+    in one 16-wavefront workgroup per CU.  acc equals per-matrix
+    lowbit_linear and the oracle bit for bit; y is within tolerance of both
+    (group partials may be combined in another order)."""
+    import torch
+    lb = pytest.importorskip("bit_weight_linear_bitlinear_amd")
+    n, count, fmt, scale, group = 405, 48, "ternary", "group", 128
+    say(f"[case] grouped large stage t={t} k={k} n={n} count={count}")
+    mats = []
+    for i in range(3):
+        w, x = workloads.random_case(900 + i, n, k, t)
+        d, p, s_, _, _ = pack_upload(w, fmt, scale, group)
+        q, sx, _ = act_quant_dev(to_dev(x))
+        mats.append((w, x, d, p, s_, q, sx))
+    pick = [mats[i % 3] for i in range(count)]
+    ys = [torch.full((t, n), float("nan"), device="cuda") for _ in range(count)]
+    accs = [torch.full((t, n, pick[0][2].n_groups), -7, dtype=torch.int32, device="cuda") for _ in range(count)]
+    lb.lowbit_linear_grouped([m[2] for m in pick], [m[3] for m in pick], [m[4] for m in pick],
+                             [m[5] for m in pick], [m[6] for m in pick], ys, accs)
+    ys_stream = [torch.full((t, n), float("nan"), device="cuda") for _ in range(count)]
+    lb.lowbit_linear_grouped([m[2] for m in pick], [m[3] for m in pick], [m[4] for m in pick],
+                             [m[5] for m in pick], [m[6] for m in pick], ys_stream)
+    torch.cuda.synchronize()
+    for i in range(3):
+        w, x, d, p, s_, q, sx = mats[i]
+        y1, a1 = linear_dev("gemv", d, p, s_, q, sx)
+        p_ref, s_ref, _, _ = oracle.quantize_and_pack(w, fmt, scale, group, False)
+        q_ref, sx_ref, _ = oracle.act_quant(x)
+        y32, y64, acc_ref = oracle.linear(p_ref, s_ref, fmt, scale, group, n, k, q_ref, sx_ref)
+        assert (a1.cpu().numpy() == acc_ref).all()
+        for j in range(i, count, 3):
+            assert torch.equal(accs[j], a1), j
+            assert torch.equal(ys_stream[j], ys[j]), j
+            assert torch.allclose(ys[j], y1, rtol=1e-5, atol=1e-6), j
+            check_y(ys[j].cpu().numpy(), y32, y64, f"grouped large stage {j}")
+
+
 @pytest.mark.parametrize("fmt,scale,group,k,t,ns", [
     ("binary", "row", 0, 192, 300, [96, 192, 768, 20, 130]),
     ("int4", "row", 0, 1280, 260, [1280, 17, 384]),
