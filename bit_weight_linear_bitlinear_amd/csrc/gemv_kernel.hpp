@@ -36,6 +36,7 @@
 // converted and accumulated in fp32 with the group's scale.
 #pragma once
 
+#include <climits>
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -618,18 +619,26 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(gemv_mi
             }
         }
     }
+    // Several tokens: y with the non-temporal hint.  The output stream is
+    // small beside the weights, but its writes reach HBM in the middle of the
+    // read stream and cost far more than their bytes (t = 4, the 4B-class
+    // pass: 17 MB of y took 24 us of a 142 us launch; non-temporal stores
+    // saved a third of that).  One token keeps y cached for its consumer.
     if (part == 0 && live && row < M.n) {
+        const __amdgpu_buffer_rsrc_t ry =
+            __builtin_amdgcn_make_buffer_rsrc(M.y, 0, (int)min((int64_t)T * M.n * 4, (int64_t)INT_MAX), 0x00020000);
         #pragma unroll
         for (int r = 0; r < NR; ++r) {
             const int t = out_token(g, r);
             if (t < T) {
-                if constexpr (GROUP) {
-                    M.y[(size_t)t * M.n + row] = sxv[r] * (yp[r] * (1.0f / (float)(1 << SHIFT)));
-                } else {
-                    M.y[(size_t)t * M.n + row] = (float)ai[r] * (sxv[r] * sw);
-                    if constexpr (ACC) {
-                        if (M.acc) M.acc[(size_t)t * M.n + row] = ai[r];
-                    }
+                float v;
+                if constexpr (GROUP) v = sxv[r] * (yp[r] * (1.0f / (float)(1 << SHIFT)));
+                else v = (float)ai[r] * (sxv[r] * sw);
+                const int off = (t * M.n + row) * 4;
+                if (T > 1) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), ry, off, 0, 2);   // nt
+                else __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), ry, off, 0, 0);
+                if constexpr (ACC && !GROUP) {
+                    if (M.acc) M.acc[(size_t)t * M.n + row] = ai[r];
                 }
             }
         }
