@@ -245,6 +245,85 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(gemv_mi
         __builtin_amdgcn_sched_barrier(0);                   // keep these loads ahead of the ring's
     }
 
+    // Stage steps [step0, step0 + nsteps) of every token row into LDS (row t
+    // at t * stride): the (token, chunk) space in batches of SB chunks per
+    // thread, every load of a batch issued before its stores, so that a
+    // thread waits for one L2 round trip per batch, not one per token row.
+    // A thread's chunks are NT apart; their (token, chunk) pairs advance
+    // incrementally (one division per phase, not one per chunk).
+    constexpr int SB = 4;
+    constexpr int CB = FMT == FMT_BINARY ? 32 : 16;          // codes per chunk
+    auto stage_issue = [&](auto vec_only, auto nb, int step0, int nsteps, int base, int& t, int& cc, i32x4* lo,
+                           i32x4* hi, int* tb, int* cb) __attribute__((always_inline)) {
+        constexpr bool VEC_ONLY = decltype(vec_only)::value;   // every q row 16-byte aligned, k % 16 == 0
+        constexpr int NBAT = decltype(nb)::value;              // chunks per thread in this batch
+        const int per_row = nsteps * SK / CB, total = T * per_row;
+        const int k0 = step0 * SK;
+        const int dt = NT / per_row, dcc = NT - dt * per_row;
+        #pragma unroll
+        for (int b = 0; b < NBAT; ++b) {
+            tb[b] = t; cb[b] = cc;
+            cc += dcc; t += dt;
+            if (cc >= per_row) { cc -= per_row; ++t; }
+            if (base + b * NT < total) {
+                const int8_t* qr = M.q + (size_t)tb[b] * K;
+                lo[b] = load_q16(qr, k0 + CB * cb[b], K, VEC_ONLY || p.q_vec, VEC_ONLY);
+                if constexpr (FMT == FMT_BINARY)
+                    hi[b] = load_q16(qr, k0 + CB * cb[b] + 16, K, VEC_ONLY || p.q_vec, VEC_ONLY);
+            }
+        }
+    };
+    auto stage_store = [&](auto nb, int nsteps, int base, const i32x4* lo, const i32x4* hi, const int* tb,
+                           const int* cb) __attribute__((always_inline)) {
+        constexpr int NBAT = decltype(nb)::value;
+        const int total = T * (nsteps * SK / CB);
+        #pragma unroll
+        for (int b = 0; b < NBAT; ++b) {
+            if (base + b * NT < total) {
+                uint8_t* dst = smem + (size_t)tb[b] * p.stride + CB * cb[b];
+                if constexpr (FMT == FMT_BINARY) {
+                    // 32-code chunks permuted to the order decode_binary yields
+                    const uint32_t X[8] = {(uint32_t)lo[b][0], (uint32_t)lo[b][1], (uint32_t)lo[b][2],
+                                           (uint32_t)lo[b][3], (uint32_t)hi[b][0], (uint32_t)hi[b][1],
+                                           (uint32_t)hi[b][2], (uint32_t)hi[b][3]};
+                    i32x4 a0, a1;
+                    perm_binary_a(X, a0, a1);
+                    *reinterpret_cast<i32x4*>(dst) = a0;
+                    *reinterpret_cast<i32x4*>(dst + 16) = a1;
+                } else {
+                    *reinterpret_cast<i32x4*>(dst) = lo[b];
+                }
+            }
+        }
+    };
+    // the batches from chunk base0 (a thread's first chunk is threadIdx.x)
+    auto stage_phase = [&](auto vec_only, int step0, int nsteps, int base0) __attribute__((always_inline)) {
+        const int per_row = nsteps * SK / CB, total = T * per_row;
+        int t = base0 / per_row, cc = base0 - t * per_row;
+        for (int base = base0; base < total; base += NT * SB) {
+            i32x4 lo[SB], hi[SB];
+            int tb[SB], cb[SB];
+            stage_issue(vec_only, std::integral_constant<int, SB>{}, step0, nsteps, base, t, cc, lo, hi, tb, cb);
+            stage_store(std::integral_constant<int, SB>{}, nsteps, base, lo, hi, tb, cb);
+        }
+    };
+    // A 16-wavefront stage (several tokens): its first two chunks per thread
+    // are loaded ahead of the weight ring, so that their wait (counted in
+    // order) is for the L2 loads alone and the stage fills while the ring's
+    // first HBM loads are in flight.  (Four-wavefront workgroups stage little
+    // and are short of registers at that point.)
+    constexpr bool EARLY = LDSA && !FUSE && WV == 16;
+    constexpr int SBE = 2;
+    const int nsteps0 = min(p.ph_steps, p.n_steps);
+    i32x4 e_lo[SBE], e_hi[SBE];
+    int e_tb[SBE], e_cb[SBE];
+    if constexpr (EARLY) {
+        const int per_row0 = nsteps0 * SK / CB;
+        int t = (int)threadIdx.x / per_row0, cc = (int)threadIdx.x - t * per_row0;
+        stage_issue(std::false_type{}, std::integral_constant<int, SBE>{}, 0, nsteps0, threadIdx.x, t, cc, e_lo, e_hi,
+                    e_tb, e_cb);
+    }
+
     // ---- ring prologue, the epilogue operands, then the activation stage
     if (FUSE || s_cnt > 0) {
         #pragma unroll
@@ -262,56 +341,6 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(gemv_mi
     float sxv[NR];                                           // token scales (loaded after the k-loop)
     const int8_t* lds_a = reinterpret_cast<const int8_t*>(smem) + (size_t)tok * p.stride + g * (KB / 4);
 
-    // Stage steps [step0, step0 + nsteps) of every token row into LDS (row t
-    // at t * stride): the (token, chunk) space in batches of SB chunks per
-    // thread, every load of a batch issued before its stores, so that a
-    // thread waits for one L2 round trip per batch, not one per token row.
-    // A thread's chunks are NT apart; their (token, chunk) pairs advance
-    // incrementally (one division per phase, not one per chunk).
-    auto stage_phase = [&](auto vec_only, int step0, int nsteps) __attribute__((always_inline)) {
-        constexpr bool VEC_ONLY = decltype(vec_only)::value;   // every q row 16-byte aligned, k % 16 == 0
-        constexpr int SB = 4;
-        constexpr int CB = FMT == FMT_BINARY ? 32 : 16;      // codes per chunk
-        const int8_t* q = M.q;
-        const int per_row = nsteps * SK / CB, total = T * per_row;
-        const int k0 = step0 * SK;
-        const int dt = NT / per_row, dcc = NT - dt * per_row;
-        int t = (int)threadIdx.x / per_row, cc = (int)threadIdx.x - t * per_row;
-        for (int base = threadIdx.x; base < total; base += NT * SB) {
-            i32x4 lo[SB], hi[SB];
-            int tb[SB], cb[SB];
-            #pragma unroll
-            for (int b = 0; b < SB; ++b) {
-                tb[b] = t; cb[b] = cc;
-                cc += dcc; t += dt;
-                if (cc >= per_row) { cc -= per_row; ++t; }
-                if (base + b * NT < total) {
-                    const int8_t* qr = q + (size_t)tb[b] * K;
-                    lo[b] = load_q16(qr, k0 + CB * cb[b], K, VEC_ONLY || p.q_vec, VEC_ONLY);
-                    if constexpr (FMT == FMT_BINARY)
-                        hi[b] = load_q16(qr, k0 + CB * cb[b] + 16, K, VEC_ONLY || p.q_vec, VEC_ONLY);
-                }
-            }
-            #pragma unroll
-            for (int b = 0; b < SB; ++b) {
-                if (base + b * NT < total) {
-                    uint8_t* dst = smem + (size_t)tb[b] * p.stride + CB * cb[b];
-                    if constexpr (FMT == FMT_BINARY) {
-                        // 32-code chunks permuted to the order decode_binary yields
-                        const uint32_t X[8] = {(uint32_t)lo[b][0], (uint32_t)lo[b][1], (uint32_t)lo[b][2],
-                                               (uint32_t)lo[b][3], (uint32_t)hi[b][0], (uint32_t)hi[b][1],
-                                               (uint32_t)hi[b][2], (uint32_t)hi[b][3]};
-                        i32x4 a0, a1;
-                        perm_binary_a(X, a0, a1);
-                        *reinterpret_cast<i32x4*>(dst) = a0;
-                        *reinterpret_cast<i32x4*>(dst + 16) = a1;
-                    } else {
-                        *reinterpret_cast<i32x4*>(dst) = lo[b];
-                    }
-                }
-            }
-        }
-    };
     if constexpr (FUSE) {
         // fp32 x -> int8 codes in the stage (one token).  Thread tid owns the
         // words (4 consecutive k) tid + 256 j and issues their loads in rounds
@@ -455,7 +484,12 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(gemv_mi
         #pragma unroll
         for (int r = 0; r < NR; ++r) sxv[r] = st;
     } else if constexpr (LDSA) {
-        stage_phase(std::false_type{}, 0, min(p.ph_steps, p.n_steps));
+        if constexpr (EARLY) {
+            stage_store(std::integral_constant<int, SBE>{}, nsteps0, threadIdx.x, e_lo, e_hi, e_tb, e_cb);
+            stage_phase(std::false_type{}, 0, nsteps0, threadIdx.x + NT * SBE);
+        } else {
+            stage_phase(std::false_type{}, 0, nsteps0, threadIdx.x);
+        }
         __syncthreads();
     }
 
@@ -479,7 +513,7 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(gemv_mi
     int ph_next = p.ph_steps;                                // first step of the next phase
     auto next_phase = [&]() __attribute__((always_inline)) {
         __syncthreads();
-        stage_phase(std::true_type{}, ph_next, min(p.ph_steps, p.n_steps - ph_next));   // phases need q_vec
+        stage_phase(std::true_type{}, ph_next, min(p.ph_steps, p.n_steps - ph_next), threadIdx.x);   // phases need q_vec
         __syncthreads();
         a_off = ph_next * SK;
         ph_next += p.ph_steps;
