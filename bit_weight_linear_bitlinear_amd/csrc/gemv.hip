@@ -136,11 +136,14 @@ hipError_t launch_gemv_group(const LinearArgs* mats, int count, hipStream_t stre
     if (spg > 0) {
         if (tiles < 4 * cus && n_steps >= 4) ksplit = 2;
         if (tiles < 2 * cus && n_steps >= 8) ksplit = 4;
-        // more parts while the launch holds fewer wavefronts than two rounds
-        // of the CUs' resident ones (32 each), unless the stage is one that
-        // needs LDS phases (those take whole k-ranges)
-        const bool phased_stage = a.t > 1 && stage + (int64_t)16 * 4 * 64 * 4 > kGemvLdsHalf;
-        while (!phased_stage && ksplit < 4 && (int64_t)tiles * ksplit < 2LL * cus * 32 && n_steps >= 4 * ksplit)
+        // several tokens: more parts while the launch holds fewer wavefronts
+        // than two rounds of the CUs' resident ones (32 each), unless the
+        // stage is one that needs LDS phases (those take whole k-ranges).
+        // (With one token each part's workgroup restages the row for one
+        // tile, and a fused launch would quantise it once more per part.)
+        const bool phased_stage = stage + (int64_t)16 * 4 * 64 * 4 > kGemvLdsHalf;
+        while (a.t > 1 && !cfg.fuse && !phased_stage && ksplit < 4 && (int64_t)tiles * ksplit < 2LL * cus * 32 &&
+               n_steps >= 4 * ksplit)
             ksplit *= 2;
     }
     int part_len = n_steps;
