@@ -236,25 +236,34 @@ def test_grouped_matches_single_and_oracle(fmt, scale, group, t, count):
         check_y(ys[i].cpu().numpy(), y32, y64, f"grouped {i}")
 
 
-@pytest.mark.parametrize("t,k", [(16, 9728), (7, 12208), (16, 9720)])
-def test_grouped_gemv_large_stages(t, k):
-    """Grouped decode GEMVs whose activation stage (t rows of k codes) exceeds
-    half a CU's LDS, with enough tiles for one part per tile: 48 products
-    (three distinct matrices of 405 rows, 26 tiles each: workgroups of 16
-    tiles, the second with 6 idle wavefronts).  With k % 16 == 0 the stage is
-    filled in phases of whole ring rounds (t = 16, k = 9728: 3 phases;
-    t = 7, k = 12208: 2, the last step ragged); k = 9720 stages the whole row
-    in one 16-wavefront workgroup per CU.  acc equals per-matrix
-    lowbit_linear and the oracle bit for bit; y is within tolerance of both
-    (group partials may be combined in another order)."""
+@pytest.mark.parametrize("fmt,t,k", [("ternary", 16, 9728), ("ternary", 7, 12208), ("ternary", 16, 9720),
+                                     ("ternary", 4, 9728), ("ternary", 16, 2560), ("int4", 16, 9728),
+                                     ("binary", 16, 9728), ("int4", 4, 2560), ("binary", 5, 3072)])
+def test_grouped_gemv_large_stages(fmt, t, k):
+    """Grouped decode GEMVs of several tokens at group-128 scales, 48
+    products (three distinct matrices of 405 rows, 26 tiles each) in one
+    launch, through every way a several-token stage is held:
+      - larger than half a CU's LDS with one part per tile: filled in phases
+        of whole ring rounds (ternary t = 16, k = 9728: 3 phases; t = 7,
+        k = 12208: 2, the last step ragged; int4 and binary at t = 16,
+        k = 9728, binary without the 8-waves-per-SIMD request), workgroups of
+        16 tiles, the second with 6 idle wavefronts; k = 9720 (no 16-byte
+        rows) stages the whole row in one 16-wavefront workgroup per CU;
+      - 16-wavefront workgroups of four k-parts (ternary t = 4, k = 9728 with
+        one token register; t = 16, k = 2560 with four);
+      - four-wavefront workgroups (int4 t = 4, binary t = 5).
+    acc equals per-matrix lowbit_linear and the oracle bit for bit, the
+    streaming kernel's y equals the integer-output kernel's, and y is within
+    tolerance of per-matrix calls and the oracle (group partials may be
+    combined in another order)."""
     import torch
     lb = pytest.importorskip("bit_weight_linear_bitlinear_amd")
-    n, count, fmt, scale, group = 405, 48, "ternary", "group", 128
-    say(f"[case] grouped large stage t={t} k={k} n={n} count={count}")
+    n, count, scale, group = 405, 48, "group", 128
+    say(f"[case] grouped large stage fmt={fmt} t={t} k={k} n={n} count={count}")
     mats = []
     for i in range(3):
         w, x = workloads.random_case(900 + i, n, k, t)
-        d, p, s_, _, _ = pack_upload(w, fmt, scale, group)
+        d, p, s_, _, _ = pack_upload(w, fmt, scale, group, fmt == "int4")
         q, sx, _ = act_quant_dev(to_dev(x))
         mats.append((w, x, d, p, s_, q, sx))
     pick = [mats[i % 3] for i in range(count)]
@@ -269,7 +278,7 @@ def test_grouped_gemv_large_stages(t, k):
     for i in range(3):
         w, x, d, p, s_, q, sx = mats[i]
         y1, a1 = linear_dev("gemv", d, p, s_, q, sx)
-        p_ref, s_ref, _, _ = oracle.quantize_and_pack(w, fmt, scale, group, False)
+        p_ref, s_ref, _, _ = oracle.quantize_and_pack(w, fmt, scale, group, fmt == "int4")
         q_ref, sx_ref, _ = oracle.act_quant(x)
         y32, y64, acc_ref = oracle.linear(p_ref, s_ref, fmt, scale, group, n, k, q_ref, sx_ref)
         assert (a1.cpu().numpy() == acc_ref).all()
