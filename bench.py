@@ -1152,6 +1152,26 @@ def extra_views(args):
         "GBps_per_grouped_launch": round(bpl / dur / 1e9, 1), "TOPS_per_grouped_launch": round(opl / dur / 1e12, 2)}
     log(f"[bench] binary gqa gemm: {ops / st / 1e12:.1f} TOPS/step, {p2.step_bytes / st / 1e9:.1f} GB/s/step")
     del p2
+
+    # group-scale prefill: the 4B-class ternary layer (group-128 scales) at
+    # 4096 tokens on the batched path, which runs group scales on the
+    # 128 x 128 tile only
+    wl3 = workloads.BY_NAME["ternary_4b"]
+    p3 = Pass(wl3, 4096, "gemm", layers=1)
+    sched, (dur, bpl, opl) = gemm_pass(p3, 3)
+    st = sched["grouped"]
+    ops = sum(p3.linear_ops)
+    views["group_prefill"] = {
+        "what": "the 4B-class ternary layer-equivalent (7 group-128 products: 4 x [2560, 2560], [9728, 2560] x 2, "
+                "[2560, 9728]) at 4096 tokens on the batched path (group scales run the 128 x 128 tile), "
+                "act-quant included, equal-k products as grouped launches",
+        "ms_per_step": round(st * 1e3, 4), "TOPS_step": round(ops / st / 1e12, 2),
+        "grouped_launches": p3.launches(p3.grouped_calls),
+        "TOPS_per_grouped_launch": round(opl / dur / 1e12, 2),
+        "pct_mfma_peak_per_grouped_launch": round(100 * opl / dur / 1e12 / I8_PEAK_TOPS, 2)}
+    log(f"[bench] group prefill: {views['group_prefill']}")
+    del p3
+    del p2
     return views
 
 

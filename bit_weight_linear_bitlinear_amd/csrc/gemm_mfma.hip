@@ -253,11 +253,16 @@ __global__ __launch_bounds__(TILE == 1 ? 512 : 256) void gemm_mfma_kernel(const 
             for (int i = 0; i < WMB; ++i) {
                 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int32_t v = C[i][jb][r] >> SHIFT;
-                    yp[i][jb][r] = yp[i][jb][r] + sg * (float)v;
+                    // C holds 2^SHIFT times the group's partial: converted
+                    // directly it is exactly 2^SHIFT times fp32(partial), and
+                    // scaling by a power of two commutes with fp32 rounding,
+                    // so yp is kept 2^SHIFT times larger bit for bit (one
+                    // shift fewer per register and group; the epilogue scales
+                    // back)
+                    yp[i][jb][r] = yp[i][jb][r] + sg * (float)C[i][jb][r];
                     if constexpr (ACC) {
                         const int t = m0 + wm * (32 * WMB) + i * 32 + 8 * (r / 4) + 4 * h + (r % 4);
-                        if (m_acc && t < T && n < m_N) m_acc[((size_t)t * m_N + n) * a.G + gi] = v;
+                        if (m_acc && t < T && n < m_N) m_acc[((size_t)t * m_N + n) * a.G + gi] = C[i][jb][r] >> SHIFT;
                     }
                 }
                 C[i][jb] = i32x16{};
@@ -432,7 +437,9 @@ __global__ __launch_bounds__(TILE == 1 ? 512 : 256) void gemm_mfma_kernel(const 
                 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int t = m0 + wm * (32 * WMB) + i * 32 + 8 * (r / 4) + 4 * h + (r % 4);
-                    if (t < T && n < m_N) __builtin_nontemporal_store(sxv[i][r] * yp[i][jb][r], &m_y[(size_t)t * m_N + n]);
+                    if (t < T && n < m_N)
+                        __builtin_nontemporal_store(sxv[i][r] * (yp[i][jb][r] * (1.0f / (float)(1 << SHIFT))),
+                                                    &m_y[(size_t)t * m_N + n]);
                 }
         }
     } else {
