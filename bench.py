@@ -1171,7 +1171,6 @@ def extra_views(args):
         "pct_mfma_peak_per_grouped_launch": round(100 * opl / dur / 1e12 / I8_PEAK_TOPS, 2)}
     log(f"[bench] group prefill: {views['group_prefill']}")
     del p3
-    del p2
     return views
 
 

@@ -132,8 +132,15 @@ __device__ __forceinline__ i32x16 mfma32(const i32x4& a, const i32x4& b, const i
     return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
 }
 
+// The 128 x 128 tile is asked for two wavefronts per SIMD (two workgroups
+// per CU): with group scales the compiler otherwise took 194 VGPRs and 128
+// accumulation registers for the partials and one workgroup per CU; at 256
+// registers per lane the group-128 products of the 4B-class layer at 4096
+// tokens ran 1.7x faster (573 -> 989 TOPS).  (Binary operands at four words
+// per lane still take one.)
 template <int FMT, int WPL, int TILE, bool GROUP, bool ACC>
-__global__ __launch_bounds__(TILE == 1 ? 512 : 256) void gemm_mfma_kernel(const GemmFastArgs a) {
+__global__ __launch_bounds__(TILE == 1 ? 512 : 256) __attribute__((amdgpu_waves_per_eu(TILE == 0 ? 2 : 1)))
+void gemm_mfma_kernel(const GemmFastArgs a) {
     using S = GemmShape<FMT, WPL, TILE>;
     constexpr int SK = S::SK, CK = S::CK, KC = S::KC, NS = S::NS, STAGE = S::STAGE, A_BYTES = S::A_BYTES;
     constexpr int BM = S::BM, BN = S::BN, NW = S::NW, CPR = S::CPR, RPP = S::RPP;
