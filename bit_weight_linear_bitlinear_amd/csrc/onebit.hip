@@ -25,13 +25,15 @@
 // halves of the same codes.  Codes past k stage as 0, so the padding signs
 // (+1) add nothing.
 //
-// Work split.  A 256-thread workgroup owns 16 tokens and 64 R rows: each
+// Work split.  A 256-thread workgroup owns 16 TT tokens and 64 R rows: each
 // wavefront streams R 16-row tiles over all of k (R = 1 at decode; R = 4 at
 // prefill, so that one staged operand serves 256 rows), reusing each
-// activation operand for its R tiles.  At decode with fewer than 1024 tiles
-// a workgroup instead owns one tile and its wavefronts split k four ways.
-// x * g of the tile's real tokens is staged up to 32 KB at a time (a decode
-// row of up to 16384 codes in one pass).
+// activation operand for its R tiles and each decoded sign operand for its
+// TT token tiles (TT = 2 or 4 at prefill).  At decode with fewer than 1024
+// tiles a workgroup instead owns one tile and its wavefronts split k four
+// ways.  x * g of the tile's real tokens is staged up to 32 KB at a time (a
+// decode row of up to 16384 codes in one pass; 64 KB at prefill), written as
+// whole 16-byte groups of the permuted chunk.
 #include <algorithm>
 
 #include "device_common.hpp"
@@ -42,9 +44,11 @@ namespace lowbit {
 namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kObLds = 32768;                     // bytes of staged x * g per workgroup
+constexpr int kObBatch = 4;                       // staged 16-byte groups per thread whose loads fly together
 
 struct OneBitArgs {
     const uint8_t* packed;
@@ -57,10 +61,6 @@ struct OneBitArgs {
     int chunk;                                     // codes staged at a time: a multiple of 512
     int vec;                                       // x and g 16-byte aligned and k % 8 == 0
 };
-
-__device__ __forceinline__ int perm32(int c) {    // staged position of code c of a 32-code chunk
-    return c < 16 ? 8 * (c >> 2) + 2 * (c & 3) : 8 * ((c - 16) >> 2) + 2 * (c & 3) + 1;
-}
 
 // R 16-row tiles per wavefront, four wavefronts: 64 R rows x 16 tokens; or
 // (KS) one 16-row tile per workgroup whose four wavefronts take every fourth
@@ -90,34 +90,75 @@ __global__ __launch_bounds__(256) void onebit_kernel(const OneBitArgs a) {
     const int kpad = a.n_steps * SK;
     for (int c0 = 0; c0 < kpad; c0 += CH) {
         const int cl = min(CH, kpad - c0);                    // a multiple of SK
-        // stage fp16(x * g) of the real tokens, eight codes per thread and
-        // pass; token rows past t are never staged (their outputs, which
-        // depend only on their own row of the operand, are not stored)
-        const int per_row = cl / 8;
-        for (int e = tid; e < tv * per_row; e += 256) {
-            const int ti = e / per_row, kk = (e - ti * per_row) * 8, kg = c0 + kk;
-            _Float16 v[8];
-            if (x_vec && kg + 8 <= K) {
-                const u32x4 xv = *reinterpret_cast<const u32x4*>(a.x + (size_t)(t0 + ti) * K + kg);
-                const u32x4 gv = *reinterpret_cast<const u32x4*>(a.g + kg);
-                #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const uint16_t xb = (uint16_t)(xv[j / 2] >> (16 * (j & 1)));
-                    const uint16_t gb = (uint16_t)(gv[j / 2] >> (16 * (j & 1)));
-                    v[j] = (_Float16)((float)__builtin_bit_cast(_Float16, xb) * (float)__builtin_bit_cast(_Float16, gb));
-                }
-            } else {
-                #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    v[j] = (_Float16)0.0f;                    // codes past k: their +1 signs add nothing
-                    if (kg + j < K)
-                        v[j] = (_Float16)((float)__builtin_bit_cast(_Float16, a.x[(size_t)(t0 + ti) * K + kg + j]) *
-                                          (float)__builtin_bit_cast(_Float16, a.g[kg + j]));
+        // stage fp16(x * g) of the real tokens; token rows past t are never
+        // staged (their outputs, which depend only on their own row of the
+        // operand, are not stored).  One unit is a 16-byte group of the
+        // permuted chunk: positions 8 m .. 8 m + 7 of chunk c hold codes
+        // 32 c + 4 m + j and 32 c + 16 + 4 m + j (j = 0 .. 3) interleaved, so a
+        // thread reads two 8-byte runs of x and of g, multiplies them as fp16
+        // pairs (the product of two fp16 values rounded once, as fp16(x * g)
+        // computed in fp32 would be: that product is exact in fp32) and writes
+        // one 16-byte word.  Each thread issues the loads of kObBatch units
+        // before using any.
+        const int n_pos = cl / 8;                             // groups per token row of this pass
+        const int units = tv * n_pos;
+        for (int e0 = 0; e0 < units; e0 += 256 * kObBatch) {
+            u32x2 xl[kObBatch], xh[kObBatch], gl[kObBatch], gh[kObBatch];
+            int ti[kObBatch], kc[kObBatch];
+            bool fast[kObBatch];
+            #pragma unroll
+            for (int u = 0; u < kObBatch; ++u) {
+                const int e = e0 + 256 * u + tid;
+                ti[u] = e / n_pos;
+                const int pos = e - ti[u] * n_pos;
+                kc[u] = c0 + 32 * (pos >> 2) + 4 * (pos & 3);   // code of the group's first half
+                fast[u] = e < units && x_vec && kc[u] + 20 <= K;
+                if (fast[u]) {
+                    const uint16_t* xr = a.x + (size_t)(t0 + ti[u]) * K;
+                    xl[u] = *reinterpret_cast<const u32x2*>(xr + kc[u]);
+                    xh[u] = *reinterpret_cast<const u32x2*>(xr + kc[u] + 16);
+                    gl[u] = *reinterpret_cast<const u32x2*>(a.g + kc[u]);
+                    gh[u] = *reinterpret_cast<const u32x2*>(a.g + kc[u] + 16);
                 }
             }
-            _Float16* dst = xs + ti * CH + (kk & ~31);
             #pragma unroll
-            for (int j = 0; j < 8; ++j) dst[perm32((kk & 31) + j)] = v[j];   // x * g exact in fp32, one rounding
+            for (int u = 0; u < kObBatch; ++u) {
+                const int e = e0 + 256 * u + tid;
+                if (e >= units) continue;
+                u32x4 o;
+                if (fast[u]) {
+                    // products of codes (kc, kc+1), (kc+2, kc+3), (kc+16, kc+17), (kc+18, kc+19)
+                    uint32_t pr[4];
+                    // (vector elements are copied out first: a bit_cast of an
+                    // element expression compiled to the element 0 here)
+                    #pragma unroll
+                    for (int w2 = 0; w2 < 2; ++w2) {
+                        const uint32_t xa = xl[u][w2], ga = gl[u][w2], xb = xh[u][w2], gb = gh[u][w2];
+                        pr[w2] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2, xa) * __builtin_bit_cast(half2, ga));
+                        pr[2 + w2] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2, xb) * __builtin_bit_cast(half2, gb));
+                    }
+                    // interleave: dword j = (code kc + j, code kc + 16 + j)
+                    o[0] = __builtin_amdgcn_perm(pr[2], pr[0], 0x05040100u);
+                    o[1] = __builtin_amdgcn_perm(pr[2], pr[0], 0x07060302u);
+                    o[2] = __builtin_amdgcn_perm(pr[3], pr[1], 0x05040100u);
+                    o[3] = __builtin_amdgcn_perm(pr[3], pr[1], 0x07060302u);
+                } else {
+                    auto prod = [](uint16_t xb, uint16_t gb) {
+                        const _Float16 v = __builtin_bit_cast(_Float16, xb) * __builtin_bit_cast(_Float16, gb);
+                        return (uint32_t)__builtin_bit_cast(uint16_t, v);
+                    };
+                    const uint16_t* xr = a.x + (size_t)(t0 + ti[u]) * K;
+                    #pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int kl = kc[u] + j, kh = kc[u] + 16 + j;   // codes past k stage as 0: their +1 signs add nothing
+                        const uint32_t lo = kl < K ? prod(xr[kl], a.g[kl]) : 0u;
+                        const uint32_t hi = kh < K ? prod(xr[kh], a.g[kh]) : 0u;
+                        o[j] = lo | (hi << 16);
+                    }
+                }
+                const int pos = e - ti[u] * n_pos;
+                *reinterpret_cast<u32x4*>(xs + ti[u] * CH + 32 * (pos >> 2) + 8 * (pos & 3)) = o;
+            }
         }
         __syncthreads();
         const int s0 = c0 / SK, s1 = s0 + cl / SK;
@@ -203,8 +244,11 @@ void launch_r(const OneBitArgs& a, dim3 grid, size_t lds, hipStream_t stream) {
 hipError_t launch_onebit(const uint8_t* packed, const uint16_t* g, const uint16_t* h, const uint16_t* x, float* y,
                          int n, int k, int t, int wpl, int step_k, int n_steps, hipStream_t stream) {
     const int tiles = (n + 15) / 16;
-    const bool prefill = t > 16;                   // two 16-token tiles per workgroup
-    const int tv = std::min(t, prefill ? 32 : 16);
+    const bool prefill = t > 16;                   // two (or four) 16-token tiles per workgroup
+    // four token tiles per workgroup (each decoded sign operand feeds four
+    // MFMAs) while that still leaves two workgroups per CU
+    const bool tt4 = prefill && (int64_t)((tiles + 15) / 16) * ((t + 63) / 64) >= 2LL * device_cu_count();
+    const int tv = std::min(t, prefill ? (tt4 ? 64 : 32) : 16);
     // staged codes per pass: what the stage (32 KB, 64 KB at prefill) holds
     // for the tile's tokens, a multiple of 512 (every k-step size divides it)
     const int budget = prefill ? 2 * kObLds : kObLds;
@@ -212,12 +256,13 @@ hipError_t launch_onebit(const uint8_t* packed, const uint16_t* g, const uint16_
     const int vec = k % 8 == 0 && (uintptr_t)x % 16 == 0 && (uintptr_t)g % 16 == 0;
     OneBitArgs a{packed, g, h, x, y, n, k, t, wpl, step_k, n_steps, tiles, chunk, vec};
     const size_t lds = (size_t)2 * tv * chunk;
-    // prefill: 256 rows and 32 tokens per workgroup, so that one staged
-    // operand serves 256 rows and one decoded sign operand two token tiles;
-    // decode: 64 rows, or one tile with k split four ways when that leaves
-    // under 256 workgroups, so that small and short-wide matrices spread over
-    // the chip
-    if (prefill) launch_r<4, false, 2>(a, dim3((unsigned)((tiles + 15) / 16), (unsigned)((t + 31) / 32)), lds, stream);
+    // prefill: 256 rows and 32 or 64 tokens per workgroup, so that one staged
+    // operand serves 256 rows and one decoded sign operand two or four token
+    // tiles; decode: 64 rows, or one tile with k split four ways when that
+    // leaves under 256 workgroups, so that small and short-wide matrices
+    // spread over the chip
+    if (tt4) launch_r<4, false, 4>(a, dim3((unsigned)((tiles + 15) / 16), (unsigned)((t + 63) / 64)), lds, stream);
+    else if (prefill) launch_r<4, false, 2>(a, dim3((unsigned)((tiles + 15) / 16), (unsigned)((t + 31) / 32)), lds, stream);
     else if (tiles < 1024) launch_r<1, true, 1>(a, dim3((unsigned)tiles, (unsigned)((t + 15) / 16)), lds, stream);
     else launch_r<1, false, 1>(a, dim3((unsigned)((tiles + 3) / 4), (unsigned)((t + 15) / 16)), lds, stream);
     return hipGetLastError();
