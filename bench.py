@@ -984,6 +984,15 @@ def onebit_view():
     return out
 
 
+def onebit_profile():
+    """OneBit's projection launches only (for profiler runs): the view's
+    shapes, each call timed on its own."""
+    rows = onebit_view()["shapes"]
+    for r in rows:
+        print(json.dumps({"onebit": [r["n"], r["k"], r["t"]], "us": r["us"], "TFLOPS": r["TFLOPS"],
+                          "GBps": r["GBps"]}), flush=True)
+
+
 def h4_profile():
     """The rotated quantiser's prefill launches only (for profiler runs)."""
     lb = __import__("bit_weight_linear_bitlinear_amd")
@@ -1193,6 +1202,8 @@ def main():
                     help="the rotated 4-bit quantiser's prefill launches only (for profiler runs)")
     ap.add_argument("--profile-a48", action="store_true",
                     help="the a4.8 quantisers' prefill launches only (for profiler runs)")
+    ap.add_argument("--profile-onebit", action="store_true",
+                    help="OneBit's projection launches only (for profiler runs)")
     ap.add_argument("--profile-pass", action="store_true",
                     help="copy calibration + grouped GEMV pass only (for profiler runs)")
     args = ap.parse_args()
@@ -1210,12 +1221,16 @@ def main():
         args.quick = args.skip_gemm = args.skip_cpu = args.skip_check = args.skip_views = True
     calib = copy_calibration()
     log(f"[bench] copy calibration: {calib}")
-    ceilings = None if args.profile_pass or args.profile_gemm or args.profile_h4 or args.profile_a48 else calibration()
+    ceilings = (None if args.profile_pass or args.profile_gemm or args.profile_h4 or args.profile_a48 or
+                args.profile_onebit else calibration())
     if ceilings:
         log(f"[bench] device ceilings: {ceilings}")
 
     if args.profile_gemm:
         gemm_profile(args)
+        return
+    if args.profile_onebit:
+        onebit_profile()
         return
     if args.profile_h4:
         h4_profile()
