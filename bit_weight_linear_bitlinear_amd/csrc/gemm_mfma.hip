@@ -104,6 +104,8 @@ template <int FMT, int WPL, int TILE> struct GemmShape {
     static constexpr int A_PIECES = A_BYTES / 1024;          // 1 KB direct loads per step
     static constexpr int B_PIECES = B_BYTES / 1024;
     static constexpr bool FITS = NS * STAGE <= 163840;
+    // room beside the stages for the tile's s_x and weight scales
+    static constexpr bool XS_FITS = NS * STAGE + 4 * (BM + BN) <= 163840;
     static constexpr int CPR = SK / 16;                      // 16-byte chunks per activation row
     static constexpr int RPP = 64 / CPR;                     // activation rows per 1 KB piece
     // swizzle: chunk c of row r sits at chunk c ^ swz(r); 16 consecutive rows
@@ -123,6 +125,11 @@ __device__ __forceinline__ void wait_vm() {
 // one 1 KB direct-to-LDS copy: lane l's 16 bytes land at lds + 16 * l
 __device__ __forceinline__ void dma16(const void* src, void* lds) {
     __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
+}
+
+// one 256-byte direct-to-LDS copy: lane l's 4 bytes land at lds + 4 * l
+__device__ __forceinline__ void dma4(const void* src, void* lds) {
+    __builtin_amdgcn_global_load_lds(src, lds, 4, 0, 0);
 }
 
 // cache-policy operand of a buffer store: the non-temporal bit
@@ -151,7 +158,12 @@ void gemm_mfma_kernel(const GemmFastArgs a) {
     constexpr int LA = S::A_PIECES / NW;
     constexpr int LB = (S::B_PIECES + NW - 1) / NW;          // past the last piece: a copy of it again
     constexpr int L = LA + LB;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
+    // the stages, then (row and tensor scales, where they fit) the tile's s_x
+    // and weight scales, copied in the prologue so that the epilogue reads
+    // them from LDS rather than wait for a global round trip
+    constexpr bool XSL = !GROUP && S::XS_FITS;
+    constexpr int XS_BYTES = XSL ? 4 * (BM + BN) : 0;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE + XS_BYTES];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -276,6 +288,24 @@ void gemm_mfma_kernel(const GemmFastArgs a) {
             }
         }
     };
+
+    // s_x of the tile's tokens and the scales of its rows (clamped indices;
+    // unused past t and n), as 256-byte pieces spread over the wavefronts.
+    // They precede step 0's copies, so step 0's wait and barrier cover them.
+    float* const xs_x = reinterpret_cast<float*>(smem + NS * STAGE);
+    float* const xs_w = xs_x + BM;
+    if constexpr (XSL) {
+        constexpr int PX = BM / 64, PW = BN / 64;
+        static_assert(BM % 64 == 0 && BN % 64 == 0, "scale pieces");
+        for (int p = wave; p < PX + PW; p += NW) {           // uniform
+            if (p < PX) {
+                dma4(m_sx + min(m0 + 64 * p + lane, T - 1), xs_x + 64 * p);
+            } else {
+                const int n = min(n0 + 64 * (p - PX) + lane, m_N - 1);
+                dma4(m_scales + (a.scale_per_row ? n : 0), xs_w + 64 * (p - PX));
+            }
+        }
+    }
 
     const int n_steps = a.n_steps;
     #pragma unroll
@@ -428,12 +458,21 @@ void gemm_mfma_kernel(const GemmFastArgs a) {
     #pragma unroll
     for (int i = 0; i < WMB; ++i)
         #pragma unroll
-        for (int r = 0; r < 16; ++r)
-            sxv[i][r] = m_sx[min(m0 + wm * (32 * WMB) + i * 32 + 8 * (r / 4) + 4 * h + (r % 4), T - 1)];
+        for (int r = 0; r < 16; ++r) {
+            const int tl = wm * (32 * WMB) + i * 32 + 8 * (r / 4) + 4 * h + (r % 4);
+            if constexpr (XSL) sxv[i][r] = xs_x[tl];
+            else sxv[i][r] = m_sx[min(m0 + tl, T - 1)];
+        }
     #pragma unroll
     for (int jb = 0; jb < WNB; ++jb) {
-        const int nc = min(n0 + wn * (32 * WNB) + jb * 32 + j, m_N - 1);
-        swv[jb] = GROUP ? 0.0f : m_scales[a.scale_per_row ? nc : 0];
+        if constexpr (GROUP) {
+            swv[jb] = 0.0f;
+        } else if constexpr (XSL) {
+            swv[jb] = xs_w[wn * (32 * WNB) + jb * 32 + j];
+        } else {
+            const int nc = min(n0 + wn * (32 * WNB) + jb * 32 + j, m_N - 1);
+            swv[jb] = m_scales[a.scale_per_row ? nc : 0];
+        }
     }
     if constexpr (GROUP) {
         #pragma unroll
