@@ -119,7 +119,9 @@ constexpr int gemv_min_waves(int fmt, int nr, int sps, bool upg1, int wv, bool a
 // per-token absmax quantiser itself (M8.8 0x02C, 0x05C: m = max|x|,
 // r = 127 / m, codes clip(rint(x r)), s_x = m / 127), every workgroup for its
 // own stage; the matrix's first workgroup also writes the codes and scale out.
-template <int FMT, int WPL, int NR, int SPS, bool UPG1, bool LDSA, bool ACC, bool FUSE, int WV, int PRE>
+// FRW (with FUSE): words of x per thread per load round of the prologue
+// quantiser.
+template <int FMT, int WPL, int NR, int SPS, bool UPG1, bool LDSA, bool ACC, bool FUSE, int WV, int PRE, int FRW = 3>
 __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(gemv_min_waves(FMT, NR, SPS, UPG1, WV, ACC)))) void gemv_kernel(const GemvParams p) {
     using S = GemvShape<FMT, WPL>;
     constexpr int D = kGemvD;
@@ -231,7 +233,7 @@ __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(gemv_mi
     // fused: the first round of x is issued ahead of the weight
     // ring, so the quantiser's reduction waits for x alone (the loads are
     // counted in order) and runs while the ring's HBM loads are in flight
-    constexpr int FR = 3;                                    // words (4 k) per thread per round
+    constexpr int FR = FRW;                                  // words (4 k) per thread per round
     const int nword = (K + 3) >> 2;                          // words holding real k
     const int tid = threadIdx.x;
     float4 xv[FR];
@@ -689,6 +691,13 @@ void gemv_launch_lds(const GemvParams& p, const GemvCfg& c, hipStream_t st) {
                     gemv_kernel<FMT, WPL, 1, SPS, UPG1, true, false, true, 4, PRE_NORM><<<grid, block, c.lds_bytes, st>>>(p);
                 else if (c.pre == PRE_SWIGLU)
                     gemv_kernel<FMT, WPL, 1, SPS, UPG1, true, false, true, 4, PRE_SWIGLU><<<grid, block, c.lds_bytes, st>>>(p);
+                else if (p.K > 256 * 3 * 4 && p.K <= 256 * 10 * 4)
+                    // a row of 3073 .. 10240 elements in one load round (86
+                    // VGPRs; these one-token launches are latency-bound, not
+                    // occupancy-bound): the max and the codes then wait for one
+                    // memory round trip, not one per 3072 elements in each of
+                    // the two passes (k = 9728: prologue 6.0 -> 4.8 us)
+                    gemv_kernel<FMT, WPL, 1, SPS, UPG1, true, false, true, 4, PRE_NONE, 10><<<grid, block, c.lds_bytes, st>>>(p);
                 else
                     gemv_kernel<FMT, WPL, 1, SPS, UPG1, true, false, true, 4, PRE_NONE><<<grid, block, c.lds_bytes, st>>>(p);
                 return;

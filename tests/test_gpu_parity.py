@@ -395,7 +395,9 @@ def test_fused_quantiser_edges(fmt):
     quantiser runs in the product kernel's prologue): rows that are ordinary,
     with NaN, with Inf, all zero, and whose 127 / max overflows, at k from one
     word round to several (64, 1000 - ending inside a k-step -, 3072 = exactly
-    one round, 4100, 9728), and rows the prologue does not take (k % 4 != 0, an
+    one round of three words per thread; 4100, 9728, 10240 in the one round of
+    ten words per thread that rows of 3073 to 10240 elements take; 12288 in
+    five rounds of three), and rows the prologue does not take (k % 4 != 0, an
     x not 16-byte aligned).  Several tokens (the quantiser kernel runs first):
     the same edge rows, 17 tokens (two launches), t * k too large for the LDS
     stage.  Then the grouped call."""
@@ -430,7 +432,8 @@ def test_fused_quantiser_edges(fmt):
 
     # one token
     for (n, k, misalign) in [(40, 64, False), (48, 1000, False), (24, 3072, False), (33, 4100, False),
-                             (20, 9728, False), (40, 1003, False), (20, 512, True)]:
+                             (20, 9728, False), (24, 10240, False), (16, 12288, False), (40, 1003, False),
+                             (20, 512, True)]:
         say(f"[case] fused quantiser t=1 fmt={fmt} n={n} k={k} misaligned_x={misalign}")
         w, x5 = workloads.random_case(900 + k, n, k, 5)
         x5[0, ::97] *= 40.0                   # outliers in the ordinary row
