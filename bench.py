@@ -756,6 +756,26 @@ def build_decode_model(lb):
     return lb.DecodeModel(d, L, H, ff, V, C, descs, embed, norms, packed, scales), cfg
 
 
+def layers_profile(args):
+    """The dependency-respecting decode schedules alone, for profiler runs:
+    the 4B-class ternary pass at one token layer by layer through the fused
+    entry (layer_fused) and as act-quant + product per call (layer_dep),
+    graph replays, then the 256-d decoder's greedy steps (decode_model_view)."""
+    import workloads
+    wl = workloads.BY_NAME["ternary_4b"]
+    p = Pass(wl, 1, "gemv", layers=args.layers)
+    p.build_schedules()
+    for sched, calls in (("layer_fused", p.layer_fused_calls), ("layer_dep", p.layer_calls)):
+        fn = (lambda sc=sched: p.step(sc))
+        run = capture(fn) or fn
+        el, _ = time_steps(run, args.steps, args.warmup)
+        st = el / args.steps
+        log(f"[bench] gemv {sched}: {p.step_bytes / st / 1e9:.1f} GB/s, {st * 1e3:.3f} ms/step, "
+            f"{p.launches(calls)} launches")
+    dm = decode_model_view()
+    log(f"[bench] decode model: {dm.get('graph')} (graph), {dm.get('eager')} (eager)")
+
+
 def decode_model_view():
     """Greedy generation with the 256-d ternary decoder at batch 1: one step
     captured in a HIP graph and replayed across the whole 128-token context
@@ -1204,6 +1224,8 @@ def main():
                     help="the a4.8 quantisers' prefill launches only (for profiler runs)")
     ap.add_argument("--profile-onebit", action="store_true",
                     help="OneBit's projection launches only (for profiler runs)")
+    ap.add_argument("--profile-layers", action="store_true",
+                    help="the layer-by-layer decode schedules and the 256-d decoder only (for profiler runs)")
     ap.add_argument("--profile-pass", action="store_true",
                     help="copy calibration + grouped GEMV pass only (for profiler runs)")
     args = ap.parse_args()
@@ -1222,7 +1244,7 @@ def main():
     calib = copy_calibration()
     log(f"[bench] copy calibration: {calib}")
     ceilings = (None if args.profile_pass or args.profile_gemm or args.profile_h4 or args.profile_a48 or
-                args.profile_onebit else calibration())
+                args.profile_onebit or args.profile_layers else calibration())
     if ceilings:
         log(f"[bench] device ceilings: {ceilings}")
 
@@ -1237,6 +1259,9 @@ def main():
         return
     if args.profile_a48:
         a48_profile()
+        return
+    if args.profile_layers:
+        layers_profile(args)
         return
 
     # ---- GEMV line: ternary_4b decode pass
