@@ -343,7 +343,7 @@ class GroupedCall:
 
 
 def lowbit_linear_batched_grouped(descs, packed, scales, q, sx, y, acc=None, stream=None) -> None:
-    """Device: several independent prefill GEMMs of equal k and t, 64 per launch."""
+    """Device: several independent prefill GEMMs of equal k and t, at most 64 per launch."""
     GroupedCall(descs, packed, scales, q, sx, y, acc, batched=True)(stream)
 
 
