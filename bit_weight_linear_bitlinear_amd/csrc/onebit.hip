@@ -48,6 +48,13 @@ typedef _Float16 half2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kObLds = 32768;                     // bytes of staged x * g per workgroup
+// Halves of padding after each staged token row.  The operand reads take 16
+// token rows at one column (lane quarters 64 bytes apart); with rows of a
+// whole number of kilobytes they met on the same banks.  Counters at 4096
+// tokens: bank-conflict cycles 0.82 of the LDS's active cycles unpadded, 0.40
+// with a pad of 8, 16 or 24 halves (16 the fastest: 4096^3 in 203 against
+// ~230 us unpadded).
+constexpr int kObPad = 16;
 constexpr int kObBatch = 4;                       // staged 16-byte groups per thread whose loads fly together
 
 struct OneBitArgs {
@@ -68,12 +75,13 @@ struct OneBitArgs {
 template <int WPL, int R, bool KS, int TT>
 __global__ __launch_bounds__(256) void onebit_kernel(const OneBitArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    _Float16* xs = reinterpret_cast<_Float16*>(smem);      // [tokens of this tile][chunk]
+    _Float16* xs = reinterpret_cast<_Float16*>(smem);      // [tokens of this tile][chunk + kObPad]
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int q = lane >> 4, r = lane & 15;
     const int t0 = blockIdx.y * 16 * TT, tv = min(16 * TT, a.t - t0);   // tokens of this tile
     const int K = a.k, SK = a.step_k, CH = a.chunk;
+    const int RS = CH + kObPad;                               // staged row stride (halves)
     const int tile0 = KS ? (int)blockIdx.x : (blockIdx.x * 4 + wave) * R;   // this wavefront's first row tile
     const uint8_t* pk[R];
     #pragma unroll
@@ -157,7 +165,7 @@ __global__ __launch_bounds__(256) void onebit_kernel(const OneBitArgs a) {
                     }
                 }
                 const int pos = e - ti[u] * n_pos;
-                *reinterpret_cast<u32x4*>(xs + ti[u] * CH + 32 * (pos >> 2) + 8 * (pos & 3)) = o;
+                *reinterpret_cast<u32x4*>(xs + ti[u] * RS + 32 * (pos >> 2) + 8 * (pos & 3)) = o;
             }
         }
         __syncthreads();
@@ -187,7 +195,7 @@ __global__ __launch_bounds__(256) void onebit_kernel(const OneBitArgs a) {
                     half8 av[TT];
                     #pragma unroll
                     for (int u = 0; u < TT; ++u)
-                        av[u] = *reinterpret_cast<const half8*>(xs + min(16 * u + r, tv - 1) * CH + kof + 8 * m);
+                        av[u] = *reinterpret_cast<const half8*>(xs + min(16 * u + r, tv - 1) * RS + kof + 8 * m);
                     #pragma unroll
                     for (int i = 0; i < R; ++i) {
                         u32x4 b;                                  // decoded once, used by the TT token tiles
@@ -255,7 +263,7 @@ hipError_t launch_onebit(const uint8_t* packed, const uint16_t* g, const uint16_
     const int chunk = std::max(512, (budget / (2 * tv)) / 512 * 512);
     const int vec = k % 8 == 0 && (uintptr_t)x % 16 == 0 && (uintptr_t)g % 16 == 0;
     OneBitArgs a{packed, g, h, x, y, n, k, t, wpl, step_k, n_steps, tiles, chunk, vec};
-    const size_t lds = (size_t)2 * tv * chunk;
+    const size_t lds = (size_t)2 * tv * (chunk + kObPad);
     // prefill: 256 rows and 32 or 64 tokens per workgroup, so that one staged
     // operand serves 256 rows and one decoded sign operand two or four token
     // tiles; decode: 64 rows, or one tile with k split four ways when that
