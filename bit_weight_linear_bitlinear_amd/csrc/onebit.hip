@@ -27,7 +27,10 @@
 //
 // Work split.  A 256-thread workgroup owns 16 TT tokens and 64 R rows: each
 // wavefront streams R 16-row tiles over all of k (R = 1 at decode; R = 4 at
-// prefill, so that one staged operand serves 256 rows), reusing each
+// prefill, so that one staged operand serves 256 rows, or 8 and 512 rows
+// where the grid still holds two workgroups per CU: 8 x 4 accumulator tiles
+// need two wavefronts per SIMD asked for, at a few spilled registers, and two
+// staged groups in flight per thread instead of four), reusing each
 // activation operand for its R tiles and each decoded sign operand for its
 // TT token tiles (TT = 2 or 4 at prefill).  At decode with fewer than 1024
 // tiles a workgroup instead owns one tile and its wavefronts split k four
@@ -73,7 +76,7 @@ struct OneBitArgs {
 // (KS) one 16-row tile per workgroup whose four wavefronts take every fourth
 // k-step, their fp32 partials summed in LDS
 template <int WPL, int R, bool KS, int TT>
-__global__ __launch_bounds__(256) void onebit_kernel(const OneBitArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(R == 8 ? 2 : 1))) void onebit_kernel(const OneBitArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     _Float16* xs = reinterpret_cast<_Float16*>(smem);      // [tokens of this tile][chunk + kObPad]
     const int tid = threadIdx.x, lane = tid & 63;
@@ -82,6 +85,7 @@ __global__ __launch_bounds__(256) void onebit_kernel(const OneBitArgs a) {
     const int t0 = blockIdx.y * 16 * TT, tv = min(16 * TT, a.t - t0);   // tokens of this tile
     const int K = a.k, SK = a.step_k, CH = a.chunk;
     const int RS = CH + kObPad;                               // staged row stride (halves)
+    constexpr int NB = R == 8 ? 2 : kObBatch;                  // (eight row tiles: fewer registers in flight)
     const int tile0 = KS ? (int)blockIdx.x : (blockIdx.x * 4 + wave) * R;   // this wavefront's first row tile
     const uint8_t* pk[R];
     #pragma unroll
@@ -110,12 +114,12 @@ __global__ __launch_bounds__(256) void onebit_kernel(const OneBitArgs a) {
         // before using any.
         const int n_pos = cl / 8;                             // groups per token row of this pass
         const int units = tv * n_pos;
-        for (int e0 = 0; e0 < units; e0 += 256 * kObBatch) {
-            u32x2 xl[kObBatch], xh[kObBatch], gl[kObBatch], gh[kObBatch];
-            int ti[kObBatch], kc[kObBatch];
-            bool fast[kObBatch];
+        for (int e0 = 0; e0 < units; e0 += 256 * NB) {
+            u32x2 xl[NB], xh[NB], gl[NB], gh[NB];
+            int ti[NB], kc[NB];
+            bool fast[NB];
             #pragma unroll
-            for (int u = 0; u < kObBatch; ++u) {
+            for (int u = 0; u < NB; ++u) {
                 const int e = e0 + 256 * u + tid;
                 ti[u] = e / n_pos;
                 const int pos = e - ti[u] * n_pos;
@@ -130,7 +134,7 @@ __global__ __launch_bounds__(256) void onebit_kernel(const OneBitArgs a) {
                 }
             }
             #pragma unroll
-            for (int u = 0; u < kObBatch; ++u) {
+            for (int u = 0; u < NB; ++u) {
                 const int e = e0 + 256 * u + tid;
                 if (e >= units) continue;
                 u32x4 o;
@@ -269,7 +273,11 @@ hipError_t launch_onebit(const uint8_t* packed, const uint16_t* g, const uint16_
     // tiles; decode: 64 rows, or one tile with k split four ways when that
     // leaves under 256 workgroups, so that small and short-wide matrices
     // spread over the chip
-    if (tt4) launch_r<4, false, 4>(a, dim3((unsigned)((tiles + 15) / 16), (unsigned)((t + 63) / 64)), lds, stream);
+    // eight row tiles per wavefront (512 rows per staged operand: half the
+    // staging per row) while that still leaves two workgroups per CU
+    const bool r8 = tt4 && (int64_t)((tiles + 31) / 32) * ((t + 63) / 64) >= 2LL * device_cu_count();
+    if (r8) launch_r<8, false, 4>(a, dim3((unsigned)((tiles + 31) / 32), (unsigned)((t + 63) / 64)), lds, stream);
+    else if (tt4) launch_r<4, false, 4>(a, dim3((unsigned)((tiles + 15) / 16), (unsigned)((t + 63) / 64)), lds, stream);
     else if (prefill) launch_r<4, false, 2>(a, dim3((unsigned)((tiles + 15) / 16), (unsigned)((t + 31) / 32)), lds, stream);
     else if (tiles < 1024) launch_r<1, true, 1>(a, dim3((unsigned)tiles, (unsigned)((t + 15) / 16)), lds, stream);
     else launch_r<1, false, 1>(a, dim3((unsigned)((tiles + 3) / 4), (unsigned)((t + 15) / 16)), lds, stream);

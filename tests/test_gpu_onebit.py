@@ -43,7 +43,9 @@ def _bound(x, gv, hv, y64, k):
 @pytest.mark.parametrize("n,k,t", [(2560, 2560, 1), (768, 192, 4), (1000, 1000, 17), (96, 8192, 3), (64, 20000, 2),
                                    (1000, 1001, 5), (4096, 1024, 300), (16400, 256, 2),
                                    (4096, 4096, 16), (300, 2048, 33), (17, 128, 1),
-                                   (4096, 1024, 2085)])   # prefill with four token tiles per workgroup, t % 64 != 0
+                                   (4096, 1024, 2085),    # prefill with four token tiles per workgroup, t % 64 != 0
+                                   (4100, 512, 4097),     # eight row tiles per wavefront (a grid of at least two
+                                   (4096, 768, 4160)])    # workgroups per CU), ragged n and t; two words per lane
 def test_projection_matches_oracle(n, k, t):
     say(f"[case] onebit projection n={n} k={k} t={t}")
     d, w, x, gv, hv, packed, y = _layer(n, k, t, n + 3 * k + t)
