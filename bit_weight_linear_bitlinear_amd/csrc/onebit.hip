@@ -25,12 +25,14 @@
 // halves of the same codes.  Codes past k stage as 0, so the padding signs
 // (+1) add nothing.
 //
-// Work split.  A 256-thread workgroup owns 16 TT tokens and 64 R rows: each
+// Work split.  A workgroup of four (or eight) wavefronts owns 16 TT tokens
+// and 64 R (128 R) rows: each
 // wavefront streams R 16-row tiles over all of k (R = 1 at decode; R = 4 at
-// prefill, so that one staged operand serves 256 rows, or 8 and 512 rows
-// where the grid still holds two workgroups per CU: 8 x 4 accumulator tiles
-// need two wavefronts per SIMD asked for, at a few spilled registers, and two
-// staged groups in flight per thread instead of four), reusing each
+// prefill, so that one staged operand serves 256 rows, or 8 with eight
+// wavefronts per workgroup and 1024 rows where that still fills every CU:
+// 8 x 4 accumulator tiles need two wavefronts per SIMD asked for, at a few
+// spilled registers, and two staged groups in flight per thread instead of
+// four), reusing each
 // activation operand for its R tiles and each decoded sign operand for its
 // TT token tiles (TT = 2 or 4 at prefill).  At decode with fewer than 1024
 // tiles a workgroup instead owns one tile and its wavefronts split k four
@@ -75,8 +77,8 @@ struct OneBitArgs {
 // R 16-row tiles per wavefront, four wavefronts: 64 R rows x 16 tokens; or
 // (KS) one 16-row tile per workgroup whose four wavefronts take every fourth
 // k-step, their fp32 partials summed in LDS
-template <int WPL, int R, bool KS, int TT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(R == 8 ? 2 : 1))) void onebit_kernel(const OneBitArgs a) {
+template <int WPL, int R, bool KS, int TT, int NWV>
+__global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(R == 8 ? 2 : 1))) void onebit_kernel(const OneBitArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     _Float16* xs = reinterpret_cast<_Float16*>(smem);      // [tokens of this tile][chunk + kObPad]
     const int tid = threadIdx.x, lane = tid & 63;
@@ -86,7 +88,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(R == 8 ? 2 
     const int K = a.k, SK = a.step_k, CH = a.chunk;
     const int RS = CH + kObPad;                               // staged row stride (halves)
     constexpr int NB = R == 8 ? 2 : kObBatch;                  // (eight row tiles: fewer registers in flight)
-    const int tile0 = KS ? (int)blockIdx.x : (blockIdx.x * 4 + wave) * R;   // this wavefront's first row tile
+    constexpr int NT = 64 * NWV;                              // threads per workgroup
+    static_assert(!KS || NWV == 4, "k split over four wavefronts");
+    const int tile0 = KS ? (int)blockIdx.x : (blockIdx.x * NWV + wave) * R;   // this wavefront's first row tile
     const uint8_t* pk[R];
     #pragma unroll
     for (int i = 0; i < R; ++i)
@@ -114,13 +118,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(R == 8 ? 2 
         // before using any.
         const int n_pos = cl / 8;                             // groups per token row of this pass
         const int units = tv * n_pos;
-        for (int e0 = 0; e0 < units; e0 += 256 * NB) {
+        for (int e0 = 0; e0 < units; e0 += NT * NB) {
             u32x2 xl[NB], xh[NB], gl[NB], gh[NB];
             int ti[NB], kc[NB];
             bool fast[NB];
             #pragma unroll
             for (int u = 0; u < NB; ++u) {
-                const int e = e0 + 256 * u + tid;
+                const int e = e0 + NT * u + tid;
                 ti[u] = e / n_pos;
                 const int pos = e - ti[u] * n_pos;
                 kc[u] = c0 + 32 * (pos >> 2) + 4 * (pos & 3);   // code of the group's first half
@@ -135,7 +139,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(R == 8 ? 2 
             }
             #pragma unroll
             for (int u = 0; u < NB; ++u) {
-                const int e = e0 + 256 * u + tid;
+                const int e = e0 + NT * u + tid;
                 if (e >= units) continue;
                 u32x4 o;
                 if (fast[u]) {
@@ -242,12 +246,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(R == 8 ? 2 
     }
 }
 
-template <int R, bool KS, int TT>
+template <int R, bool KS, int TT, int NWV = 4>
 void launch_r(const OneBitArgs& a, dim3 grid, size_t lds, hipStream_t stream) {
     switch (a.wpl) {
-        case 4: onebit_kernel<4, R, KS, TT><<<grid, 256, lds, stream>>>(a); break;
-        case 2: onebit_kernel<2, R, KS, TT><<<grid, 256, lds, stream>>>(a); break;
-        default: onebit_kernel<1, R, KS, TT><<<grid, 256, lds, stream>>>(a); break;
+        case 4: onebit_kernel<4, R, KS, TT, NWV><<<grid, 64 * NWV, lds, stream>>>(a); break;
+        case 2: onebit_kernel<2, R, KS, TT, NWV><<<grid, 64 * NWV, lds, stream>>>(a); break;
+        default: onebit_kernel<1, R, KS, TT, NWV><<<grid, 64 * NWV, lds, stream>>>(a); break;
     }
 }
 
@@ -273,10 +277,11 @@ hipError_t launch_onebit(const uint8_t* packed, const uint16_t* g, const uint16_
     // tiles; decode: 64 rows, or one tile with k split four ways when that
     // leaves under 256 workgroups, so that small and short-wide matrices
     // spread over the chip
-    // eight row tiles per wavefront (512 rows per staged operand: half the
-    // staging per row) while that still leaves two workgroups per CU
-    const bool r8 = tt4 && (int64_t)((tiles + 31) / 32) * ((t + 63) / 64) >= 2LL * device_cu_count();
-    if (r8) launch_r<8, false, 4>(a, dim3((unsigned)((tiles + 31) / 32), (unsigned)((t + 63) / 64)), lds, stream);
+    // eight row tiles per wavefront and eight wavefronts per workgroup (1024
+    // rows per staged operand: a quarter of the staging per row; one
+    // workgroup per CU) while that still fills every CU
+    const bool w8 = tt4 && (int64_t)((tiles + 63) / 64) * ((t + 63) / 64) >= device_cu_count();
+    if (w8) launch_r<8, false, 4, 8>(a, dim3((unsigned)((tiles + 63) / 64), (unsigned)((t + 63) / 64)), lds, stream);
     else if (tt4) launch_r<4, false, 4>(a, dim3((unsigned)((tiles + 15) / 16), (unsigned)((t + 63) / 64)), lds, stream);
     else if (prefill) launch_r<4, false, 2>(a, dim3((unsigned)((tiles + 15) / 16), (unsigned)((t + 31) / 32)), lds, stream);
     else if (tiles < 1024) launch_r<1, true, 1>(a, dim3((unsigned)tiles, (unsigned)((t + 15) / 16)), lds, stream);
