@@ -131,6 +131,24 @@ def test_sparse8_rejected_and_degenerate_rows():
             assert got[2] == 3 and got[1][2] == 0 and not got[0][2].any()
 
 
+@pytest.mark.parametrize("k", [640, 2560, 3072])
+def test_sparse8_many_rows(k):
+    """Rows of up to 3072 elements (256 threads, 3 float4 each), more rows
+    than stay resident at once, so that workgroups start as others end:
+    every row bit for bit, real-valued rows and rows with many ties at the
+    threshold."""
+    t = 2600
+    g = np.random.default_rng(k + 1)
+    ties = (g.integers(-4, 5, (t, k)) * 0.375).astype(np.float32)
+    ties[::7, ::3] = -0.0
+    for name, x in (("real", _rows(t, k, 5 * k)), ("ties", ties)):
+        xd = to_dev(x)
+        for keep in (1, k // 2, k - 1):
+            say(f"[case] sparse8 many rows t={t} k={k} {name} keep={keep}")
+            got = _run(lib().lowbit_act_quant_sparse8, xd, keep)
+            _check(got, a48.sparse_codes(x, keep), f"sparse8 many rows k={k} {name} keep={keep}")
+
+
 @pytest.mark.parametrize("k", [2560, 9728])
 def test_sparse8_prefill_widths(k):
     """The 4096-token prefill in front of the attention output (k = 2560) and
