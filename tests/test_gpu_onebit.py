@@ -46,7 +46,8 @@ def _bound(x, gv, hv, y64, k):
                                    (4096, 1024, 2085),    # prefill with four token tiles per workgroup, t % 64 != 0
                                    (4100, 512, 4097),     # eight row tiles per wavefront (a grid of at least two
                                    (4096, 768, 4160),     # workgroups per CU), ragged n and t; two words per lane
-                                   (4104, 1288, 4100)])   # the same with three passes, the last ragged (k % 32 != 0)
+                                   (4104, 1288, 4100),    # the same with three passes, the last ragged (k % 32 != 0)
+                                   (4104, 1004, 4100)])   # k % 8 != 0: x and g staged element by element
 def test_projection_matches_oracle(n, k, t):
     say(f"[case] onebit projection n={n} k={k} t={t}")
     d, w, x, gv, hv, packed, y = _layer(n, k, t, n + 3 * k + t)
